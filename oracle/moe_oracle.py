@@ -1,0 +1,541 @@
+"""CPU oracle of the single-GPU MoE routed-expert layer (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import, call or execute this file.
+It shares no code with the HIP library and imports nothing from it.
+
+Sources (page title, then section):
+
+* "M6.6 - MoE Runtime Systems: Placement, Dispatch, Kernels, and Topology"
+  (cited as *M6.6*): §0x03A router-side tensors, §0x03B count / prefix /
+  stable permute, §0x03C3 inverse composition and weighted scatter-add
+  combine, §0x04A SwiGLU expert and its FLOP count, §0x04B-§0x04F row
+  ledgers, §0x0AE dtype roles, §0x0CD route and combine assertions.
+* "M6.2 - Expert Parallelism and DeepSeek MoE" (cited as *M6.2*): §0x01C
+  capacity, §0x03B count / prefix / permute, §0x03C forward transpose,
+  §0x03G executable logical transpose and its rejection list, §0x04D the two
+  layouts (token-major repeat vs expert-major sort), §0x06L1 family table
+  (Mixtral row: FP32 softmax, top-k, renormalise to one).
+* "Fixed pooled-wave all-to-all for the 8-of-384 MoE" (cited as *pooled
+  wave*): §02 pools and stripe rule, §03 one wave, §04 capacities, §05 drop
+  metrics, §07 fixed source order on the receiver.
+* "Dispatch and combine: preserve token identity across expert ranks"
+  (cited as *dispatch and combine*): keep the inverse map; bijection.
+
+Every floating-point value is computed in float64 from the exact stored
+input values (fp32 and bf16 upcast without rounding).  Integer results are
+unique given the readings below, so they are compared bit-exactly.
+
+Readings where the pages leave a step open (each is also listed in the design
+notes):
+
+* Selection is done on the fp32 logits (softmax is monotone); equal values
+  (-0.0 == +0.0) rank the lower expert index first.
+* A token with any non-finite logit is invalid: all of its slots get expert
+  id -1 and weight 0 (id -1 is the "no route" sentinel downstream).
+* Inside a segment routes keep route order ``r = t*k + j``; a capacity keeps
+  the first ``C`` routes of an expert in that order and drops the rest.
+* A dropped route contributes nothing; the gates are never renormalised
+  after a drop.
+* Pooled-wave stripe: a route's ordinal among this sender's routes to the
+  same destination is its destination rank; ``wave = rank mod n_waves``,
+  ``pool row = rank div n_waves``.  Expert ``e`` lives on destination
+  ``e div experts_per_dest`` as local expert ``e mod experts_per_dest``.
+* Header row: row 0 of each pool; element ``i`` is the 16-bit local expert id
+  of data row ``i`` (pool row ``1 + i``) or 0xFFFF when that row is empty;
+  elements past ``pool_rows`` are 0xFFFF.  Empty data rows are zero.  (This
+  bit format is not printed on the pages: parity unpinned by them.)
+* Receiver order is (source pool, row) ascending; a local expert keeps its
+  first ``cap`` arrivals.  Rows the receiver drops return as zero rows.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "HEADER_EMPTY", "bf16_to_f64", "to_f64",
+    "route_topk", "DispatchPlan", "dispatch_plan", "check_dispatch",
+    "gather_rows", "silu", "swiglu_expert", "swiglu_bank", "scalar_bank", "run_segments",
+    "combine", "moe_layer_token_major", "moe_layer_expert_major",
+    "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
+    "capacity_ceil", "drop_rates", "swiglu_flops", "padded_exec_rows",
+    "block_exec_rows",
+]
+
+HEADER_EMPTY = 0xFFFF
+
+
+# ----------------------------------------------------------------------------
+# exact upcasts
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the pattern is the top half of an
+    IEEE binary32 word, so shifting it up and reinterpreting is exact."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """fp32 arrays and bf16 bit arrays (uint16) to exact float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# a1: router top-k with softmax-renormalised gates
+# ----------------------------------------------------------------------------
+
+def route_topk(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Softmax over all experts, keep the top ``k``, renormalise the kept mass.
+
+    M6.2 §0x06L1 (Mixtral row): FP32 softmax over all experts, top-2,
+    selected probabilities renormalised to one.  M6.6 §0x0AE: logits and
+    the top-k comparison are FP32.  M6.6 §0x03A: the router emits
+    ``topk_ids [T,k]`` and ``topk_weights [T,k]``.
+
+    Returns ``(ids int32 [T,k], gates float64 [T,k], invalid bool [T])``.
+    """
+    z = np.asarray(logits, dtype=np.float32)
+    T, E = z.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    invalid = ~np.isfinite(z).all(axis=1)
+    zc = (z + np.float32(0.0)).astype(np.float64)   # -0.0 becomes +0.0
+    expert = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: last key is primary.  Descending logit, then ascending expert.
+    order = np.lexsort((expert, -zc), axis=-1)
+    ids = order[:, :k].astype(np.int32)
+
+    # softmax over all E experts in float64, then select and renormalise
+    zz = np.where(invalid[:, None], 0.0, zc)
+    m = zz.max(axis=1, keepdims=True)
+    p = np.exp(zz - m)
+    p /= p.sum(axis=1, keepdims=True)
+    psel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    gates = psel / psel.sum(axis=1, keepdims=True)
+
+    ids[invalid] = -1
+    gates[invalid] = 0.0
+    return ids, gates, invalid
+
+
+# ----------------------------------------------------------------------------
+# a2: count, exclusive prefix, stable permutation, capacity, inverse
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DispatchPlan:
+    sel: np.ndarray       # [B] routes that selected each bucket (before capacity)
+    counts: np.ndarray    # [B] accepted routes per bucket
+    offsets: np.ndarray   # [B+1] exclusive prefix of counts, offsets[B] = accepted
+    pos: np.ndarray       # [R] rank of the route inside its bucket (route order), -1 if no bucket
+    inv: np.ndarray       # [R] packed position of the route, -1 if dropped
+    src: np.ndarray       # [R] route at each packed position, -1 past the accepted total
+    accepted: int
+    dropped: int
+    bad: np.ndarray       # [R] bucket id outside [-1, B)
+
+
+def _exclusive_prefix(c: np.ndarray) -> np.ndarray:
+    o = np.zeros(c.size + 1, dtype=np.int64)
+    np.cumsum(c, out=o[1:])
+    return o
+
+
+def dispatch_plan(bucket: np.ndarray, n_buckets: int, capacity: int = -1) -> DispatchPlan:
+    """Group routes by bucket with a stable order and keep the inverse map.
+
+    M6.2 §0x03B: ``c_e`` counts routes of expert ``e``; ``o`` is the exclusive
+    prefix with ``o_{E} = R``; ``pi`` is the stable argsort of route ids by
+    ``(expert, route_id)``; ``inverse_pi[pi[j]] = j``.  M6.2 §0x01C: a
+    capacity ``C`` bounds each expert's buffer and the overflow is dropped
+    (first ``C`` routes in route order are kept).  M6.6 §0x0CD: accepted plus
+    dropped equals ``T*k`` and the counts sum to the accepted total.
+
+    ``bucket`` lists one bucket id per route in route order; -1 means "no
+    route" (dropped, not an error); ids below -1 or at least ``n_buckets``
+    are bad (dropped and reported in ``bad``).
+    """
+    b = np.asarray(bucket).reshape(-1).astype(np.int64)
+    R = b.size
+    valid = (b >= 0) & (b < n_buckets)
+    bad = (b < -1) | (b >= n_buckets)
+    route_id = np.arange(R, dtype=np.int64)
+
+    sel = np.bincount(b[valid], minlength=n_buckets).astype(np.int64)
+    sel_off = _exclusive_prefix(sel)
+    # stable argsort by (bucket, route id); routes without a bucket sort last
+    key = np.where(valid, b, n_buckets)
+    order = np.argsort(key, kind="stable")
+    n_valid = int(valid.sum())
+    pos = np.full(R, -1, dtype=np.int64)
+    first = order[:n_valid]
+    pos[first] = np.arange(n_valid) - sel_off[b[first]]
+
+    keep = valid if capacity < 0 else valid & (pos < capacity)
+    counts = np.bincount(b[keep], minlength=n_buckets).astype(np.int64)
+    offsets = _exclusive_prefix(counts)
+    inv = np.full(R, -1, dtype=np.int64)
+    inv[keep] = offsets[b[keep]] + pos[keep]
+    src = np.full(R, -1, dtype=np.int64)
+    src[inv[keep]] = route_id[keep]
+    accepted = int(keep.sum())
+    return DispatchPlan(sel=sel, counts=counts, offsets=offsets, pos=pos, inv=inv,
+                        src=src, accepted=accepted, dropped=R - accepted, bad=bad)
+
+
+def check_dispatch(bucket: np.ndarray, plan: DispatchPlan, gates: Optional[np.ndarray] = None,
+                   capacity: int = -1) -> None:
+    """Reject an inconsistent dispatch plan (raises ``ValueError``).
+
+    M6.2 §0x03G rejection list: non-bijective permutation, count/offset
+    mismatch, duplicate route identity, nonfinite gate.  M6.6 §0x0CD:
+    accepted + dropped = expected routes; counts sum to accepted.
+    "Dispatch and combine": the inverse must be a real bijection over its
+    entries.
+    """
+    b = np.asarray(bucket).reshape(-1).astype(np.int64)
+    R = b.size
+    B = plan.counts.size
+    A = plan.accepted
+    if plan.accepted + plan.dropped != R:
+        raise ValueError("accepted + dropped != routes")
+    if int(plan.counts.sum()) != A or int(plan.offsets[-1]) != A:
+        raise ValueError("counts/offsets do not sum to the accepted total")
+    if plan.offsets[0] != 0 or np.any(np.diff(plan.offsets) != plan.counts):
+        raise ValueError("offsets are not the exclusive prefix of counts")
+    if capacity >= 0 and np.any(plan.counts > capacity):
+        raise ValueError("a bucket exceeds its capacity")
+    if np.any(plan.counts > plan.sel):
+        raise ValueError("more accepted than selected routes")
+    head = plan.src[:A]
+    if np.any(head < 0) or np.any(head >= R) or np.any(plan.src[A:] != -1):
+        raise ValueError("src has holes or stray entries")
+    if np.unique(head).size != A:
+        raise ValueError("duplicate route identity in src")
+    if np.any(plan.inv[head] != np.arange(A)):
+        raise ValueError("inv is not the inverse of src")
+    if int((plan.inv >= 0).sum()) != A:
+        raise ValueError("inv marks a different number of routes")
+    for e in range(B):
+        seg = head[plan.offsets[e]:plan.offsets[e + 1]]
+        if np.any(b[seg] != e):
+            raise ValueError("a route sits in another bucket's segment")
+        if np.any(np.diff(seg) <= 0):
+            raise ValueError("segment is not in route order")
+    if gates is not None:
+        g = np.asarray(gates, dtype=np.float64).reshape(-1)
+        if not np.all(np.isfinite(g[head])):
+            raise ValueError("nonfinite gate on an accepted route")
+
+
+def gather_rows(x: np.ndarray, src: np.ndarray, k: int, accepted: int) -> np.ndarray:
+    """Packed rows ``X_perm[p] = X[src[p] div k]`` for ``p < accepted``
+    (M6.6 §0x03A: route rows are gathered from hidden states)."""
+    return np.asarray(x)[np.asarray(src[:accepted]) // k]
+
+
+# ----------------------------------------------------------------------------
+# a4/a5: SwiGLU expert over ragged segments
+# ----------------------------------------------------------------------------
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v))."""
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_expert(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """M6.6 §0x04A: ``E(X) = (SiLU(X W_g^T) (.) X W_u^T) W_2^T``, bias-free
+    (M6.2 §0x04C1 writes the same bias-free form per expert)."""
+    g = x @ wg.T
+    u = x @ wu.T
+    return (silu(g) * u) @ wd.T
+
+
+ExpertFn = Callable[[int, np.ndarray], np.ndarray]
+"""An expert bank: ``f(e, rows_f64) -> outputs_f64`` for expert ``e``."""
+
+
+def swiglu_bank(weights: Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]) -> ExpertFn:
+    """Expert bank of bias-free SwiGLU experts; ``weights(e)`` returns the
+    stored ``(W_g [d_ff,d], W_u [d_ff,d], W_d [d,d_ff])`` (fp32 or bf16 bits)."""
+    def run(e: int, x: np.ndarray) -> np.ndarray:
+        wg, wu, wd = (to_f64(w) for w in weights(e))
+        return swiglu_expert(x, wg, wu, wd)
+    return run
+
+
+def scalar_bank(scales) -> ExpertFn:
+    """Teaching experts ``E_e(x) = s_e x`` (M6.6 §0x04A; M6.2 §0x03C)."""
+    s = [float(v) for v in scales]
+    return lambda e, x: s[e] * x
+
+
+def run_segments(rows: np.ndarray, seg_start: np.ndarray, seg_count: np.ndarray,
+                 expert: ExpertFn, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Run expert ``e`` on ``rows[seg_start[e] : seg_start[e]+seg_count[e]]``.
+
+    M6.6 §0x04C: one problem per non-empty segment, with the segment's own
+    expert (zero-row experts are skipped without shifting the binding of
+    later segments).  Rows outside every segment stay zero in a fresh output.
+    """
+    x = to_f64(rows)
+    for e in range(len(seg_count)):
+        n = int(seg_count[e])
+        if n == 0:
+            continue
+        s = int(seg_start[e])
+        z = expert(e, x[s:s + n])
+        if out is None:
+            out = np.zeros((x.shape[0], z.shape[1]), dtype=np.float64)
+        out[s:s + n] = z
+    if out is None:
+        out = np.zeros_like(x)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a6: un-permute and gate-weighted combine
+# ----------------------------------------------------------------------------
+
+def combine(z_rows: np.ndarray, idx: np.ndarray, gates: Optional[np.ndarray], T: int, k: int,
+            lo: int = 0, hi: Optional[int] = None, y: Optional[np.ndarray] = None) -> np.ndarray:
+    """Weighted scatter-add back to token rows over the semantic key.
+
+    M6.6 §0x03C3: ``y_t = sum_{r: origin(r)=t} g_r z_r``, with ``z_r`` read
+    through the inverse map; M6.6 §0x0CD: gather by the inverse permutation,
+    multiply by the route's gate, scatter-add by origin token.  Route
+    ``r = t*k + j`` reads row ``idx[r] - lo`` of ``z_rows`` when
+    ``lo <= idx[r] < hi``; other routes (dropped, -1, or outside the window)
+    add nothing.  Slots are added in ascending ``j``.  ``gates`` None means
+    weight 1.  ``y`` (float64) is accumulated into when given.
+    """
+    z = to_f64(z_rows)
+    if hi is None:
+        hi = lo + z.shape[0]
+    idx = np.asarray(idx, dtype=np.int64).reshape(T, k)
+    g = np.ones((T, k)) if gates is None else np.asarray(gates, dtype=np.float64).reshape(T, k)
+    if y is None:
+        y = np.zeros((T, z.shape[1]), dtype=np.float64)
+    for j in range(k):
+        i = idx[:, j]
+        live = (i >= lo) & (i < hi)
+        t = np.nonzero(live)[0]
+        y[t] += g[t, j, None] * z[i[t] - lo]
+    return y
+
+
+def moe_layer_token_major(x: np.ndarray, ids: np.ndarray, gates: np.ndarray,
+                          expert: ExpertFn, E: int,
+                          keep: Optional[np.ndarray] = None) -> np.ndarray:
+    """The semantic definition, evaluated token-major.
+
+    M6.6 §0x0AE: ``y_t = sum_j g_{t,j} E_{e_{t,j}}(h_t)``.  Layout as in the
+    DeepSeekMoE training branch (M6.2 §0x04D): repeat every token ``k`` times,
+    run each expert on its masked rows, reshape to ``[T,k,d]`` and take the
+    gate-weighted sum.  ``keep`` (bool ``[T,k]``) removes dropped routes.
+    """
+    xf = to_f64(x)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    live = flat >= 0 if keep is None else (flat >= 0) & keep.reshape(-1)
+    routed_x = np.repeat(xf, k, axis=0)
+    routed_y = None
+    for e in range(E):
+        mask = live & (flat == e)
+        if not mask.any():
+            continue
+        z = expert(e, routed_x[mask])
+        if routed_y is None:
+            routed_y = np.zeros((T * k, z.shape[1]))
+        routed_y[mask] = z
+    if routed_y is None:
+        return np.zeros_like(xf)
+    g = np.where(live.reshape(T, k), np.asarray(gates, dtype=np.float64), 0.0)
+    return (routed_y.reshape(T, k, -1) * g[..., None]).sum(axis=1)
+
+
+def moe_layer_expert_major(x: np.ndarray, ids: np.ndarray, gates: np.ndarray,
+                           expert: ExpertFn, E: int, capacity: int = -1):
+    """The same layer evaluated expert-major (M6.2 §0x03G): count, prefix,
+    stable permutation, gather, run each segment, gather back through the
+    inverse, weighted scatter-add.  Returns ``(y, plan)``."""
+    T, k = ids.shape
+    plan = dispatch_plan(ids, E, capacity)
+    xp = gather_rows(x, plan.src, k, plan.accepted)
+    z = run_segments(xp, plan.offsets[:-1], plan.counts, expert)
+    y = combine(z, plan.inv, gates, T, k)
+    return y, plan
+
+
+# ----------------------------------------------------------------------------
+# a7: pooled-wave sender pack
+# ----------------------------------------------------------------------------
+
+def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest: int,
+              n_waves: int, pool_rows: int, *, with_pools: bool = True):
+    """Pack one sender's routes into fixed destination pools.
+
+    Pooled wave §02: expert id gives a destination and a local expert id;
+    "wave = rank mod 3, pool row = rank / 3" with rank read as the route's
+    ordinal among this sender's routes to that destination; each
+    destination gets ``pool_rows`` rows per wave and extra rows are dropped;
+    the first full-width row of a pool carries the packed local expert ids.
+    §03: pool shape ``[n_dest, pool_rows + 1, d]`` per wave.
+
+    Returns a dict with ``pools`` (uint16 ``[n_waves, n_dest, pool_rows+1, d]``,
+    or None when ``with_pools`` is False), ``route_loc`` (int64 ``[T*k]``:
+    flat pool row ``(w*n_dest + dest)*(pool_rows+1) + 1 + row`` or -1),
+    ``dest_counts`` (routes per destination before the cap),
+    ``sender_dropped`` (routes not placed, including "no route" ids) and the
+    per-route ``wave``/``row``/``dest``/``local``.
+    """
+    T, k = ids.shape
+    e = np.asarray(ids, dtype=np.int64).reshape(-1)
+    n_exp = n_dest * experts_per_dest
+    valid = (e >= 0) & (e < n_exp)
+    dest = np.where(valid, e // experts_per_dest, -1)
+    local = np.where(valid, e % experts_per_dest, -1)
+    plan = dispatch_plan(dest, n_dest)
+    rank = plan.pos
+    wave = np.where(valid, rank % n_waves, -1)
+    row = np.where(valid, rank // n_waves, -1)
+    acc = valid & (row < pool_rows)
+    P1 = pool_rows + 1
+    route_loc = np.where(acc, (wave * n_dest + dest) * P1 + 1 + row, -1)
+    pools = None
+    if with_pools:
+        x = np.asarray(x_bits, dtype=np.uint16)
+        d = x.shape[1]
+        if pool_rows > d:
+            raise ValueError("one header row holds at most d ids")
+        pools = np.zeros((n_waves, n_dest, P1, d), dtype=np.uint16)
+        pools[:, :, 0, :] = HEADER_EMPTY
+        r = np.nonzero(acc)[0]
+        pools[wave[r], dest[r], 1 + row[r]] = x[r // k]
+        pools[wave[r], dest[r], 0, row[r]] = local[r].astype(np.uint16)
+    return dict(pools=pools, route_loc=route_loc, dest_counts=plan.sel,
+                sender_dropped=int(e.size - acc.sum()), wave=wave, row=row,
+                dest=dest, local=local, accepted=acc, bad=plan.bad)
+
+
+# ----------------------------------------------------------------------------
+# a8: receiver compaction into static per-expert arrays
+# ----------------------------------------------------------------------------
+
+def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool = True):
+    """Group one wave's incoming rows into ``[n_local, cap, d]`` arrays.
+
+    Pooled wave §02/§03: the receiver reads each row's local expert id from
+    the header row and groups rows into six static expert arrays, dropping
+    rows above the receiver capacity; §07: rows keep a fixed source order
+    (source pool, then row) and overflow does not look at router scores.
+
+    Returns a dict with ``compact`` (uint16 ``[n_local, cap, d]``, rows past
+    ``counts[h]`` zero; None when ``with_rows`` is False), ``counts``,
+    ``arrived``, ``row_slot`` (int64 ``[n_src*(pool_rows+1)]``: ``h*cap + q``
+    or -1; header rows -1), ``recv_dropped`` and ``bad_header`` (count of
+    header ids that are neither a local id nor 0xFFFF).
+    """
+    pools = np.asarray(pools, dtype=np.uint16)
+    S, P1, d = pools.shape
+    P = P1 - 1
+    h = pools[:, 0, :P].astype(np.int64).reshape(-1)        # (s, i) order
+    valid = h < n_local
+    bad = (h != HEADER_EMPTY) & ~valid
+    plan = dispatch_plan(np.where(valid, h, -1), n_local, capacity=cap)
+    q = plan.pos
+    acc = plan.inv >= 0
+    s_idx, i_idx = np.divmod(np.arange(S * P), P)
+    row_slot = np.full(S * P1, -1, dtype=np.int64)
+    row_slot[s_idx * P1 + 1 + i_idx] = np.where(acc, h * cap + q, -1)
+    compact = None
+    if with_rows:
+        compact = np.zeros((n_local, cap, d), dtype=np.uint16)
+        r = np.nonzero(acc)[0]
+        compact[h[r], q[r]] = pools[s_idx[r], 1 + i_idx[r]]
+    return dict(compact=compact, counts=plan.counts, arrived=plan.sel, row_slot=row_slot,
+                recv_dropped=int(plan.sel.sum() - plan.counts.sum()),
+                bad_header=int(bad.sum()))
+
+
+def expand_rows(z_static: np.ndarray, row_slot: np.ndarray) -> np.ndarray:
+    """Return buffer in pool-row order: ``ret[i] = z[row_slot[i]]`` or zeros
+    (header, empty and receiver-dropped rows; M6.6 §0x04B: padding never
+    reaches combine).  Same as :func:`combine` with one slot and unit
+    weights."""
+    n = row_slot.size
+    return combine(z_static, row_slot, None, n, 1)
+
+
+def loopback_layer(x_bits: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert: ExpertFn,
+                   experts_per_dest: int, n_dest: int, n_waves: int, pool_rows: int,
+                   recv_cap: int):
+    """One sender's pools fed back as one receiver's incoming pools.
+
+    A single-GPU stand-in for the fixed exchange: the sender's wave-``w``
+    pools (one per destination) are read as the ``n_dest`` source pools of a
+    receiver whose ``experts_per_dest`` local experts serve every local id.
+    Pooled wave §03: per wave, compaction, one batched SwiGLU over the local
+    experts, expansion back to pool rows, and the waves add into one FP32
+    accumulator through the sender's route locations.  The result equals the
+    layer in which expert ``e`` uses local expert ``e mod experts_per_dest``'s
+    weights and routes dropped by the sender or the receiver add nothing.
+    Returns ``(y [T,d] float64, details)``.
+    """
+    T, k = ids.shape
+    pk = pool_pack(x_bits, ids, experts_per_dest, n_dest, n_waves, pool_rows)
+    P1 = pool_rows + 1
+    d = np.asarray(x_bits).shape[1]
+    y = np.zeros((T, d))
+    waves = []
+    for w in range(n_waves):
+        rc = recv_compact(pk["pools"][w], experts_per_dest, recv_cap)
+        starts = np.arange(experts_per_dest) * recv_cap
+        z = run_segments(rc["compact"].reshape(-1, d), starts, rc["counts"], expert)
+        ret = expand_rows(z, rc["row_slot"])
+        lo = w * n_dest * P1
+        combine(ret, pk["route_loc"], gates, T, k, lo=lo, hi=lo + n_dest * P1, y=y)
+        waves.append(rc)
+    return y, dict(pack=pk, waves=waves)
+
+
+# ----------------------------------------------------------------------------
+# ledgers and capacities
+# ----------------------------------------------------------------------------
+
+def capacity_ceil(factor_num: int, factor_den: int, assignments: int, parts: int) -> int:
+    """``ceil(c_f * assignments / parts)`` with ``c_f = factor_num/factor_den``
+    in exact integer arithmetic (M6.2 §0x01C; pooled wave §04)."""
+    num = factor_num * assignments
+    den = factor_den * parts
+    return -(-num // den)
+
+
+def drop_rates(assignments: int, sender_dropped: int, recv_dropped: int):
+    """Pooled wave §05: additive rates ``S/T`` and ``R/T`` and the
+    conditional receiver rate ``R/(T-S)``."""
+    T, S, R = float(assignments), float(sender_dropped), float(recv_dropped)
+    return S / T, R / T, (R / (T - S) if T > S else 0.0)
+
+
+def swiglu_flops(rows: int, d: int, d_ff: int) -> int:
+    """M6.6 §0x04A: three matmuls, ``2 n d d_ff`` each, ``6 n d d_ff`` total."""
+    return 6 * rows * d * d_ff
+
+
+def padded_exec_rows(n_slots: int, capacity: int, align: int) -> int:
+    """M6.6 §0x04B: ``C_exec = a * ceil(C / a)`` rows for each physical slot."""
+    return n_slots * align * (-(-capacity // align))
+
+
+def block_exec_rows(counts, block_rows: int) -> int:
+    """M6.6 §0x04D: every expert rounded up to whole row blocks."""
+    return int(sum(block_rows * (-(-int(n) // block_rows)) for n in counts))
