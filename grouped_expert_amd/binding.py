@@ -1,0 +1,233 @@
+"""Thin ctypes binding of ``libgrouped_expert_amd.so``.
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream.
+The functions keep the C names without the ``moe_`` prefix, allocate their
+outputs (and the workspaces the library asks for) as torch tensors on the
+input's device, and raise :class:`MoEError` on a negative status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgrouped_expert_amd.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATING_SOFTMAX_TOPK_RENORM = 0
+FLAG_BAD_EXPERT, FLAG_NONFINITE_LOGIT, FLAG_BAD_HEADER, FLAG_BAD_INDEX, FLAG_BAD_SEGMENT = 1, 2, 4, 8, 16
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+_i32, _i64, _sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "moe_strerror": (ctypes.c_char_p, [_i32]),
+    "moe_version": (ctypes.c_int, []),
+    "moe_route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "moe_permute_workspace": (_sz, [_i64, _i32, _i32]),
+    "moe_permute": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p, _p,
+                                   _p, _sz, _p, _p]),
+    "moe_grouped_swiglu_workspace": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_grouped_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _i32, _p,
+                                          _sz, _p, _p]),
+    "moe_unpermute_combine": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p]),
+    "moe_pool_pack_workspace": (_sz, [_i64, _i32, _i32]),
+    "moe_pool_pack": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
+                                     _p, _p, _sz, _p, _p]),
+    "moe_recv_compact_workspace": (_sz, [_i32, _i32, _i32]),
+    "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+}
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions declared in ``include/moe.h``."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with grouped_expert_amd.build.build() "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = load_library()
+
+
+def strerror(status: int) -> str:
+    return lib.moe_strerror(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoEError(fn, status, strerror(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def new_flags(device) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+# ---------------------------------------------------------------------------
+
+def route_topk(logits: torch.Tensor, k: int, gating: int = MOE_GATING_SOFTMAX_TOPK_RENORM,
+               flags: Optional[torch.Tensor] = None):
+    """Returns ``(topk_ids int32 [T,k], topk_w fp32 [T,k])``."""
+    _need_gpu(logits, flags)
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, gating, _ptr(ids), _ptr(w), _ptr(flags),
+                                                _stream(logits.device)))
+    return ids, w
+
+
+def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity: int = -1,
+            materialize: bool = True, flags: Optional[torch.Tensor] = None):
+    """``topk_ids`` is ``[T, k]``.  Returns a dict with x_perm (None when not
+    materialised), src, inv, sel, counts, offsets, dropped."""
+    _need_gpu(x, topk_ids, flags)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    R = T * k
+    xp = None
+    if materialize:
+        d = x.shape[1]
+        xp = torch.empty((R, d), dtype=x.dtype, device=dev)
+    src = torch.empty(R, dtype=torch.int32, device=dev)
+    inv = torch.empty(R, dtype=torch.int32, device=dev)
+    sel = torch.empty(E, dtype=torch.int32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    nbytes = lib.moe_permute_workspace(T, k, E)
+    ws = _ws(nbytes, dev)
+    dt = _dtype_code(x) if x is not None else MOE_BF16
+    _check("moe_permute", lib.moe_permute(_ptr(x), dt, T, 0 if x is None else x.shape[1], _ptr(topk_ids), k, E,
+                                          capacity, _ptr(xp), _ptr(src), _ptr(inv), _ptr(sel), _ptr(counts),
+                                          _ptr(offsets), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags),
+                                          _stream(dev)))
+    return dict(x_perm=xp, src=src, inv=inv, sel=sel, counts=counts, offsets=offsets, dropped=dropped)
+
+
+def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor, w_gate: torch.Tensor,
+                   w_up: torch.Tensor, w_down: torch.Tensor, z_dtype=torch.float32,
+                   z: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None):
+    """Runs expert ``e`` on rows ``[seg_start[e], seg_start[e]+seg_count[e])``
+    of ``x``; returns ``z`` (rows outside every segment are left as allocated)."""
+    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags)
+    rows, d = x.shape
+    E, d_ff, _ = w_gate.shape
+    dev = x.device
+    if z is None:
+        z = torch.empty((rows, d), dtype=z_dtype, device=dev)
+    dt = _dtype_code(x)
+    ws = _ws(lib.moe_grouped_swiglu_workspace(rows, E, d_ff, dt), dev)
+    _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
+        _ptr(x), dt, d, d_ff, E, _ptr(seg_start), _ptr(seg_count), rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(z), _dtype_code(z), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+    return z
+
+
+def unpermute_combine(z: torch.Tensor, idx: torch.Tensor, gates: Optional[torch.Tensor], T: int, k: int,
+                      lo: int = 0, hi: Optional[int] = None, y: Optional[torch.Tensor] = None,
+                      accumulate: bool = False, flags: Optional[torch.Tensor] = None):
+    """``y[t] (+)= sum_j g[t,j] z[idx[t,j] - lo]`` over routes inside ``[lo, hi)``."""
+    _need_gpu(z, idx, gates, y, flags)
+    d = z.shape[-1]
+    if hi is None:
+        hi = lo + z.shape[0]
+    dev = idx.device
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        accumulate = False
+    _check("moe_unpermute_combine", lib.moe_unpermute_combine(
+        _ptr(z), _dtype_code(z), d, _ptr(idx), lo, hi, _ptr(gates), T, k, _ptr(y), int(accumulate), _ptr(flags),
+        _stream(dev)))
+    return y
+
+
+def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest: int, n_dest: int, n_waves: int,
+              pool_rows: int, wave: int = -1, pools: Optional[torch.Tensor] = None,
+              flags: Optional[torch.Tensor] = None):
+    """Returns a dict with pools (bf16), route_loc, dest_counts, sender_dropped."""
+    _need_gpu(x, topk_ids, pools, flags)
+    T, d = x.shape
+    k = topk_ids.shape[-1]
+    dev = x.device
+    shape = (n_waves, n_dest, pool_rows + 1, d) if wave < 0 else (n_dest, pool_rows + 1, d)
+    if pools is None:
+        pools = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    route_loc = torch.empty(T * k, dtype=torch.int32, device=dev)
+    dest_counts = torch.empty(n_dest, dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _ws(lib.moe_pool_pack_workspace(T, k, n_dest), dev)
+    _check("moe_pool_pack", lib.moe_pool_pack(
+        _ptr(x), T, d, _ptr(topk_ids), k, E, experts_per_dest, n_dest, n_waves, pool_rows, wave, _ptr(pools),
+        _ptr(route_loc), _ptr(dest_counts), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+    return dict(pools=pools, route_loc=route_loc, dest_counts=dest_counts, sender_dropped=dropped)
+
+
+def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Optional[torch.Tensor] = None,
+                 flags: Optional[torch.Tensor] = None):
+    """Returns a dict with compact [n_local, cap, d], counts, arrived, row_slot, recv_dropped."""
+    _need_gpu(pools_in, compact, flags)
+    S, P1, d = pools_in.shape
+    dev = pools_in.device
+    if compact is None:
+        compact = torch.empty((n_local, cap, d), dtype=torch.bfloat16, device=dev)
+    counts = torch.empty(n_local, dtype=torch.int32, device=dev)
+    arrived = torch.empty(n_local, dtype=torch.int32, device=dev)
+    row_slot = torch.empty(S * P1, dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _ws(lib.moe_recv_compact_workspace(S, P1 - 1, n_local), dev)
+    _check("moe_recv_compact", lib.moe_recv_compact(
+        _ptr(pools_in), S, P1 - 1, d, n_local, cap, _ptr(compact), _ptr(counts), _ptr(arrived), _ptr(row_slot),
+        _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+    return dict(compact=compact, counts=counts, arrived=arrived, row_slot=row_slot, recv_dropped=dropped)

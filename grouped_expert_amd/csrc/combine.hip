@@ -1,0 +1,118 @@
+// Un-permute and gate-weighted FP32 combine.
+//
+// "M6.6 - MoE Runtime Systems", 0x03C3: the return path applies the inverse
+// permutation and the combine is a weighted scatter-add over the semantic key
+// (origin token); 0x0CD: gather by the inverse, multiply by the route's gate,
+// add into the token row; 0x0AE: gate and token accumulation in FP32.
+//
+// The scatter-add is turned into a gather: one workgroup owns one token row
+// slice, reads the k route rows through idx in ascending slot order and adds
+// them in registers, so every output element is written once, with no
+// atomics, in a fixed order (deterministic).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename ZT>
+struct Vec;
+
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* v) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+};
+
+template <>
+struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16_t* p, float* v) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <typename ZT>
+__global__ __launch_bounds__(256) void combine_kernel(const ZT* __restrict__ z, int32_t d,
+                                                      const int32_t* __restrict__ idx, int64_t lo, int64_t hi,
+                                                      const float* __restrict__ gates, int32_t k,
+                                                      float* __restrict__ y, int32_t accumulate, uint32_t* flags) {
+  constexpr int N = Vec<ZT>::N;
+  const int64_t t = blockIdx.x;
+  const int64_t col = (static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x) * N;
+  float acc[N];
+  float* yrow = y + t * d + col;
+  const bool live = col < d;
+  if (live && accumulate) {
+#pragma unroll
+    for (int q = 0; q < N; q += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(yrow + q);
+      acc[q] = a.x; acc[q + 1] = a.y; acc[q + 2] = a.z; acc[q + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int64_t r = t * k + j;
+    const int32_t i = idx[r];
+    if (i < -1) {
+      if (threadIdx.x == 0 && blockIdx.y == 0) flag_or(flags, MOE_FLAG_BAD_INDEX);
+      continue;
+    }
+    if (i < lo || i >= hi) continue;
+    const float g = gates ? gates[r] : 1.0f;
+    if (!live) continue;
+    float v[N];
+    Vec<ZT>::load(z + (i - lo) * d + col, v);
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+  }
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < N; q += 4)
+      *reinterpret_cast<float4*>(yrow + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+  }
+}
+
+template <typename ZT>
+void launch(const void* z, int32_t d, const int32_t* idx, int64_t lo, int64_t hi, const float* gates, int64_t T,
+            int32_t k, float* y, int32_t acc, uint32_t* flags, hipStream_t s) {
+  constexpr int N = Vec<ZT>::N;
+  const int64_t lanes = (d + N - 1) / N;
+  const int threads = static_cast<int>(lanes >= 256 ? 256 : ((lanes + 63) / 64) * 64);
+  const unsigned gy = static_cast<unsigned>((lanes + threads - 1) / threads);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(combine_kernel<ZT>), dim3(static_cast<unsigned>(T), gy), dim3(threads), 0, s,
+                     static_cast<const ZT*>(z), d, idx, lo, hi, gates, k, y, acc, flags);
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API int moe_unpermute_combine(const void* z, int32_t z_dtype, int32_t d, const int32_t* idx, int64_t lo,
+                                  int64_t hi, const float* gates, int64_t T, int32_t k, float* y,
+                                  int32_t accumulate, uint32_t* dev_flags, hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK(z_dtype == MOE_F32 || z_dtype == MOE_BF16, MOE_EINVAL);
+  MOE_CHECK(T >= 0 && k >= 1 && d >= 1 && lo >= 0 && hi >= lo, MOE_EINVAL);
+  MOE_CHECK(T <= INT32_MAX / k && T <= 0x7fffffffLL, MOE_EUNSUPPORTED);
+  MOE_CHECK(d % (z_dtype == MOE_F32 ? 4 : 8) == 0, MOE_EINVAL);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(idx && y && (z || hi == lo), MOE_EINVAL);
+  MOE_CHECK((z == nullptr || aligned16(z)) && aligned16(y) && aligned4(idx), MOE_EINVAL);
+  MOE_CHECK(gates == nullptr || aligned4(gates), MOE_EINVAL);
+  if (z_dtype == MOE_F32)
+    launch<float>(z, d, idx, lo, hi, gates, T, k, y, accumulate, dev_flags, stream);
+  else
+    launch<bf16_t>(z, d, idx, lo, hi, gates, T, k, y, accumulate, dev_flags, stream);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

@@ -1,0 +1,15 @@
+// Status strings and version of the C ABI.
+#include "common.h"
+
+MOE_API const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_version(void) { return 100; }

@@ -1,0 +1,106 @@
+// Dispatch permutation: expert histogram, exclusive prefix, capacity and
+// stable ranks (shared bucket-rank passes), then the row gather.
+//
+// "M6.2 - Expert Parallelism and DeepSeek MoE", 0x03B: counts, exclusive
+// prefix with the final sentinel, stable permutation by (expert, route id)
+// and its inverse; 0x01C: capacity turns routing into bounded buffers and the
+// overflow is dropped.  "M6.6 - MoE Runtime Systems", 0x03A: route rows are
+// gathered from the hidden states (one copy per route); 0x0CD: accepted plus
+// dropped routes equal T*k and the counts sum to the accepted total.
+#include "bucket_rank.h"
+
+namespace moe {
+namespace {
+
+struct ExpertBucket {
+  const int32_t* ids;
+  int32_t E;
+  __device__ int operator()(int64_t r, uint32_t* flags) const {
+    const int32_t e = ids[r];
+    if (e >= 0 && e < E) return e;
+    if (e != -1) flag_or(flags, MOE_FLAG_BAD_EXPERT);
+    return -1;
+  }
+};
+
+struct PermuteEmit {
+  int64_t cap, R;
+  const int32_t* offsets;
+  int32_t* inv;
+  int32_t* src;
+  __device__ void operator()(int64_t r, int e, int32_t pos) const {
+    if (e >= 0 && (cap < 0 || pos < cap)) {
+      const int32_t p = offsets[e] + pos;
+      inv[r] = p;
+      if (p >= 0 && p < R) src[p] = static_cast<int32_t>(r);
+    } else {
+      inv[r] = -1;
+    }
+  }
+};
+
+constexpr int kRowsPerBlock = 4;   // one wavefront per packed row
+
+// x_perm[p] = x[src[p] / k] for p < A; src[p] = -1 for A <= p < R.
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void gather_rows_kernel(
+    const vec16* __restrict__ x, int64_t row_vecs, int32_t k, int64_t R, const int32_t* __restrict__ accepted,
+    int32_t* __restrict__ src, vec16* __restrict__ x_perm) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (p >= R) return;
+  const int32_t A = *accepted;
+  if (p >= A) {
+    if (lane == 0) src[p] = -1;
+    return;
+  }
+  if (!x_perm) return;
+  const int32_t r = src[p];
+  if (r < 0 || r >= R) return;
+  const int64_t t = r / k;
+  const vec16* in = x + t * row_vecs;
+  vec16* out = x_perm + p * row_vecs;
+  for (int64_t c = lane; c < row_vecs; c += kWave) out[c] = in[c];
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API size_t moe_permute_workspace(int64_t T, int32_t k, int32_t E) {
+  using namespace moe;
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  return rank_table_bytes(rank_geom(T * k, E));
+}
+
+MOE_API int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d, const int32_t* topk_ids,
+                        int32_t k, int32_t E, int64_t capacity, void* x_perm, int32_t* src, int32_t* inv,
+                        int32_t* sel_counts, int32_t* counts, int32_t* offsets, int32_t* n_dropped, void* ws,
+                        size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL);
+  MOE_CHECK(T <= INT32_MAX / k, MOE_EUNSUPPORTED);
+  MOE_CHECK(capacity >= -1, MOE_EINVAL);
+  MOE_CHECK(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_EINVAL);
+  const int elt = x_dtype == MOE_F32 ? 4 : 2;
+  MOE_CHECK(counts && offsets && n_dropped, MOE_EINVAL);
+  MOE_CHECK(T == 0 || (topk_ids && src && inv), MOE_EINVAL);
+  if (x_perm) {
+    MOE_CHECK(x && d >= 1 && (static_cast<int64_t>(d) * elt) % 16 == 0, MOE_EINVAL);
+    MOE_CHECK(aligned16(x) && aligned16(x_perm), MOE_EINVAL);
+  }
+  const RankGeom g = rank_geom(T * k, E);
+  MOE_CHECK(ws && ws_bytes >= rank_table_bytes(g), MOE_EWORKSPACE);
+  const int64_t R = T * k;
+  int32_t* table = static_cast<int32_t*>(ws);
+  RankScanOut out{sel_counts, counts, offsets, n_dropped, 1};
+  int st = bucket_rank(g, ExpertBucket{topk_ids, E}, PermuteEmit{capacity, R, offsets, inv, src}, capacity, out,
+                       table, dev_flags, stream);
+  if (st != MOE_OK) return st;
+  if (R > 0) {
+    const int64_t row_vecs = x_perm ? static_cast<int64_t>(d) * elt / 16 : 0;
+    const unsigned blocks = static_cast<unsigned>((R + kRowsPerBlock - 1) / kRowsPerBlock);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
+                       static_cast<const vec16*>(x), row_vecs, k, R, offsets + E, src, static_cast<vec16*>(x_perm));
+    MOE_LAUNCH_CHECK();
+  }
+  return MOE_OK;
+}

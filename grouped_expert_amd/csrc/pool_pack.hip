@@ -1,0 +1,183 @@
+// Pooled-wave sender pack into fixed destination pools with a header row.
+//
+// "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02: the sender keeps
+// one pool per destination GPU and wave; an expert id gives a destination and
+// a local expert id; "wave = rank mod 3, pool row = rank / 3", where the rank
+// is read as the route's ordinal among this sender's routes to that
+// destination (the only reading that fits the pool shape [64, 3005, 3072]
+// per wave and the per-destination, per-wave capacity of 04); extra rows are
+// dropped; the first full-width row of a pool carries the packed local expert
+// ids so that no count exchange is needed.  03: every wave has the same
+// static shape.
+//
+// Launches: the shared bucket-rank passes with bucket = destination (pass 3
+// writes route_loc and the header id of every placed row), a token-major
+// scatter that reads each token row once and writes its placed copies, and a
+// fill of the unused rows (zero data, 0xFFFF header tail) so that the pools
+// are fully defined.
+#include "bucket_rank.h"
+
+namespace moe {
+namespace {
+
+struct DestBucket {
+  const int32_t* ids;
+  int32_t E, epd;
+  __device__ int operator()(int64_t r, uint32_t* flags) const {
+    const int32_t e = ids[r];
+    if (e >= 0 && e < E) return e / epd;
+    if (e != -1) flag_or(flags, MOE_FLAG_BAD_EXPERT);
+    return -1;
+  }
+};
+
+struct PackEmit {
+  const int32_t* ids;
+  int32_t epd, n_dest, n_waves, pool_rows, d, wave_sel;
+  int32_t* route_loc;
+  bf16_t* pools;
+  __device__ void operator()(int64_t r, int dest, int32_t o) const {
+    if (dest < 0) {
+      route_loc[r] = -1;
+      return;
+    }
+    const int32_t w = o % n_waves, row = o / n_waves;
+    if (row >= pool_rows) {
+      route_loc[r] = -1;
+      return;
+    }
+    const int64_t P1 = pool_rows + 1;
+    route_loc[r] = static_cast<int32_t>((static_cast<int64_t>(w) * n_dest + dest) * P1 + 1 + row);
+    if (wave_sel < 0 || wave_sel == w) {
+      const int64_t slab = wave_sel < 0 ? w : 0;
+      pools[((slab * n_dest + dest) * P1) * d + row] = static_cast<bf16_t>(ids[r] % epd);
+    }
+  }
+};
+
+// One wavefront per token: the row is read once into registers (in pieces of
+// up to 8 x 16 B per lane) and written to each of the token's placed slots.
+constexpr int kTokPerBlock = 4;
+constexpr int kPiece = 8;
+
+__global__ __launch_bounds__(kTokPerBlock * kWave) void pack_rows_kernel(
+    const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ route_loc,
+    int64_t slab_lo, int64_t slab_hi, vec16* __restrict__ pools) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  int32_t loc[MOE_MAX_TOPK];
+  int live = 0;
+  for (int j = 0; j < k; ++j) {
+    const int32_t l = route_loc[t * k + j];
+    if (l >= slab_lo && l < slab_hi) loc[live++] = static_cast<int32_t>(l - slab_lo);
+  }
+  if (live == 0) return;
+  const vec16* in = x + t * row_vecs;
+  for (int64_t c0 = 0; c0 < row_vecs; c0 += kPiece * kWave) {
+    vec16 v[kPiece];
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t c = c0 + u * kWave + lane;
+      if (c < row_vecs) v[u] = ld_stream(in + c);
+    }
+    for (int j = 0; j < live; ++j) {
+      vec16* out = pools + static_cast<int64_t>(loc[j]) * row_vecs;
+#pragma unroll
+      for (int u = 0; u < kPiece; ++u) {
+        const int64_t c = c0 + u * kWave + lane;
+        if (c < row_vecs) st_stream(v[u], out + c);
+      }
+    }
+  }
+}
+
+// Unused rows of each written pool: zero data rows past the wave's fill and
+// 0xFFFF header elements past it.  grid = (row blocks, pools).
+constexpr int kFillRows = 16;
+
+__global__ __launch_bounds__(256) void pack_fill_kernel(const int32_t* __restrict__ dest_counts, int32_t n_dest,
+                                                        int32_t n_waves, int32_t pool_rows, int32_t d,
+                                                        int32_t wave_sel, bf16_t* __restrict__ pools) {
+  const int64_t pool = blockIdx.y;                     // slab * n_dest + dest
+  const int32_t dest = static_cast<int32_t>(pool % n_dest);
+  const int32_t w = wave_sel < 0 ? static_cast<int32_t>(pool / n_dest) : wave_sel;
+  const int64_t cap_all = static_cast<int64_t>(n_waves) * pool_rows;
+  const int64_t n = dest_counts[dest];
+  const int64_t m = n < cap_all ? n : cap_all;
+  const int32_t filled = m > w ? static_cast<int32_t>((m - w + n_waves - 1) / n_waves) : 0;
+  const int64_t P1 = pool_rows + 1;
+  bf16_t* base = pools + pool * P1 * d;
+  if (blockIdx.x == 0) {
+    for (int32_t i = filled + threadIdx.x; i < d; i += blockDim.x) base[i] = 0xFFFF;
+  }
+  const int32_t r0 = blockIdx.x * kFillRows;
+  if (r0 + kFillRows <= filled) return;
+  const int64_t row_vecs = static_cast<int64_t>(d) / 8;
+  const vec16 zero = {0u, 0u, 0u, 0u};
+  for (int32_t rr = 0; rr < kFillRows; ++rr) {
+    const int32_t row = r0 + rr;
+    if (row < filled || row >= pool_rows) continue;
+    vec16* out = reinterpret_cast<vec16*>(base + (1 + static_cast<int64_t>(row)) * d);
+    for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) st_stream(zero, out + c);
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API size_t moe_pool_pack_workspace(int64_t T, int32_t k, int32_t n_dest) {
+  using namespace moe;
+  if (T < 0 || k < 1 || n_dest < 1 || n_dest > MOE_MAX_EXPERTS) return 0;
+  return rank_table_bytes(rank_geom(T * k, n_dest)) + align_up((n_dest + 1) * sizeof(int32_t), 256);
+}
+
+MOE_API int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k, int32_t E,
+                          int32_t experts_per_dest, int32_t n_dest, int32_t n_waves, int32_t pool_rows,
+                          int32_t wave, void* pools, int32_t* route_loc, int32_t* dest_counts,
+                          int32_t* sender_dropped, void* ws, size_t ws_bytes, uint32_t* dev_flags,
+                          hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && E >= 1, MOE_EINVAL);
+  MOE_CHECK(T <= INT32_MAX / k, MOE_EUNSUPPORTED);
+  MOE_CHECK(experts_per_dest >= 1 && experts_per_dest < 0xFFFF, MOE_EINVAL);
+  MOE_CHECK(n_dest >= 1 && n_dest <= MOE_MAX_EXPERTS && n_waves >= 1 && pool_rows >= 0, MOE_EINVAL);
+  MOE_CHECK(E <= static_cast<int64_t>(n_dest) * experts_per_dest, MOE_EINVAL);
+  MOE_CHECK(wave >= -1 && wave < n_waves, MOE_EINVAL);
+  MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
+  MOE_CHECK(pool_rows <= d, MOE_EUNSUPPORTED);           // one header row holds one id per element
+  const int64_t P1 = static_cast<int64_t>(pool_rows) + 1;
+  MOE_CHECK(static_cast<int64_t>(n_waves) * n_dest * P1 <= INT32_MAX, MOE_EUNSUPPORTED);
+  MOE_CHECK(pools && dest_counts && sender_dropped, MOE_EINVAL);
+  MOE_CHECK(T == 0 || (x_bf16 && topk_ids && route_loc), MOE_EINVAL);
+  MOE_CHECK(aligned16(pools) && (T == 0 || aligned16(x_bf16)), MOE_EINVAL);
+  const RankGeom g = rank_geom(T * k, n_dest);
+  const size_t tb = rank_table_bytes(g);
+  MOE_CHECK(ws && ws_bytes >= moe_pool_pack_workspace(T, k, n_dest), MOE_EWORKSPACE);
+  int32_t* table = static_cast<int32_t*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + tb);
+  const int64_t cap_all = static_cast<int64_t>(n_waves) * pool_rows;
+  RankScanOut out{dest_counts, nullptr, offsets, sender_dropped, 1};
+  bf16_t* pb = static_cast<bf16_t*>(pools);
+  int st = bucket_rank(g, DestBucket{topk_ids, E, experts_per_dest},
+                       PackEmit{topk_ids, experts_per_dest, n_dest, n_waves, pool_rows, d, wave, route_loc, pb},
+                       cap_all, out, table, dev_flags, stream);
+  if (st != MOE_OK) return st;
+  const int64_t row_vecs = d / 8;
+  if (T > 0) {
+    const int64_t slab_rows = static_cast<int64_t>(n_dest) * P1;
+    const int64_t lo = wave < 0 ? 0 : wave * slab_rows;
+    const int64_t hi = wave < 0 ? n_waves * slab_rows : lo + slab_rows;
+    const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
+    hipLaunchKernelGGL(pack_rows_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream,
+                       static_cast<const vec16*>(x_bf16), T, row_vecs, k, route_loc, lo, hi,
+                       static_cast<vec16*>(pools));
+    MOE_LAUNCH_CHECK();
+  }
+  const unsigned n_pools = static_cast<unsigned>((wave < 0 ? n_waves : 1) * n_dest);
+  const unsigned rb = static_cast<unsigned>((pool_rows + kFillRows - 1) / kFillRows);
+  hipLaunchKernelGGL(pack_fill_kernel, dim3(rb > 0 ? rb : 1, n_pools), dim3(256), 0, stream, dest_counts, n_dest,
+                     n_waves, pool_rows, d, wave, pb);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

@@ -1,0 +1,108 @@
+// Receiver compaction of one wave's incoming pools into static per-expert
+// arrays.
+//
+// "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02/03: the receiver
+// reads each row's local expert id from the header row of its pool and groups
+// the rows into static [n_local, cap, d] expert arrays, dropping rows above
+// the receiver capacity; 04: the capacity is per local expert per wave; 07:
+// rows keep a fixed source order and overflow does not look at router scores.
+// "M6.6 - MoE Runtime Systems", 0x03C2: this is the second, receive-side
+// stable permutation into local-expert order.
+//
+// Launches: the shared bucket-rank passes over rows in (source, row) order
+// with bucket = header id (pass 3 writes row_slot), then a row copy that
+// moves every accepted row to its slot and marks header rows -1.
+#include "bucket_rank.h"
+
+namespace moe {
+namespace {
+
+struct HeaderBucket {
+  const bf16_t* pools;
+  int64_t P, P1, d;
+  int32_t L;
+  __device__ int operator()(int64_t i, uint32_t* flags) const {
+    const int64_t s = i / P, r = i - s * P;
+    const uint32_t h = pools[s * P1 * d + r];
+    if (h < static_cast<uint32_t>(L)) return static_cast<int>(h);
+    if (h != 0xFFFFu) flag_or(flags, MOE_FLAG_BAD_HEADER);
+    return -1;
+  }
+};
+
+struct CompactEmit {
+  int64_t P, P1, cap;
+  int32_t* row_slot;
+  __device__ void operator()(int64_t i, int h, int32_t q) const {
+    const int64_t s = i / P, r = i - s * P;
+    const int32_t slot = (h >= 0 && q < cap) ? static_cast<int32_t>(h * cap + q) : -1;
+    row_slot[s * P1 + 1 + r] = slot;
+  }
+};
+
+constexpr int kRowsPerBlock = 4;   // one wavefront per incoming row
+
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_rows_kernel(
+    const vec16* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t row_vecs, int32_t* __restrict__ row_slot,
+    vec16* __restrict__ compact) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= n_rows) return;
+  if (row % P1 == 0) {
+    if (lane == 0) row_slot[row] = -1;
+    return;
+  }
+  const int32_t slot = row_slot[row];
+  if (slot < 0) return;
+  const vec16* in = pools + row * row_vecs;
+  vec16* out = compact + static_cast<int64_t>(slot) * row_vecs;
+  for (int64_t c = lane; c < row_vecs; c += kWave) st_stream(ld_stream(in + c), out + c);
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int32_t n_local) {
+  using namespace moe;
+  if (n_src < 0 || pool_rows < 0 || n_local < 1 || n_local > MOE_MAX_EXPERTS) return 0;
+  const int64_t n = static_cast<int64_t>(n_src) * pool_rows;
+  return rank_table_bytes(rank_geom(n, n_local)) + 2 * align_up((n_local + 1) * sizeof(int32_t), 256);
+}
+
+MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d, int32_t n_local,
+                             int32_t cap, void* compact, int32_t* counts, int32_t* arrived, int32_t* row_slot,
+                             int32_t* recv_dropped, void* ws, size_t ws_bytes, uint32_t* dev_flags,
+                             hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK(n_src >= 0 && pool_rows >= 0 && n_local >= 1 && n_local <= MOE_MAX_EXPERTS && cap >= 0, MOE_EINVAL);
+  MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
+  MOE_CHECK(pool_rows <= d, MOE_EUNSUPPORTED);
+  const int64_t P1 = static_cast<int64_t>(pool_rows) + 1;
+  const int64_t n_rows = static_cast<int64_t>(n_src) * P1;
+  MOE_CHECK(n_rows <= INT32_MAX && static_cast<int64_t>(n_local) * cap <= INT32_MAX, MOE_EUNSUPPORTED);
+  MOE_CHECK(counts && recv_dropped, MOE_EINVAL);
+  MOE_CHECK(n_src == 0 || (pools_in && row_slot), MOE_EINVAL);
+  MOE_CHECK(n_src == 0 || cap == 0 || compact, MOE_EINVAL);
+  MOE_CHECK((pools_in == nullptr || aligned16(pools_in)) && (compact == nullptr || aligned16(compact)), MOE_EINVAL);
+  const int64_t n = static_cast<int64_t>(n_src) * pool_rows;
+  const RankGeom g = rank_geom(n, n_local);
+  const size_t tb = rank_table_bytes(g);
+  MOE_CHECK(ws && ws_bytes >= moe_recv_compact_workspace(n_src, pool_rows, n_local), MOE_EWORKSPACE);
+  int32_t* table = static_cast<int32_t*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + tb);
+  int32_t* arrived_ws = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + tb +
+                                                   align_up((n_local + 1) * sizeof(int32_t), 256));
+  RankScanOut out{arrived ? arrived : arrived_ws, counts, offsets, recv_dropped, 0};
+  const bf16_t* pb = static_cast<const bf16_t*>(pools_in);
+  int st = bucket_rank(g, HeaderBucket{pb, pool_rows, P1, d, n_local}, CompactEmit{pool_rows, P1, cap, row_slot},
+                       cap, out, table, dev_flags, stream);
+  if (st != MOE_OK) return st;
+  if (n_rows > 0) {
+    const unsigned blocks = static_cast<unsigned>((n_rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    hipLaunchKernelGGL(compact_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
+                       static_cast<const vec16*>(pools_in), n_rows, P1, static_cast<int64_t>(d) / 8, row_slot,
+                       static_cast<vec16*>(compact));
+    MOE_LAUNCH_CHECK();
+  }
+  return MOE_OK;
+}

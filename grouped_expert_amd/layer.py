@@ -1,0 +1,56 @@
+"""The layer as a chain of library calls (marshalling only).
+
+``moe_layer`` is one pass of the routed-expert layer on a token batch:
+route -> permute -> grouped SwiGLU -> un-permute/combine, all on the current
+stream with no host synchronisation ("M6.6 - MoE Runtime Systems", 0x0CC
+forward blueprint, reduced to one GPU).  ``loopback_wave`` is one wave of
+the pooled-wave receiver path fed with a sender's pools ("Fixed pooled-wave
+all-to-all for the 8-of-384 MoE", 03): compaction -> batched SwiGLU over the
+static arrays -> expansion to pool rows -> sender combine into the FP32
+accumulator.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+def moe_layer(x: torch.Tensor, logits: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+              w_down: torch.Tensor, k: int, capacity: int = -1, z_dtype: Optional[torch.dtype] = None,
+              flags: Optional[torch.Tensor] = None):
+    """Returns ``(y fp32 [T, d], state)`` where state holds the intermediate
+    routing and dispatch tensors."""
+    E = w_gate.shape[0]
+    T = x.shape[0]
+    if z_dtype is None:
+        z_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
+    ids, gates = B.route_topk(logits, k, flags=flags)
+    plan = B.permute(x, ids, E, capacity, flags=flags)
+    z = B.grouped_swiglu(plan["x_perm"], plan["offsets"], plan["counts"], w_gate, w_up, w_down,
+                         z_dtype=z_dtype, flags=flags)
+    y = B.unpermute_combine(z, plan["inv"], gates, T, k, flags=flags)
+    return y, dict(ids=ids, gates=gates, plan=plan, z=z)
+
+
+def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: torch.Tensor, gates: torch.Tensor,
+                  T: int, k: int, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, cap: int,
+                  y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None):
+    """One wave of the receiver path; adds the wave's contributions into ``y``.
+
+    ``pools_w`` is ``[n_src, pool_rows + 1, d]`` (one wave's pools).  ``bufs``
+    may hold preallocated ``compact``/``z``/``ret`` tensors to reuse."""
+    S, P1, d = pools_w.shape
+    L = w_gate.shape[0]
+    bufs = {} if bufs is None else bufs
+    rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags)
+    starts = torch.arange(L, dtype=torch.int32, device=pools_w.device) * cap
+    z = B.grouped_swiglu(rc["compact"].view(L * cap, d), starts, rc["counts"], w_gate, w_up, w_down,
+                         z_dtype=torch.float32, z=bufs.get("z"), flags=flags)
+    ret = B.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, y=bufs.get("ret"), accumulate=False,
+                              flags=flags)
+    lo = wave * S * P1
+    B.unpermute_combine(ret, route_loc, gates, T, k, lo=lo, hi=lo + S * P1, y=y, accumulate=True, flags=flags)
+    return rc, z, ret

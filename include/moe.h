@@ -1,0 +1,260 @@
+/*
+ * grouped_expert_amd: single-GPU MoE routed-expert layer for AMD Instinct
+ * MI355X (gfx950).  C ABI.
+ *
+ * The layer (pages cited by title and section):
+ *   route    "M6.6 - MoE Runtime Systems", 0x03A router-side tensors;
+ *            "M6.2 - Expert Parallelism and DeepSeek MoE", 0x06L1 family
+ *            table, Mixtral row (FP32 softmax, top-k, renormalise to one).
+ *   permute  M6.2 0x03B count / exclusive prefix / stable permutation and
+ *            inverse; M6.2 0x01C capacity; M6.6 0x0CD route assertions.
+ *   experts  M6.6 0x04A bias-free SwiGLU expert; 0x04C variable grouped GEMM
+ *            over ragged expert segments.
+ *   combine  M6.6 0x03C3 inverse permutation and weighted scatter-add over
+ *            the semantic key; 0x0AE FP32 gate and FP32 token accumulation.
+ *   pack     "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02-04:
+ *            destination pools per wave, stripe rule, header row of local
+ *            expert ids, sender capacity.
+ *   compact  pooled wave 02-04 and 07: receiver groups rows into static
+ *            per-expert arrays in fixed source order, drops above capacity.
+ *
+ * Conventions for every call
+ *   - Pointers named as device buffers are device pointers (HBM).  Sizes and
+ *     flags are host values.  Index arrays are int32.  bf16 data is raw
+ *     16-bit storage (the upper half of the binary32 pattern), i.e. the
+ *     layout of torch.bfloat16.  All tensors are dense row-major.
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     workspaces sized by the *_workspace queries.  The library never
+ *     allocates or frees memory and keeps no pointer after a call returns
+ *     (apart from the kernels it has enqueued).  It holds no mutable global
+ *     state.
+ *   - Synchrony: a call only enqueues kernels on `stream` and returns; no
+ *     call synchronises with the host.  Counts, offsets and drop totals are
+ *     written to device memory.  Buffers may be read once the stream has
+ *     reached the call's work.
+ *   - Errors: argument violations the host can see (null pointer, bad size,
+ *     unsupported shape, misalignment, workspace too small) return a
+ *     negative moe_status before anything is enqueued, and nothing is
+ *     written.  A failed kernel launch returns MOE_EHIP.  Violations that
+ *     live in device data never abort: the offending route or row is treated
+ *     as dropped and a bit is OR-ed into *dev_flags (when dev_flags is not
+ *     NULL).  The library never clears dev_flags; the caller zeroes it.
+ *   - Device-pointer arguments must be 16-byte aligned unless stated.
+ */
+#ifndef GROUPED_EXPERT_AMD_MOE_H
+#define GROUPED_EXPERT_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument */
+  MOE_EUNSUPPORTED = -2,  /* valid but not supported by this build (shape / dtype) */
+  MOE_EWORKSPACE = -3,    /* workspace missing or smaller than the query returns */
+  MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gating families.  M6.2 0x06L1, Mixtral row: FP32 softmax over all experts,
+ * keep the top k, renormalise the kept probabilities to one. */
+typedef enum { MOE_GATING_SOFTMAX_TOPK_RENORM = 0 } moe_gating;
+
+/* Bits OR-ed into *dev_flags. */
+#define MOE_FLAG_BAD_EXPERT      1u  /* expert id < -1 or >= E (route dropped) */
+#define MOE_FLAG_NONFINITE_LOGIT 2u  /* token with a NaN/Inf logit (all slots id -1) */
+#define MOE_FLAG_BAD_HEADER      4u  /* header id neither < n_local nor 0xFFFF (row ignored) */
+#define MOE_FLAG_BAD_INDEX       8u  /* combine index < -1 (route ignored) */
+#define MOE_FLAG_BAD_SEGMENT    16u  /* expert segment outside [0, rows) (expert skipped) */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024   /* E, n_dest, n_local */
+#define MOE_MAX_TOPK    16
+
+/* Human-readable name of a moe_status value.  Never NULL. */
+const char* moe_strerror(int status);
+
+/* ABI version of this library (major * 100 + minor). */
+int moe_version(void);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_topk -- router top-k with renormalised softmax gates.
+ *
+ * For every token t (M6.6 0x03A; M6.2 0x06L1 Mixtral row):
+ *   topk_ids[t, j]  j-th largest logit's expert, j = 0..k-1, ordered by
+ *                   descending fp32 logit; equal logits (-0 == +0) place the
+ *                   lower expert index first.
+ *   topk_w[t, j]    exp(z_j - z_0) / sum_i exp(z_i - z_0) over the k kept
+ *                   experts (= softmax over all E, keep k, renormalise).
+ * A token whose logits contain NaN or +-Inf gets ids -1 and weights 0 in all
+ * k slots and sets MOE_FLAG_NONFINITE_LOGIT.
+ *
+ *   logits    device, fp32 [T, E]
+ *   T >= 0; 1 <= k <= min(E, MOE_MAX_TOPK); 1 <= E <= MOE_MAX_EXPERTS
+ *   gating    MOE_GATING_SOFTMAX_TOPK_RENORM
+ *   topk_ids  device, int32 [T, k]       (4-byte alignment suffices)
+ *   topk_w    device, fp32  [T, k]       (4-byte alignment suffices)
+ *   dev_flags device uint32 or NULL
+ * ------------------------------------------------------------------------- */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t gating,
+                   int32_t* topk_ids, float* topk_w, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute -- group routes by expert, stable, with capacity and inverse.
+ *
+ * Routes are r = t*k + j (token-major, then slot).  With e_r = topk_ids[r]
+ * (M6.2 0x03B, 0x01C; M6.6 0x0CD):
+ *   sel[e]     = #{r : e_r = e}
+ *   pos_r      = #{r' < r : e_r' = e_r}            (rank in route order)
+ *   accepted   iff capacity < 0 (dropless) or pos_r < capacity
+ *   counts[e]  = accepted routes of e = min(sel[e], capacity)
+ *   offsets    exclusive prefix of counts, offsets[E] = A (accepted total)
+ *   inv[r]     = offsets[e_r] + pos_r, or -1 if dropped
+ *   src[p]     = r with inv[r] = p for p < A; -1 for A <= p < T*k
+ *   x_perm[p]  = x[src[p] / k] for p < A (rows p >= A are not written)
+ *   n_dropped  = T*k - A
+ * Expert id -1 means "no route" (dropped, not flagged); ids < -1 or >= E
+ * are dropped and set MOE_FLAG_BAD_EXPERT.
+ *
+ *   x          device, [T, d] of x_dtype; may be NULL when x_perm is NULL
+ *   x_dtype    MOE_F32 (d % 4 == 0) or MOE_BF16 (d % 8 == 0)
+ *   topk_ids   device int32 [T*k]
+ *   capacity   -1 (dropless) or >= 0
+ *   x_perm     device [T*k, d] of x_dtype, or NULL (metadata only)
+ *   src, inv   device int32 [T*k]
+ *   sel_counts device int32 [E] or NULL; counts int32 [E]; offsets int32 [E+1]
+ *   n_dropped  device int32 [1]
+ *   ws         device workspace of at least moe_permute_workspace(T, k, E) bytes
+ * ------------------------------------------------------------------------- */
+size_t moe_permute_workspace(int64_t T, int32_t k, int32_t E);
+int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d,
+                const int32_t* topk_ids, int32_t k, int32_t E, int64_t capacity,
+                void* x_perm, int32_t* src, int32_t* inv,
+                int32_t* sel_counts, int32_t* counts, int32_t* offsets, int32_t* n_dropped,
+                void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu -- bias-free SwiGLU experts over ragged row segments.
+ *
+ * For every expert e with seg_count[e] > 0, rows
+ * X_e = x[seg_start[e] .. seg_start[e] + seg_count[e]) (M6.6 0x04A, 0x04C):
+ *   G = X_e W_gate[e]^T,  U = X_e W_up[e]^T            (fp32 accumulate)
+ *   H = SiLU(G) * U,      SiLU(v) = v / (1 + exp(-v))  (fp32)
+ *   z rows of the segment = H W_down[e]^T              (fp32 accumulate)
+ * bf16 path: operands bf16 on MFMA, H rounded to bf16 (nearest-even) between
+ * the two products, z stored as z_dtype (bf16 or fp32).  fp32 path: every
+ * value fp32 (z_dtype must be MOE_F32).  Rows not covered by a segment are
+ * not written.  A segment with start < 0, count < 0 or start + count > rows
+ * sets MOE_FLAG_BAD_SEGMENT and is skipped; zero-row experts are skipped
+ * without shifting later experts' weights.
+ *
+ *   x          device [rows, d] of dtype
+ *   d % 64 == 0, d_ff % 64 == 0, 1 <= E
+ *   seg_start, seg_count   device int32 [E] (e.g. offsets and counts of
+ *              moe_permute, or e*cap and counts of moe_recv_compact)
+ *   rows       rows of x and z (upper bound of every segment end): T*k for a
+ *              permuted batch, n_local*cap for static arrays
+ *   w_gate, w_up  device [E, d_ff, d] of dtype; w_down device [E, d, d_ff]
+ *   z          device [rows, d] of z_dtype
+ *   ws         device workspace of moe_grouped_swiglu_workspace(rows, E, d_ff, dtype)
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype);
+int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t d_ff, int32_t E,
+                       const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       void* z, int32_t z_dtype, void* ws, size_t ws_bytes,
+                       uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_unpermute_combine -- inverse permutation + gate-weighted FP32 combine.
+ *
+ * For every token t (M6.6 0x03C3, 0x0CD; 0x0AE FP32 accumulation):
+ *   y[t] (=, or += when accumulate) sum over j = 0..k-1 in ascending order of
+ *        g[t*k+j] * z[idx[t*k+j] - lo]   for every j with lo <= idx < hi
+ * Other routes add nothing: idx == -1 (dropped) or idx outside the window
+ * [lo, hi) (held by another window, e.g. another wave).  idx < -1 sets
+ * MOE_FLAG_BAD_INDEX.  No renormalisation is applied.  With k = 1 and
+ * gates = NULL this is the row expansion of a static-array result back to
+ * pool-row order (zero rows where idx is -1).
+ *
+ *   z          device [hi - lo, d] of z_dtype (MOE_F32 or MOE_BF16)
+ *   d % 4 == 0 (fp32) or d % 8 == 0 (bf16)
+ *   idx        device int32 [T*k]
+ *   0 <= lo <= hi
+ *   gates      device fp32 [T*k], or NULL for weight 1 (4-byte alignment suffices)
+ *   y          device fp32 [T, d]
+ * ------------------------------------------------------------------------- */
+int moe_unpermute_combine(const void* z, int32_t z_dtype, int32_t d,
+                          const int32_t* idx, int64_t lo, int64_t hi,
+                          const float* gates, int64_t T, int32_t k,
+                          float* y, int32_t accumulate, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_pool_pack -- pooled-wave sender pack into fixed destination pools.
+ *
+ * For route r = t*k + j with valid expert e = topk_ids[r] (pooled wave 02-04):
+ *   dest = e / experts_per_dest,  local = e % experts_per_dest
+ *   o_r  = #{r' < r : dest_r' = dest_r}     (the route's destination rank)
+ *   wave = o_r % n_waves,  row = o_r / n_waves,  accepted iff row < pool_rows
+ *   pools[wave][dest][1 + row][:] = x[t]
+ *   pools[wave][dest][0][row]     = local   (header row, uint16)
+ *   route_loc[r] = (wave*n_dest + dest)*(pool_rows + 1) + 1 + row, else -1
+ * Every other header element is 0xFFFF and every data row without a route
+ * is zero.  dest_counts[dest] = routes to dest before the cap;
+ * sender_dropped = T*k - accepted (routes above the cap plus routes whose id
+ * is -1 or invalid; invalid ids set MOE_FLAG_BAD_EXPERT).
+ *
+ *   x_bf16     device bf16 [T, d], d % 8 == 0, pool_rows <= d
+ *   E <= n_dest * experts_per_dest, n_dest <= MOE_MAX_EXPERTS, 1 <= n_waves
+ *   wave       -1: pools is [n_waves][n_dest][pool_rows + 1][d] (all waves);
+ *              w >= 0: pools is [n_dest][pool_rows + 1][d], only wave w's rows
+ *              and headers are written (route_loc keeps the all-wave index)
+ *   route_loc  device int32 [T*k]; dest_counts int32 [n_dest]; sender_dropped int32 [1]
+ *   ws         device workspace of moe_pool_pack_workspace(T, k, n_dest)
+ * ------------------------------------------------------------------------- */
+size_t moe_pool_pack_workspace(int64_t T, int32_t k, int32_t n_dest);
+int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k,
+                  int32_t E, int32_t experts_per_dest, int32_t n_dest, int32_t n_waves,
+                  int32_t pool_rows, int32_t wave, void* pools, int32_t* route_loc,
+                  int32_t* dest_counts, int32_t* sender_dropped, void* ws, size_t ws_bytes,
+                  uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_recv_compact -- receiver compaction into static per-expert arrays.
+ *
+ * Over one wave's incoming pools, visited in fixed source order s = 0..n_src-1,
+ * then i = 0..pool_rows-1 (pooled wave 02-04, 07):
+ *   h = header[s][i] (uint16 at pools_in[s][0][i]); 0xFFFF = empty row
+ *   q = number of earlier rows with the same h
+ *   accepted iff q < cap:  compact[h][q][:] = pools_in[s][1 + i][:]
+ *   row_slot[s*(pool_rows+1) + 1 + i] = h*cap + q, else -1
+ *   row_slot of header rows and empty rows = -1
+ *   arrived[h] = rows with id h, counts[h] = min(arrived[h], cap),
+ *   recv_dropped = sum_h arrived[h] - counts[h]
+ * Header ids >= n_local other than 0xFFFF set MOE_FLAG_BAD_HEADER and the
+ * row is ignored.  compact rows at or past counts[h] are not written.
+ *
+ *   pools_in   device bf16 [n_src][pool_rows + 1][d], d % 8 == 0, pool_rows <= d
+ *   1 <= n_local <= MOE_MAX_EXPERTS, cap >= 0
+ *   compact    device bf16 [n_local][cap][d]
+ *   counts int32 [n_local]; arrived int32 [n_local] or NULL;
+ *   row_slot int32 [n_src*(pool_rows + 1)]; recv_dropped int32 [1]
+ *   ws         device workspace of moe_recv_compact_workspace(n_src, pool_rows, n_local)
+ * ------------------------------------------------------------------------- */
+size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int32_t n_local);
+int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d,
+                     int32_t n_local, int32_t cap, void* compact, int32_t* counts,
+                     int32_t* arrived, int32_t* row_slot, int32_t* recv_dropped,
+                     void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROUPED_EXPERT_AMD_MOE_H */

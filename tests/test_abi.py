@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every function ``include/moe.h``
+declares, and rejects bad arguments on the host before touching the GPU
+(these calls return before any HIP call, so they run without a GPU)."""
+import ctypes
+
+import pytest
+
+from grouped_expert_amd import binding as B
+
+lib = B.lib
+NULL = None
+EINVAL, EUNSUP, EWS = -1, -2, -3
+
+
+def test_exports_every_header_symbol():
+    names = B.header_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS)
+
+
+def test_strerror_and_version():
+    assert B.strerror(0) == "ok"
+    assert B.strerror(-3).startswith("workspace")
+    assert B.strerror(12345) == "unknown status"
+    assert lib.moe_version() >= 100
+
+
+def _fake(n=1):
+    # host buffer addresses: never dereferenced because validation fails first
+    buf = (ctypes.c_char * (64 * n))()
+    return ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15), buf
+
+
+def test_route_validation():
+    p, _keep = _fake()
+    assert lib.moe_route_topk(p, 10, 8, 0, 0, p, p, NULL, NULL) == EINVAL         # k < 1
+    assert lib.moe_route_topk(p, 10, 8, 9, 0, p, p, NULL, NULL) == EINVAL         # k > E
+    assert lib.moe_route_topk(p, 10, 2000, 2, 0, p, p, NULL, NULL) == EINVAL      # E too large
+    assert lib.moe_route_topk(p, 10, 32, 17, 0, p, p, NULL, NULL) == EINVAL       # k > 16
+    assert lib.moe_route_topk(p, 10, 8, 2, 7, p, p, NULL, NULL) == EUNSUP         # unknown gating
+    assert lib.moe_route_topk(NULL, 10, 8, 2, 0, p, p, NULL, NULL) == EINVAL      # null logits
+    assert lib.moe_route_topk(NULL, 0, 8, 2, 0, NULL, NULL, NULL, NULL) == 0      # empty batch
+
+
+def test_permute_validation():
+    p, _keep = _fake()
+    ws = lib.moe_permute_workspace(100, 8, 128)
+    assert ws > 0
+    args = [p, 1, 100, 64, p, 8, 128, -1, p, p, p, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[7] = -2                                   # capacity < -1
+    assert lib.moe_permute(*bad) == EINVAL
+    bad = list(args); bad[16] = ws - 1                              # workspace too small
+    assert lib.moe_permute(*bad) == EWS
+    bad = list(args); bad[15] = NULL                                # no workspace
+    assert lib.moe_permute(*bad) == EWS
+    bad = list(args); bad[3] = 60                                   # bf16 row not 16-byte multiple
+    assert lib.moe_permute(*bad) == EINVAL
+    bad = list(args); bad[1] = 5                                    # unknown dtype
+    assert lib.moe_permute(*bad) == EINVAL
+    bad = list(args); bad[13] = NULL                                # offsets required
+    assert lib.moe_permute(*bad) == EINVAL
+    q = ctypes.c_void_p(p.value + 4)
+    bad = list(args); bad[0] = q                                    # misaligned rows
+    assert lib.moe_permute(*bad) == EINVAL
+
+
+def test_swiglu_validation():
+    p, _keep = _fake()
+    ws = lib.moe_grouped_swiglu_workspace(1000, 8, 256, 1)
+    assert ws >= 1000 * 256 * 2
+    args = [p, 1, 128, 256, 8, p, p, 1000, p, p, p, p, 1, p, ws, NULL, NULL]
+    assert lib.moe_grouped_swiglu(*args[:14], ws - 1, NULL, NULL) == EWS
+    bad = list(args); bad[2] = 100                                  # d not a multiple of 64
+    assert lib.moe_grouped_swiglu(*bad) == EUNSUP
+    bad = list(args); bad[1] = 0; bad[12] = 1                       # fp32 in, bf16 out
+    assert lib.moe_grouped_swiglu(*bad) == EUNSUP
+    bad = list(args); bad[8] = NULL                                 # no gate weights
+    assert lib.moe_grouped_swiglu(*bad) == EINVAL
+    bad = list(args); bad[4] = 0                                    # no experts
+    assert lib.moe_grouped_swiglu(*bad) == EINVAL
+
+
+def test_combine_validation():
+    p, _keep = _fake()
+    assert lib.moe_unpermute_combine(p, 1, 60, p, 0, 10, NULL, 10, 2, p, 0, NULL, NULL) == EINVAL   # d % 8
+    assert lib.moe_unpermute_combine(p, 0, 64, p, 5, 2, NULL, 10, 2, p, 0, NULL, NULL) == EINVAL    # hi < lo
+    assert lib.moe_unpermute_combine(p, 0, 64, NULL, 0, 2, NULL, 10, 2, p, 0, NULL, NULL) == EINVAL  # idx
+    assert lib.moe_unpermute_combine(p, 0, 64, p, 0, 2, NULL, 0, 2, p, 0, NULL, NULL) == 0          # empty
+
+
+def test_pool_pack_validation():
+    p, _keep = _fake()
+    ws = lib.moe_pool_pack_workspace(100, 8, 64)
+    args = [p, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[5] = 385                                  # E > n_dest * epd
+    assert lib.moe_pool_pack(*bad) == EINVAL
+    bad = list(args); bad[9] = 4000                                 # header row cannot hold the ids
+    assert lib.moe_pool_pack(*bad) == EUNSUP
+    bad = list(args); bad[10] = 3                                   # wave out of range
+    assert lib.moe_pool_pack(*bad) == EINVAL
+    bad = list(args); bad[16] = 8                                   # workspace too small
+    assert lib.moe_pool_pack(*bad) == EWS
+
+
+def test_recv_compact_validation():
+    p, _keep = _fake()
+    ws = lib.moe_recv_compact_workspace(64, 3004, 6)
+    args = [p, 64, 3004, 3072, 6, 33497, p, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[5] = -1                                   # negative capacity
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[4] = 0                                    # no local experts
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[12] = 0                                   # workspace
+    assert lib.moe_recv_compact(*bad) == EWS
+    bad = list(args); bad[3] = 1000                                 # header row too narrow
+    assert lib.moe_recv_compact(*bad) == EUNSUP
+
+
+def test_workspace_queries_reject_bad_sizes():
+    assert lib.moe_permute_workspace(-1, 8, 8) == 0
+    assert lib.moe_permute_workspace(10, 8, 5000) == 0
+    assert lib.moe_grouped_swiglu_workspace(10, 8, 64, 7) == 0
+    assert lib.moe_pool_pack_workspace(10, 0, 8) == 0
+    assert lib.moe_recv_compact_workspace(4, 4, 0) == 0

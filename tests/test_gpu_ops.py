@@ -1,0 +1,273 @@
+"""GPU parity of each C-ABI call against the CPU oracle, at sizes the oracle
+finishes in seconds that still span several tiles and ragged tails, plus the
+degenerate cases (empty inputs, capacity 0, invalid ids, NaN logits).
+
+Integer outputs are compared bit-exactly; floating-point outputs by the
+per-row relative error rule of ``tests/helpers.py`` (2e-2 against fp64)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O
+from tests.helpers import as_f64, assert_rows_close, row_rel_err, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import grouped_expert_amd as ge
+    return ge
+
+
+def _bf16(a32):
+    import workloads as W
+    return W.f32_to_bf16_bits(a32)
+
+
+# ---------------------------------------------------------------------------
+# route
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (300, 8, 2), (257, 128, 8), (190, 384, 8), (70, 1024, 16),
+                                   (64, 65, 5), (0, 16, 2)])
+def test_route_topk(ge, T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    if T > 10:
+        z[:5] = np.round(z[:5])                      # ties
+        z[5, : min(E, 3)] = -0.0
+        z[6, :] = 0.0
+        z[7, E // 2] = np.nan
+        z[8, 0] = np.inf
+    flags = ge.new_flags("cuda")
+    ids, w = ge.route_topk(to_gpu(z), k, flags=flags)
+    rid, rg, inv = O.route_topk(z, k)
+    assert np.array_equal(to_np(ids), rid)
+    gw = to_np(w).astype(np.float64)
+    assert np.all(np.abs(gw - rg) <= 1e-5 * np.maximum(rg, 1e-30) + 1e-7)
+    assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
+
+
+# ---------------------------------------------------------------------------
+# permute
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,E,cap,dt", [(256, 2, 8, -1, "f32"), (1000, 8, 128, -1, "bf16"),
+                                          (999, 8, 128, 40, "bf16"), (64, 8, 384, -1, "bf16"),
+                                          (3000, 4, 1024, 7, "bf16"), (500, 3, 5, 0, "bf16"),
+                                          (0, 2, 4, -1, "bf16"), (40000, 8, 64, 4000, "bf16")])
+def test_permute(ge, T, k, E, cap, dt):
+    rng = np.random.default_rng(T + E + k)
+    d = 64
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 20:
+        ids[3, 0] = -1
+        ids[4, 1] = E + 3
+        ids[5, 0] = -7
+    x32 = rng.standard_normal((T, d)).astype(np.float32)
+    x = x32 if dt == "f32" else _bf16(x32)
+    flags = ge.new_flags("cuda")
+    out = ge.permute(to_gpu(x) if T else torch.empty((0, d), device="cuda", dtype=torch.float32 if dt == "f32"
+                                                    else torch.bfloat16),
+                     to_gpu(ids) if T else torch.empty((0, k), dtype=torch.int32, device="cuda"),
+                     E, cap, flags=flags)
+    plan = O.dispatch_plan(ids, E, cap)
+    assert to_np(out["sel"]).tolist() == plan.sel.tolist()
+    assert to_np(out["counts"]).tolist() == plan.counts.tolist()
+    assert to_np(out["offsets"]).tolist() == plan.offsets.tolist()
+    assert to_np(out["inv"]).tolist() == plan.inv.tolist()
+    assert to_np(out["src"]).tolist() == plan.src.tolist()
+    assert int(to_np(out["dropped"])[0]) == plan.dropped
+    A = plan.accepted
+    xp = to_np(out["x_perm"])[:A]
+    assert np.array_equal(xp, O.gather_rows(x, plan.src, k, A))
+    assert (int(to_np(flags)[0]) & 1 != 0) == bool(plan.bad.any())
+
+
+# ---------------------------------------------------------------------------
+# grouped SwiGLU
+# ---------------------------------------------------------------------------
+
+def _segments(rng, E, rows, mode):
+    if mode == "packed":
+        counts = rng.multinomial(rows, rng.dirichlet(np.ones(E) * 0.3))
+        counts[rng.integers(0, E)] = 0
+        starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    else:   # static arrays with gaps
+        cap = rows // E
+        counts = rng.integers(0, cap + 1, size=E)
+        counts[0] = cap
+        starts = np.arange(E) * cap
+    return starts.astype(np.int32), counts.astype(np.int32)
+
+
+@pytest.mark.parametrize("E,rows,d,d_ff,dt,zdt,mode", [
+    (8, 512, 128, 256, "f32", "f32", "packed"),
+    (6, 900, 256, 128, "bf16", "f32", "static"),
+    (5, 700, 128, 192, "bf16", "bf16", "packed"),
+    (16, 300, 384, 64, "bf16", "bf16", "packed"),
+    (3, 1, 128, 64, "bf16", "f32", "packed"),
+])
+def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
+    rng = np.random.default_rng(rows + E)
+    starts, counts = _segments(rng, E, rows, mode)
+    x32 = rng.standard_normal((rows, d)).astype(np.float32)
+    ws = [(0.05 * rng.standard_normal(s)).astype(np.float32) for s in
+          [(E, d_ff, d), (E, d_ff, d), (E, d, d_ff)]]
+    if dt == "bf16":
+        x = _bf16(x32)
+        ws = [_bf16(w) for w in ws]
+    else:
+        x = x32
+    zt = torch.float32 if zdt == "f32" else torch.bfloat16
+    z0 = torch.zeros((rows, d), dtype=zt, device="cuda")
+    flags = ge.new_flags("cuda")
+    z = ge.grouped_swiglu(to_gpu(x), to_gpu(starts), to_gpu(counts), *[to_gpu(w) for w in ws], z=z0, flags=flags)
+    bank = O.swiglu_bank(lambda e: (ws[0][e], ws[1][e], ws[2][e]))
+    want = O.run_segments(x, starts, counts, bank)
+    got = as_f64(z)
+    covered = np.zeros(rows, bool)
+    for s, c in zip(starts, counts):
+        covered[s:s + c] = True
+    assert_rows_close(got[covered], want[covered], what="swiglu")
+    assert np.all(got[~covered] == 0)
+    assert int(to_np(flags)[0]) == 0
+
+
+def test_grouped_swiglu_bad_segment_flag(ge):
+    rng = np.random.default_rng(1)
+    E, rows, d, d_ff = 3, 256, 128, 64
+    x = _bf16(rng.standard_normal((rows, d)).astype(np.float32))
+    ws = [_bf16((0.05 * rng.standard_normal(s)).astype(np.float32)) for s in
+          [(E, d_ff, d), (E, d_ff, d), (E, d, d_ff)]]
+    starts = np.array([0, 100, 250], np.int32)
+    counts = np.array([100, 100, 50], np.int32)      # last one overruns rows
+    flags = ge.new_flags("cuda")
+    z = ge.grouped_swiglu(to_gpu(x), to_gpu(starts), to_gpu(counts), *[to_gpu(w) for w in ws],
+                          z=torch.zeros((rows, d), dtype=torch.float32, device="cuda"), flags=flags)
+    assert int(to_np(flags)[0]) & 16
+    counts_ok = counts.copy()
+    counts_ok[2] = 0
+    want = O.run_segments(x, starts, counts_ok, O.swiglu_bank(lambda e: (ws[0][e], ws[1][e], ws[2][e])))
+    assert_rows_close(as_f64(z)[:200], want[:200], what="swiglu")
+    assert np.all(as_f64(z)[200:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,d,zdt,window,acc", [(100, 2, 128, "f32", None, False),
+                                                  (333, 8, 2048, "bf16", None, True),
+                                                  (50, 1, 3072, "f32", (40, 90), False),
+                                                  (0, 4, 64, "bf16", None, False),
+                                                  (77, 8, 24, "bf16", (10, 200), True)])
+def test_unpermute_combine(ge, T, k, d, zdt, window, acc):
+    rng = np.random.default_rng(T + d)
+    nz = 256
+    z32 = rng.standard_normal((nz, d)).astype(np.float32)
+    z = z32 if zdt == "f32" else _bf16(z32)
+    idx = rng.integers(-1, nz, size=T * k).astype(np.int32)
+    g = rng.random(T * k).astype(np.float32)
+    lo, hi = window if window else (0, nz)
+    y0 = rng.standard_normal((T, d)).astype(np.float32)
+    flags = ge.new_flags("cuda")
+    zt = to_gpu(z[lo:hi] if window else z)
+    y = to_gpu(y0.copy()) if acc else None
+    out = ge.unpermute_combine(zt, to_gpu(idx) if T else torch.empty(0, dtype=torch.int32, device="cuda"),
+                               to_gpu(g) if T else None, T, k, lo=lo, hi=hi, y=y, accumulate=acc, flags=flags)
+    want = O.combine(z[lo:hi], idx, g, T, k, lo=lo, hi=hi, y=y0.astype(np.float64).copy() if acc else None)
+    if T:
+        assert_rows_close(to_np(out), want, tol=1e-5, what="combine")
+    assert int(to_np(flags)[0]) == 0
+
+
+def test_combine_bad_index_flag(ge):
+    z = to_gpu(np.ones((4, 8), np.float32))
+    idx = to_gpu(np.array([0, -5, 1, 2], np.int32))
+    flags = ge.new_flags("cuda")
+    y = ge.unpermute_combine(z, idx, None, 2, 2, flags=flags)
+    assert int(to_np(flags)[0]) == 8
+    assert to_np(y).tolist() == [[1.0] * 8, [2.0] * 8]
+
+
+# ---------------------------------------------------------------------------
+# pooled-wave pack and receiver compaction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,epd,D,W,P,d,wave", [(200, 4, 6, 8, 3, 40, 64, -1),
+                                                  (500, 8, 3, 16, 2, 100, 128, -1),
+                                                  (500, 8, 3, 16, 2, 100, 128, 1),
+                                                  (64, 2, 1, 4, 1, 0, 8, -1),
+                                                  (0, 2, 2, 3, 3, 5, 8, -1),
+                                                  (3000, 8, 6, 64, 3, 30, 64, 2)])
+def test_pool_pack(ge, T, k, epd, D, W, P, d, wave):
+    rng = np.random.default_rng(T + D + P)
+    E = D * epd
+    z = rng.standard_normal((max(T, 1), E)).astype(np.float32)[:T]
+    z[:, :epd] += 1.5
+    ids = O.route_topk(z, k)[0] if T else np.zeros((0, k), np.int32)
+    if T > 10:
+        ids[2, 0] = -1
+        ids[3, 1] = E + 5
+    x = _bf16(rng.standard_normal((T, d)).astype(np.float32))
+    flags = ge.new_flags("cuda")
+    out = ge.pool_pack(to_gpu(x) if T else torch.empty((0, d), dtype=torch.bfloat16, device="cuda"),
+                       to_gpu(ids) if T else torch.empty((0, k), dtype=torch.int32, device="cuda"),
+                       E, epd, D, W, P, wave=wave, flags=flags)
+    pk = O.pool_pack(x, ids, epd, D, W, P)
+    want_pools = pk["pools"] if wave < 0 else pk["pools"][wave]
+    assert np.array_equal(to_np(out["pools"]), want_pools)
+    assert to_np(out["route_loc"]).tolist() == pk["route_loc"].tolist()
+    assert to_np(out["dest_counts"]).tolist() == pk["dest_counts"].tolist()
+    assert int(to_np(out["sender_dropped"])[0]) == pk["sender_dropped"]
+    assert (int(to_np(flags)[0]) & 1 != 0) == bool(pk["bad"].any())
+
+
+@pytest.mark.parametrize("S,P,d,L,cap", [(8, 40, 64, 6, 30), (64, 100, 128, 6, 700), (5, 6, 8, 3, 0),
+                                         (3, 0, 8, 2, 4), (40, 200, 256, 17, 100)])
+def test_recv_compact(ge, S, P, d, L, cap):
+    rng = np.random.default_rng(S * P + L)
+    pools = rng.integers(0, 2 ** 16, size=(S, P + 1, d)).astype(np.uint16)
+    p = (np.arange(1, L + 1) ** -1.1)
+    hdr = rng.choice(L, size=(S, P), p=p / p.sum()).astype(np.uint16)
+    if P > 3:
+        hdr[1, 2] = 0xFFFF
+        hdr[0, 3] = L + 1                         # bad id
+    pools[:, 0, :] = 0xFFFF
+    pools[:, 0, :P] = hdr
+    flags = ge.new_flags("cuda")
+    compact0 = torch.zeros((L, cap, d), dtype=torch.bfloat16, device="cuda")
+    out = ge.recv_compact(to_gpu(pools), L, cap, compact=compact0, flags=flags)
+    rc = O.recv_compact(pools, L, cap)
+    assert np.array_equal(to_np(out["compact"]), rc["compact"])
+    assert to_np(out["counts"]).tolist() == rc["counts"].tolist()
+    assert to_np(out["arrived"]).tolist() == rc["arrived"].tolist()
+    assert to_np(out["row_slot"]).tolist() == rc["row_slot"].tolist()
+    assert int(to_np(out["recv_dropped"])[0]) == rc["recv_dropped"]
+    assert (int(to_np(flags)[0]) & 4 != 0) == (rc["bad_header"] > 0)
+
+
+# ---------------------------------------------------------------------------
+# chained: identity check through permute + combine (no GEMM)
+# ---------------------------------------------------------------------------
+
+def test_permute_combine_identity(ge):
+    """combine(permute(x)) with Z = X_perm and renormalised gates gives x
+    back; with a capacity it gives the kept gate mass times x."""
+    rng = np.random.default_rng(4)
+    T, E, k, d = 1500, 32, 4, 256
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    x32 = rng.standard_normal((T, d)).astype(np.float32)
+    x = to_gpu(x32)
+    for cap in (-1, 150):
+        ids, g = ge.route_topk(to_gpu(z), k)
+        plan = ge.permute(x, ids, E, cap)
+        y = ge.unpermute_combine(plan["x_perm"], plan["inv"], g, T, k)
+        keep = (to_np(plan["inv"]) >= 0).reshape(T, k)
+        mass = (to_np(g).astype(np.float64) * keep).sum(1)
+        assert row_rel_err(to_np(y), mass[:, None] * x32) < 1e-5
