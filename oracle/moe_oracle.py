@@ -380,7 +380,7 @@ def moe_layer_expert_major(x: np.ndarray, ids: np.ndarray, gates: np.ndarray,
 # ----------------------------------------------------------------------------
 
 def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest: int,
-              n_waves: int, pool_rows: int, *, with_pools: bool = True):
+              n_waves: int, pool_rows: int, *, with_pools: bool = True, E: Optional[int] = None):
     """Pack one sender's routes into fixed destination pools.
 
     Pooled wave §02: expert id gives a destination and a local expert id;
@@ -395,11 +395,12 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
     flat pool row ``(w*n_dest + dest)*(pool_rows+1) + 1 + row`` or -1),
     ``dest_counts`` (routes per destination before the cap),
     ``sender_dropped`` (routes not placed, including "no route" ids) and the
-    per-route ``wave``/``row``/``dest``/``local``.
+    per-route ``wave``/``row``/``dest``/``local``; ``bad`` marks expert ids
+    that are neither -1 nor below ``E`` (default ``n_dest*experts_per_dest``).
     """
     T, k = ids.shape
     e = np.asarray(ids, dtype=np.int64).reshape(-1)
-    n_exp = n_dest * experts_per_dest
+    n_exp = n_dest * experts_per_dest if E is None else E
     valid = (e >= 0) & (e < n_exp)
     dest = np.where(valid, e // experts_per_dest, -1)
     local = np.where(valid, e % experts_per_dest, -1)
@@ -423,7 +424,7 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
         pools[wave[r], dest[r], 0, row[r]] = local[r].astype(np.uint16)
     return dict(pools=pools, route_loc=route_loc, dest_counts=plan.sel,
                 sender_dropped=int(e.size - acc.sum()), wave=wave, row=row,
-                dest=dest, local=local, accepted=acc, bad=plan.bad)
+                dest=dest, local=local, accepted=acc, bad=(e < -1) | (e >= n_exp))
 
 
 # ----------------------------------------------------------------------------
