@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert layer on one MI355X.
+
+One step is one pass of the layer over one synthetic batch that is already
+resident in HBM:
+
+* layer workloads (mid_bf16 = the default, tiny_fp32, decode_bf16):
+  route -> permute -> grouped SwiGLU -> un-permute/combine;
+* recv_share_bf16: three waves of receiver compaction -> grouped SwiGLU over
+  the static per-expert arrays -> expansion to pool rows (fp32);
+* sender_pack_bf16: route -> pooled-wave pack of all three waves.
+
+Inputs rotate over ``--banks`` independent copies (distinct HBM addresses) so
+that no step finds the previous step's operands in the 256 MB last-level
+cache.  Every call is timed with HIP events on the stream it runs on; the
+JSON line reports whole-step throughput, the roofline of the dominant call
+(algorithmic bytes or flops per launch over its measured duration) and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "routed tokens/s per MoE layer on 1 MI355X; HBM GB/s & MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3        # fp32 vector
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mid_bf16", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--banks", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens/rows of the CPU oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+class OpTimer:
+    """Per-call HIP event pairs recorded on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []          # (name, start_event, end_event)
+
+    def run(self, name, fn, *a, **kw):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn(*a, **kw)
+        e.record()
+        self.marks.append((name, s, e))
+        return out
+
+    def totals_ms(self):
+        agg = {}
+        for name, s, e in self.marks:
+            agg.setdefault(name, []).append(s.elapsed_time(e))
+        return agg
+
+
+def to_dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def layer_setup(torch, w, banks):
+    logits = W.router_logits(w)
+    x = W.tokens(w)
+    wg, wu, wd = W.all_expert_weights(w)
+    host = dict(logits=logits, x=x, wg=wg, wu=wu, wd=wd)
+    b0 = {k: to_dev(torch, v) for k, v in host.items()}
+    bank_list = [b0] + [{k: v.clone() for k, v in b0.items()} for _ in range(banks - 1)]
+    return host, bank_list
+
+
+def layer_step(ge, timer, w, bank, flags):
+    import torch
+    T = w.T
+    ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, flags=flags)
+    plan = timer.run("permute", ge.permute, bank["x"], ids, w.E, w.capacity, flags=flags)
+    zdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    z = timer.run("swiglu", ge.grouped_swiglu, plan["x_perm"], plan["offsets"], plan["counts"], bank["wg"],
+                  bank["wu"], bank["wd"], z_dtype=zdt, flags=flags)
+    y = timer.run("combine", ge.unpermute_combine, z, plan["inv"], gates, T, w.k, flags=flags)
+    return dict(y=y, ids=ids, gates=gates, plan=plan)
+
+
+def layer_ledger(w, counts):
+    """Algorithmic bytes / flops per call (unique inputs + outputs + index
+    metadata; the H round trip is excluded)."""
+    b = 4 if w.dtype == "f32" else 2
+    bz = b
+    A = int(counts.sum())
+    E_act = int((counts > 0).sum())
+    T, k, d, dff, E = w.T, w.k, w.d, w.d_ff, w.E
+    return {
+        "route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
+        "permute": dict(bytes=4 * T * k + T * d * b + A * d * b + 8 * T * k + 4 * (2 * E + 1), flops=0),
+        "swiglu": dict(bytes=A * d * b + E_act * 3 * d * dff * b + A * d * bz, flops=6 * A * d * dff),
+        "combine": dict(bytes=A * d * bz + 8 * T * k + 4 * T * d, flops=2 * A * d),
+    }
+
+
+def layer_cpu_baseline(w, host, sample):
+    """The oracle layer (route, plan, expert-major SwiGLU, combine) on the first
+    ``sample`` tokens of the batch."""
+    import oracle as O
+    s = min(sample, w.T)
+    t0 = time.perf_counter()
+    ids, gates, _ = O.route_topk(host["logits"][:s], w.k)
+    bank = O.swiglu_bank(lambda e: (host["wg"][e], host["wu"][e], host["wd"][e]))
+    O.moe_layer_expert_major(host["x"][:s], ids, gates, bank, w.E, w.capacity)
+    dt = time.perf_counter() - t0
+    return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"first {s} of {w.T} tokens of {w.name}, full layer (route, dispatch plan, "
+                       f"fp64 SwiGLU of every routed row, combine); {dt:.2f} s")
+
+
+def recv_setup(torch, w, banks):
+    pools = [W.recv_pools(w, wave) for wave in range(w.n_waves)]
+    wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
+    host = dict(pools=pools, wg=wg, wu=wu, wd=wd)
+    b0 = dict(pools=[to_dev(torch, p) for p in pools], wg=to_dev(torch, wg), wu=to_dev(torch, wu),
+              wd=to_dev(torch, wd))
+    bank_list = [b0]
+    for _ in range(banks - 1):
+        bank_list.append(dict(pools=[p.clone() for p in b0["pools"]], wg=b0["wg"].clone(), wu=b0["wu"].clone(),
+                              wd=b0["wd"].clone()))
+    return host, bank_list
+
+
+def recv_step(ge, timer, w, bank, flags, bufs):
+    import torch
+    S, P1, L, cap, d = w.n_src, w.pool_rows + 1, w.n_local, w.recv_cap, w.d
+    starts = bufs["starts"]
+    outs = []
+    for wave in range(w.n_waves):
+        rc = timer.run("recv_compact", ge.recv_compact, bank["pools"][wave], L, cap, compact=bufs["compact"],
+                       flags=flags)
+        z = timer.run("swiglu", ge.grouped_swiglu, bufs["compact"].view(L * cap, d), starts, rc["counts"],
+                      bank["wg"], bank["wu"], bank["wd"], z_dtype=torch.float32, z=bufs["z"], flags=flags)
+        ret = timer.run("expand", ge.unpermute_combine, z, rc["row_slot"], None, S * P1, 1,
+                        y=bufs["ret"][wave], flags=flags)
+        outs.append((rc, ret))
+    return outs
+
+
+def recv_ledger(w, counts_per_wave):
+    S, P, P1, d, dff = w.n_src, w.pool_rows, w.pool_rows + 1, w.d, w.d_ff
+    V = S * P
+    led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0),
+           "expand": dict(bytes=0, flops=0)}
+    for counts in counts_per_wave:
+        A = int(counts.sum())
+        E_act = int((counts > 0).sum())
+        led["recv_compact"]["bytes"] += S * d * 2 + V * d * 2 + A * d * 2 + 4 * S * P1
+        led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * 4
+        led["swiglu"]["flops"] += 6 * A * d * dff
+        led["expand"]["bytes"] += A * d * 4 + 4 * S * P1 + S * P1 * d * 4
+    return led
+
+
+def recv_cpu_baseline(w, host, sample):
+    """Oracle compaction of one wave (integer part in full, rows copied) plus
+    the fp64 SwiGLU of the first ``sample`` accepted rows."""
+    import oracle as O
+    t0 = time.perf_counter()
+    rc = O.recv_compact(host["pools"][0], w.n_local, w.recv_cap)
+    comp = rc["compact"]
+    n = 0
+    for e in range(w.n_local):
+        take = min(int(rc["counts"][e]), max(0, sample - n))
+        if take == 0:
+            continue
+        O.swiglu_expert(O.to_f64(comp[e, :take]), O.to_f64(host["wg"][e]), O.to_f64(host["wu"][e]),
+                        O.to_f64(host["wd"][e]))
+        n += take
+    dt = time.perf_counter() - t0
+    return dict(value=w.n_src * w.pool_rows / dt if n >= int(rc["counts"].sum()) else n / dt,
+                unit="incoming rows/s", cores=cpu_threads(), kind="oracle",
+                sample=f"wave 0 compaction of {w.n_src}x{w.pool_rows} rows plus fp64 SwiGLU of {n} accepted rows; "
+                       f"rate = SwiGLU rows / {dt:.2f} s")
+
+
+def pack_setup(torch, w, banks):
+    logits = W.router_logits(w)
+    x = W.tokens(w)
+    host = dict(logits=logits, x=x)
+    b0 = {k: to_dev(torch, v) for k, v in host.items()}
+    return host, [b0] + [{k: v.clone() for k, v in b0.items()} for _ in range(banks - 1)]
+
+
+def pack_step(ge, timer, w, bank, flags, bufs):
+    ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, flags=flags)
+    out = timer.run("pool_pack", ge.pool_pack, bank["x"], ids, w.E, w.experts_per_dest, w.n_dest, w.n_waves,
+                    w.pool_rows, pools=bufs["pools"], flags=flags)
+    return dict(ids=ids, gates=gates, pack=out)
+
+
+def pack_ledger(w):
+    T, k, d, E = w.T, w.k, w.d, w.E
+    return {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
+            "pool_pack": dict(bytes=8 * T * k + T * d * 2 + w.n_waves * w.n_dest * (w.pool_rows + 1) * d * 2,
+                              flops=0)}
+
+
+def pack_cpu_baseline(w, host, sample):
+    import oracle as O
+    s = min(sample, w.T)
+    t0 = time.perf_counter()
+    ids, _, _ = O.route_topk(host["logits"][:s], w.k)
+    O.pool_pack(host["x"][:s], ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
+    dt = time.perf_counter() - t0
+    return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"first {s} of {w.T} tokens of {w.name}: route + pack of all waves; {dt:.2f} s")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import grouped_expert_amd as ge
+
+    w = W.WORKLOADS[args.workload]
+    banks = max(1, args.banks)
+    torch.cuda.set_device(0)
+    flags = ge.new_flags("cuda")
+    kind = ("recv" if w.name.startswith("recv") else "pack" if w.name.startswith("sender") else "layer")
+    print(f"[bench] workload {w.name}: generating inputs ({banks} bank(s))", file=sys.stderr, flush=True)
+    bufs = {}
+    if kind == "layer":
+        host, bank_list = layer_setup(torch, w, banks)
+        step = lambda tm, b: layer_step(ge, tm, w, b, flags)
+    elif kind == "recv":
+        host, bank_list = recv_setup(torch, w, banks)
+        L, cap, d = w.n_local, w.recv_cap, w.d
+        bufs = dict(compact=torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda"),
+                    z=torch.empty((L * cap, d), dtype=torch.float32, device="cuda"),
+                    ret=[torch.empty((w.n_src * (w.pool_rows + 1), d), dtype=torch.float32, device="cuda")
+                         for _ in range(w.n_waves)],
+                    starts=torch.arange(L, dtype=torch.int32, device="cuda") * cap)
+        step = lambda tm, b: recv_step(ge, tm, w, b, flags, bufs)
+    else:
+        host, bank_list = pack_setup(torch, w, banks)
+        bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, w.pool_rows + 1, w.d), dtype=torch.bfloat16,
+                                      device="cuda"))
+        step = lambda tm, b: pack_step(ge, tm, w, b, flags, bufs)
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        last = step(OpTimer(torch), bank_list[i % banks])
+    torch.cuda.synchronize()
+
+    timer = OpTimer(torch)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        last = step(timer, bank_list[i % banks])
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / max(1, args.steps)
+    per_op = {k: float(np.mean(v)) for k, v in timer.totals_ms().items()}
+    n_calls = {k: len(v) for k, v in timer.totals_ms().items()}
+    if int(flags.item()) != 0:
+        print(f"[bench] warning: dev_flags = {int(flags.item())}", file=sys.stderr)
+
+    # ledger and dominant call
+    if kind == "layer":
+        counts = last["plan"]["counts"].cpu().numpy()
+        led = layer_ledger(w, counts)
+        units, unit = w.T, "tokens/s"
+        per_step_calls = 1
+    elif kind == "recv":
+        cw = [rc["counts"].cpu().numpy() for rc, _ in last]
+        led = recv_ledger(w, cw)
+        units, unit = w.n_waves * w.n_src * w.pool_rows, "incoming rows/s"
+        per_step_calls = w.n_waves
+    else:
+        led = pack_ledger(w)
+        units, unit = w.T, "tokens/s"
+        per_step_calls = 1
+    value = units / (ms_per_step / 1e3)
+    # dominant = the call with the largest time per step
+    dom = max(per_op, key=lambda k: per_op[k] * n_calls[k])
+    dom_ms = per_op[dom]                                  # average duration of one launch of that call
+    per_launch_bytes = led[dom]["bytes"] / per_step_calls if dom in ("recv_compact", "swiglu", "expand") and \
+        kind == "recv" else led[dom]["bytes"]
+    per_launch_flops = led[dom]["flops"] / per_step_calls if kind == "recv" else led[dom]["flops"]
+    t_s = dom_ms / 1e3
+    peak_f = F32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
+    bw = per_launch_bytes / t_s / 1e9
+    tf = per_launch_flops / t_s / 1e12
+    mfma_bound = per_launch_flops / (peak_f * 1e12) > per_launch_bytes / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = dict(bound="mfma", achieved=round(tf, 2), peak=peak_f, unit="TFLOP/s", frac=round(tf / peak_f, 4),
+                    traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(bw, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(bw / HBM_PEAK_GBS, 4), traffic=None)
+    roof["kernel"] = dom
+    roof["launch_ms"] = round(dom_ms, 4)
+    roof["alg_bytes_per_launch"] = int(per_launch_bytes)
+    roof["alg_flops_per_launch"] = int(per_launch_flops)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        if kind == "layer":
+            cpu = layer_cpu_baseline(w, host, args.cpu_sample or min(w.T, 2048))
+        elif kind == "recv":
+            cpu = recv_cpu_baseline(w, host, args.cpu_sample or 4096)
+        else:
+            cpu = pack_cpu_baseline(w, host, args.cpu_sample or 16384)
+
+    cfg = {"workload": w.name, "dtype": w.dtype}
+    for key in ("T", "d", "E", "k", "d_ff", "capacity", "experts_per_dest", "n_dest", "n_waves", "pool_rows",
+                "n_src", "n_local", "recv_cap"):
+        v = getattr(w, key)
+        if v:
+            cfg[key] = v
+    cfg["banks"] = banks
+    ops = {k: dict(ms=round(per_op[k], 4), calls_per_step=n_calls[k] // max(1, args.steps),
+                   alg_GBps=round(led[k]["bytes"] / (per_step_calls if kind == "recv" else 1) / (per_op[k] / 1e3)
+                                  / 1e9, 1) if k in led else None)
+           for k in per_op}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu, "ops": ops,
+        "wall_s": round(wall_s, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
