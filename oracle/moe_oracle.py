@@ -420,8 +420,10 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
         pools = np.zeros((n_waves, n_dest, P1, d), dtype=np.uint16)
         pools[:, :, 0, :] = HEADER_EMPTY
         r = np.nonzero(acc)[0]
-        pools[wave[r], dest[r], 1 + row[r]] = x[r // k]
-        pools[wave[r], dest[r], 0, row[r]] = local[r].astype(np.uint16)
+        flat = pools.reshape(-1, d)                      # rows indexed like route_loc
+        flat[route_loc[r]] = x[r // k]
+        header = (wave[r] * n_dest + dest[r]) * P1       # row 0 of the route's pool
+        flat[header, row[r]] = local[r].astype(np.uint16)
     return dict(pools=pools, route_loc=route_loc, dest_counts=plan.sel,
                 sender_dropped=int(e.size - acc.sum()), wave=wave, row=row,
                 dest=dest, local=local, accepted=acc, bad=(e < -1) | (e >= n_exp))

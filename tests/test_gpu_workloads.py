@@ -1,0 +1,261 @@
+"""GPU parity at the five workloads' full sizes, through the same library calls
+(and so the same launch configurations) that bench.py times.
+
+Integer outputs (ids, plans, pools, headers, compaction maps, drop counts) are
+compared in full and bit-exactly.  Floating-point outputs are compared on
+sampled rows that the fp64 oracle computes one by one (each expert's first and
+last row among them), with the 2e-2 per-row relative error rule."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O
+import workloads as W
+from tests.helpers import as_f64, assert_rows_close, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import grouped_expert_amd as ge
+    return ge
+
+
+def _sample_rows(rng, offsets, counts, n_random):
+    rows = set(rng.choice(int(offsets[-1]), size=min(n_random, int(offsets[-1])), replace=False).tolist())
+    for o, c in zip(offsets[:-1], counts):
+        if c:
+            rows.add(int(o))
+            rows.add(int(o + c - 1))
+    return np.array(sorted(rows))
+
+
+def _layer_case(ge, w, n_tok_sample, n_row_sample):
+    logits = W.router_logits(w)
+    x = W.tokens(w)
+    wg, wu, wd = W.all_expert_weights(w)
+    flags = ge.new_flags("cuda")
+    y, st = ge.moe_layer(to_gpu(x), to_gpu(logits), to_gpu(wg), to_gpu(wu), to_gpu(wd), w.k, w.capacity,
+                         flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+
+    ids, gates, invalid = O.route_topk(logits, w.k)
+    assert np.array_equal(to_np(st["ids"]), ids)
+    assert np.all(np.abs(to_np(st["gates"]) - gates) <= 1e-5 * gates + 1e-7)
+    plan = O.dispatch_plan(ids, w.E, w.capacity)
+    gp = st["plan"]
+    for key in ("sel", "counts", "offsets", "inv", "src"):
+        assert np.array_equal(to_np(gp[key]), getattr(plan, key)), key
+    assert int(to_np(gp["dropped"])[0]) == plan.dropped
+    A = plan.accepted
+    assert np.array_equal(to_np(gp["x_perm"])[:A], O.gather_rows(x, plan.src, w.k, A))
+
+    bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
+    rng = np.random.default_rng(0)
+    # expert outputs on sampled packed rows
+    rows = _sample_rows(rng, plan.offsets, plan.counts, n_row_sample)
+    seg = np.searchsorted(plan.offsets, rows, side="right") - 1
+    xz = O.to_f64(O.gather_rows(x, plan.src, w.k, A)[rows])
+    want_z = np.zeros((rows.size, w.d))
+    for e in np.unique(seg):
+        m = seg == e
+        want_z[m] = bank(int(e), xz[m])
+    assert_rows_close(as_f64(st["z"])[rows], want_z, what="expert rows")
+    # layer output on sampled tokens
+    tok = np.unique(np.concatenate([rng.choice(w.T, size=min(n_tok_sample, w.T), replace=False),
+                                    src_tokens_of_extreme_experts(plan, w.k)]))
+    want_y = O.moe_layer_token_major(x[tok], ids[tok], gates[tok], bank, w.E)
+    assert_rows_close(to_np(y)[tok], want_y, what="layer output")
+    return plan
+
+
+def src_tokens_of_extreme_experts(plan, k):
+    """Tokens that route to the most and the least loaded non-empty expert."""
+    c = plan.counts
+    hot = int(np.argmax(c))
+    live = np.nonzero(c)[0]
+    cold = int(live[np.argmin(c[live])])
+    out = []
+    for e in (hot, cold):
+        out.extend((plan.src[plan.offsets[e]:plan.offsets[e + 1]][:8] // k).tolist())
+    return np.array(out, dtype=np.int64)
+
+
+def test_tiny_fp32_full(ge):
+    """Tiny layer: every token and every packed row against the oracle, both
+    oracle layouts."""
+    w = W.TINY
+    plan = _layer_case(ge, w, n_tok_sample=w.T, n_row_sample=w.R)
+    assert plan.dropped == 0
+
+
+def test_mid_bf16(ge):
+    w = W.MID
+    plan = _layer_case(ge, w, n_tok_sample=96, n_row_sample=256)
+    assert plan.counts.max() > 3 * plan.counts.mean()          # skewed loads reached the GEMM
+
+
+def test_decode_bf16(ge):
+    """Decode: all 64 tokens; most experts hold 0-2 rows."""
+    w = W.DECODE
+    plan = _layer_case(ge, w, n_tok_sample=w.T, n_row_sample=64)
+    assert (plan.counts == 0).sum() > 50 and plan.counts.max() <= 8
+
+
+@pytest.fixture(scope="module")
+def send_case():
+    """Inputs and the oracle's routing and pack of the sender-pack workload
+    (computed once for the tests that use them)."""
+    w = W.SEND
+    logits = W.router_logits(w)
+    x = W.tokens(w)
+    ids, gates, _ = O.route_topk(logits, w.k)
+    pk = O.pool_pack(x, ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
+    return dict(w=w, logits=logits, x=x, ids=ids, gates=gates, pk=pk)
+
+
+def test_sender_pack_full(ge, send_case):
+    """Sender pack of 65,536 tokens x top-8 over 384 experts into three waves of
+    [64, 3005, 3072] pools: every byte of every pool, every route location."""
+    c = send_case
+    w, pk = c["w"], c["pk"]
+    flags = ge.new_flags("cuda")
+    ids_g, gates_g = ge.route_topk(to_gpu(c["logits"]), w.k, flags=flags)
+    out = ge.pool_pack(to_gpu(c["x"]), ids_g, w.E, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows,
+                       flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+    assert np.array_equal(to_np(ids_g), c["ids"])
+    assert np.array_equal(to_np(out["route_loc"]), pk["route_loc"])
+    assert np.array_equal(to_np(out["dest_counts"]), pk["dest_counts"])
+    assert int(to_np(out["sender_dropped"])[0]) == pk["sender_dropped"]
+    for wave in range(w.n_waves):
+        for d0 in range(0, w.n_dest, 16):
+            got = to_np(out["pools"][wave, d0:d0 + 16])
+            assert np.array_equal(got, pk["pools"][wave, d0:d0 + 16]), (wave, d0)
+    rate = pk["sender_dropped"] / (w.T * w.k)
+    assert 0.0 < rate < 0.1
+
+
+def test_recv_share(ge):
+    """Receiver share: three waves of 64 x 3004 incoming rows, six local
+    experts, capacity 33,497.  Wave 0's compaction in full; all waves'
+    counters; expert outputs and the fp32 expansion on sampled rows."""
+    w = W.RECV
+    wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
+    bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
+    gw = [to_gpu(a) for a in (wg, wu, wd)]
+    L, cap, d, S, P1 = w.n_local, w.recv_cap, w.d, w.n_src, w.pool_rows + 1
+    compact = torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((L * cap, d), dtype=torch.float32, device="cuda")
+    starts = torch.arange(L, dtype=torch.int32, device="cuda") * cap
+    rng = np.random.default_rng(1)
+    total_drop = 0
+    for wave in range(w.n_waves):
+        pools = W.recv_pools(w, wave)
+        flags = ge.new_flags("cuda")
+        rc = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags)
+        ge.grouped_swiglu(compact.view(L * cap, d), starts, rc["counts"], *gw, z=z, flags=flags)
+        ret = ge.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, flags=flags)
+        torch.cuda.synchronize()
+        assert int(to_np(flags)[0]) == 0
+        orc = O.recv_compact(pools, L, cap, with_rows=(wave == 0))
+        counts = to_np(rc["counts"])
+        assert np.array_equal(counts, orc["counts"])
+        assert np.array_equal(to_np(rc["arrived"]), orc["arrived"])
+        assert np.array_equal(to_np(rc["row_slot"]), orc["row_slot"])
+        assert int(to_np(rc["recv_dropped"])[0]) == orc["recv_dropped"]
+        total_drop += orc["recv_dropped"]
+        if wave == 0:
+            for h in range(L):
+                n = int(counts[h])
+                assert np.array_equal(to_np(compact[h, :n]), orc["compact"][h, :n]), h
+        # sampled expert rows (first / last / random per expert) and their expansion
+        slots, srcrows = [], []
+        row_slot = orc["row_slot"]
+        for h in range(L):
+            n = int(counts[h])
+            pick = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=6)]))
+            for q in pick:
+                slots.append(h * cap + q)
+        slots = np.array(slots)
+        inv_slot = {int(s): i for i, s in enumerate(row_slot) if s >= 0}
+        srcrows = np.array([inv_slot[int(s)] for s in slots])
+        xin = O.to_f64(pools.reshape(-1, d)[srcrows])
+        want = np.zeros((slots.size, d))
+        for h in range(L):
+            m = slots // cap == h
+            want[m] = bank(h, xin[m])
+        assert_rows_close(to_np(z)[slots], want, what=f"wave {wave} expert rows")
+        assert np.array_equal(to_np(ret)[srcrows], to_np(z)[slots])           # expansion is a copy
+        dropped_rows = np.nonzero(row_slot < 0)[0][:64]
+        assert np.all(to_np(ret)[dropped_rows] == 0)
+    assert total_drop > 0
+
+
+@pytest.mark.parametrize("cap", [33497, 28400])
+def test_loopback_sender_to_receiver(ge, send_case, cap):
+    """Sender pools of the sender-pack workload fed back to a receiver with
+    six local experts (the receiver workload's weights): for sampled tokens
+    the FP32 accumulation over the three waves equals the sum of gated
+    outputs of the routes that both capacities kept.  The receiver capacity
+    is the page's 33,497 (no receiver drop with a single sender's traffic)
+    and a lower 28,400 that makes the receiver drop rows."""
+    c = send_case
+    ws, wr = c["w"], W.RECV
+    ids, gates, pk, x = c["ids"], c["gates"], c["pk"], c["x"]
+    wg, wu, wd = W.all_expert_weights(wr, n_experts=wr.n_local)
+    gw = [to_gpu(a) for a in (wg, wu, wd)]
+    flags = ge.new_flags("cuda")
+    ids_g, gates_g = ge.route_topk(to_gpu(c["logits"]), ws.k, flags=flags)
+    pk_g = ge.pool_pack(to_gpu(x), ids_g, ws.E, ws.experts_per_dest, ws.n_dest, ws.n_waves, ws.pool_rows,
+                        flags=flags)
+    y = torch.zeros((ws.T, ws.d), dtype=torch.float32, device="cuda")
+    bufs = dict(compact=torch.empty((wr.n_local, cap, ws.d), dtype=torch.bfloat16, device="cuda"),
+                z=torch.empty((wr.n_local * cap, ws.d), dtype=torch.float32, device="cuda"))
+    slots, drops = [], 0
+    for wave in range(ws.n_waves):
+        rc, _, _ = ge.loopback_wave(pk_g["pools"][wave], wave, ws.n_waves, pk_g["route_loc"], gates_g, ws.T, ws.k,
+                                    *gw, cap, y, flags=flags, bufs=bufs)
+        slots.append(to_np(rc["row_slot"]))
+        drops += int(to_np(rc["recv_dropped"])[0])
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+
+    P1 = ws.pool_rows + 1
+    loc = pk["route_loc"]
+    kept = np.zeros(loc.size, dtype=bool)
+    want_drops = 0
+    for wave in range(ws.n_waves):
+        rc = O.recv_compact(pk["pools"][wave], wr.n_local, cap, with_rows=False)
+        assert np.array_equal(slots[wave], rc["row_slot"])
+        want_drops += rc["recv_dropped"]
+        lo = wave * ws.n_dest * P1
+        inw = (loc >= lo) & (loc < lo + ws.n_dest * P1)
+        kept[inw] = rc["row_slot"][loc[inw] - lo] >= 0
+    assert drops == want_drops
+    assert (want_drops > 0) == (cap < 33497)
+    rng = np.random.default_rng(2)
+    tok = np.unique(np.concatenate([rng.choice(ws.T, size=40, replace=False),
+                                    np.nonzero(~kept.reshape(ws.T, ws.k).all(axis=1))[0][:8]]))
+    bank = O.swiglu_bank(lambda l: (wg[l], wu[l], wd[l]))
+    xf = O.to_f64(x[tok])
+    out = {}                                    # (sample index, slot) -> expert output
+    for l in range(ws.experts_per_dest):
+        pairs = [(i, j) for i, t in enumerate(tok) for j in range(ws.k)
+                 if kept[t * ws.k + j] and ids[t, j] % ws.experts_per_dest == l]
+        if pairs:
+            zl = bank(l, xf[[i for i, _ in pairs]])
+            for (i, j), row in zip(pairs, zl):
+                out[(i, j)] = row
+    want = np.zeros((tok.size, ws.d))
+    for i, t in enumerate(tok):
+        for j in range(ws.k):                   # ascending slot order
+            if (i, j) in out:
+                want[i] += gates[t, j] * out[(i, j)]
+    assert_rows_close(to_np(y)[tok], want, what="loopback output")

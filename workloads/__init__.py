@@ -154,13 +154,17 @@ def router_logits(w: Workload) -> np.ndarray:
 
 
 def tokens(w: Workload) -> np.ndarray:
-    """Token rows ``[T, d]`` (fp32, or bf16 bits)."""
-    rng = _rng(w.seed, _TAG_TOKENS)
-    chunk = 8192
+    """Token rows ``[T, d]`` (fp32, or bf16 bits).  Blocks of 4096 rows have
+    their own streams and are drawn in parallel threads."""
+    chunk = 4096
     out = np.empty((w.T, w.d), dtype=np.float32 if w.dtype == "f32" else np.uint16)
-    for t0 in range(0, w.T, chunk):
-        t1 = min(w.T, t0 + chunk)
-        out[t0:t1] = _store(_normal(rng, (t1 - t0, w.d), w.x_std), w.dtype)
+
+    def one(i):
+        t0, t1 = i * chunk, min(w.T, (i + 1) * chunk)
+        out[t0:t1] = _store(_normal(_rng(w.seed, _TAG_TOKENS, i), (t1 - t0, w.d), w.x_std), w.dtype)
+
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range((w.T + chunk - 1) // chunk)))
     return out
 
 
