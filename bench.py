@@ -38,6 +38,7 @@ METRIC = "routed tokens/s per MoE layer on 1 MI355X; HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3        # fp32 vector
+COPY_CALIB_BYTES = 256 << 20   # size of the calibration copy (read and written once)
 
 
 def parse():
@@ -286,6 +287,12 @@ def main():
         bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, w.pool_rows + 1, w.d), dtype=torch.bfloat16,
                                       device="cuda"))
         step = lambda tm, b: pack_step(ge, tm, w, b, flags, bufs)
+    # one plain device copy of known size (untimed): under rocprofv3 --pmc its
+    # FETCH_SIZE / WRITE_SIZE readings calibrate the counters to bytes
+    calib = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    del calib, calib_dst
     torch.cuda.synchronize()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)

@@ -43,8 +43,10 @@ inline RankGeom rank_geom(int64_t n, int32_t B) {
   RankGeom g;
   g.n = n;
   g.B = B;
-  int64_t s = (n + 64 * 1024 - 1) / (64 * 1024);
-  g.steps = static_cast<int32_t>(s < 1 ? 1 : (s > 32 ? 32 : s));
+  // at least 4 steps (256 items) per chunk and at most 32 (2048 items), aiming
+  // at about 64 chunks, so that the one-workgroup scan stays short
+  int64_t s = (n + 64 * 64 - 1) / (64 * 64);
+  g.steps = static_cast<int32_t>(s < 4 ? 4 : (s > 32 ? 32 : s));
   const int64_t chunk = 64ll * g.steps;
   g.chunks = (n + chunk - 1) / chunk;
   int bits = 0;
@@ -106,13 +108,16 @@ __global__ __launch_bounds__(1024) void rank_scan_kernel(RankGeom g, int64_t cap
   const int64_t c0 = static_cast<int64_t>(sub) * per;
   const int64_t c1 = c0 + per < g.chunks ? c0 + per : g.chunks;
   int32_t sum = 0;
-  if (t < active)
+  if (t < active) {
+#pragma unroll 8
     for (int64_t c = c0; c < c1; ++c) sum += table[c * g.B + b];
+  }
   part[t] = t < active ? sum : 0;
   __syncthreads();
   if (t < active) {
     int32_t run = 0;
     for (int s = 0; s < sub; ++s) run += part[s * g.B + b];
+#pragma unroll 8
     for (int64_t c = c0; c < c1; ++c) {
       const int32_t v = table[c * g.B + b];
       table[c * g.B + b] = run;

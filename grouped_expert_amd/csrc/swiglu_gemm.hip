@@ -32,8 +32,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// One M-tile of one expert segment.  first / ntile locate the expert's run of
+// tiles in the table (used by the expert-blocked workgroup order).
 struct TileEntry {
-  int32_t expert, row0, row_end, pad;
+  int32_t expert, row0, row_end, first, ntile, pad0, pad1, pad2;
 };
 
 // ---------------------------------------------------------------------------
@@ -59,10 +61,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   const int32_t cnt = (c + BM - 1) / BM;
   int32_t total = 0;
   const int32_t pre = block_exclusive_scan_1024(cnt, sh16, &total);
-  for (int32_t i = 0; i < cnt; ++i) {
-    const int32_t idx = pre + i;
-    if (idx < max_tiles) tiles[idx] = TileEntry{t, s + i * BM, s + c, 0};
-  }
+  // an expert whose tiles would run past the table (only with overlapping
+  // segments) keeps the tiles that fit, so its run stays self-consistent
+  const int32_t keep = pre >= max_tiles ? 0 : (cnt < max_tiles - pre ? cnt : max_tiles - pre);
+  for (int32_t i = 0; i < keep; ++i)
+    tiles[pre + i] = TileEntry{t, s + i * BM, s + c, pre, keep, 0, 0, 0};
   if (t == 0) {
     n_tiles[0] = total < max_tiles ? total : max_tiles;
     if (total > max_tiles) flag_or(flags, MOE_FLAG_BAD_SEGMENT);   // overlapping segments
@@ -72,166 +75,238 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 // 2./3. bf16 MFMA GEMM:  C[m, n] = sum_k A[m, k] * B[n, k]
 // ---------------------------------------------------------------------------
+// One workgroup (4 wavefronts) owns a BM x BN_OUT output tile.  The K loop
+// runs over BK = 64 slices held in an LDS ring of STAGES slices; each slice
+// holds the BM rows of A followed by the BNB rows of B, 128 bytes per row.
+// Slices are filled by direct global -> LDS loads (global_load_lds_dwordx4:
+// 16 bytes per lane, no staging registers), so STAGES - 1 slices are in
+// flight while one is consumed.  Each load instruction of a wavefront fills
+// 1 KB = 8 consecutive LDS rows; a lane picks the global 16-byte chunk that
+// must land at its LDS position, which realises the XOR swizzle below.
+//
+// LDS row r, 16-byte chunk c is stored at r * 128 + ((c ^ ((r >> 1) & 7)) * 16):
+// the 16 lanes of one 256-byte LDS phase (16 rows, one chunk, two rows per
+// bank line) then hit 16 different bank groups on fragment reads.
 constexpr int kThreads = 256;   // 4 wavefronts
+constexpr int kBK = 64;
 
-// LDS tile of R rows x BK bf16 (BK = 64: 8 chunks of 16 B per row).  The chunk
-// index is XOR-swizzled with (row / 2) so that the 16 lanes of one 256-byte
-// LDS access phase hit 16 different bank groups for both the fragment reads
-// (lanes walk rows) and the tile writes (lanes walk chunks of two rows).
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-template <int BM, int BNB, int WM, int WN, bool GATEUP, bool OUT_F32>
-struct GemmCfg {
-  static constexpr int BK = 64;
-  static constexpr int WTM = BM / WM;                     // rows per wave
-  static constexpr int TM = WTM / 32;                     // 32-row MFMA tiles per wave
-  // GATEUP: the B tile holds BNB/2 gate rows then BNB/2 up rows; the output
-  // tile has BNB/2 columns of H.  Otherwise BNB output columns.
-  static constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
-  static constexpr int WTN = BN_OUT / WN;                 // output columns per wave
-  static constexpr int TN = WTN / 32;
-  static constexpr int NB = GATEUP ? 2 : 1;               // B halves per output tile
-  static constexpr int A_VECS = BM * BK / 8 / kThreads;   // 16-byte loads per thread per K tile
-  static constexpr int B_VECS = BNB * BK / 8 / kThreads;
-  static_assert(WM * WN == 4, "four wavefronts");
-  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  static_assert(A_VECS >= 1 && B_VECS >= 1, "tile too small");
-};
+__device__ __forceinline__ int swz_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence: a fence would wait for every
+// outstanding LDS DMA, including the slices still meant to be in flight.
+// The empty asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int BM, int BNB, int WM, int WN, bool GATEUP, bool OUT_F32>
+// SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false>
+struct Cfg {
+  static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr bool GATEUP = GATEUP_, OUT_F32 = OUT_F32_, EXPERT_BLOCKED = EB_;
+  static constexpr int WTM = BM / WM;                     // rows per wavefront
+  static constexpr int TM = WTM / 32;                     // 32-row MFMA tiles per wavefront
+  // GATEUP: B holds BNB/2 gate rows then BNB/2 up rows and the output tile has
+  // BNB/2 columns of H.  Otherwise BNB output columns.
+  static constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
+  static constexpr int WTN = BN_OUT / WN;                 // output columns per wavefront
+  static constexpr int TN = WTN / 32;
+  static constexpr int NB = GATEUP ? 2 : 1;
+  static constexpr int ROWS = BM + BNB;                   // LDS rows per slice
+  static constexpr int SLICE = ROWS * kBK;                // bf16 elements per slice
+  static constexpr int LOADS = ROWS / 8 / 4;              // load instructions per wavefront per slice
+  static_assert(WM * WN == 4, "four wavefronts");
+  static_assert(TM >= 1 && TN >= 1, "wavefront tile too small");
+  static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
+};
+
+// Issue the loads of one K slice into an LDS stage.  Load i of a wavefront
+// reads from a wave-uniform base (A, or the expert's gate / up / down
+// matrix) plus a per-lane 32-bit element offset; ko is the slice's K offset.
+template <class C>
+__device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* base, const uint32_t* off,
+                                            uint32_t ko, int wave) {
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + ko)),
+                                     (lds_ptr_t)(stage + (wave * C::LOADS + i) * 512), 16, 0, 0);
+}
+
+// Consume one K slice.  Fragments are software-pipelined: the LDS read of the
+// next B fragment (and, at the last group of a k-step, of the next k-step's A
+// fragments) is issued before the MFMA group that uses the current one, so
+// LDS latency hides behind matrix-core work.  sched_barrier keeps the
+// compiler from regrouping the reads behind the MFMAs.
+template <class C>
+__device__ __forceinline__ void compute_slice(const bf16_t* stage, f32x16 (&acc)[C::NB][C::TM][C::TN], int wm,
+                                              int wn, int lane) {
+  constexpr int KS = kBK / 16;                 // MFMA k-steps per slice
+  constexpr int NF = C::NB * C::TN;            // B fragments per k-step
+  const int lr = lane % 32, lk = lane / 32;
+  const char* sbase = reinterpret_cast<const char*>(stage);
+  auto a_frag = [&](int kk, int i) {
+    return *reinterpret_cast<const bf16x8*>(sbase + swz_off(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
+  };
+  auto b_frag = [&](int kk, int f) {
+    const int h = f / C::TN, j = f % C::TN;
+    const int brow = C::BM + h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
+    return *reinterpret_cast<const bf16x8*>(sbase + swz_off(brow, kk * 2 + lk));
+  };
+  bf16x8 a_cur[C::TM], a_nxt[C::TM];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) a_cur[i] = a_frag(0, i);
+  bf16x8 b_cur = b_frag(0, 0), b_nxt;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + 1 < NF) {
+        b_nxt = b_frag(kk, f + 1);
+      } else if (kk + 1 < KS) {
+        b_nxt = b_frag(kk + 1, 0);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) a_nxt[i] = a_frag(kk + 1, i);
+      }
+      const int h = f / C::TN, j = f % C::TN;
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i], b_cur, acc[h][i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      b_cur = b_nxt;
+    }
+    if (kk + 1 < KS) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) a_cur[i] = a_nxt[i];
+    }
+  }
+}
+
+template <class C>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    void* __restrict__ C, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
-  using Cfg = GemmCfg<BM, BNB, WM, WN, GATEUP, OUT_F32>;
-  constexpr int BK = Cfg::BK;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BNB * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
   if (blockIdx.x >= total) return;
   const uint32_t logical = xcd_remap(blockIdx.x, total);
-  const int mt = static_cast<int>(logical / n_tiles_n);
-  const int nt = static_cast<int>(logical % n_tiles_n);
+  int mt, nt;
+  if (C::EXPERT_BLOCKED) {
+    // all N-tiles of one expert form a block; inside it the M-tiles of one
+    // N-tile are adjacent, so they run together and share that weight slice
+    const TileEntry tq = tiles[logical / n_tiles_n];
+    const int local = static_cast<int>(logical) - tq.first * n_tiles_n;
+    nt = local / tq.ntile;
+    mt = tq.first + local % tq.ntile;
+  } else {
+    mt = static_cast<int>(logical / n_tiles_n);
+    nt = static_cast<int>(logical % n_tiles_n);
+  }
   const TileEntry te = tiles[mt];
   const int64_t e = te.expert;
   const int32_t row0 = te.row0, row_end = te.row_end;
-  const int32_t n0 = nt * Cfg::BN_OUT;
+  const int32_t n0 = nt * C::BN_OUT;
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / WN, wn = wave % WN;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // global -> register staging coordinates
-  const bf16_t* a_src[Cfg::A_VECS];
-  bool a_ok[Cfg::A_VECS];
-  int a_lds[Cfg::A_VECS];
+  // Source of every load instruction: LDS row rr of the slice; the lane's
+  // physical chunk p = lane % 8 holds logical chunk p ^ swizzle(rr).  Rows
+  // past the segment (A) or past N (B) read a valid row instead; their
+  // results are never stored.  All offsets fit 32 bits (checked on the host).
+  const bf16_t* base[C::LOADS];
+  uint32_t off[C::LOADS];
+  const bf16_t* Bexp0 = B0 + e * N * static_cast<int64_t>(K);
+  const bf16_t* Bexp1 = C::GATEUP ? B1 + e * N * static_cast<int64_t>(K) : Bexp0;
 #pragma unroll
-  for (int v = 0; v < Cfg::A_VECS; ++v) {
-    const int idx = tid + v * kThreads;
-    const int r = idx / 8, c = idx % 8;
-    const int32_t row = row0 + r;
-    a_ok[v] = row < row_end;
-    a_src[v] = A + static_cast<int64_t>(a_ok[v] ? row : row0) * K + c * 8;
-    a_lds[v] = lds_off(r, c);
-  }
-  const bf16_t* b_src[Cfg::B_VECS];
-  int b_lds[Cfg::B_VECS];
-#pragma unroll
-  for (int v = 0; v < Cfg::B_VECS; ++v) {
-    const int idx = tid + v * kThreads;
-    const int r = idx / 8, c = idx % 8;
-    const bf16_t* base;
-    int n;
-    if (GATEUP) {
-      const bool up = r >= BNB / 2;
-      base = up ? B1 : B0;
-      n = n0 + (up ? r - BNB / 2 : r);
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int blk = wave * C::LOADS + i;                   // 8-row block (wave-uniform)
+    const int rr = blk * 8 + lane / 8;
+    const int c = (lane % 8) ^ ((rr >> 1) & 7);
+    if (blk * 8 < C::BM) {
+      int32_t row = row0 + rr;
+      row = row < row_end ? row : row_end - 1;
+      base[i] = A;
+      off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + c * 8;
     } else {
-      base = B0;
-      n = n0 + r;
+      const int r = rr - C::BM;
+      const bool up = C::GATEUP && r >= C::BNB / 2;
+      int n = n0 + (up ? r - C::BNB / 2 : r);
+      n = n < N ? n : N - 1;
+      base[i] = up ? Bexp1 : Bexp0;
+      off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8;
     }
-    b_src[v] = base + (e * N + n) * static_cast<int64_t>(K) + c * 8;
-    b_lds[v] = lds_off(r, c);
   }
 
-  f32x16 acc[Cfg::NB][Cfg::TM][Cfg::TN];
+  f32x16 acc[C::NB][C::TM][C::TN];
 #pragma unroll
-  for (int h = 0; h < Cfg::NB; ++h)
+  for (int h = 0; h < C::NB; ++h)
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
+      for (int j = 0; j < C::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
 
-  uint4 ra[Cfg::A_VECS], rb[Cfg::B_VECS];
-  auto gload = [&](int kt) {
-    const int64_t ko = static_cast<int64_t>(kt) * BK;
+  // K loop over an LDS ring of STAGES slices: wait for slice kt (the loads of
+  // the STAGES - 2 younger slices may stay in flight), barrier (every wave's
+  // part of slice kt has landed and everyone is done with slice kt - 1),
+  // refill the freed stage with slice kt + STAGES - 1, consume slice kt.
+  const int KT = K / kBK;
 #pragma unroll
-    for (int v = 0; v < Cfg::A_VECS; ++v)
-      ra[v] = a_ok[v] ? *reinterpret_cast<const uint4*>(a_src[v] + ko) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < Cfg::B_VECS; ++v) rb[v] = *reinterpret_cast<const uint4*>(b_src[v] + ko);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < Cfg::A_VECS; ++v) *reinterpret_cast<uint4*>(&As[buf][a_lds[v]]) = ra[v];
-#pragma unroll
-    for (int v = 0; v < Cfg::B_VECS; ++v) *reinterpret_cast<uint4*>(&Bs[buf][b_lds[v]]) = rb[v];
-  };
-
-  const int KT = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const int lr = lane % 32, lk = lane / 32;
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < KT) issue_slice<C>(ring + s * C::SLICE, base, off, static_cast<uint32_t>(s * kBK), wave);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int chunk = kk * 2 + lk;
-      bf16x8 af[Cfg::TM];
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][lds_off(wm * Cfg::WTM + i * 32 + lr, chunk)]);
-#pragma unroll
-      for (int h = 0; h < Cfg::NB; ++h) {
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j) {
-          const int brow = h * (BNB / 2) + wn * Cfg::WTN + j * 32 + lr;
-          const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(&Bs[buf][lds_off(brow, chunk)]);
-#pragma unroll
-          for (int i = 0; i < Cfg::TM; ++i)
-            acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[h][i][j], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
+    if (kt + C::STAGES - 2 < KT)
+      wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
+    else
+      wait_vmcnt<0>();
+    barrier_nofence();
+    const int nk = kt + C::STAGES - 1;
+    if (nk < KT) issue_slice<C>(ring + (nk % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(nk * kBK), wave);
+    compute_slice<C>(ring + (kt % C::STAGES) * C::SLICE, acc, wm, wn, lane);
   }
 
   // epilogue: acc[q] holds C[m = 8*(q/4) + 4*(lane/32) + q%4][n = lane%32]
+  const int lr = lane % 32, lk = lane / 32;
+  const bool full_rows = row0 + C::BM <= row_end;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
+  for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
-      const int col = n0 + wn * Cfg::WTN + j * 32 + lr;
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = n0 + wn * C::WTN + j * 32 + lr;
+      if (col >= N) continue;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int32_t row = row0 + wm * Cfg::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-        if (row >= row_end) continue;
+        const int32_t row = row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+        if (!full_rows && row >= row_end) continue;
         const int64_t o = static_cast<int64_t>(row) * N + col;
-        if (GATEUP) {
-          const float h = silu_f32(acc[0][i][j][q]) * acc[Cfg::NB - 1][i][j][q];
-          static_cast<bf16_t*>(C)[o] = f32_to_bf16(h);
-        } else if (OUT_F32) {
-          static_cast<float*>(C)[o] = acc[0][i][j][q];
+        if (C::GATEUP) {
+          const float h = silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q];
+          static_cast<bf16_t*>(Cout)[o] = f32_to_bf16(h);
+        } else if (C::OUT_F32) {
+          static_cast<float*>(Cout)[o] = acc[0][i][j][q];
         } else {
-          static_cast<bf16_t*>(C)[o] = f32_to_bf16(acc[0][i][j][q]);
+          static_cast<bf16_t*>(Cout)[o] = f32_to_bf16(acc[0][i][j][q]);
         }
       }
     }
@@ -309,9 +384,40 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int kBM = 128;                  // rows per M-tile, bf16 path
-constexpr int kGU_BNB = 128;              // gate/up B rows per tile (64 gate + 64 up) -> 64 H columns
-constexpr int kDN_BNB = 128;              // down output columns per tile
+// Three tile shapes, chosen from the mean rows per expert (rows / E), which the
+// host knows without reading the device counts:
+//   large  (mean >= 768 rows): 256 x 256 tiles, 2-slice ring (128 KB LDS) --
+//          long MFMA-bound segments (static receiver arrays);
+//   medium (mean >= 48 rows):  128 x 256 tiles, 3-slice ring (144 KB) --
+//          prefill-like batches, weight streaming with two slices in flight;
+//   small  (otherwise):        32 x 256 tiles, 4-slice ring (144 KB) --
+//          decode-like segments of a few rows, pure weight streaming.
+// Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
+// hold 256 output columns.
+using CfgLgGU = Cfg<256, 256, 2, 2, 2, true, false>;
+using CfgLgDF = Cfg<256, 256, 2, 2, 2, false, true>;
+using CfgLgDB = Cfg<256, 256, 2, 2, 2, false, false>;
+using CfgMdGU = Cfg<128, 256, 2, 2, 3, true, false>;
+using CfgMdDF = Cfg<128, 256, 2, 2, 3, false, true>;
+using CfgMdDB = Cfg<128, 256, 2, 2, 3, false, false>;
+using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
+using CfgSmDF = Cfg<32, 256, 1, 4, 4, false, true>;
+using CfgSmDB = Cfg<32, 256, 1, 4, 4, false, false>;
+
+enum TileKind { kLarge = 0, kMedium = 1, kSmall = 2 };
+
+inline TileKind pick_tiles(int64_t rows, int32_t E) {
+  const int64_t mean = rows / E;
+  return mean >= 768 ? kLarge : (mean >= 48 ? kMedium : kSmall);
+}
+
+inline int32_t tile_bm(int32_t dtype, TileKind t) {
+  if (dtype == MOE_F32) return kF32BM;
+  return t == kLarge ? CfgLgGU::BM : (t == kMedium ? CfgMdGU::BM : CfgSmGU::BM);
+}
+static_assert(CfgLgGU::BM == CfgLgDF::BM && CfgLgGU::BM == CfgLgDB::BM, "one M tiling per kind");
+static_assert(CfgMdGU::BM == CfgMdDF::BM && CfgMdGU::BM == CfgMdDB::BM, "one M tiling per kind");
+static_assert(CfgSmGU::BM == CfgSmDF::BM && CfgSmGU::BM == CfgSmDB::BM, "one M tiling per kind");
 
 struct WsLayout {
   size_t h_off, h_bytes, tiles_off, ntiles_off, total;
@@ -320,7 +426,7 @@ struct WsLayout {
 
 inline WsLayout ws_layout(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype) {
   WsLayout w;
-  w.bm = dtype == MOE_F32 ? kF32BM : kBM;
+  w.bm = tile_bm(dtype, pick_tiles(rows, E));
   const size_t elt = dtype == MOE_F32 ? 4 : 2;
   w.max_tiles = static_cast<int32_t>((rows + w.bm - 1) / w.bm + E);
   w.h_off = 0;
@@ -329,6 +435,29 @@ inline WsLayout ws_layout(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype) 
   w.ntiles_off = w.tiles_off + align_up(static_cast<size_t>(w.max_tiles) * sizeof(TileEntry), 256);
   w.total = w.ntiles_off + 256;
   return w;
+}
+
+template <class GU, class DF, class DB>
+int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
+                void* z, int32_t z_dtype, const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles,
+                hipStream_t stream) {
+  const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
+  const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
+  MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<GU>), dim3(max_tiles * nt1), dim3(kThreads), 0,
+                     stream, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg),
+                     static_cast<const bf16_t*>(wu), H, d, d_ff, tiles, n_tiles, nt1);
+  MOE_LAUNCH_CHECK();
+  if (z_dtype == MOE_F32)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<DF>), dim3(max_tiles * nt2), dim3(kThreads), 0,
+                       stream, static_cast<const bf16_t*>(H), static_cast<const bf16_t*>(wdn),
+                       static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles, n_tiles, nt2);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<DB>), dim3(max_tiles * nt2), dim3(kThreads), 0,
+                       stream, static_cast<const bf16_t*>(H), static_cast<const bf16_t*>(wdn),
+                       static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles, n_tiles, nt2);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 }  // namespace
@@ -350,8 +479,10 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   MOE_CHECK(dtype == MOE_BF16 || z_dtype == MOE_F32, MOE_EUNSUPPORTED);
   MOE_CHECK(E >= 1 && E <= MOE_MAX_EXPERTS && d >= 1 && d_ff >= 1 && rows >= 0, MOE_EINVAL);
   MOE_CHECK(d % 64 == 0 && d_ff % 64 == 0, MOE_EUNSUPPORTED);
-  if (dtype == MOE_BF16) MOE_CHECK(d % kDN_BNB == 0 && d_ff % (kGU_BNB / 2) == 0, MOE_EUNSUPPORTED);
-  MOE_CHECK(rows <= INT32_MAX - kBM, MOE_EUNSUPPORTED);
+  MOE_CHECK(rows <= INT32_MAX - 256, MOE_EUNSUPPORTED);
+  // element offsets inside x / H and inside one expert's matrices are 32-bit
+  MOE_CHECK(rows * (d > d_ff ? d : d_ff) < (int64_t(1) << 32) &&
+                static_cast<int64_t>(d) * d_ff < (int64_t(1) << 32), MOE_EUNSUPPORTED);
   MOE_CHECK(seg_start && seg_count && w_gate && w_up && w_down, MOE_EINVAL);
   MOE_CHECK(rows == 0 || (x && z), MOE_EINVAL);
   MOE_CHECK((x == nullptr || aligned16(x)) && (z == nullptr || aligned16(z)), MOE_EINVAL);
@@ -380,24 +511,15 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
-
-  const int nt1 = d_ff / (kGU_BNB / 2), nt2 = d / kDN_BNB;
-  MOE_CHECK(static_cast<int64_t>(L.max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
-  const bf16_t* xb = static_cast<const bf16_t*>(x);
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<kBM, kGU_BNB, 2, 2, true, false>),
-                     dim3(L.max_tiles * nt1), dim3(kThreads), 0, stream, xb, static_cast<const bf16_t*>(w_gate),
-                     static_cast<const bf16_t*>(w_up), H, d, d_ff, tiles, n_tiles, nt1);
-  MOE_LAUNCH_CHECK();
-  if (z_dtype == MOE_F32)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<kBM, kDN_BNB, 2, 2, false, true>),
-                       dim3(L.max_tiles * nt2), dim3(kThreads), 0, stream, static_cast<const bf16_t*>(H),
-                       static_cast<const bf16_t*>(w_down), static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles,
-                       n_tiles, nt2);
-  else
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<kBM, kDN_BNB, 2, 2, false, false>),
-                       dim3(L.max_tiles * nt2), dim3(kThreads), 0, stream, static_cast<const bf16_t*>(H),
-                       static_cast<const bf16_t*>(w_down), static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles,
-                       n_tiles, nt2);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  switch (pick_tiles(rows, E)) {
+    case kLarge:
+      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+                                                    L.max_tiles, stream);
+    case kMedium:
+      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+                                                    L.max_tiles, stream);
+    default:
+      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+                                                    L.max_tiles, stream);
+  }
 }

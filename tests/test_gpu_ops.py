@@ -111,6 +111,8 @@ def _segments(rng, E, rows, mode):
     (5, 700, 128, 192, "bf16", "bf16", "packed"),
     (16, 300, 384, 64, "bf16", "bf16", "packed"),
     (3, 1, 128, 64, "bf16", "f32", "packed"),
+    (2, 2100, 128, 128, "bf16", "f32", "static"),       # >= 768 rows per expert: 256-row tiles
+    (3, 2400, 192, 256, "bf16", "bf16", "packed"),
 ])
 def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     rng = np.random.default_rng(rows + E)
