@@ -24,6 +24,8 @@
 //
 // The fp32 variant (dtype MOE_F32) runs the same three steps with an LDS-tiled
 // FMA kernel in fp32.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -288,25 +290,190 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
 
   // epilogue: acc[q] holds C[m = 8*(q/4) + 4*(lane/32) + q%4][n = lane%32]
   const int lr = lane % 32, lk = lane / 32;
-  const bool full_rows = row0 + C::BM <= row_end;
+  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+  constexpr int OUT_ROW = C::BN_OUT * static_cast<int>(sizeof(OutT));          // bytes per tile row
+  constexpr bool STAGED = C::BM * OUT_ROW <= C::STAGES * C::SLICE * 2;         // tile fits the ring
+  auto value = [&](int i, int j, int q) -> OutT {
+    if constexpr (C::GATEUP) {
+      return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
+    } else if constexpr (C::OUT_F32) {
+      return acc[0][i][j][q];
+    } else {
+      return f32_to_bf16(acc[0][i][j][q]);
+    }
+  };
+  if constexpr (STAGED) {
+    // Transpose through LDS: every wave writes its fragments into a row-major
+    // BM x BN_OUT tile, then all threads store whole rows with 16-byte writes.
+    char* tile = reinterpret_cast<char*>(ring);
+    barrier_nofence();                                   // every wave is done reading the ring
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int col = n0 + wn * C::WTN + j * 32 + lr;
-      if (col >= N) continue;
+      for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int32_t row = row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-        if (!full_rows && row >= row_end) continue;
-        const int64_t o = static_cast<int64_t>(row) * N + col;
-        if (C::GATEUP) {
-          const float h = silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q];
-          static_cast<bf16_t*>(Cout)[o] = f32_to_bf16(h);
-        } else if (C::OUT_F32) {
-          static_cast<float*>(Cout)[o] = acc[0][i][j][q];
-        } else {
-          static_cast<bf16_t*>(Cout)[o] = f32_to_bf16(acc[0][i][j][q]);
+        for (int q = 0; q < 16; ++q) {
+          const int r = wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+          const int cc = wn * C::WTN + j * 32 + lr;
+          *reinterpret_cast<OutT*>(tile + r * OUT_ROW + cc * sizeof(OutT)) = value(i, j, q);
+        }
+    __syncthreads();
+    constexpr int VPR = OUT_ROW / 16;                    // 16-byte vectors per tile row
+    const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
+    const int cols_here = N - n0 < C::BN_OUT ? N - n0 : C::BN_OUT;
+    const int vec_cols = cols_here * static_cast<int>(sizeof(OutT)) / 16;   // N is a multiple of 64
+    for (int v = threadIdx.x; v < C::BM * VPR; v += kThreads) {
+      const int r = v / VPR, cv = v % VPR;
+      if (r >= rows_here || cv >= vec_cols) continue;
+      const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
+      char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(row0 + r) * N + n0) * sizeof(OutT) + cv * 16;
+      *reinterpret_cast<vec16*>(dst) = val;
+    }
+  } else {
+    const bool full_rows = row0 + C::BM <= row_end;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int col = n0 + wn * C::WTN + j * 32 + lr;
+        if (col >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int32_t row = row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+          if (!full_rows && row >= row_end) continue;
+          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = value(i, j, q);
+        }
+      }
+    }
+  }
+}
+
+// Dynamic wait for the oldest in-flight slice: `after` younger slices (0 ..
+// STAGES-2) may stay in flight.
+template <class C, int N = C::STAGES - 2>
+__device__ __forceinline__ void wait_slice(int after) {
+  if constexpr (N <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= N)
+      wait_vmcnt<N * C::LOADS>();
+    else
+      wait_slice<C, N - 1>(after);
+  }
+}
+
+// Persistent form: gridDim.x workgroups walk the tile list with a static
+// stride (round r takes tiles r*G + remap(b)), and the K-slice ring runs on
+// across tile boundaries: the first slices of the next tile are already in
+// flight while the current tile finishes and writes its outputs (direct
+// stores), so neither the pipeline fill nor the epilogue leaves the CU idle.
+template <class C>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_persistent(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
+  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+
+  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
+  const uint32_t G = gridDim.x;
+  const uint32_t slot = xcd_remap(blockIdx.x, G);
+  if (slot >= total) return;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int KT = K / kBK;
+
+  struct Coords { int64_t e; int32_t row0, row_end, n0; };
+  auto coords = [&](uint32_t logical) {
+    const int mt = static_cast<int>(logical / n_tiles_n), nt = static_cast<int>(logical % n_tiles_n);
+    const TileEntry te = tiles[mt];
+    return Coords{te.expert, te.row0, te.row_end, nt * C::BN_OUT};
+  };
+
+  // loader state: tile being loaded and its per-lane sources
+  const bf16_t* base[C::LOADS];
+  uint32_t off[C::LOADS];
+  auto set_sources = [&](const Coords& t) {
+    const bf16_t* Bexp0 = B0 + t.e * N * static_cast<int64_t>(K);
+    const bf16_t* Bexp1 = C::GATEUP ? B1 + t.e * N * static_cast<int64_t>(K) : Bexp0;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int blk = wave * C::LOADS + i;
+      const int rr = blk * 8 + lane / 8;
+      const int c = (lane % 8) ^ ((rr >> 1) & 7);
+      if (blk * 8 < C::BM) {
+        int32_t row = t.row0 + rr;
+        row = row < t.row_end ? row : t.row_end - 1;
+        base[i] = A;
+        off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + c * 8;
+      } else {
+        const int r = rr - C::BM;
+        const bool up = C::GATEUP && r >= C::BNB / 2;
+        int n = t.n0 + (up ? r - C::BNB / 2 : r);
+        n = n < N ? n : N - 1;
+        base[i] = up ? Bexp1 : Bexp0;
+        off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8;
+      }
+    }
+  };
+  uint32_t ld_tile = slot;
+  int ld_k = 0;
+  bool ld_live = true;
+  set_sources(coords(ld_tile));
+  int issued = 0, consumed = 0;
+  auto issue_next = [&]() {
+    if (!ld_live) return;
+    issue_slice<C>(ring + (issued % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(ld_k * kBK), wave);
+    ++issued;
+    if (++ld_k == KT) {
+      ld_k = 0;
+      ld_tile += G;
+      ld_live = ld_tile < total;
+      if (ld_live) set_sources(coords(ld_tile));
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s) issue_next();
+
+  f32x16 acc[C::NB][C::TM][C::TN];
+  const int lr = lane % 32, lk = lane / 32;
+  for (uint32_t tile = slot; tile < total; tile += G) {
+    const Coords t = coords(tile);
+#pragma unroll
+    for (int h = 0; h < C::NB; ++h)
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_slice<C>(issued - consumed - 1);
+      barrier_nofence();
+      issue_next();
+      compute_slice<C>(ring + (consumed % C::STAGES) * C::SLICE, acc, wm, wn, lane);
+      ++consumed;
+    }
+    const bool full_rows = t.row0 + C::BM <= t.row_end;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int col = t.n0 + wn * C::WTN + j * 32 + lr;
+        if (col >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int32_t row = t.row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+          if (!full_rows && row >= t.row_end) continue;
+          OutT v;
+          if constexpr (C::GATEUP)
+            v = f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
+          else if constexpr (C::OUT_F32)
+            v = acc[0][i][j][q];
+          else
+            v = f32_to_bf16(acc[0][i][j][q]);
+          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = v;
         }
       }
     }
@@ -404,6 +571,8 @@ using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
 using CfgSmDF = Cfg<32, 256, 1, 4, 4, false, true>;
 using CfgSmDB = Cfg<32, 256, 1, 4, 4, false, false>;
 
+constexpr bool kPersistLg = false, kPersistMd = false, kPersistSm = true;
+
 enum TileKind { kLarge = 0, kMedium = 1, kSmall = 2 };
 
 inline TileKind pick_tiles(int64_t rows, int32_t E) {
@@ -437,25 +606,49 @@ inline WsLayout ws_layout(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype) 
   return w;
 }
 
-template <class GU, class DF, class DB>
+// Compute units of the current device (cached per device; the library keeps
+// no other state).
+inline int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <class C>
+void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
+                const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream) {
+  const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
+  if (persistent) {
+    const int64_t g = upper < device_cus() ? upper : device_cus();      // one 4-wave workgroup per CU
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
+                       dim3(kThreads), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                       static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
+  } else {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(upper)),
+                       dim3(kThreads), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                       static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
+  }
+}
+
+template <class GU, class DF, class DB, bool PERSIST>
 int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
                 void* z, int32_t z_dtype, const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles,
                 hipStream_t stream) {
   const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
   const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
   MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<GU>), dim3(max_tiles * nt1), dim3(kThreads), 0,
-                     stream, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg),
-                     static_cast<const bf16_t*>(wu), H, d, d_ff, tiles, n_tiles, nt1);
+  launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<DF>), dim3(max_tiles * nt2), dim3(kThreads), 0,
-                       stream, static_cast<const bf16_t*>(H), static_cast<const bf16_t*>(wdn),
-                       static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles, n_tiles, nt2);
+    launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
   else
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<DB>), dim3(max_tiles * nt2), dim3(kThreads), 0,
-                       stream, static_cast<const bf16_t*>(H), static_cast<const bf16_t*>(wdn),
-                       static_cast<const bf16_t*>(nullptr), z, d_ff, d, tiles, n_tiles, nt2);
+    launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -513,13 +706,13 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   }
   switch (pick_tiles(rows, E)) {
     case kLarge:
-      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
                                                     L.max_tiles, stream);
     case kMedium:
-      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
                                                     L.max_tiles, stream);
     default:
-      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
                                                     L.max_tiles, stream);
   }
 }
