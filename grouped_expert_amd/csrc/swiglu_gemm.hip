@@ -89,13 +89,19 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 // LDS row r, 16-byte chunk c is stored at r * 128 + ((c ^ ((r >> 1) & 7)) * 16):
 // the 16 lanes of one 256-byte LDS phase (16 rows, one chunk, two rows per
 // bank line) then hit 16 different bank groups on fragment reads.
-constexpr int kThreads = 256;   // 4 wavefronts
-constexpr int kBK = 64;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-__device__ __forceinline__ int swz_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// Byte offset of logical 16-byte chunk c of LDS row r in a slice whose rows
+// are RB bytes long (RB = 2 * BK): rows sharing a 256-byte bank line are
+// told apart by their position in the line, the XOR separates rows that
+// share a position.
+template <int RB>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  constexpr int RPL = 256 / RB, CPR = RB / 16;
+  return r * RB + ((c ^ ((r / RPL) % CPR)) << 4);
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
 template <int N>
@@ -118,9 +124,17 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 // SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false>
+template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
+          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4>
 struct Cfg {
-  static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int NW = NW_;                          // wavefronts per workgroup
+  static constexpr int THREADS = NW * 64;
+  static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
+  static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
+  static constexpr int OCC = OCC_;                        // workgroups per CU the registers must allow
+  static constexpr int RB = BK * 2;                       // bytes per LDS row
+  static constexpr int CPR = BK / 8;                      // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;                   // rows filled by one wave-wide DMA load
   static constexpr bool GATEUP = GATEUP_, OUT_F32 = OUT_F32_, EXPERT_BLOCKED = EB_;
   static constexpr int WTM = BM / WM;                     // rows per wavefront
   static constexpr int TM = WTM / 32;                     // 32-row MFMA tiles per wavefront
@@ -131,9 +145,11 @@ struct Cfg {
   static constexpr int TN = WTN / 32;
   static constexpr int NB = GATEUP ? 2 : 1;
   static constexpr int ROWS = BM + BNB;                   // LDS rows per slice
-  static constexpr int SLICE = ROWS * kBK;                // bf16 elements per slice
-  static constexpr int LOADS = ROWS / 8 / 4;              // load instructions per wavefront per slice
-  static_assert(WM * WN == 4, "four wavefronts");
+  static constexpr int SLICE = ROWS * BK;                 // bf16 elements per slice
+  static constexpr int LOADS = ROWS / RPI / NW;           // load instructions per wavefront per slice
+  static_assert(BK == 32 || BK == 64, "slice depth");
+  static_assert(ROWS % (RPI * NW) == 0 && BM % RPI == 0 && (BNB / 2) % RPI == 0, "slice rows vs DMA blocks");
+  static_assert(WM * WN == NW, "wavefront grid");
   static_assert(TM >= 1 && TN >= 1, "wavefront tile too small");
   static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
@@ -159,17 +175,17 @@ __device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* 
 template <class C>
 __device__ __forceinline__ void compute_slice(const bf16_t* stage, f32x16 (&acc)[C::NB][C::TM][C::TN], int wm,
                                               int wn, int lane) {
-  constexpr int KS = kBK / 16;                 // MFMA k-steps per slice
+  constexpr int KS = C::BK / 16;               // MFMA k-steps per slice
   constexpr int NF = C::NB * C::TN;            // B fragments per k-step
   const int lr = lane % 32, lk = lane / 32;
   const char* sbase = reinterpret_cast<const char*>(stage);
   auto a_frag = [&](int kk, int i) {
-    return *reinterpret_cast<const bf16x8*>(sbase + swz_off(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
+    return *reinterpret_cast<const bf16x8*>(sbase + swz_off<C::RB>(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
   };
   auto b_frag = [&](int kk, int f) {
     const int h = f / C::TN, j = f % C::TN;
     const int brow = C::BM + h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
-    return *reinterpret_cast<const bf16x8*>(sbase + swz_off(brow, kk * 2 + lk));
+    return *reinterpret_cast<const bf16x8*>(sbase + swz_off<C::RB>(brow, kk * 2 + lk));
   };
   bf16x8 a_cur[C::TM], a_nxt[C::TM];
 #pragma unroll
@@ -201,7 +217,7 @@ __device__ __forceinline__ void compute_slice(const bf16_t* stage, f32x16 (&acc)
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
@@ -218,6 +234,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
     const int local = static_cast<int>(logical) - tq.first * n_tiles_n;
     nt = local / tq.ntile;
     mt = tq.first + local % tq.ntile;
+  } else if (C::GROUP_M > 1) {
+    // bands of GROUP_M M-tiles: inside a band the M-tiles of one N-tile are
+    // adjacent, so the workgroups running together on an XCD share both the
+    // A rows of the band and the weight slices of a few N-tiles
+    const int n_mt = static_cast<int>(total / n_tiles_n);
+    const int band = static_cast<int>(logical) / (C::GROUP_M * n_tiles_n);
+    const int idx = static_cast<int>(logical) - band * C::GROUP_M * n_tiles_n;
+    const int gm = n_mt - band * C::GROUP_M < C::GROUP_M ? n_mt - band * C::GROUP_M : C::GROUP_M;
+    nt = idx / gm;
+    mt = band * C::GROUP_M + idx % gm;
   } else {
     mt = static_cast<int>(logical / n_tiles_n);
     nt = static_cast<int>(logical % n_tiles_n);
@@ -232,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
   const int wm = wave / C::WN, wn = wave % C::WN;
 
   // Source of every load instruction: LDS row rr of the slice; the lane's
-  // physical chunk p = lane % 8 holds logical chunk p ^ swizzle(rr).  Rows
+  // physical chunk p = lane % CPR holds logical chunk p ^ swizzle(rr).  Rows
   // past the segment (A) or past N (B) read a valid row instead; their
   // results are never stored.  All offsets fit 32 bits (checked on the host).
   const bf16_t* base[C::LOADS];
@@ -242,9 +268,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int blk = wave * C::LOADS + i;                   // 8-row block (wave-uniform)
-    const int rr = blk * 8 + lane / 8;
-    const int c = (lane % 8) ^ ((rr >> 1) & 7);
-    if (blk * 8 < C::BM) {
+    const int rr = blk * C::RPI + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
+    if (blk * C::RPI < C::BM) {
       int32_t row = row0 + rr;
       row = row < row_end ? row : row_end - 1;
       base[i] = A;
@@ -273,10 +299,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
   // the STAGES - 2 younger slices may stay in flight), barrier (every wave's
   // part of slice kt has landed and everyone is done with slice kt - 1),
   // refill the freed stage with slice kt + STAGES - 1, consume slice kt.
-  const int KT = K / kBK;
+  const int KT = K / C::BK;
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < KT) issue_slice<C>(ring + s * C::SLICE, base, off, static_cast<uint32_t>(s * kBK), wave);
+    if (s < KT) issue_slice<C>(ring + s * C::SLICE, base, off, static_cast<uint32_t>(s * C::BK), wave);
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + C::STAGES - 2 < KT)
       wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
@@ -284,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
       wait_vmcnt<0>();
     barrier_nofence();
     const int nk = kt + C::STAGES - 1;
-    if (nk < KT) issue_slice<C>(ring + (nk % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(nk * kBK), wave);
+    if (nk < KT) issue_slice<C>(ring + (nk % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(nk * C::BK), wave);
     compute_slice<C>(ring + (kt % C::STAGES) * C::SLICE, acc, wm, wn, lane);
   }
 
@@ -322,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(
     const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
     const int cols_here = N - n0 < C::BN_OUT ? N - n0 : C::BN_OUT;
     const int vec_cols = cols_here * static_cast<int>(sizeof(OutT)) / 16;   // N is a multiple of 64
-    for (int v = threadIdx.x; v < C::BM * VPR; v += kThreads) {
+    for (int v = threadIdx.x; v < C::BM * VPR; v += C::THREADS) {
       const int r = v / VPR, cv = v % VPR;
       if (r >= rows_here || cv >= vec_cols) continue;
       const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
@@ -368,7 +394,7 @@ __device__ __forceinline__ void wait_slice(int after) {
 // flight while the current tile finishes and writes its outputs (direct
 // stores), so neither the pipeline fill nor the epilogue leaves the CU idle.
 template <class C>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_persistent(
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
@@ -382,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_persistent(
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int KT = K / kBK;
+  const int KT = K / C::BK;
 
   struct Coords { int64_t e; int32_t row0, row_end, n0; };
   auto coords = [&](uint32_t logical) {
@@ -400,9 +426,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_persistent(
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int blk = wave * C::LOADS + i;
-      const int rr = blk * 8 + lane / 8;
-      const int c = (lane % 8) ^ ((rr >> 1) & 7);
-      if (blk * 8 < C::BM) {
+      const int rr = blk * C::RPI + lane / C::CPR;
+      const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
+      if (blk * C::RPI < C::BM) {
         int32_t row = t.row0 + rr;
         row = row < t.row_end ? row : t.row_end - 1;
         base[i] = A;
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_persistent(
   int issued = 0, consumed = 0;
   auto issue_next = [&]() {
     if (!ld_live) return;
-    issue_slice<C>(ring + (issued % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(ld_k * kBK), wave);
+    issue_slice<C>(ring + (issued % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(ld_k * C::BK), wave);
     ++issued;
     if (++ld_k == KT) {
       ld_k = 0;
@@ -553,20 +579,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // ---------------------------------------------------------------------------
 // Three tile shapes, chosen from the mean rows per expert (rows / E), which the
 // host knows without reading the device counts:
-//   large  (mean >= 768 rows): 256 x 256 tiles, 2-slice ring (128 KB LDS) --
-//          long MFMA-bound segments (static receiver arrays);
-//   medium (mean >= 48 rows):  128 x 256 tiles, 3-slice ring (144 KB) --
-//          prefill-like batches, weight streaming with two slices in flight;
-//   small  (otherwise):        32 x 256 tiles, 4-slice ring (144 KB) --
-//          decode-like segments of a few rows, pure weight streaming.
+//   large  (mean >= 768 rows): 256 x 256 tiles, 8 wavefronts (two per SIMD, so
+//          one wave's MFMAs cover the other's waits), 2-slice ring (128 KB),
+//          bands of 4 M-tiles for L2 reuse -- long MFMA-bound segments
+//          (static receiver arrays);
+//   medium (mean >= 48 rows):  128 x 256 tiles, 8 wavefronts, 3-slice ring
+//          (144 KB), bands of 2 M-tiles -- prefill-like weight streaming;
+//   small  (otherwise):        32 x 256 tiles, 4 wavefronts, 4-slice ring
+//          (144 KB), persistent -- decode-like segments of a few rows.
 // Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
 // hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 2, 2, 2, true, false>;
-using CfgLgDF = Cfg<256, 256, 2, 2, 2, false, true>;
-using CfgLgDB = Cfg<256, 256, 2, 2, 2, false, false>;
-using CfgMdGU = Cfg<128, 256, 2, 2, 3, true, false>;
-using CfgMdDF = Cfg<128, 256, 2, 2, 3, false, true>;
-using CfgMdDB = Cfg<128, 256, 2, 2, 3, false, false>;
+using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8>;
+using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8>;
+using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8>;
+using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
+using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
+using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
 using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
 using CfgSmDF = Cfg<32, 256, 1, 4, 4, false, true>;
 using CfgSmDB = Cfg<32, 256, 1, 4, 4, false, false>;
@@ -627,11 +655,11 @@ void launch_one(bool persistent, const void* a, const void* b0, const void* b1, 
   if (persistent) {
     const int64_t g = upper < device_cus() ? upper : device_cus();      // one 4-wave workgroup per CU
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
-                       dim3(kThreads), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                       dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
   } else {
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(upper)),
-                       dim3(kThreads), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                       dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
   }
 }
