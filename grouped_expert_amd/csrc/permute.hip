@@ -1,5 +1,6 @@
 // Dispatch permutation: expert histogram, exclusive prefix, capacity and
-// stable ranks (shared bucket-rank passes), then the row gather.
+// stable ranks (shared bucket-rank passes), then the row movement (token-major
+// scatter: each token row is read once and written to its accepted slots).
 //
 // "M6.2 - Expert Parallelism and DeepSeek MoE", 0x03B: counts, exclusive
 // prefix with the final sentinel, stable permutation by (expert, route id)
@@ -39,27 +40,48 @@ struct PermuteEmit {
   }
 };
 
-constexpr int kRowsPerBlock = 4;   // one wavefront per packed row
+// One wavefront per token: the token row is read once into registers (up to
+// kPiece x 16 B per lane at a time) and written to each of its accepted
+// slots x_perm[inv[t*k + j]], so x is read once instead of k times.  Every
+// thread also clears one entry of the tail src[A .. R) (the grid has 64T >= R
+// threads), which the bucket-rank passes leave unwritten.
+constexpr int kTokPerBlock = 4;
+constexpr int kPiece = 8;
 
-// x_perm[p] = x[src[p] / k] for p < A; src[p] = -1 for A <= p < R.
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void gather_rows_kernel(
-    const vec16* __restrict__ x, int64_t row_vecs, int32_t k, int64_t R, const int32_t* __restrict__ accepted,
-    int32_t* __restrict__ src, vec16* __restrict__ x_perm) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
-  if (p >= R) return;
+__global__ __launch_bounds__(kTokPerBlock * kWave) void scatter_rows_kernel(
+    const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ inv, int32_t* __restrict__ src, vec16* __restrict__ x_perm) {
+  const int64_t R = T * k;
   const int32_t A = *accepted;
-  if (p >= A) {
-    if (lane == 0) src[p] = -1;
-    return;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (A + gid < R) src[A + gid] = -1;
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T || !x_perm) return;
+  int32_t slot[MOE_MAX_TOPK];
+  int live = 0;
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = inv[t * k + j];
+    if (p >= 0 && p < A) slot[live++] = p;
   }
-  if (!x_perm) return;
-  const int32_t r = src[p];
-  if (r < 0 || r >= R) return;
-  const int64_t t = r / k;
+  if (live == 0) return;
   const vec16* in = x + t * row_vecs;
-  vec16* out = x_perm + p * row_vecs;
-  for (int64_t c = lane; c < row_vecs; c += kWave) out[c] = in[c];
+  for (int64_t c0 = 0; c0 < row_vecs; c0 += kPiece * kWave) {
+    vec16 v[kPiece];
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t c = c0 + u * kWave + lane;
+      if (c < row_vecs) v[u] = ld_stream(in + c);
+    }
+    for (int j = 0; j < live; ++j) {
+      vec16* out = x_perm + static_cast<int64_t>(slot[j]) * row_vecs;
+#pragma unroll
+      for (int u = 0; u < kPiece; ++u) {
+        const int64_t c = c0 + u * kWave + lane;
+        if (c < row_vecs) out[c] = v[u];
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -97,9 +119,10 @@ MOE_API int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d, co
   if (st != MOE_OK) return st;
   if (R > 0) {
     const int64_t row_vecs = x_perm ? static_cast<int64_t>(d) * elt / 16 : 0;
-    const unsigned blocks = static_cast<unsigned>((R + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
-                       static_cast<const vec16*>(x), row_vecs, k, R, offsets + E, src, static_cast<vec16*>(x_perm));
+    const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream,
+                       static_cast<const vec16*>(x), T, row_vecs, k, offsets + E, inv, src,
+                       static_cast<vec16*>(x_perm));
     MOE_LAUNCH_CHECK();
   }
   return MOE_OK;
