@@ -41,6 +41,10 @@ F32_PEAK_TFLOPS = 157.3        # fp32 vector
 COPY_CALIB_BYTES = 256 << 20   # size of the calibration copy (read and written once)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC_DIR = os.path.join(ROOT, "grouped_expert_amd", "csrc")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -50,7 +54,125 @@ def parse():
     ap.add_argument("--banks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens/rows of the CPU oracle sample (0 = auto)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: read the counter CSVs of two rocprofv3 --pmc runs of this script "
+                         "(FETCH_SIZE, then WRITE_SIZE) for --workload and record HBM bytes per call in "
+                         "profiles/hbm_traffic.json")
+    ap.add_argument("--pmc-command", default="", help="with --record-traffic: the profiling command, stored "
+                                                      "beside the figures")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from hardware counters
+# ---------------------------------------------------------------------------
+
+# kernel sources of each call (plus the shared header and the C ABI)
+_CALL_SOURCES = {"route": ["route_topk.hip"], "permute": ["permute.hip", "bucket_rank.h"],
+                 "swiglu": ["swiglu_gemm.hip"], "combine": ["combine.hip"], "expand": ["combine.hip"],
+                 "pool_pack": ["pool_pack.hip", "bucket_rank.h"],
+                 "recv_compact": ["recv_compact.hip", "bucket_rank.h"]}
+
+
+def sources_digest(call):
+    """sha256 over the kernel sources of one call; recorded traffic is used
+    only while the sources it was measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    paths = [os.path.join(CSRC_DIR, n) for n in _CALL_SOURCES[call] + ["common.h"]]
+    paths.append(os.path.join(ROOT, "include", "moe.h"))
+    for path in paths:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _call_of(kernel, kind):
+    """The library call a dispatched kernel belongs to (None: not ours).
+    Bucket-rank kernels are shared by three calls and are given to the call
+    of the next dispatch, by the caller of this function."""
+    table = (("route_topk_kernel", "route"), ("build_tiles_kernel", "swiglu"), ("grouped_gemm_", "swiglu"),
+             ("scatter_rows_kernel", "permute"), ("pack_rows_kernel", "pool_pack"),
+             ("pack_fill_kernel", "pool_pack"), ("compact_rows_kernel", "recv_compact"),
+             ("combine_kernel", "expand" if kind == "recv" else "combine"), ("rank_", "rank"))
+    for pat, call in table:
+        if pat in kernel:
+            return call
+    return None
+
+
+# one dispatch per call instance: counts the launches of each call
+_ANCHORS = {"route": "route_topk_kernel", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
+            "combine": "combine_kernel", "expand": "combine_kernel", "pool_pack": "pack_fill_kernel",
+            "recv_compact": "compact_rows_kernel"}
+
+
+def record_traffic(args):
+    import csv
+    w = W.WORKLOADS[args.workload]
+    kind = workload_kind(w)
+    per = {}
+    for counter, d in (("FETCH_SIZE", args.record_traffic[0]), ("WRITE_SIZE", args.record_traffic[1])):
+        rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        names = [r["Kernel_Name"] for r in rows]
+        first_ours = next(i for i, n in enumerate(names) if _call_of(n, kind))
+        # the calibration copy is the last plain device copy before the first library kernel
+        calib = max(i for i in range(first_ours) if "copyBuffer" in names[i])
+        factor = COPY_CALIB_BYTES / (float(rows[calib]["Counter_Value"]) * 1024.0)
+        calls = [_call_of(n, kind) for n in names]
+        nxt = None
+        for i in range(len(calls) - 1, first_ours - 1, -1):    # rank kernels -> call of the next dispatch
+            if calls[i] == "rank":
+                calls[i] = nxt
+            elif calls[i]:
+                nxt = calls[i]
+        kib, launches = {}, {}
+        for i in range(first_ours, len(rows)):
+            c = calls[i]
+            if not c:
+                continue
+            kib[c] = kib.get(c, 0.0) + float(rows[i]["Counter_Value"])
+            if _ANCHORS[c] in names[i]:
+                launches[c] = launches.get(c, 0) + 1
+        per[counter] = dict(factor=factor, bytes={c: kib[c] * 1024.0 * factor / launches[c] for c in kib},
+                            launches=launches)
+    entry = dict(command=args.pmc_command,
+                 calibration=dict(copy_bytes=COPY_CALIB_BYTES, fetch_factor=round(per["FETCH_SIZE"]["factor"], 4),
+                                  write_factor=round(per["WRITE_SIZE"]["factor"], 4)),
+                 calls={c: dict(sources_sha256=sources_digest(c), read_bytes=int(per["FETCH_SIZE"]["bytes"][c]),
+                                write_bytes=int(per["WRITE_SIZE"]["bytes"].get(c, 0.0)),
+                                launches=per["FETCH_SIZE"]["launches"][c])
+                        for c in sorted(per["FETCH_SIZE"]["bytes"])})
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    data[w.name] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({w.name: entry}, indent=1))
+
+
+def recorded_traffic(w, call):
+    """HBM bytes per launch of ``call`` recorded for this workload, or None
+    when nothing is recorded or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f)[w.name]
+    except (OSError, KeyError, ValueError):
+        return None
+    c = entry.get("calls", {}).get(call)
+    if not c or c.get("sources_sha256") != sources_digest(call):
+        return None
+    return c["read_bytes"] + c["write_bytes"]
+
+
+def workload_kind(w):
+    return "recv" if w.name.startswith("recv") else "pack" if w.name.startswith("sender") else "layer"
 
 
 # ---------------------------------------------------------------------------
@@ -184,13 +306,13 @@ def recv_step(ge, timer, w, bank, flags, bufs):
 
 def recv_ledger(w, counts_per_wave):
     S, P, P1, d, dff = w.n_src, w.pool_rows, w.pool_rows + 1, w.d, w.d_ff
-    V = S * P
     led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0),
            "expand": dict(bytes=0, flops=0)}
     for counts in counts_per_wave:
         A = int(counts.sum())
         E_act = int((counts > 0).sum())
-        led["recv_compact"]["bytes"] += S * d * 2 + V * d * 2 + A * d * 2 + 4 * S * P1
+        # header ids, accepted rows read and written (receiver-dropped rows are never read), row_slot
+        led["recv_compact"]["bytes"] += S * P * 2 + 2 * A * d * 2 + 4 * S * P1
         led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * 4
         led["swiglu"]["flops"] += 6 * A * d * dff
         led["expand"]["bytes"] += A * d * 4 + 4 * S * P1 + S * P1 * d * 4
@@ -256,6 +378,9 @@ def pack_cpu_baseline(w, host, sample):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -267,7 +392,7 @@ def main():
     banks = max(1, args.banks)
     torch.cuda.set_device(0)
     flags = ge.new_flags("cuda")
-    kind = ("recv" if w.name.startswith("recv") else "pack" if w.name.startswith("sender") else "layer")
+    kind = workload_kind(w)
     print(f"[bench] workload {w.name}: generating inputs ({banks} bank(s))", file=sys.stderr, flush=True)
     bufs = {}
     if kind == "layer":
@@ -345,12 +470,16 @@ def main():
     bw = per_launch_bytes / t_s / 1e9
     tf = per_launch_flops / t_s / 1e12
     mfma_bound = per_launch_flops / (peak_f * 1e12) > per_launch_bytes / (HBM_PEAK_GBS * 1e9)
+    traffic = recorded_traffic(w, dom)
     if mfma_bound:
         roof = dict(bound="mfma", achieved=round(tf, 2), peak=peak_f, unit="TFLOP/s", frac=round(tf / peak_f, 4),
-                    traffic=None)
+                    traffic=traffic)
     else:
         roof = dict(bound="hbm", achieved=round(bw, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(bw / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(bw / HBM_PEAK_GBS, 4), traffic=traffic)
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    if traffic:
+        roof["traffic_over_alg"] = round(traffic / max(1, per_launch_bytes), 3)
     roof["kernel"] = dom
     roof["launch_ms"] = round(dom_ms, 4)
     roof["alg_bytes_per_launch"] = int(per_launch_bytes)

@@ -1,0 +1,69 @@
+"""Host logic of bench.py that needs no GPU: the one-GPU guard and the
+attribution of counter readings to library calls."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_counters(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for i, (name, kib) in enumerate(rows, start=1):
+            wr.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib})
+
+
+def test_record_traffic_attributes_kernels_to_calls(tmp_path, monkeypatch):
+    calib_kib = bench.COPY_CALIB_BYTES / 1024
+    step = [("void moe::(anonymous namespace)::route_topk_kernel<2>(float const*)", 10.0),
+            ("void moe::(anonymous namespace)::rank_count_kernel<ExpertBucket>(x)", 1.0),
+            ("moe::(anonymous namespace)::rank_scan_kernel(x)", 2.0),
+            ("void moe::(anonymous namespace)::rank_emit_kernel<ExpertBucket, PermuteEmit>(x)", 3.0),
+            ("moe::(anonymous namespace)::scatter_rows_kernel(x)", 100.0),
+            ("moe::(anonymous namespace)::build_tiles_kernel(x)", 0.5),
+            ("void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<Cfg<...> >(x)", 1000.0),
+            ("void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<Cfg<...> >(y)", 500.0),
+            ("void moe::(anonymous namespace)::combine_kernel<unsigned short>(x)", 50.0)]
+    head = [("at::native::FillFunctor", 7.0), ("__amd_rocclr_copyBuffer", 12345.0)]
+    # FETCH_SIZE reads half of the calibration copy, WRITE_SIZE all of it
+    fetch = head + [("__amd_rocclr_copyBuffer", calib_kib / 2)] + step + step
+    write = head + [("__amd_rocclr_copyBuffer", calib_kib)] + [(n, v / 10) for n, v in step] * 2
+    _write_counters(tmp_path / "f", "FETCH_SIZE", fetch)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "mid_bf16", "--record-traffic", str(tmp_path / "f"),
+                                      str(tmp_path / "w")])
+    bench.record_traffic(bench.parse())
+    e = json.load(open(out))["mid_bf16"]
+    assert e["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert e["calibration"]["write_factor"] == pytest.approx(1.0)
+    c = e["calls"]
+    assert c["route"]["read_bytes"] == int(10.0 * 1024 * 2)
+    assert c["permute"]["read_bytes"] == int(106.0 * 1024 * 2)        # rank passes belong to the permute
+    assert c["swiglu"]["read_bytes"] == int(1500.5 * 1024 * 2)
+    assert c["combine"]["write_bytes"] == int(5.0 * 1024)
+    assert all(v["launches"] == 2 for v in c.values())
+    # recorded figures are used only while the sources match
+    w = bench.W.WORKLOADS["mid_bf16"]
+    assert bench.recorded_traffic(w, "swiglu") == int(1500.5 * 1024 * 2) + int(150.05 * 1024)
+    data = json.load(open(out))
+    data["mid_bf16"]["calls"]["swiglu"]["sources_sha256"] = "0" * 64
+    json.dump(data, open(out, "w"))
+    assert bench.recorded_traffic(w, "swiglu") is None
