@@ -125,9 +125,13 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
-          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4>
+          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false>
 struct Cfg {
   static constexpr int NW = NW_;                          // wavefronts per workgroup
+  // RS: the weight (B) rows of a slice travel HBM -> registers -> LDS through
+  // two register stages, so two B slices are in flight with a two-stage LDS
+  // ring; the A rows keep the direct LDS DMA (else: everything by DMA)
+  static constexpr bool RS = RS_;
   static constexpr int THREADS = NW * 64;
   static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
   static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
@@ -153,6 +157,18 @@ struct Cfg {
   static_assert(TM >= 1 && TN >= 1, "wavefront tile too small");
   static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
+  static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
+  // with RS every wavefront issues LA loads of A blocks and LB of B blocks
+  static constexpr int LA = RS ? BM / RPI / NW : LOADS;
+  static constexpr int LB = RS ? BNB / RPI / NW : 0;
+  static_assert(!RS || (BM % (RPI * NW) == 0 && BNB % (RPI * NW) == 0 && LA + LB == LOADS && LB > 0),
+                "register staging splits every wavefront's loads between A and B");
+  static_assert(!RS || !GATEUP || (BNB / 2) % (LB * RPI) == 0,
+                "with register staging all B rows of a wavefront come from one matrix");
+  // 8-row block of the slice filled by load i of wavefront w
+  static __device__ __forceinline__ int block(int w, int i) {
+    return !RS ? w * LOADS + i : (i < LA ? w * LA + i : BM / RPI + w * LB + (i - LA));
+  }
 };
 
 // Issue the loads of one K slice into an LDS stage.  Load i of a wavefront
@@ -164,7 +180,7 @@ __device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* 
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + ko)),
-                                     (lds_ptr_t)(stage + (wave * C::LOADS + i) * 512), 16, 0, 0);
+                                     (lds_ptr_t)(stage + C::block(wave, i) * 512), 16, 0, 0);
 }
 
 // Consume one K slice.  Fragments are software-pipelined: the LDS read of the
@@ -172,20 +188,24 @@ __device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* 
 // fragments) is issued before the MFMA group that uses the current one, so
 // LDS latency hides behind matrix-core work.  sched_barrier keeps the
 // compiler from regrouping the reads behind the MFMAs.
+// A rows of the slice sit at a_stage (row r at r * RB bytes), B rows at
+// b_stage (B row r likewise); the swizzle repeats every 16 rows and BM is a
+// multiple of 16, so both halves use their local row index.
 template <class C>
-__device__ __forceinline__ void compute_slice(const bf16_t* stage, f32x16 (&acc)[C::NB][C::TM][C::TN], int wm,
-                                              int wn, int lane) {
+__device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_t* b_stage,
+                                              f32x16 (&acc)[C::NB][C::TM][C::TN], int wm, int wn, int lane) {
   constexpr int KS = C::BK / 16;               // MFMA k-steps per slice
   constexpr int NF = C::NB * C::TN;            // B fragments per k-step
   const int lr = lane % 32, lk = lane / 32;
-  const char* sbase = reinterpret_cast<const char*>(stage);
+  const char* abase = reinterpret_cast<const char*>(a_stage);
+  const char* bbase = reinterpret_cast<const char*>(b_stage);
   auto a_frag = [&](int kk, int i) {
-    return *reinterpret_cast<const bf16x8*>(sbase + swz_off<C::RB>(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
+    return *reinterpret_cast<const bf16x8*>(abase + swz_off<C::RB>(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
   };
   auto b_frag = [&](int kk, int f) {
     const int h = f / C::TN, j = f % C::TN;
-    const int brow = C::BM + h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
-    return *reinterpret_cast<const bf16x8*>(sbase + swz_off<C::RB>(brow, kk * 2 + lk));
+    const int brow = h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
+    return *reinterpret_cast<const bf16x8*>(bbase + swz_off<C::RB>(brow, kk * 2 + lk));
   };
   bf16x8 a_cur[C::TM], a_nxt[C::TM];
 #pragma unroll
@@ -221,6 +241,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
+  // The K-slice ring.  With register staging the A rows of the two stages
+  // come first and the B rows of the two stages follow.  (One LDS array only:
+  // with several, the compiler tracks the LDS DMA per array and waits for it
+  // before every LDS read of that array.)
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
   const bf16_t* Bexp1 = C::GATEUP ? B1 + e * N * static_cast<int64_t>(K) : Bexp0;
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int blk = wave * C::LOADS + i;                   // 8-row block (wave-uniform)
+    const int blk = C::block(wave, i);                     // 8-row block (wave-uniform)
     const int rr = blk * C::RPI + lane / C::CPR;
     const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
     if (blk * C::RPI < C::BM) {
@@ -295,14 +319,106 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
 
+  auto issue_group = [&](int slice) {
+    issue_slice<C>(ring + (slice % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(slice * C::BK), wave);
+  };
+
   // K loop over an LDS ring of STAGES slices: wait for slice kt (the loads of
   // the STAGES - 2 younger slices may stay in flight), barrier (every wave's
   // part of slice kt has landed and everyone is done with slice kt - 1),
   // refill the freed stage with slice kt + STAGES - 1, consume slice kt.
   const int KT = K / C::BK;
+  if constexpr (C::RS) {
+    // Two-stage LDS ring; A rows by LDS DMA one slice ahead, B rows through
+    // register stages rb0 / rb1: B of slice s is loaded at step s - 3 (or in
+    // the prologue), written to LDS at step s - 1 and consumed at step s, so
+    // during the compute of slice kt the B loads of slices kt + 2 and kt + 3
+    // are in flight.  Step kt: wait for this wave's DMA of slice kt (exactly
+    // the LB loads of B(kt + 2) are younger) and for its LDS writes, then the
+    // barrier publishes slice kt and frees the other stage, which takes the
+    // register copy of B(kt + 1) and the DMA of A(kt + 1).  Loads past the
+    // last slice re-read the last slice into the stage that is free at that
+    // step (never consumed), so every step issues the same instructions and
+    // the compiler's own waits for the register loads stay exact.  Inside a
+    // step the LDS writes come before the DMA (an LDS write behind an
+    // outstanding LDS DMA would make the compiler wait for it) and the DMA
+    // before the B loads (the vmcnt count above).
+    vec16 rb0[C::LB], rb1[C::LB];
+    auto clamp = [&](int slice) { return slice < KT ? slice : KT - 1; };
+    // A rows by LDS DMA.  (The global form: the compiler does not track it
+    // as an LDS write, so it adds no waits of its own before LDS accesses.)
+    auto dma_a = [&](int stage, int slice) {
+      bf16_t* st = ring + stage * (C::BM * C::BK);
+#pragma unroll
+      for (int i = 0; i < C::LA; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + static_cast<uint32_t>(slice * C::BK))),
+                                         (lds_ptr_t)(st + C::block(wave, i) * 512), 16, 0, 0);
+    };
+    // B loads are buffer loads over the wave's weight matrix (all B rows of a
+    // wavefront come from one of gate / up): a per-lane byte offset fixed for
+    // the tile plus the slice's K offset in a scalar register, so no address
+    // arithmetic or 64-bit address registers per slice.  The matrix is
+    // N * K * 2 bytes (< 2^32, checked on the host).
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(base[C::LA]), 0, static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 2u),
+        0x00020000);
+    uint32_t boff[C::LB];
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) boff[i] = off[C::LA + i] * 2u;
+    auto gload_b = [&](vec16 (&r)[C::LB], int slice) {
+#pragma unroll
+      for (int i = 0; i < C::LB; ++i)
+        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, static_cast<int>(boff[i]), slice * C::BK * 2, 0);
+    };
+    bf16_t* const ring_b = ring + 2 * C::BM * C::BK;
+    auto lstore_b = [&](int stage, const vec16 (&r)[C::LB]) {
+      bf16_t* st = ring_b + stage * (C::BNB * C::BK) + lane * 8;
+#pragma unroll
+      for (int i = 0; i < C::LB; ++i)
+        *reinterpret_cast<vec16*>(st + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) = r[i];
+    };
+    auto step_sync = [&]() {
+      wait_vmcnt<C::LB>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
+      barrier_nofence();
+    };
+    const bf16_t* const a0 = ring;
+    const bf16_t* const a1 = ring + C::BM * C::BK;
+    const bf16_t* const b0 = ring_b;
+    const bf16_t* const b1 = ring_b + C::BNB * C::BK;
+    dma_a(0, 0);
+    gload_b(rb0, 0);
+    lstore_b(0, rb0);
+    asm volatile("" ::: "memory");
+    gload_b(rb1, clamp(1));
+    asm volatile("" ::: "memory");           // B(1) strictly older than B(2)
+    gload_b(rb0, clamp(2));
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {             // an even and an odd step; no early exit
+      step_sync();
+      lstore_b(1, rb1);                        // B(kt + 1)
+      asm volatile("" ::: "memory");
+      dma_a(1, kt + 1);
+      asm volatile("" ::: "memory");
+      gload_b(rb1, clamp(kt + 3));
+      compute_slice<C>(a0, b0, acc, wm, wn, lane);
+      step_sync();
+      lstore_b(0, rb0);                        // B(kt + 2), or a repeat past the end
+      asm volatile("" ::: "memory");
+      dma_a(0, clamp(kt + 2));
+      asm volatile("" ::: "memory");
+      gload_b(rb0, clamp(kt + 4));
+      compute_slice<C>(a1, b1, acc, wm, wn, lane);
+    }
+    if (kt < KT) {                             // odd slice count: the last slice is in stage 0
+      step_sync();
+      compute_slice<C>(a0, b0, acc, wm, wn, lane);
+    }
+    wait_vmcnt<0>();                           // no DMA may still land in the ring
+  } else {
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < KT) issue_slice<C>(ring + s * C::SLICE, base, off, static_cast<uint32_t>(s * C::BK), wave);
+    if (s < KT) issue_group(s);
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + C::STAGES - 2 < KT)
       wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
@@ -310,15 +426,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
       wait_vmcnt<0>();
     barrier_nofence();
     const int nk = kt + C::STAGES - 1;
-    if (nk < KT) issue_slice<C>(ring + (nk % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(nk * C::BK), wave);
-    compute_slice<C>(ring + (kt % C::STAGES) * C::SLICE, acc, wm, wn, lane);
+    if (nk < KT) issue_group(nk);
+    compute_slice<C>(ring + (kt % C::STAGES) * C::SLICE, ring + (kt % C::STAGES) * C::SLICE + C::BM * C::BK, acc, wm, wn,
+                     lane);
+  }
   }
 
   // epilogue: acc[q] holds C[m = 8*(q/4) + 4*(lane/32) + q%4][n = lane%32]
   const int lr = lane % 32, lk = lane / 32;
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
   constexpr int OUT_ROW = C::BN_OUT * static_cast<int>(sizeof(OutT));          // bytes per tile row
-  constexpr bool STAGED = C::BM * OUT_ROW <= C::STAGES * C::SLICE * 2;         // tile fits the ring
+  constexpr bool STAGED = C::BM * OUT_ROW <= static_cast<int>(sizeof(ring));  // tile fits the ring
   auto value = [&](int i, int j, int q) -> OutT {
     if constexpr (C::GATEUP) {
       return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
@@ -425,7 +543,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
     const bf16_t* Bexp1 = C::GATEUP ? B1 + t.e * N * static_cast<int64_t>(K) : Bexp0;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int blk = wave * C::LOADS + i;
+      const int blk = C::block(wave, i);
       const int rr = blk * C::RPI + lane / C::CPR;
       const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
       if (blk * C::RPI < C::BM) {
@@ -478,7 +596,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
       wait_slice<C>(issued - consumed - 1);
       barrier_nofence();
       issue_next();
-      compute_slice<C>(ring + (consumed % C::STAGES) * C::SLICE, acc, wm, wn, lane);
+      compute_slice<C>(ring + (consumed % C::STAGES) * C::SLICE, ring + (consumed % C::STAGES) * C::SLICE + C::BM * C::BK,
+                         acc, wm, wn, lane);
       ++consumed;
     }
     const bool full_rows = t.row0 + C::BM <= t.row_end;
@@ -580,18 +699,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // Three tile shapes, chosen from the mean rows per expert (rows / E), which the
 // host knows without reading the device counts:
 //   large  (mean >= 768 rows): 256 x 256 tiles, 8 wavefronts (two per SIMD, so
-//          one wave's MFMAs cover the other's waits), 2-slice ring (128 KB),
-//          bands of 4 M-tiles for L2 reuse -- long MFMA-bound segments
-//          (static receiver arrays);
+//          one wave's MFMAs cover the other's waits), 2-slice ring (128 KB)
+//          with the weight rows register-staged two slices ahead, bands of 4
+//          M-tiles for L2 reuse -- long MFMA-bound segments (static receiver
+//          arrays);
 //   medium (mean >= 48 rows):  128 x 256 tiles, 8 wavefronts, 3-slice ring
 //          (144 KB), bands of 2 M-tiles -- prefill-like weight streaming;
 //   small  (otherwise):        32 x 256 tiles, 4 wavefronts, 4-slice ring
 //          (144 KB), persistent -- decode-like segments of a few rows.
 // Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
 // hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8>;
-using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8>;
-using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8>;
+using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true>;
+using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true>;
+using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true>;
 using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
 using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
 using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
@@ -703,7 +823,7 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   MOE_CHECK(rows <= INT32_MAX - 256, MOE_EUNSUPPORTED);
   // element offsets inside x / H and inside one expert's matrices are 32-bit
   MOE_CHECK(rows * (d > d_ff ? d : d_ff) < (int64_t(1) << 32) &&
-                static_cast<int64_t>(d) * d_ff < (int64_t(1) << 32), MOE_EUNSUPPORTED);
+                static_cast<int64_t>(d) * d_ff * 2 < (int64_t(1) << 32), MOE_EUNSUPPORTED);
   MOE_CHECK(seg_start && seg_count && w_gate && w_up && w_down, MOE_EINVAL);
   MOE_CHECK(rows == 0 || (x && z), MOE_EINVAL);
   MOE_CHECK((x == nullptr || aligned16(x)) && (z == nullptr || aligned16(z)), MOE_EINVAL);

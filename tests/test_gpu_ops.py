@@ -112,7 +112,8 @@ def _segments(rng, E, rows, mode):
     (16, 300, 384, 64, "bf16", "bf16", "packed"),
     (3, 1, 128, 64, "bf16", "f32", "packed"),
     (2, 2100, 128, 128, "bf16", "f32", "static"),       # >= 768 rows per expert: 256-row tiles
-    (3, 2400, 192, 256, "bf16", "bf16", "packed"),
+    (3, 2400, 192, 256, "bf16", "bf16", "packed"),     # 256-row tiles, odd slice count (d / 64 = 3)
+    (2, 1700, 320, 192, "bf16", "f32", "static"),      # 256-row tiles, odd slice counts, partial N-tiles
 ])
 def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     rng = np.random.default_rng(rows + E)
