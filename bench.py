@@ -93,8 +93,8 @@ def _call_of(kernel, kind):
     Bucket-rank kernels are shared by three calls and are given to the call
     of the next dispatch, by the caller of this function."""
     table = (("route_topk_kernel", "route"), ("build_tiles_kernel", "swiglu"), ("grouped_gemm_", "swiglu"),
-             ("scatter_rows_kernel", "permute"), ("pack_rows_kernel", "pool_pack"),
-             ("pack_fill_kernel", "pool_pack"), ("compact_rows_kernel", "recv_compact"),
+             ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
+             ("compact_rows_kernel", "recv_compact"),
              ("combine_kernel", "expand" if kind == "recv" else "combine"), ("rank_", "rank"))
     for pat, call in table:
         if pat in kernel:
@@ -104,7 +104,7 @@ def _call_of(kernel, kind):
 
 # one dispatch per call instance: counts the launches of each call
 _ANCHORS = {"route": "route_topk_kernel", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
-            "combine": "combine_kernel", "expand": "combine_kernel", "pool_pack": "pack_fill_kernel",
+            "combine": "combine_kernel", "expand": "combine_kernel", "pool_pack": "pack_kernel",
             "recv_compact": "compact_rows_kernel"}
 
 

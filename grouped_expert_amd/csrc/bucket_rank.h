@@ -10,6 +10,10 @@
 // This is the count / exclusive prefix / stable permutation of "M6.2 -
 // Expert Parallelism and DeepSeek MoE", 0x03B, with the capacity of 0x01C.
 //
+// A Bucket functor has load(i) -> raw 32-bit value of item i (no side
+// effects) and classify(raw, flags) -> bucket or -1 (may raise a flag), so
+// that a wavefront can issue the loads of all its steps before using any.
+//
 // Three launches:
 //   1. count: one wavefront walks one chunk of 64*steps items and builds the
 //      chunk's bucket histogram in LDS (LDS atomics: counts do not depend on
@@ -30,6 +34,7 @@ namespace {   // every translation unit gets its own copy of these kernels
 
 constexpr int kRankWaves = 4;                 // wavefronts per workgroup in passes 1 and 3
 constexpr int kRankThreads = kRankWaves * kWave;
+constexpr int kRankMaxSteps = 32;             // steps per chunk (bounded by rank_geom)
 
 struct RankGeom {
   int64_t n;       // items
@@ -43,10 +48,11 @@ inline RankGeom rank_geom(int64_t n, int32_t B) {
   RankGeom g;
   g.n = n;
   g.B = B;
-  // at least 4 steps (256 items) per chunk and at most 32 (2048 items), aiming
-  // at about 64 chunks, so that the one-workgroup scan stays short
-  int64_t s = (n + 64 * 64 - 1) / (64 * 64);
-  g.steps = static_cast<int32_t>(s < 4 ? 4 : (s > 32 ? 32 : s));
+  // at least 4 steps (256 items) per chunk and at most 32 (2048 items),
+  // aiming at about 512 chunks: two wavefronts per CU in passes 1 and 3,
+  // while the one-workgroup scan still reads only chunks * B table entries
+  int64_t s = (n + 64 * 512 - 1) / (64 * 512);
+  g.steps = static_cast<int32_t>(s < 4 ? 4 : (s > kRankMaxSteps ? kRankMaxSteps : s));
   const int64_t chunk = 64ll * g.steps;
   g.chunks = (n + chunk - 1) / chunk;
   int bits = 0;
@@ -73,10 +79,17 @@ __global__ __launch_bounds__(kRankThreads) void rank_count_kernel(Bucket bucket,
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kRankWaves + w;
   if (c < g.chunks) {
     const int64_t base = c * 64 * g.steps;
-    for (int s = 0; s < g.steps; ++s) {
+    uint32_t raw[kRankMaxSteps];
+#pragma unroll
+    for (int s = 0; s < kRankMaxSteps; ++s) {
       const int64_t i = base + s * 64 + lane;
-      if (i < g.n) {
-        const int b = bucket(i, flags);
+      if (s < g.steps && i < g.n) raw[s] = bucket.load(i);
+    }
+#pragma unroll
+    for (int s = 0; s < kRankMaxSteps; ++s) {
+      const int64_t i = base + s * 64 + lane;
+      if (s < g.steps && i < g.n) {
+        const int b = bucket.classify(raw[s], flags);
         if (b >= 0) atomicAdd(&h[b], 1);
       }
     }
@@ -162,25 +175,37 @@ __global__ __launch_bounds__(kRankThreads) void rank_emit_kernel(Bucket bucket, 
   if (c >= g.chunks) return;
   const uint64_t lt = lanemask_lt();
   const int64_t base = c * 64 * g.steps;
-  for (int s = 0; s < g.steps; ++s) {
-    const int64_t i = base + s * 64 + lane;
-    const bool in = i < g.n;
-    const int b = in ? bucket(i, nullptr) : -1;
-    const int code = b >= 0 ? b : g.B;
-    uint64_t peers = ~0ull;
-    for (int bit = 0; bit < g.nbits; ++bit) {
-      const bool on = (code >> bit) & 1;
-      const uint64_t m = ballot(on);
-      peers &= on ? m : ~m;
+  // batches of 8 steps: the 8 loads are issued before the first is used
+  for (int s0 = 0; s0 < g.steps; s0 += 8) {
+    uint32_t raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = base + (s0 + u) * 64 + lane;
+      if (s0 + u < g.steps && i < g.n) raw[u] = bucket.load(i);
     }
-    if (b >= 0) {
-      const int32_t rank = __popcll(peers & lt);
-      const int32_t cnt = __popcll(peers);
-      const int32_t start = h[b];
-      emit(i, b, start + rank);
-      if (rank == 0) h[b] = start + cnt;
-    } else if (in) {
-      emit(i, -1, -1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < g.steps) {
+        const int64_t i = base + (s0 + u) * 64 + lane;
+        const bool in = i < g.n;
+        const int b = in ? bucket.classify(raw[u], nullptr) : -1;
+        const int code = b >= 0 ? b : g.B;
+        uint64_t peers = ~0ull;
+        for (int bit = 0; bit < g.nbits; ++bit) {
+          const bool on = (code >> bit) & 1;
+          const uint64_t m = ballot(on);
+          peers &= on ? m : ~m;
+        }
+        if (b >= 0) {
+          const int32_t rank = __popcll(peers & lt);
+          const int32_t cnt = __popcll(peers);
+          const int32_t start = h[b];
+          emit(i, b, start + rank);
+          if (rank == 0) h[b] = start + cnt;
+        } else if (in) {
+          emit(i, -1, -1);
+        }
+      }
     }
   }
 }

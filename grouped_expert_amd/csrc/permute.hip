@@ -16,8 +16,9 @@ namespace {
 struct ExpertBucket {
   const int32_t* ids;
   int32_t E;
-  __device__ int operator()(int64_t r, uint32_t* flags) const {
-    const int32_t e = ids[r];
+  __device__ uint32_t load(int64_t r) const { return static_cast<uint32_t>(ids[r]); }
+  __device__ int classify(uint32_t raw, uint32_t* flags) const {
+    const int32_t e = static_cast<int32_t>(raw);
     if (e >= 0 && e < E) return e;
     if (e != -1) flag_or(flags, MOE_FLAG_BAD_EXPERT);
     return -1;

@@ -11,10 +11,10 @@
 // static shape.
 //
 // Launches: the shared bucket-rank passes with bucket = destination (pass 3
-// writes route_loc and the header id of every placed row), a token-major
-// scatter that reads each token row once and writes its placed copies, and a
-// fill of the unused rows (zero data, 0xFFFF header tail) so that the pools
-// are fully defined.
+// writes route_loc and the header id of every placed row), then one launch
+// whose blocks either scatter token rows (each token row read once, written to
+// its placed copies) or fill the unused rows (zero data, 0xFFFF header tail)
+// so that the pools are fully defined.
 #include "bucket_rank.h"
 
 namespace moe {
@@ -23,8 +23,9 @@ namespace {
 struct DestBucket {
   const int32_t* ids;
   int32_t E, epd;
-  __device__ int operator()(int64_t r, uint32_t* flags) const {
-    const int32_t e = ids[r];
+  __device__ uint32_t load(int64_t r) const { return static_cast<uint32_t>(ids[r]); }
+  __device__ int classify(uint32_t raw, uint32_t* flags) const {
+    const int32_t e = static_cast<int32_t>(raw);
     if (e >= 0 && e < E) return e / epd;
     if (e != -1) flag_or(flags, MOE_FLAG_BAD_EXPERT);
     return -1;
@@ -57,14 +58,17 @@ struct PackEmit {
 
 // One wavefront per token: the row is read once into registers (in pieces of
 // up to 8 x 16 B per lane) and written to each of the token's placed slots.
+// Plain (cached) loads and stores: measured faster here than the streaming
+// forms.
 constexpr int kTokPerBlock = 4;
 constexpr int kPiece = 8;
+constexpr int kPackThreads = kTokPerBlock * kWave;
 
-__global__ __launch_bounds__(kTokPerBlock * kWave) void pack_rows_kernel(
-    const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ route_loc,
-    int64_t slab_lo, int64_t slab_hi, vec16* __restrict__ pools) {
+__device__ __forceinline__ void pack_token_rows(const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k,
+                                                const int32_t* __restrict__ route_loc, int64_t slab_lo,
+                                                int64_t slab_hi, vec16* __restrict__ pools, int64_t blk) {
   const int lane = threadIdx.x % kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  const int64_t t = blk * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
   int32_t loc[MOE_MAX_TOPK];
   int live = 0;
@@ -79,27 +83,27 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void pack_rows_kernel(
 #pragma unroll
     for (int u = 0; u < kPiece; ++u) {
       const int64_t c = c0 + u * kWave + lane;
-      if (c < row_vecs) v[u] = ld_stream(in + c);
+      if (c < row_vecs) v[u] = in[c];
     }
     for (int j = 0; j < live; ++j) {
       vec16* out = pools + static_cast<int64_t>(loc[j]) * row_vecs;
 #pragma unroll
       for (int u = 0; u < kPiece; ++u) {
         const int64_t c = c0 + u * kWave + lane;
-        if (c < row_vecs) st_stream(v[u], out + c);
+        if (c < row_vecs) out[c] = v[u];
       }
     }
   }
 }
 
-// Unused rows of each written pool: zero data rows past the wave's fill and
-// 0xFFFF header elements past it.  grid = (row blocks, pools).
+// Unused rows of one pool (row block rblk of pool `pool` = slab * n_dest +
+// dest): zero data rows past the wave's fill and 0xFFFF header elements past
+// it.  These rows are disjoint from every placed row.
 constexpr int kFillRows = 16;
 
-__global__ __launch_bounds__(256) void pack_fill_kernel(const int32_t* __restrict__ dest_counts, int32_t n_dest,
-                                                        int32_t n_waves, int32_t pool_rows, int32_t d,
-                                                        int32_t wave_sel, bf16_t* __restrict__ pools) {
-  const int64_t pool = blockIdx.y;                     // slab * n_dest + dest
+__device__ __forceinline__ void pack_fill_rows(const int32_t* __restrict__ dest_counts, int32_t n_dest,
+                                               int32_t n_waves, int32_t pool_rows, int32_t d, int32_t wave_sel,
+                                               bf16_t* __restrict__ pools, int64_t pool, int32_t rblk) {
   const int32_t dest = static_cast<int32_t>(pool % n_dest);
   const int32_t w = wave_sel < 0 ? static_cast<int32_t>(pool / n_dest) : wave_sel;
   const int64_t cap_all = static_cast<int64_t>(n_waves) * pool_rows;
@@ -108,10 +112,10 @@ __global__ __launch_bounds__(256) void pack_fill_kernel(const int32_t* __restric
   const int32_t filled = m > w ? static_cast<int32_t>((m - w + n_waves - 1) / n_waves) : 0;
   const int64_t P1 = pool_rows + 1;
   bf16_t* base = pools + pool * P1 * d;
-  if (blockIdx.x == 0) {
+  if (rblk == 0) {
     for (int32_t i = filled + threadIdx.x; i < d; i += blockDim.x) base[i] = 0xFFFF;
   }
-  const int32_t r0 = blockIdx.x * kFillRows;
+  const int32_t r0 = rblk * kFillRows;
   if (r0 + kFillRows <= filled) return;
   const int64_t row_vecs = static_cast<int64_t>(d) / 8;
   const vec16 zero = {0u, 0u, 0u, 0u};
@@ -120,6 +124,24 @@ __global__ __launch_bounds__(256) void pack_fill_kernel(const int32_t* __restric
     if (row < filled || row >= pool_rows) continue;
     vec16* out = reinterpret_cast<vec16*>(base + (1 + static_cast<int64_t>(row)) * d);
     for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) st_stream(zero, out + c);
+  }
+}
+
+// One launch for both: blocks [0, tok_blocks) scatter token rows, the rest
+// fill unused rows (fill_blocks_per_pool row blocks per pool), so the fill's
+// writes overlap the scatter instead of following it.
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(
+    const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ route_loc,
+    int64_t slab_lo, int64_t slab_hi, int64_t tok_blocks, const int32_t* __restrict__ dest_counts, int32_t n_dest,
+    int32_t n_waves, int32_t pool_rows, int32_t d, int32_t wave_sel, int32_t fill_blocks_per_pool,
+    bf16_t* __restrict__ pools) {
+  const int64_t b = blockIdx.x;
+  if (b < tok_blocks) {
+    pack_token_rows(x, T, row_vecs, k, route_loc, slab_lo, slab_hi, reinterpret_cast<vec16*>(pools), b);
+  } else {
+    const int64_t f = b - tok_blocks;
+    pack_fill_rows(dest_counts, n_dest, n_waves, pool_rows, d, wave_sel, pools, f / fill_blocks_per_pool,
+                   static_cast<int32_t>(f % fill_blocks_per_pool));
   }
 }
 
@@ -164,20 +186,18 @@ MOE_API int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_
                        cap_all, out, table, dev_flags, stream);
   if (st != MOE_OK) return st;
   const int64_t row_vecs = d / 8;
-  if (T > 0) {
-    const int64_t slab_rows = static_cast<int64_t>(n_dest) * P1;
-    const int64_t lo = wave < 0 ? 0 : wave * slab_rows;
-    const int64_t hi = wave < 0 ? n_waves * slab_rows : lo + slab_rows;
-    const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
-    hipLaunchKernelGGL(pack_rows_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream,
-                       static_cast<const vec16*>(x_bf16), T, row_vecs, k, route_loc, lo, hi,
-                       static_cast<vec16*>(pools));
-    MOE_LAUNCH_CHECK();
-  }
-  const unsigned n_pools = static_cast<unsigned>((wave < 0 ? n_waves : 1) * n_dest);
-  const unsigned rb = static_cast<unsigned>((pool_rows + kFillRows - 1) / kFillRows);
-  hipLaunchKernelGGL(pack_fill_kernel, dim3(rb > 0 ? rb : 1, n_pools), dim3(256), 0, stream, dest_counts, n_dest,
-                     n_waves, pool_rows, d, wave, pb);
+  const int64_t slab_rows = static_cast<int64_t>(n_dest) * P1;
+  const int64_t lo = wave < 0 ? 0 : wave * slab_rows;
+  const int64_t hi = wave < 0 ? n_waves * slab_rows : lo + slab_rows;
+  const int64_t tok_blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
+  const int64_t n_pools = static_cast<int64_t>(wave < 0 ? n_waves : 1) * n_dest;
+  const int32_t rb = (pool_rows + kFillRows - 1) / kFillRows;
+  const int32_t fill_per_pool = rb > 0 ? rb : 1;
+  const int64_t blocks = tok_blocks + n_pools * fill_per_pool;
+  MOE_CHECK(blocks <= INT32_MAX, MOE_EUNSUPPORTED);
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPackThreads), 0, stream,
+                     static_cast<const vec16*>(x_bf16), T, row_vecs, k, route_loc, lo, hi, tok_blocks, dest_counts,
+                     n_dest, n_waves, pool_rows, d, wave, fill_per_pool, pb);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -21,9 +21,11 @@ struct HeaderBucket {
   const bf16_t* pools;
   int64_t P, P1, d;
   int32_t L;
-  __device__ int operator()(int64_t i, uint32_t* flags) const {
+  __device__ uint32_t load(int64_t i) const {
     const int64_t s = i / P, r = i - s * P;
-    const uint32_t h = pools[s * P1 * d + r];
+    return pools[s * P1 * d + r];
+  }
+  __device__ int classify(uint32_t h, uint32_t* flags) const {
     if (h < static_cast<uint32_t>(L)) return static_cast<int>(h);
     if (h != 0xFFFFu) flag_or(flags, MOE_FLAG_BAD_HEADER);
     return -1;
