@@ -57,7 +57,8 @@ import numpy as np
 
 __all__ = [
     "HEADER_EMPTY", "bf16_to_f64", "to_f64",
-    "route_topk", "DispatchPlan", "dispatch_plan", "check_dispatch",
+    "route_topk", "route_v1", "group_limited_select", "route_v2", "sigmoid_f32", "route_v3",
+    "DispatchPlan", "dispatch_plan", "check_dispatch",
     "gather_rows", "silu", "swiglu_expert", "swiglu_bank", "scalar_bank", "run_segments",
     "combine", "moe_layer_token_major", "moe_layer_expert_major",
     "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
@@ -120,6 +121,131 @@ def route_topk(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray, np.n
     psel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
     gates = psel / psel.sum(axis=1, keepdims=True)
 
+    ids[invalid] = -1
+    gates[invalid] = 0.0
+    return ids, gates, invalid
+
+
+# ----------------------------------------------------------------------------
+# a1 gating variants: V1 (no renormalisation), V2 (group-limited greedy on
+# softmax, scaled), V3 (sigmoid affinity, selection bias, group top-2 sums,
+# renormalised original affinities, scaled)
+# ----------------------------------------------------------------------------
+
+def _softmax64(z32: np.ndarray) -> np.ndarray:
+    zz = z32.astype(np.float64)
+    m = zz.max(axis=1, keepdims=True)
+    p = np.exp(zz - m)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def route_v1(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Softmax over all experts, keep the top ``k``, no renormalisation.
+
+    M6.2 §0x04D (released DeepSeekMoE checkpoint: softmax scores, top-6,
+    norm_topk_prob false) and §0x06L3-§0x06L4 (V1 keeps the selected full
+    probability mass, scale 1: selected sums 0.70 / 0.75 in the reduced
+    fixture).  Selection is that of ``route_topk``; only the gates differ.
+    """
+    ids, _, invalid = route_topk(logits, k)
+    z = np.asarray(logits, dtype=np.float32)
+    p = _softmax64(np.where(invalid[:, None], np.float32(0), z))
+    gates = np.take_along_axis(p, np.maximum(ids, 0).astype(np.int64), axis=1)
+    gates[invalid] = 0.0
+    return ids, gates, invalid
+
+
+def _top2_sum_f32(v: np.ndarray) -> np.float32:
+    """Sum of the two largest values, added in fp32 (larger + smaller)."""
+    srt = np.sort(v.astype(np.float32))[::-1]
+    return np.float32(srt[0] + srt[1])
+
+
+def group_limited_select(scores: np.ndarray, n_group: int, topk_group: int, k: int,
+                         group_stat: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-restricted top-k on selection scores ``[T, E]``.
+
+    M6.2 §0x05A-§0x05B (V2: score each contiguous group by its best expert,
+    keep ``topk_group`` groups, mask the others, then take ``k`` experts from
+    the survivors) and §0x06B-§0x06C (V3: score a group by the sum of its two
+    largest corrected scores, keep ``topk_group`` groups, then top-``k``).
+    Groups are contiguous expert-id ranges of ``E / n_group``.  Groups and
+    experts are ranked by descending score, ties to the lower index; the
+    expert top-k ranges over the experts of the kept groups only.
+
+    ``group_stat``: ``"max"`` or ``"top2sum"`` (the latter added in fp32,
+    the precision the scores are given in).  Returns ``(ids int32 [T,k],
+    groups int32 [T,topk_group])``, both in rank order.
+    """
+    sc = np.asarray(scores)
+    T, E = sc.shape
+    if E % n_group or not 1 <= topk_group <= n_group or k > topk_group * (E // n_group):
+        raise ValueError("bad group geometry")
+    gs = E // n_group
+    ids = np.empty((T, k), dtype=np.int32)
+    groups = np.empty((T, topk_group), dtype=np.int32)
+    for t in range(T):
+        row = sc[t]
+        stat = []
+        for g in range(n_group):
+            members = row[g * gs:(g + 1) * gs]
+            stat.append(float(members.max()) if group_stat == "max" else float(_top2_sum_f32(members)))
+        g_order = sorted(range(n_group), key=lambda g: (-stat[g], g))[:topk_group]
+        groups[t] = g_order
+        eligible = [e for g in g_order for e in range(g * gs, (g + 1) * gs)]
+        e_order = sorted(eligible, key=lambda e: (-float(row[e]), e))[:k]
+        ids[t] = e_order
+    return ids, groups
+
+
+def route_v2(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+             route_scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """V2: FP32 softmax over all experts, group-limited greedy, no
+    renormalisation, gates scaled by ``route_scale`` (M6.2 §0x05B: 8 groups,
+    keep 3, top-6, scale 16).  Softmax is strictly monotone, so ranking groups
+    by their best probability and experts by probability equals ranking by
+    the fp32 logits; the selection is taken on the logits (-0.0 == +0.0)."""
+    z = np.asarray(logits, dtype=np.float32)
+    invalid = ~np.isfinite(z).all(axis=1)
+    zc = np.where(invalid[:, None], np.float32(0), z + np.float32(0.0)).astype(np.float64)
+    ids, _ = group_limited_select(zc, n_group, topk_group, k, "max")
+    p = _softmax64(zc.astype(np.float32))
+    gates = np.take_along_axis(p, ids.astype(np.int64), axis=1) * route_scale
+    ids[invalid] = -1
+    gates[invalid] = 0.0
+    return ids, gates, invalid
+
+
+def sigmoid_f32(z: np.ndarray) -> np.ndarray:
+    """Sigmoid evaluated in fp32, 1 / (1 + exp(-z)): the precision in which
+    V3 makes its selection decisions (M6.2 §0x06I: sigmoid scores plus an FP32
+    correction bias)."""
+    z32 = np.asarray(z, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return (np.float32(1.0) / (np.float32(1.0) + np.exp(-z32))).astype(np.float32)
+
+
+def route_v3(logits: np.ndarray, bias: Optional[np.ndarray], k: int, n_group: int, topk_group: int,
+             route_scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """V3: sigmoid affinity ``s``, corrected score ``s + b`` (fp32) decides
+    groups (sum of each group's two largest corrected scores) and experts;
+    the gates return to the original affinities of the selected experts,
+    renormalised and scaled by ``route_scale`` (M6.2 §0x06A-§0x06D, §0x06I:
+    8 groups of 32, keep 4, top-8, scale 2.5).
+
+    Decisions use fp32 scores; gates use the fp64 sigmoid of the logits.
+    """
+    z = np.asarray(logits, dtype=np.float32)
+    T, E = z.shape
+    b = np.zeros(E, np.float32) if bias is None else np.asarray(bias, dtype=np.float32)
+    s32 = sigmoid_f32(z)
+    corrected = (s32 + b[None, :]).astype(np.float32)
+    invalid = ~(np.isfinite(z).all(axis=1) & np.isfinite(corrected).all(axis=1))
+    corrected = np.where(invalid[:, None], np.float32(0), corrected)
+    ids, _ = group_limited_select(corrected, n_group, topk_group, k, "top2sum")
+    s64 = 1.0 / (1.0 + np.exp(-np.where(invalid[:, None], 0.0, z.astype(np.float64))))
+    ssel = np.take_along_axis(s64, ids.astype(np.int64), axis=1)
+    gates = route_scale * ssel / ssel.sum(axis=1, keepdims=True)
     ids[invalid] = -1
     gates[invalid] = 0.0
     return ids, gates, invalid
