@@ -172,6 +172,8 @@ def recorded_traffic(w, call):
 
 
 def workload_kind(w):
+    if w.name.startswith("router"):
+        return "router"
     return "recv" if w.name.startswith("recv") else "pack" if w.name.startswith("sender") else "layer"
 
 
@@ -374,6 +376,43 @@ def pack_cpu_baseline(w, host, sample):
                 sample=f"first {s} of {w.T} tokens of {w.name}: route + pack of all waves; {dt:.2f} s")
 
 
+def router_setup(torch, w, banks):
+    logits = W.router_logits(w)
+    bias = W.router_bias(w)
+    host = dict(logits=logits, bias=bias)
+    b0 = {k: to_dev(torch, v) for k, v in host.items()}
+    return host, [b0] + [{k: v.clone() for k, v in b0.items()} for _ in range(banks - 1)]
+
+
+def router_step(ge, timer, w, bank, flags):
+    if w.gating in (2, 3):
+        ids, gates = timer.run("route", ge.route_topk_grouped, bank["logits"], w.k, w.gating, w.n_group,
+                               w.topk_group, w.route_scale, bias=bank["bias"] if w.gating == 3 else None,
+                               flags=flags)
+    else:
+        ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, gating=w.gating, flags=flags)
+    return dict(ids=ids, gates=gates)
+
+
+def router_ledger(w):
+    return {"route": dict(bytes=4 * w.T * w.E + 8 * w.T * w.k + (4 * w.E if w.gating == 3 else 0), flops=0)}
+
+
+def router_cpu_baseline(w, host, sample):
+    import oracle as O
+    s = min(sample, w.T)
+    t0 = time.perf_counter()
+    if w.gating == 3:
+        O.route_v3(host["logits"][:s], host["bias"], w.k, w.n_group, w.topk_group, w.route_scale)
+    elif w.gating == 2:
+        O.route_v2(host["logits"][:s], w.k, w.n_group, w.topk_group, w.route_scale)
+    else:
+        O.route_topk(host["logits"][:s], w.k)
+    dt = time.perf_counter() - t0
+    return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"first {s} of {w.T} tokens of {w.name}: the oracle router; {dt:.2f} s")
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -407,6 +446,9 @@ def main():
                          for _ in range(w.n_waves)],
                     starts=torch.arange(L, dtype=torch.int32, device="cuda") * cap)
         step = lambda tm, b: recv_step(ge, tm, w, b, flags, bufs)
+    elif kind == "router":
+        host, bank_list = router_setup(torch, w, banks)
+        step = lambda tm, b: router_step(ge, tm, w, b, flags)
     else:
         host, bank_list = pack_setup(torch, w, banks)
         bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, w.pool_rows + 1, w.d), dtype=torch.bfloat16,
@@ -454,6 +496,10 @@ def main():
         led = recv_ledger(w, cw)
         units, unit = w.n_waves * w.n_src * w.pool_rows, "incoming rows/s"
         per_step_calls = w.n_waves
+    elif kind == "router":
+        led = router_ledger(w)
+        units, unit = w.T, "tokens/s"
+        per_step_calls = 1
     else:
         led = pack_ledger(w)
         units, unit = w.T, "tokens/s"
@@ -492,12 +538,14 @@ def main():
             cpu = layer_cpu_baseline(w, host, args.cpu_sample or min(w.T, 2048))
         elif kind == "recv":
             cpu = recv_cpu_baseline(w, host, args.cpu_sample or 4096)
+        elif kind == "router":
+            cpu = router_cpu_baseline(w, host, args.cpu_sample or 32768)
         else:
             cpu = pack_cpu_baseline(w, host, args.cpu_sample or 16384)
 
     cfg = {"workload": w.name, "dtype": w.dtype}
     for key in ("T", "d", "E", "k", "d_ff", "capacity", "experts_per_dest", "n_dest", "n_waves", "pool_rows",
-                "n_src", "n_local", "recv_cap"):
+                "n_src", "n_local", "recv_cap", "gating", "n_group", "topk_group"):
         v = getattr(w, key)
         if v:
             cfg[key] = v

@@ -21,6 +21,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATING_SOFTMAX_TOPK_RENORM = 0
+MOE_GATING_SOFTMAX_TOPK = 1                 # V1
+MOE_GATING_SOFTMAX_GROUP_LIMITED = 2        # V2
+MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 = 3      # V3
 FLAG_BAD_EXPERT, FLAG_NONFINITE_LOGIT, FLAG_BAD_HEADER, FLAG_BAD_INDEX, FLAG_BAD_SEGMENT = 1, 2, 4, 8, 16
 
 
@@ -36,6 +39,8 @@ _SIGS = {
     "moe_strerror": (ctypes.c_char_p, [_i32]),
     "moe_version": (ctypes.c_int, []),
     "moe_route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "moe_route_topk_grouped": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p, _p,
+                                              _p, _p]),
     "moe_permute_workspace": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p, _p,
                                    _p, _sz, _p, _p]),
@@ -125,6 +130,20 @@ def route_topk(logits: torch.Tensor, k: int, gating: int = MOE_GATING_SOFTMAX_TO
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, gating, _ptr(ids), _ptr(w), _ptr(flags),
                                                 _stream(logits.device)))
+    return ids, w
+
+
+def route_topk_grouped(logits: torch.Tensor, k: int, gating: int, n_group: int, topk_group: int,
+                       route_scale: float, bias: Optional[torch.Tensor] = None,
+                       flags: Optional[torch.Tensor] = None):
+    """Group-restricted router (V2 / V3).  Returns ``(topk_ids, topk_w)``."""
+    _need_gpu(logits, bias, flags)
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk_grouped",
+           lib.moe_route_topk_grouped(_ptr(logits), T, E, k, gating, n_group, topk_group, float(route_scale),
+                                      _ptr(bias), _ptr(ids), _ptr(w), _ptr(flags), _stream(logits.device)))
     return ids, w
 
 

@@ -12,6 +12,8 @@
 // wavefront min of the expert indices holding that key (ties go to the lower
 // expert), both as DPP / lane-swap butterflies without LDS; the winner's owner
 // lane clears that key.
+#include <cmath>
+
 #include "common.h"
 
 namespace moe {
@@ -90,35 +92,15 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 constexpr int kTokensPerBlock = 4;
 
+// k selection rounds over the keys of one wavefront (expert lane + 64 v):
+// the largest key, then the lowest expert holding it; the winner's owner lane
+// clears that key.  Lane j keeps the j-th winner; top_key is the first one.
 template <int V>
-__global__ __launch_bounds__(kTokensPerBlock * kWave) void route_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t* __restrict__ ids,
-    float* __restrict__ weights, uint32_t* flags) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / kWave;
-  if (t >= T) return;                                   // whole wavefront leaves together
-  const float* row = logits + t * E;
-
-  // key[v]: order key of expert lane + 64 v (0 = no expert; a finite or
-  // infinite logit has a key >= 0x007FFFFF)
-  uint32_t key[V];
-  bool bad = false;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = lane + v * kWave;
-    key[v] = 0;
-    if (e < E) {
-      const float z = row[e];
-      bad |= !isfinite(z);
-      key[v] = order_key(z);
-    }
-  }
-  const bool token_bad = ballot(bad) != 0;
-
-  // k selection rounds: the largest key, then the lowest expert holding it;
-  // lane j keeps the j-th winner.  The winner's owner lane clears that key.
-  uint32_t mine_key = 0, top_key = 0;
-  int32_t mine_e = 0;
+__device__ __forceinline__ void select_topk(uint32_t (&key)[V], int k, int lane, uint32_t& mine_key,
+                                            int32_t& mine_e, uint32_t& top_key) {
+  mine_key = 0;
+  mine_e = 0;
+  top_key = 0;
   for (int j = 0; j < k; ++j) {
     uint32_t lmax = key[0];
 #pragma unroll
@@ -138,11 +120,53 @@ __global__ __launch_bounds__(kTokensPerBlock * kWave) void route_topk_kernel(
     }
     if (j == 0) top_key = K;
   }
+}
+
+// full_mass = 0: gates renormalised over the k kept experts;
+// full_mass = 1 (V1): gates are the kept full-softmax probabilities.
+template <int V>
+__global__ __launch_bounds__(kTokensPerBlock * kWave) void route_topk_kernel(
+    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t full_mass, int32_t* __restrict__ ids,
+    float* __restrict__ weights, uint32_t* flags) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;                                   // whole wavefront leaves together
+  const float* row = logits + t * E;
+
+  // key[v]: order key of expert lane + 64 v (0 = no expert; a finite or
+  // infinite logit has a key >= 0x007FFFFF); zf[v] the logit itself
+  uint32_t key[V];
+  float zf[V];
+  bool bad = false;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = lane + v * kWave;
+    key[v] = 0;
+    zf[v] = -INFINITY;
+    if (e < E) {
+      const float z = row[e];
+      bad |= !isfinite(z);
+      key[v] = order_key(z);
+      zf[v] = z;
+    }
+  }
+  const bool token_bad = ballot(bad) != 0;
+
+  uint32_t mine_key, top_key;
+  int32_t mine_e;
+  select_topk<V>(key, k, lane, mine_key, mine_e, top_key);
 
   const float z = key_value(mine_key);
   const float z0 = key_value(top_key);
   const float p = lane < k ? expf(z - z0) : 0.0f;
-  const float s = wave_sum_f32(p);
+  float mass = 0.0f;
+  if (full_mass) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) mass += expf(zf[v] - z0);
+  } else {
+    mass = p;
+  }
+  const float s = wave_sum_f32(mass);
   if (lane < k) {
     ids[t * k + lane] = token_bad ? -1 : mine_e;
     weights[t * k + lane] = token_bad ? 0.0f : p / s;
@@ -151,11 +175,148 @@ __global__ __launch_bounds__(kTokensPerBlock * kWave) void route_topk_kernel(
 }
 
 template <int V>
-void launch(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w, uint32_t* flags,
-            hipStream_t s) {
+void launch(const float* logits, int64_t T, int32_t E, int32_t k, int32_t full_mass, int32_t* ids, float* w,
+            uint32_t* flags, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock);
   hipLaunchKernelGGL(HIP_KERNEL_NAME(route_topk_kernel<V>), dim3(blocks), dim3(kTokensPerBlock * kWave), 0, s,
-                     logits, T, E, k, ids, w, flags);
+                     logits, T, E, k, full_mass, ids, w, flags);
+}
+
+// Group-restricted router (V2 when sigmoid_bias = 0, V3 when 1).  One
+// wavefront per token.  Each lane turns its logits into selection keys (V2:
+// the logit; V3: sigmoid + bias in fp32) and stores them in the wavefront's
+// LDS row; lane g < n_group then scans group g's G contiguous keys for the
+// group score (V2: largest key; V3: fp32 sum of the two largest corrected
+// scores).  topk_group rounds of max / lowest-index pick the groups, the
+// experts outside them get key 0, and the usual k rounds pick the experts.
+template <int V>
+__global__ __launch_bounds__(kTokensPerBlock * kWave) void route_grouped_kernel(
+    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t sigmoid_bias, int32_t n_group,
+    int32_t topk_group, float route_scale, const float* __restrict__ bias, int32_t* __restrict__ ids,
+    float* __restrict__ weights, uint32_t* flags) {
+  extern __shared__ uint32_t keys_lds[];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave;
+  if (t >= T) return;                                   // whole wavefront leaves together
+  const float* row = logits + t * E;
+  uint32_t* lk = keys_lds + wave * E;                   // this wavefront's LDS row
+
+  uint32_t key[V];
+  float val[V];                                         // V2: logit; V3: sigmoid affinity
+  bool bad = false;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = lane + v * kWave;
+    key[v] = 0;
+    val[v] = -INFINITY;
+    if (e < E) {
+      const float z = row[e];
+      bad |= !isfinite(z);
+      if (sigmoid_bias) {
+        const float sg = 1.0f / (1.0f + expf(-z));
+        const float c = sg + (bias ? bias[e] : 0.0f);
+        bad |= !isfinite(c);
+        key[v] = order_key(c);
+        val[v] = sg;
+      } else {
+        key[v] = order_key(z);
+        val[v] = z;
+      }
+      lk[e] = key[v];
+    }
+  }
+  const bool token_bad = ballot(bad) != 0;
+  // the LDS row is written and read by this wavefront only: its LDS accesses
+  // complete in order; the fence keeps the compiler from reordering them
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // group scores: lane g scans group g
+  const int G = E / n_group;
+  uint32_t gkey = 0;
+  if (lane < n_group) {
+    if (sigmoid_bias) {
+      uint32_t k1 = 0, k2 = 0;                          // two largest keys, k1 >= k2
+      for (int i = 0; i < G; ++i) {
+        const uint32_t x = lk[lane * G + i];
+        if (x > k1) {
+          k2 = k1;
+          k1 = x;
+        } else if (x > k2) {
+          k2 = x;
+        }
+      }
+      gkey = order_key(key_value(k1) + key_value(k2));
+    } else {
+      for (int i = 0; i < G; ++i) gkey = umax(gkey, lk[lane * G + i]);
+    }
+  }
+  // topk_group rounds over groups (one group per lane)
+  uint64_t kept = 0;
+  for (int r = 0; r < topk_group; ++r) {
+    const uint32_t K = uniform(wave_max_u32(gkey));
+    const uint32_t gw = uniform(wave_min_u32(gkey == K && lane < n_group ? static_cast<uint32_t>(lane) : 0xFFFFFFFFu));
+    kept |= 1ull << (gw & 63u);
+    if (lane == static_cast<int>(gw)) gkey = 0;
+  }
+  // experts outside the kept groups leave the selection
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = lane + v * kWave;
+    if (e < E && !((kept >> (e / G)) & 1ull)) key[v] = 0;
+  }
+
+  uint32_t mine_key, top_key;
+  int32_t mine_e;
+  select_topk<V>(key, k, lane, mine_key, mine_e, top_key);
+  (void)top_key;
+
+  // the selected expert's value, fetched from its owner lane
+  float mine_val = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(mine_e, j);
+    const int vw = ej / kWave, lw = ej % kWave;
+    float vv = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) vv = v == vw ? val[v] : vv;
+    const float got = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vv), lw));
+    if (lane == j) mine_val = got;
+  }
+
+  float gate;
+  if (sigmoid_bias) {
+    const float ssum = wave_sum_f32(lane < k ? mine_val : 0.0f);
+    gate = route_scale * mine_val / ssum;
+  } else {
+    // full softmax over all E experts: the largest logit of the token
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = lane + v * kWave;
+      if (e < E) lmax = umax(lmax, order_key(val[v]));
+    }
+    const float zmax = key_value(uniform(wave_max_u32(lmax)));
+    float mass = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) mass += expf(val[v] - zmax);
+    const float denom = wave_sum_f32(mass);
+    gate = route_scale * expf(mine_val - zmax) / denom;
+  }
+  if (lane < k) {
+    ids[t * k + lane] = token_bad ? -1 : mine_e;
+    weights[t * k + lane] = token_bad ? 0.0f : gate;
+  }
+  if (token_bad && lane == 0) flag_or(flags, MOE_FLAG_NONFINITE_LOGIT);
+}
+
+template <int V>
+void launch_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t sigmoid_bias, int32_t n_group,
+                    int32_t topk_group, float scale, const float* bias, int32_t* ids, float* w, uint32_t* flags,
+                    hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock);
+  const size_t lds = static_cast<size_t>(kTokensPerBlock) * E * sizeof(uint32_t);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(route_grouped_kernel<V>), dim3(blocks), dim3(kTokensPerBlock * kWave), lds, s,
+                     logits, T, E, k, sigmoid_bias, n_group, topk_group, scale, bias, ids, w, flags);
 }
 
 }  // namespace
@@ -166,18 +327,47 @@ MOE_API int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
   using namespace moe;
   MOE_CHECK(T >= 0 && E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL);
   MOE_CHECK(k >= 1 && k <= E && k <= MOE_MAX_TOPK, MOE_EINVAL);
-  MOE_CHECK(gating == MOE_GATING_SOFTMAX_TOPK_RENORM, MOE_EUNSUPPORTED);
+  MOE_CHECK(gating == MOE_GATING_SOFTMAX_TOPK_RENORM || gating == MOE_GATING_SOFTMAX_TOPK, MOE_EUNSUPPORTED);
   MOE_CHECK(T <= INT32_MAX / k, MOE_EUNSUPPORTED);          // routes are int32-indexed
   if (T == 0) return MOE_OK;
   MOE_CHECK(logits && topk_ids && topk_w, MOE_EINVAL);
   MOE_CHECK(aligned4(logits) && aligned4(topk_ids) && aligned4(topk_w), MOE_EINVAL);
+  const int full = gating == MOE_GATING_SOFTMAX_TOPK ? 1 : 0;
   const int V = (E + kWave - 1) / kWave;
-  if (V <= 1) launch<1>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 2) launch<2>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 4) launch<4>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 6) launch<6>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 8) launch<8>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
-  else launch<16>(logits, T, E, k, topk_ids, topk_w, dev_flags, stream);
+  if (V <= 1) launch<1>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 2) launch<2>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 4) launch<4>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 6) launch<6>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 8) launch<8>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  else launch<16>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+MOE_API int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t gating,
+                                   int32_t n_group, int32_t topk_group, float route_scale, const float* bias,
+                                   int32_t* topk_ids, float* topk_w, uint32_t* dev_flags, hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK(gating == MOE_GATING_SOFTMAX_GROUP_LIMITED || gating == MOE_GATING_SIGMOID_BIAS_GROUP_TOP2,
+            MOE_EUNSUPPORTED);
+  const int sig = gating == MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 ? 1 : 0;
+  MOE_CHECK(T >= 0 && E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL);
+  MOE_CHECK(n_group >= 1 && n_group <= kWave && E % n_group == 0, MOE_EINVAL);
+  MOE_CHECK(topk_group >= 1 && topk_group <= n_group, MOE_EINVAL);
+  MOE_CHECK(k >= 1 && k <= MOE_MAX_TOPK && k <= topk_group * (E / n_group), MOE_EINVAL);
+  MOE_CHECK(!sig || E / n_group >= 2, MOE_EINVAL);
+  MOE_CHECK(sig || bias == nullptr, MOE_EINVAL);
+  MOE_CHECK(std::isfinite(route_scale), MOE_EINVAL);
+  MOE_CHECK(T <= INT32_MAX / k, MOE_EUNSUPPORTED);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(logits && topk_ids && topk_w, MOE_EINVAL);
+  MOE_CHECK(aligned4(logits) && aligned4(topk_ids) && aligned4(topk_w) && (!bias || aligned4(bias)), MOE_EINVAL);
+  const int V = (E + kWave - 1) / kWave;
+  if (V <= 1) launch_grouped<1>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 2) launch_grouped<2>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 4) launch_grouped<4>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+  else if (V <= 8) launch_grouped<8>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+  else launch_grouped<16>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -773,7 +773,8 @@ void launch_one(bool persistent, const void* a, const void* b0, const void* b1, 
                 const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream) {
   const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
   if (persistent) {
-    const int64_t g = upper < device_cus() ? upper : device_cus();      // one 4-wave workgroup per CU
+    const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
+    const int64_t g = upper < slots ? upper : slots;
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
                        dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);

@@ -62,9 +62,26 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Gating families.  M6.2 0x06L1, Mixtral row: FP32 softmax over all experts,
- * keep the top k, renormalise the kept probabilities to one. */
-typedef enum { MOE_GATING_SOFTMAX_TOPK_RENORM = 0 } moe_gating;
+/* Gating families ("M6.2 - Expert Parallelism and DeepSeek MoE").
+ *   SOFTMAX_TOPK_RENORM   0x06L1, Mixtral row: FP32 softmax over all experts,
+ *                         keep the top k, renormalise the kept probabilities.
+ *   SOFTMAX_TOPK          0x04D, 0x06L3 (V1): same selection, the selected
+ *                         full-softmax probabilities are kept as they are.
+ *   SOFTMAX_GROUP_LIMITED 0x05A-0x05B (V2): group-limited greedy on the
+ *                         softmax, no renormalisation, times a route scale.
+ *   SIGMOID_BIAS_GROUP_TOP2  0x06A-0x06D, 0x06I (V3): sigmoid affinity plus a
+ *                         selection bias picks groups by their two largest
+ *                         corrected scores, then experts; gates are the
+ *                         selected original affinities renormalised, times a
+ *                         route scale.
+ * The first two are served by moe_route_topk, the last two by
+ * moe_route_topk_grouped. */
+typedef enum {
+  MOE_GATING_SOFTMAX_TOPK_RENORM = 0,
+  MOE_GATING_SOFTMAX_TOPK = 1,
+  MOE_GATING_SOFTMAX_GROUP_LIMITED = 2,
+  MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 = 3
+} moe_gating;
 
 /* Bits OR-ed into *dev_flags. */
 #define MOE_FLAG_BAD_EXPERT      1u  /* expert id < -1 or >= E (route dropped) */
@@ -90,20 +107,58 @@ int moe_version(void);
  *   topk_ids[t, j]  j-th largest logit's expert, j = 0..k-1, ordered by
  *                   descending fp32 logit; equal logits (-0 == +0) place the
  *                   lower expert index first.
- *   topk_w[t, j]    exp(z_j - z_0) / sum_i exp(z_i - z_0) over the k kept
- *                   experts (= softmax over all E, keep k, renormalise).
+ *   topk_w[t, j]    MOE_GATING_SOFTMAX_TOPK_RENORM: exp(z_j - z_0) /
+ *                   sum over the k kept experts of exp(z_i - z_0) (= softmax
+ *                   over all E, keep k, renormalise);
+ *                   MOE_GATING_SOFTMAX_TOPK (V1): exp(z_j - z_0) / sum over
+ *                   all E experts of exp(z_i - z_0) (the kept softmax mass).
  * A token whose logits contain NaN or +-Inf gets ids -1 and weights 0 in all
  * k slots and sets MOE_FLAG_NONFINITE_LOGIT.
  *
  *   logits    device, fp32 [T, E]
  *   T >= 0; 1 <= k <= min(E, MOE_MAX_TOPK); 1 <= E <= MOE_MAX_EXPERTS
- *   gating    MOE_GATING_SOFTMAX_TOPK_RENORM
+ *   gating    MOE_GATING_SOFTMAX_TOPK_RENORM or MOE_GATING_SOFTMAX_TOPK
+ *             (others: MOE_EUNSUPPORTED)
  *   topk_ids  device, int32 [T, k]       (4-byte alignment suffices)
  *   topk_w    device, fp32  [T, k]       (4-byte alignment suffices)
  *   dev_flags device uint32 or NULL
  * ------------------------------------------------------------------------- */
 int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t gating,
                    int32_t* topk_ids, float* topk_w, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_topk_grouped -- group-restricted router top-k (V2, V3).
+ *
+ * "M6.2 - Expert Parallelism and DeepSeek MoE", 0x05A-0x05B (V2) and
+ * 0x06A-0x06D, 0x06I (V3).  Experts form n_group contiguous groups of
+ * G = E / n_group ids.  For every token t:
+ *   MOE_GATING_SOFTMAX_GROUP_LIMITED (V2): group score = largest logit in
+ *     the group (softmax is monotone, so this ranks groups as their best
+ *     probability does); keep topk_group groups; the k largest logits among
+ *     the kept groups' experts, descending; topk_w = softmax probability over
+ *     all E experts times route_scale (no renormalisation).  bias must be NULL.
+ *   MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 (V3): s_e = 1 / (1 + exp(-z_e)) and
+ *     c_e = s_e + bias[e] in fp32 (bias NULL = 0); group score = sum of the
+ *     group's two largest c; keep topk_group groups; the k largest c among the
+ *     kept groups' experts, descending; topk_w = route_scale * s_j / sum over
+ *     the k selected of s.
+ * Groups and experts of equal score rank the lower index first.  A token
+ * with a non-finite logit (or corrected score) gets ids -1, weights 0 and
+ * sets MOE_FLAG_NONFINITE_LOGIT.
+ *
+ *   logits      device, fp32 [T, E]
+ *   T >= 0; 1 <= E <= MOE_MAX_EXPERTS; 1 <= k <= MOE_MAX_TOPK
+ *   n_group     1..64 dividing E; 1 <= topk_group <= n_group;
+ *               k <= topk_group * E / n_group; V3 also needs E / n_group >= 2
+ *   route_scale finite (V2: 16 in the released V2 checkpoint; V3: 2.5)
+ *   bias        device, fp32 [E] or NULL (V3 only)
+ *   topk_ids, topk_w, dev_flags as for moe_route_topk
+ * Returns MOE_EINVAL for any violated bound, MOE_EUNSUPPORTED for another
+ * gating value; nothing is launched then.
+ * ------------------------------------------------------------------------- */
+int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t gating,
+                           int32_t n_group, int32_t topk_group, float route_scale, const float* bias,
+                           int32_t* topk_ids, float* topk_w, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_permute -- group routes by expert, stable, with capacity and inverse.

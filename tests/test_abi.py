@@ -14,7 +14,7 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 def test_exports_every_header_symbol():
     names = B.header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
@@ -42,6 +42,35 @@ def test_route_validation():
     assert lib.moe_route_topk(p, 10, 8, 2, 7, p, p, NULL, NULL) == EUNSUP         # unknown gating
     assert lib.moe_route_topk(NULL, 10, 8, 2, 0, p, p, NULL, NULL) == EINVAL      # null logits
     assert lib.moe_route_topk(NULL, 0, 8, 2, 0, NULL, NULL, NULL, NULL) == 0      # empty batch
+    assert lib.moe_route_topk(NULL, 0, 8, 2, 1, NULL, NULL, NULL, NULL) == 0      # V1 accepted
+    assert lib.moe_route_topk(p, 10, 8, 2, 2, p, p, NULL, NULL) == EUNSUP         # V2 needs the grouped call
+
+
+def test_route_grouped_validation():
+    p, _keep = _fake()
+    f = lib.moe_route_topk_grouped
+    V2, V3 = 2, 3
+    ok = [p, 10, 256, 8, V3, 8, 4, 2.5, p, p, p, NULL, NULL]
+    assert f(NULL, 0, *ok[2:]) == 0                                           # empty batch, valid geometry
+    for i, v, want in [(4, 0, EUNSUP),          # plain softmax gating belongs to moe_route_topk
+                       (4, 1, EUNSUP),
+                       (5, 0, EINVAL),          # n_group < 1
+                       (5, 65, EINVAL),         # more groups than lanes
+                       (5, 7, EINVAL),          # 256 % 7 != 0
+                       (6, 0, EINVAL),          # topk_group < 1
+                       (6, 9, EINVAL),          # topk_group > n_group
+                       (3, 17, EINVAL),         # k > 16
+                       (7, float("inf"), EINVAL)]:
+        bad = list(ok); bad[i] = v
+        assert f(*bad) == want, (i, v)
+    bad = list(ok); bad[5] = 128; bad[6] = 2; bad[3] = 8                       # 2 experts per group, keep 2: k <= 4
+    assert f(*bad) == EINVAL
+    bad = list(ok); bad[4] = V2                                                 # bias is V3-only
+    assert f(*bad) == EINVAL
+    bad = list(ok); bad[2] = 8; bad[5] = 8; bad[6] = 4; bad[3] = 2              # V3 needs >= 2 experts per group
+    assert f(*bad) == EINVAL
+    bad = list(ok); bad[0] = NULL                                               # null logits
+    assert f(*bad) == EINVAL
 
 
 def test_permute_validation():

@@ -52,6 +52,91 @@ def test_route_topk(ge, T, E, k):
     assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
 
 
+def _route_inputs(T, E, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    if T > 10:
+        z[:3] = np.round(z[:3])                      # ties
+        z[3, :] = 0.0
+        z[4, E // 2] = np.nan
+    return z
+
+
+def _gates_close(gw, rg):
+    gw = np.asarray(gw, dtype=np.float64)
+    return np.all(np.abs(gw - rg) <= 1e-5 * np.abs(rg) + 1e-7)
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 64, 6), (257, 128, 8), (190, 384, 8), (40, 1024, 16), (1, 8, 2)])
+def test_route_topk_v1(ge, T, E, k):
+    z = _route_inputs(T, E, T + E)
+    flags = ge.new_flags("cuda")
+    ids, w = ge.route_topk(to_gpu(z), k, gating=ge.binding.MOE_GATING_SOFTMAX_TOPK, flags=flags)
+    rid, rg, inv = O.route_v1(z, k)
+    assert np.array_equal(to_np(ids), rid)
+    assert _gates_close(to_np(w), rg)
+    assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
+
+
+@pytest.mark.parametrize("T,E,k,ng,tg,scale", [(300, 160, 6, 8, 3, 16.0), (257, 64, 4, 4, 2, 1.0),
+                                              (120, 256, 8, 8, 4, 2.0), (64, 1024, 16, 64, 5, 1.0),
+                                              (33, 16, 3, 1, 1, 1.0)])
+def test_route_grouped_v2(ge, T, E, k, ng, tg, scale):
+    z = _route_inputs(T, E, 3 * T + E)
+    flags = ge.new_flags("cuda")
+    ids, w = ge.route_topk_grouped(to_gpu(z), k, ge.binding.MOE_GATING_SOFTMAX_GROUP_LIMITED, ng, tg, scale,
+                                   flags=flags)
+    rid, rg, inv = O.route_v2(z, k, ng, tg, scale)
+    assert np.array_equal(to_np(ids), rid)
+    assert _gates_close(to_np(w), rg)
+    assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
+
+
+def _v3_agree(z, bias, gids, rid, k, ng, tg):
+    """Expert ids must match; a differing token is accepted only when its
+    decision was a tie within fp32 rounding of the sigmoid (the kernel's expf
+    and numpy's exp may differ by an ulp)."""
+    if np.array_equal(gids, rid):
+        return
+    c = (O.sigmoid_f32(z) + bias[None, :]).astype(np.float32)
+    for t in np.nonzero((gids != rid).any(axis=1))[0]:
+        diff = set(gids[t].tolist()) ^ set(rid[t].tolist())
+        ref = float(c[t, rid[t, -1]])
+        assert all(abs(float(c[t, e]) - ref) <= 4 * np.spacing(np.float32(abs(ref) + 1)) for e in diff), t
+
+
+@pytest.mark.parametrize("T,E,k,ng,tg,scale", [(300, 256, 8, 8, 4, 2.5), (200, 64, 6, 8, 3, 1.0),
+                                              (100, 384, 8, 16, 4, 2.5), (40, 12, 4, 4, 2, 2.5)])
+def test_route_grouped_v3(ge, T, E, k, ng, tg, scale):
+    z = _route_inputs(T, E, 5 * T + E)
+    bias = (0.05 * np.random.default_rng(E).standard_normal(E)).astype(np.float32)
+    flags = ge.new_flags("cuda")
+    ids, w = ge.route_topk_grouped(to_gpu(z), k, ge.binding.MOE_GATING_SIGMOID_BIAS_GROUP_TOP2, ng, tg, scale,
+                                   bias=to_gpu(bias), flags=flags)
+    rid, rg, inv = O.route_v3(z, bias, k, ng, tg, scale)
+    gids = to_np(ids)
+    _v3_agree(z, bias, gids, rid, k, ng, tg)
+    same = (gids == rid).all(axis=1)
+    assert _gates_close(to_np(w)[same], rg[same])
+    assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
+
+
+def test_route_grouped_page_tokens(ge, golden):
+    g = golden("m62_gating_fixtures.json")
+    f = g["v3_t0"]
+    s = np.array(f["affinity"], dtype=np.float64)
+    z = np.log(s / (1 - s)).astype(np.float32)[None, :]
+    ids, w = ge.route_topk_grouped(to_gpu(z), f["k"], ge.binding.MOE_GATING_SIGMOID_BIAS_GROUP_TOP2, f["n_group"],
+                                   f["topk_group"], f["route_scale"], bias=to_gpu(np.array(f["bias"], np.float32)))
+    assert to_np(ids)[0].tolist() == f["experts"]
+    assert np.allclose(to_np(w)[0], f["gates"], atol=2e-6)
+    v = g["v2_t2"]
+    zs = np.log(np.array([v["scores"]], dtype=np.float64)).astype(np.float32)
+    ids2, _ = ge.route_topk_grouped(to_gpu(zs), v["k"], ge.binding.MOE_GATING_SOFTMAX_GROUP_LIMITED, v["n_group"],
+                                    v["topk_group"], v["route_scale"])
+    assert to_np(ids2)[0].tolist() == v["limited_top3"]
+
+
 # ---------------------------------------------------------------------------
 # permute
 # ---------------------------------------------------------------------------

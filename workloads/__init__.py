@@ -45,6 +45,7 @@ _TAG_TOKENS = 2
 _TAG_WEIGHTS = 3
 _TAG_RECV_IDS = 4
 _TAG_RECV_ROWS = 5
+_TAG_BIAS = 6
 
 HEADER_EMPTY = 0xFFFF
 
@@ -75,6 +76,12 @@ class Workload:
     n_local: int = 0
     recv_cap: int = 0
     recv_zipf: float = 0.0
+    # group-restricted router (gating variants)
+    gating: int = 0            # 0 softmax-renorm, 1 V1, 2 V2, 3 V3 (the library's moe_gating ids)
+    n_group: int = 0
+    topk_group: int = 0
+    route_scale: float = 1.0
+    bias_std: float = 0.0      # V3 selection bias ~ N(0, bias_std), its own stream
 
     @property
     def R(self) -> int:
@@ -94,7 +101,12 @@ SEND = Workload(name="sender_pack_bf16", seed=3, dtype="bf16", T=65536, d=3072,
 DECODE = Workload(name="decode_bf16", seed=4, dtype="bf16", T=64, d=3072, E=384,
                   k=8, d_ff=1536, logits="normal", x_std=1.0, w_std=0.02)
 
-WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE)}
+# The V3 router at the pages' released shape ("M6.2", 0x06I: 256 experts in
+# 8 groups, keep 4, top-8, route scale 2.5) over the sender's 65,536 tokens.
+ROUTER_V3 = Workload(name="router_v3_f32", seed=5, dtype="f32", T=65536, E=256, k=8, logits="normal",
+                     gating=3, n_group=8, topk_group=4, route_scale=2.5, bias_std=0.05)
+
+WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
@@ -151,6 +163,11 @@ def router_logits(w: Workload) -> np.ndarray:
         bias = (np.arange(1, w.E + 1, dtype=np.float64) ** (-w.zipf_bias)).astype(np.float32)
         z += bias[None, :]
     return z
+
+
+def router_bias(w: Workload) -> np.ndarray:
+    """fp32 per-expert selection bias ``[E]`` ~ N(0, bias_std)."""
+    return _normal(_rng(w.seed, _TAG_BIAS), (w.E,), w.bias_std) if w.bias_std else np.zeros(w.E, np.float32)
 
 
 def tokens(w: Workload) -> np.ndarray:
