@@ -61,7 +61,7 @@ __all__ = [
     "DispatchPlan", "dispatch_plan", "check_dispatch",
     "gather_rows", "silu", "swiglu_expert", "swiglu_bank", "scalar_bank", "run_segments",
     "combine", "moe_layer_token_major", "moe_layer_expert_major",
-    "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
+    "header_rows", "pool_rows_of", "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
     "capacity_ceil", "drop_rates", "swiglu_flops", "padded_exec_rows",
     "block_exec_rows",
 ]
@@ -505,20 +505,41 @@ def moe_layer_expert_major(x: np.ndarray, ids: np.ndarray, gates: np.ndarray,
 # a7: pooled-wave sender pack
 # ----------------------------------------------------------------------------
 
+def header_rows(pool_rows: int, d: int) -> int:
+    """Full-width header rows of a pool: one 16-bit id per data row, ``d``
+    per header row (pooled wave §02 uses one row for 3004 ids at d = 3072;
+    more rows are the configurable-header variant, e.g. the two-wave profile
+    of §05 needs 4506 ids per pool).  At least one."""
+    return max(1, -(-int(pool_rows) // int(d)))
+
+
+def pool_rows_of(pool_height: int, d: int) -> int:
+    """The ``pool_rows`` whose pool has ``pool_height`` rows (data rows plus
+    their header rows); unique because the height grows with pool_rows."""
+    for h in range(1, pool_height + 1):
+        p = pool_height - h
+        if header_rows(p, d) == h:
+            return p
+    raise ValueError("no pool_rows gives this pool height")
+
+
 def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest: int,
               n_waves: int, pool_rows: int, *, with_pools: bool = True, E: Optional[int] = None):
     """Pack one sender's routes into fixed destination pools.
 
     Pooled wave §02: expert id gives a destination and a local expert id;
     "wave = rank mod 3, pool row = rank / 3" with rank read as the route's
-    ordinal among this sender's routes to that destination; each
-    destination gets ``pool_rows`` rows per wave and extra rows are dropped;
-    the first full-width row of a pool carries the packed local expert ids.
-    §03: pool shape ``[n_dest, pool_rows + 1, d]`` per wave.
+    ordinal among this sender's routes to that destination (generalised to
+    ``n_waves``: the two-wave profile of §05); each destination gets
+    ``pool_rows`` rows per wave and extra rows are dropped; the first
+    full-width rows of a pool carry the packed local expert ids (element ``i``
+    of the header, row ``i // d`` column ``i % d``, holds data row ``i``'s id;
+    ``H = header_rows(pool_rows, d)``, one at the pages' sizes).  §03: pool
+    shape ``[n_dest, pool_rows + H, d]`` per wave.
 
-    Returns a dict with ``pools`` (uint16 ``[n_waves, n_dest, pool_rows+1, d]``,
+    Returns a dict with ``pools`` (uint16 ``[n_waves, n_dest, pool_rows+H, d]``,
     or None when ``with_pools`` is False), ``route_loc`` (int64 ``[T*k]``:
-    flat pool row ``(w*n_dest + dest)*(pool_rows+1) + 1 + row`` or -1),
+    flat pool row ``(w*n_dest + dest)*(pool_rows+H) + H + row`` or -1),
     ``dest_counts`` (routes per destination before the cap),
     ``sender_dropped`` (routes not placed, including "no route" ids) and the
     per-route ``wave``/``row``/``dest``/``local``; ``bad`` marks expert ids
@@ -535,21 +556,20 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
     wave = np.where(valid, rank % n_waves, -1)
     row = np.where(valid, rank // n_waves, -1)
     acc = valid & (row < pool_rows)
-    P1 = pool_rows + 1
-    route_loc = np.where(acc, (wave * n_dest + dest) * P1 + 1 + row, -1)
+    d = np.asarray(x_bits).shape[1]
+    H = header_rows(pool_rows, d)
+    P1 = pool_rows + H
+    route_loc = np.where(acc, (wave * n_dest + dest) * P1 + H + row, -1)
     pools = None
     if with_pools:
         x = np.asarray(x_bits, dtype=np.uint16)
-        d = x.shape[1]
-        if pool_rows > d:
-            raise ValueError("one header row holds at most d ids")
         pools = np.zeros((n_waves, n_dest, P1, d), dtype=np.uint16)
-        pools[:, :, 0, :] = HEADER_EMPTY
+        pools[:, :, :H, :] = HEADER_EMPTY
         r = np.nonzero(acc)[0]
         flat = pools.reshape(-1, d)                      # rows indexed like route_loc
         flat[route_loc[r]] = x[r // k]
-        header = (wave[r] * n_dest + dest[r]) * P1       # row 0 of the route's pool
-        flat[header, row[r]] = local[r].astype(np.uint16)
+        header = (wave[r] * n_dest + dest[r]) * P1       # first header row of the route's pool
+        flat[header + row[r] // d, row[r] % d] = local[r].astype(np.uint16)
     return dict(pools=pools, route_loc=route_loc, dest_counts=plan.sel,
                 sender_dropped=int(e.size - acc.sum()), wave=wave, row=row,
                 dest=dest, local=local, accepted=acc, bad=(e < -1) | (e >= n_exp))
@@ -559,37 +579,47 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
 # a8: receiver compaction into static per-expert arrays
 # ----------------------------------------------------------------------------
 
-def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool = True):
+def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool = True, rotation: int = 0):
     """Group one wave's incoming rows into ``[n_local, cap, d]`` arrays.
 
     Pooled wave §02/§03: the receiver reads each row's local expert id from
-    the header row and groups rows into six static expert arrays, dropping
+    the header rows and groups rows into six static expert arrays, dropping
     rows above the receiver capacity; §07: rows keep a fixed source order
     (source pool, then row) and overflow does not look at router scores.
+    ``rotation`` is the per-receiver rotation proposed in §07: sources are
+    visited in the order ``rotation, rotation+1, ..., n_src-1, 0, ...`` so
+    that overflow does not always fall on the same last source (0 = the
+    fixed order).  The pool height is ``pool_rows + header_rows(pool_rows, d)``.
 
     Returns a dict with ``compact`` (uint16 ``[n_local, cap, d]``, rows past
     ``counts[h]`` zero; None when ``with_rows`` is False), ``counts``,
-    ``arrived``, ``row_slot`` (int64 ``[n_src*(pool_rows+1)]``: ``h*cap + q``
+    ``arrived``, ``row_slot`` (int64 ``[n_src*(pool_rows+H)]``: ``h*cap + q``
     or -1; header rows -1), ``recv_dropped`` and ``bad_header`` (count of
     header ids that are neither a local id nor 0xFFFF).
     """
     pools = np.asarray(pools, dtype=np.uint16)
     S, P1, d = pools.shape
-    P = P1 - 1
-    h = pools[:, 0, :P].astype(np.int64).reshape(-1)        # (s, i) order
+    P = pool_rows_of(P1, d)
+    H = P1 - P
+    if not 0 <= rotation < max(S, 1):
+        raise ValueError("rotation must be in [0, n_src)")
+    order = (np.arange(S) + rotation) % S if S else np.arange(0)
+    # ids in visiting order: source order[v], then data row i
+    h = pools[order, :H, :].reshape(S, H * d)[:, :P].astype(np.int64).reshape(-1)
     valid = h < n_local
     bad = (h != HEADER_EMPTY) & ~valid
     plan = dispatch_plan(np.where(valid, h, -1), n_local, capacity=cap)
     q = plan.pos
     acc = plan.inv >= 0
-    s_idx, i_idx = np.divmod(np.arange(S * P), P)
+    v_idx, i_idx = np.divmod(np.arange(S * P), P)
+    s_idx = order[v_idx] if S else v_idx
     row_slot = np.full(S * P1, -1, dtype=np.int64)
-    row_slot[s_idx * P1 + 1 + i_idx] = np.where(acc, h * cap + q, -1)
+    row_slot[s_idx * P1 + H + i_idx] = np.where(acc, h * cap + q, -1)
     compact = None
     if with_rows:
         compact = np.zeros((n_local, cap, d), dtype=np.uint16)
         r = np.nonzero(acc)[0]
-        compact[h[r], q[r]] = pools[s_idx[r], 1 + i_idx[r]]
+        compact[h[r], q[r]] = pools[s_idx[r], H + i_idx[r]]
     return dict(compact=compact, counts=plan.counts, arrived=plan.sel, row_slot=row_slot,
                 recv_dropped=int(plan.sel.sum() - plan.counts.sum()),
                 bad_header=int(bad.sum()))
@@ -621,8 +651,8 @@ def loopback_layer(x_bits: np.ndarray, ids: np.ndarray, gates: np.ndarray, exper
     """
     T, k = ids.shape
     pk = pool_pack(x_bits, ids, experts_per_dest, n_dest, n_waves, pool_rows)
-    P1 = pool_rows + 1
     d = np.asarray(x_bits).shape[1]
+    P1 = pool_rows + header_rows(pool_rows, d)
     y = np.zeros((T, d))
     waves = []
     for w in range(n_waves):

@@ -250,10 +250,15 @@ def test_combine_window_and_accumulate():
 # ---------------------------------------------------------------------------
 
 def brute_pack(x, ids, epd, D, W, P):
+    """Route-by-route pack.  Header: as many full-width rows as the P ids need
+    (at least one); data row ``row`` sits below them."""
     T, k = ids.shape
     d = x.shape[1]
-    pools = np.zeros((W, D, P + 1, d), dtype=np.uint16)
-    pools[:, :, 0, :] = 0xFFFF
+    H = 1
+    while H * d < P:
+        H += 1
+    pools = np.zeros((W, D, P + H, d), dtype=np.uint16)
+    pools[:, :, :H, :] = 0xFFFF
     loc = [-1] * (T * k)
     ordinal = [0] * D
     for t in range(T):
@@ -267,17 +272,19 @@ def brute_pack(x, ids, epd, D, W, P):
             w, row = o % W, o // W
             if row >= P:
                 continue
-            pools[w, dst, 1 + row] = x[t]
-            pools[w, dst, 0, row] = l
-            loc[t * k + j] = (w * D + dst) * (P + 1) + 1 + row
+            pools[w, dst, H + row] = x[t]
+            pools[w, dst, row // d, row % d] = l
+            loc[t * k + j] = (w * D + dst) * (P + H) + H + row
     return pools, loc, ordinal
 
 
-@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("seed", range(8))
 def test_pool_pack_brute_force(seed):
     rng = np.random.default_rng(300 + seed)
-    epd, D, W, P = 3, 4, 2, int(rng.integers(1, 5))
-    T, k, d = 9, 2, 8
+    epd, D, W = 3, 4, int(rng.integers(1, 4))
+    # pools of up to three header rows (d = 8 ids per header row)
+    P = int(rng.integers(1, 5)) if seed < 4 else int(rng.integers(9, 21))
+    T, k, d = 30 if seed >= 4 else 9, 2, 8
     ids = rng.integers(-1, D * epd, size=(T, k))
     x = rng.integers(0, 2 ** 16, size=(T, d)).astype(np.uint16)
     pk = O.pool_pack(x, ids, epd, D, W, P)
@@ -314,37 +321,44 @@ def test_pool_pack_invariants():
     assert np.all(hdr[:, :, P:] == 0xFFFF)
 
 
-def brute_compact(pools, L, cap):
+def brute_compact(pools, L, cap, P, rotation=0):
+    """Row-by-row compaction, sources visited from ``rotation`` onward."""
     S, P1, d = pools.shape
+    H = P1 - P
     comp = np.zeros((L, cap, d), dtype=np.uint16)
     cnt = [0] * L
     slot = [-1] * (S * P1)
-    for s in range(S):
-        for i in range(P1 - 1):
-            h = int(pools[s, 0, i])
+    for v in range(S):
+        s = (rotation + v) % S
+        for i in range(P):
+            h = int(pools[s, i // d, i % d])
             if h >= L:
                 continue
             q = cnt[h]
             cnt[h] += 1
             if q < cap:
-                comp[h, q] = pools[s, 1 + i]
-                slot[s * P1 + 1 + i] = h * cap + q
+                comp[h, q] = pools[s, H + i]
+                slot[s * P1 + H + i] = h * cap + q
     return comp, cnt, slot
 
 
-@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("seed", range(8))
 def test_recv_compact_brute_force(seed):
     rng = np.random.default_rng(400 + seed)
-    S, P, d, L = 5, 6, 8, 3
+    S, d, L = 5, 8, 3
+    P = 6 if seed < 4 else int(rng.integers(9, 21))          # one to three header rows
+    H = -(-P // d)
+    rotation = 0 if seed % 2 == 0 else int(rng.integers(1, S))
     cap = int(rng.integers(1, 9))
-    pools = rng.integers(0, 2 ** 16, size=(S, P + 1, d)).astype(np.uint16)
+    pools = rng.integers(0, 2 ** 16, size=(S, P + H, d)).astype(np.uint16)
     hdr = rng.integers(0, L + 1, size=(S, P))
     hdr[hdr == L] = 0xFFFF
     hdr[0, 0] = 7                                             # bad id
-    pools[:, 0, :] = 0xFFFF
-    pools[:, 0, :P] = hdr
-    rc = O.recv_compact(pools, L, cap)
-    comp, cnt, slot = brute_compact(pools, L, cap)
+    flat = np.full((S, H * d), 0xFFFF, dtype=np.uint16)
+    flat[:, :P] = hdr
+    pools[:, :H, :] = flat.reshape(S, H, d)
+    rc = O.recv_compact(pools, L, cap, rotation=rotation)
+    comp, cnt, slot = brute_compact(pools, L, cap, P, rotation)
     assert np.array_equal(rc["compact"], comp)
     assert rc["arrived"].tolist() == cnt
     assert rc["counts"].tolist() == [min(c, cap) for c in cnt]
@@ -367,7 +381,7 @@ def test_loopback_identity_experts():
     y, det = O.loopback_layer(bits, ids, g, lambda e, rows: rows, epd, D, W, P, cap)
     loc = det["pack"]["route_loc"]
     kept = np.zeros(T * k, dtype=bool)
-    P1 = P + 1
+    P1 = P + O.header_rows(P, d)
     for w, rc in enumerate(det["waves"]):
         lo = w * D * P1
         inwave = (loc >= lo) & (loc < lo + D * P1)
@@ -379,3 +393,53 @@ def test_loopback_identity_experts():
     assert sent == arrived
     acc = sum(int(rc["counts"].sum()) for rc in det["waves"])
     assert acc + sum(rc["recv_dropped"] for rc in det["waves"]) == arrived
+
+
+def test_rotation_moves_overflow_to_the_last_visited_source():
+    """Pooled wave §07: with the fixed order, receiver overflow always falls
+    on the last sources; a rotation makes the last visited source take it."""
+    S, P, d, L, cap = 4, 5, 8, 2, 12
+    pools = np.zeros((S, P + 1, d), dtype=np.uint16)
+    pools[:, 0, :] = 0xFFFF
+    pools[:, 0, :P] = 0                                       # every row wants local expert 0
+    for rot in range(S):
+        rc = O.recv_compact(pools, L, cap, rotation=rot)
+        dropped_src = {s for s in range(S) for i in range(P) if rc["row_slot"][s * (P + 1) + 1 + i] < 0}
+        # 20 rows, 12 accepted: the last 8 visited rows (sources rot-1 and rot-2, wrapping) are dropped
+        assert dropped_src == {(rot - 1) % S, (rot - 2) % S}
+        assert rc["recv_dropped"] == S * P - cap
+        assert rc["counts"].tolist() == [cap, 0]
+
+
+def test_two_wave_profile_geometry():
+    """Pooled wave §04/§05: at two waves the sender pool grows to
+    ceil(1.10 * 524288 / 64 / 2) rows, which needs two header rows at
+    d = 3072, and the receiver array to ceil(1.15 * 524288 / 6 / 2)."""
+    P2 = O.capacity_ceil(110, 100, 524288, 64 * 2)
+    assert P2 == 4506 and O.header_rows(P2, 3072) == 2
+    assert O.capacity_ceil(115, 100, 524288, 6 * 2) == 50245
+    P3 = O.capacity_ceil(110, 100, 524288, 64 * 3)
+    assert P3 == 3004 and O.header_rows(P3, 3072) == 1
+    assert O.pool_rows_of(P2 + 2, 3072) == P2 and O.pool_rows_of(P3 + 1, 3072) == P3
+    # both profiles hold the same number of incoming rows per receiver
+    assert 2 * 64 * P2 == 3 * 64 * P3
+
+
+def test_loopback_identity_experts_two_header_rows():
+    rng = np.random.default_rng(13)
+    epd, D, W, P, cap = 3, 4, 2, 19, 40                       # 19 ids need three 8-wide header rows
+    T, k, d = 60, 2, 8
+    z = rng.standard_normal((T, D * epd)).astype(np.float32)
+    ids, g, _ = O.route_topk(z, k)
+    bits = rng.integers(0, 2 ** 15, size=(T, d)).astype(np.uint16)
+    y, det = O.loopback_layer(bits, ids, g, lambda e, rows: rows, epd, D, W, P, cap)
+    loc = det["pack"]["route_loc"]
+    H = O.header_rows(P, d)
+    assert H == 3
+    kept = np.zeros(T * k, dtype=bool)
+    for w, rc in enumerate(det["waves"]):
+        lo = w * D * (P + H)
+        inwave = (loc >= lo) & (loc < lo + D * (P + H))
+        kept |= inwave & (rc["row_slot"][np.where(inwave, loc - lo, 0)] >= 0)
+    mass = (g.reshape(-1) * kept).reshape(T, k).sum(1)
+    np.testing.assert_allclose(y, O.bf16_to_f64(bits) * mass[:, None], rtol=1e-12, atol=1e-300)
