@@ -88,14 +88,14 @@ def sources_digest(call):
     return h.hexdigest()
 
 
-def _call_of(kernel, kind):
+def _call_of(kernel):
     """The library call a dispatched kernel belongs to (None: not ours).
     Bucket-rank kernels are shared by three calls and are given to the call
     of the next dispatch, by the caller of this function."""
     table = (("route_topk_kernel", "route"), ("build_tiles_kernel", "swiglu"), ("grouped_gemm_", "swiglu"),
              ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
-             ("compact_rows_kernel", "recv_compact"),
-             ("combine_kernel", "expand" if kind == "recv" else "combine"), ("rank_", "rank"))
+             ("compact_rows_kernel", "recv_compact"), ("expand_rows_kernel", "expand"),
+             ("combine_kernel", "combine"), ("rank_", "rank"))
     for pat, call in table:
         if pat in kernel:
             return call
@@ -104,25 +104,24 @@ def _call_of(kernel, kind):
 
 # one dispatch per call instance: counts the launches of each call
 _ANCHORS = {"route": "route_topk_kernel", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
-            "combine": "combine_kernel", "expand": "combine_kernel", "pool_pack": "pack_kernel",
+            "combine": "combine_kernel", "expand": "expand_rows_kernel", "pool_pack": "pack_kernel",
             "recv_compact": "compact_rows_kernel"}
 
 
 def record_traffic(args):
     import csv
     w = W.WORKLOADS[args.workload]
-    kind = workload_kind(w)
     per = {}
     for counter, d in (("FETCH_SIZE", args.record_traffic[0]), ("WRITE_SIZE", args.record_traffic[1])):
         rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
                 if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         names = [r["Kernel_Name"] for r in rows]
-        first_ours = next(i for i, n in enumerate(names) if _call_of(n, kind))
+        first_ours = next(i for i, n in enumerate(names) if _call_of(n))
         # the calibration copy is the last plain device copy before the first library kernel
         calib = max(i for i in range(first_ours) if "copyBuffer" in names[i])
         factor = COPY_CALIB_BYTES / (float(rows[calib]["Counter_Value"]) * 1024.0)
-        calls = [_call_of(n, kind) for n in names]
+        calls = [_call_of(n) for n in names]
         nxt = None
         for i in range(len(calls) - 1, first_ours - 1, -1):    # rank kernels -> call of the next dispatch
             if calls[i] == "rank":
@@ -292,22 +291,22 @@ def recv_setup(torch, w, banks):
 
 def recv_step(ge, timer, w, bank, flags, bufs):
     import torch
-    S, P1, L, cap, d = w.n_src, w.pool_rows + 1, w.n_local, w.recv_cap, w.d
+    S, P1, L, cap, d = w.n_src, ge.pool_height(w.pool_rows, w.d), w.n_local, w.recv_cap, w.d
     starts = bufs["starts"]
     outs = []
     for wave in range(w.n_waves):
         rc = timer.run("recv_compact", ge.recv_compact, bank["pools"][wave], L, cap, compact=bufs["compact"],
                        flags=flags)
         z = timer.run("swiglu", ge.grouped_swiglu, bufs["compact"].view(L * cap, d), starts, rc["counts"],
-                      bank["wg"], bank["wu"], bank["wd"], z_dtype=torch.float32, z=bufs["z"], flags=flags)
-        ret = timer.run("expand", ge.unpermute_combine, z, rc["row_slot"], None, S * P1, 1,
-                        y=bufs["ret"][wave], flags=flags)
+                      bank["wg"], bank["wu"], bank["wd"], z=bufs["z"], flags=flags)
+        ret = timer.run("expand", ge.expand_rows, z, rc["row_slot"], ret=bufs["ret"][wave], flags=flags)
         outs.append((rc, ret))
     return outs
 
 
 def recv_ledger(w, counts_per_wave):
-    S, P, P1, d, dff = w.n_src, w.pool_rows, w.pool_rows + 1, w.d, w.d_ff
+    S, P, P1, d, dff = w.n_src, w.pool_rows, W.recv_header_rows(w) + w.pool_rows, w.d, w.d_ff
+    zb = 2 if w.ret_dtype == "bf16" else 4      # bytes per expert-output / return element
     led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0),
            "expand": dict(bytes=0, flops=0)}
     for counts in counts_per_wave:
@@ -315,9 +314,9 @@ def recv_ledger(w, counts_per_wave):
         E_act = int((counts > 0).sum())
         # header ids, accepted rows read and written (receiver-dropped rows are never read), row_slot
         led["recv_compact"]["bytes"] += S * P * 2 + 2 * A * d * 2 + 4 * S * P1
-        led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * 4
+        led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * zb
         led["swiglu"]["flops"] += 6 * A * d * dff
-        led["expand"]["bytes"] += A * d * 4 + 4 * S * P1 + S * P1 * d * 4
+        led["expand"]["bytes"] += A * d * zb + 4 * S * P1 + S * P1 * d * zb
     return led
 
 
@@ -361,7 +360,7 @@ def pack_step(ge, timer, w, bank, flags, bufs):
 def pack_ledger(w):
     T, k, d, E = w.T, w.k, w.d, w.E
     return {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
-            "pool_pack": dict(bytes=8 * T * k + T * d * 2 + w.n_waves * w.n_dest * (w.pool_rows + 1) * d * 2,
+            "pool_pack": dict(bytes=8 * T * k + T * d * 2 + w.n_waves * w.n_dest * (W.recv_header_rows(w) + w.pool_rows) * d * 2,
                               flops=0)}
 
 
@@ -440,9 +439,10 @@ def main():
     elif kind == "recv":
         host, bank_list = recv_setup(torch, w, banks)
         L, cap, d = w.n_local, w.recv_cap, w.d
+        rdt = torch.bfloat16 if w.ret_dtype == "bf16" else torch.float32
         bufs = dict(compact=torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda"),
-                    z=torch.empty((L * cap, d), dtype=torch.float32, device="cuda"),
-                    ret=[torch.empty((w.n_src * (w.pool_rows + 1), d), dtype=torch.float32, device="cuda")
+                    z=torch.empty((L * cap, d), dtype=rdt, device="cuda"),
+                    ret=[torch.empty((w.n_src * ge.pool_height(w.pool_rows, d), d), dtype=rdt, device="cuda")
                          for _ in range(w.n_waves)],
                     starts=torch.arange(L, dtype=torch.int32, device="cuda") * cap)
         step = lambda tm, b: recv_step(ge, tm, w, b, flags, bufs)
@@ -451,7 +451,7 @@ def main():
         step = lambda tm, b: router_step(ge, tm, w, b, flags)
     else:
         host, bank_list = pack_setup(torch, w, banks)
-        bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, w.pool_rows + 1, w.d), dtype=torch.bfloat16,
+        bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, ge.pool_height(w.pool_rows, w.d), w.d), dtype=torch.bfloat16,
                                       device="cuda"))
         step = lambda tm, b: pack_step(ge, tm, w, b, flags, bufs)
     # one plain device copy of known size (untimed): under rocprofv3 --pmc its

@@ -52,7 +52,9 @@ _SIGS = {
     "moe_pool_pack": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
                                      _p, _p, _sz, _p, _p]),
     "moe_recv_compact_workspace": (_sz, [_i32, _i32, _i32]),
-    "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_expand_rows": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i32, _p, _p]),
+    "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p,
+                                        _p]),
 }
 
 
@@ -212,6 +214,40 @@ def unpermute_combine(z: torch.Tensor, idx: torch.Tensor, gates: Optional[torch.
     return y
 
 
+def header_rows(pool_rows: int, d: int) -> int:
+    """Header rows of a pool as the library lays it out: one 16-bit id per
+    data row, ``d`` ids per row, at least one row."""
+    return max(1, -(-int(pool_rows) // int(d)))
+
+
+def pool_height(pool_rows: int, d: int) -> int:
+    """Rows of one pool: data rows plus header rows."""
+    return int(pool_rows) + header_rows(pool_rows, d)
+
+
+def pool_rows_of_height(height: int, d: int) -> int:
+    """Data rows of a pool that is ``height`` rows tall."""
+    for h in range(1, int(height) + 1):
+        if header_rows(height - h, d) == h:
+            return int(height) - h
+    raise ValueError(f"no pool of row width {d} is {height} rows tall")
+
+
+def expand_rows(z: torch.Tensor, row_slot: torch.Tensor, ret_dtype: torch.dtype = torch.float32,
+                ret: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None):
+    """``ret[i] = z[row_slot[i]]`` (converted) or a zero row; returns ``ret``."""
+    _need_gpu(z, row_slot, ret, flags)
+    d = z.shape[-1]
+    n_slots = z.numel() // d
+    n = row_slot.numel()
+    if ret is None:
+        ret = torch.empty((n, d), dtype=ret_dtype, device=row_slot.device)
+    _check("moe_expand_rows", lib.moe_expand_rows(
+        _ptr(z), _dtype_code(z), d, _ptr(row_slot), n, n_slots, _ptr(ret), _dtype_code(ret), _ptr(flags),
+        _stream(row_slot.device)))
+    return ret
+
+
 def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest: int, n_dest: int, n_waves: int,
               pool_rows: int, wave: int = -1, pools: Optional[torch.Tensor] = None,
               flags: Optional[torch.Tensor] = None):
@@ -220,7 +256,8 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
     T, d = x.shape
     k = topk_ids.shape[-1]
     dev = x.device
-    shape = (n_waves, n_dest, pool_rows + 1, d) if wave < 0 else (n_dest, pool_rows + 1, d)
+    PH = pool_height(pool_rows, d)
+    shape = (n_waves, n_dest, PH, d) if wave < 0 else (n_dest, PH, d)
     if pools is None:
         pools = torch.empty(shape, dtype=torch.bfloat16, device=dev)
     route_loc = torch.empty(T * k, dtype=torch.int32, device=dev)
@@ -234,10 +271,14 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
 
 
 def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Optional[torch.Tensor] = None,
-                 flags: Optional[torch.Tensor] = None):
-    """Returns a dict with compact [n_local, cap, d], counts, arrived, row_slot, recv_dropped."""
+                 flags: Optional[torch.Tensor] = None, rotation: int = 0):
+    """Returns a dict with compact [n_local, cap, d], counts, arrived, row_slot, recv_dropped.
+
+    ``pools_in`` is ``[n_src, pool_height, d]``; sources are visited from
+    ``rotation`` onwards."""
     _need_gpu(pools_in, compact, flags)
     S, P1, d = pools_in.shape
+    P = pool_rows_of_height(P1, d)
     dev = pools_in.device
     if compact is None:
         compact = torch.empty((n_local, cap, d), dtype=torch.bfloat16, device=dev)
@@ -245,8 +286,8 @@ def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Option
     arrived = torch.empty(n_local, dtype=torch.int32, device=dev)
     row_slot = torch.empty(S * P1, dtype=torch.int32, device=dev)
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
-    ws = _ws(lib.moe_recv_compact_workspace(S, P1 - 1, n_local), dev)
+    ws = _ws(lib.moe_recv_compact_workspace(S, P, n_local), dev)
     _check("moe_recv_compact", lib.moe_recv_compact(
-        _ptr(pools_in), S, P1 - 1, d, n_local, cap, _ptr(compact), _ptr(counts), _ptr(arrived), _ptr(row_slot),
-        _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+        _ptr(pools_in), S, P, d, n_local, cap, rotation, _ptr(compact), _ptr(counts), _ptr(arrived),
+        _ptr(row_slot), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
     return dict(compact=compact, counts=counts, arrived=arrived, row_slot=row_slot, recv_dropped=dropped)

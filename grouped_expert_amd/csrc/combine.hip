@@ -1,4 +1,4 @@
-// Un-permute and gate-weighted FP32 combine.
+// Un-permute and gate-weighted FP32 combine, and the receiver's row expansion.
 //
 // "M6.6 - MoE Runtime Systems", 0x03C3: the return path applies the inverse
 // permutation and the combine is a weighted scatter-add over the semantic key
@@ -94,8 +94,102 @@ void launch(const void* z, int32_t d, const int32_t* idx, int64_t lo, int64_t hi
                      static_cast<const ZT*>(z), d, idx, lo, hi, gates, k, y, acc, flags);
 }
 
+// Row expansion: one wavefront per output row, each lane moving 16-byte
+// output pieces (8 bf16 or 4 fp32 values) read from the slot's row.
+constexpr int kExpandRows = 4;
+
+template <typename ZT, typename RT>
+__device__ __forceinline__ vec16 expand_piece(const ZT* zrow, int64_t c);
+
+template <>
+__device__ __forceinline__ vec16 expand_piece<bf16_t, bf16_t>(const bf16_t* zrow, int64_t c) {
+  return reinterpret_cast<const vec16*>(zrow)[c];
+}
+
+template <>
+__device__ __forceinline__ vec16 expand_piece<float, float>(const float* zrow, int64_t c) {
+  return reinterpret_cast<const vec16*>(zrow)[c];
+}
+
+template <>
+__device__ __forceinline__ vec16 expand_piece<float, bf16_t>(const float* zrow, int64_t c) {
+  const float4 a = reinterpret_cast<const float4*>(zrow)[2 * c];
+  const float4 b = reinterpret_cast<const float4*>(zrow)[2 * c + 1];
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  vec16 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+  return o;
+}
+
+template <>
+__device__ __forceinline__ vec16 expand_piece<bf16_t, float>(const bf16_t* zrow, int64_t c) {
+  const uint2 q = reinterpret_cast<const uint2*>(zrow)[c];
+  vec16 o;
+  o[0] = q.x << 16;
+  o[1] = q.x & 0xffff0000u;
+  o[2] = q.y << 16;
+  o[3] = q.y & 0xffff0000u;
+  return o;
+}
+
+template <typename ZT, typename RT>
+__global__ __launch_bounds__(kExpandRows * kWave) void expand_rows_kernel(
+    const ZT* __restrict__ z, int64_t d, const int32_t* __restrict__ row_slot, int64_t n_rows, int64_t n_slots,
+    RT* __restrict__ ret, uint32_t* flags) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kExpandRows + threadIdx.x / kWave;
+  if (row >= n_rows) return;
+  const int32_t s = row_slot[row];
+  const bool live = s >= 0 && s < n_slots;
+  if (!live && s != -1 && lane == 0) flag_or(flags, MOE_FLAG_BAD_INDEX);
+  const int64_t pieces = d * static_cast<int64_t>(sizeof(RT)) / 16;
+  vec16* out = reinterpret_cast<vec16*>(ret + row * d);
+  if (!live) {
+    const vec16 zero = {0u, 0u, 0u, 0u};
+    for (int64_t c = lane; c < pieces; c += kWave) st_stream(zero, out + c);
+    return;
+  }
+  const ZT* zrow = z + static_cast<int64_t>(s) * d;
+  for (int64_t c = lane; c < pieces; c += kWave) st_stream(expand_piece<ZT, RT>(zrow, c), out + c);
+}
+
+template <typename ZT, typename RT>
+void launch_expand(const void* z, int32_t d, const int32_t* row_slot, int64_t n_rows, int64_t n_slots, void* ret,
+                   uint32_t* flags, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((n_rows + kExpandRows - 1) / kExpandRows);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(expand_rows_kernel<ZT, RT>), dim3(blocks), dim3(kExpandRows * kWave), 0, s,
+                     static_cast<const ZT*>(z), static_cast<int64_t>(d), row_slot, n_rows, n_slots,
+                     static_cast<RT*>(ret), flags);
+}
+
 }  // namespace
 }  // namespace moe
+
+MOE_API int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* row_slot, int64_t n_rows,
+                            int64_t n_slots, void* ret, int32_t ret_dtype, uint32_t* dev_flags,
+                            hipStream_t stream) {
+  using namespace moe;
+  MOE_CHECK((z_dtype == MOE_F32 || z_dtype == MOE_BF16) && (ret_dtype == MOE_F32 || ret_dtype == MOE_BF16),
+            MOE_EINVAL);
+  MOE_CHECK(d >= 8 && d % 8 == 0 && n_rows >= 0 && n_slots >= 0, MOE_EINVAL);
+  // the launch's total work-item count must fit 32 bits
+  MOE_CHECK(n_rows <= 0xFFFFFFFFLL / kWave && n_slots <= 0x80000000LL, MOE_EUNSUPPORTED);
+  if (n_rows == 0) return MOE_OK;
+  MOE_CHECK(row_slot && ret && (z || n_slots == 0), MOE_EINVAL);
+  MOE_CHECK(aligned16(ret) && (z == nullptr || aligned16(z)) && aligned4(row_slot), MOE_EINVAL);
+  if (z_dtype == MOE_BF16 && ret_dtype == MOE_BF16)
+    launch_expand<bf16_t, bf16_t>(z, d, row_slot, n_rows, n_slots, ret, dev_flags, stream);
+  else if (z_dtype == MOE_F32 && ret_dtype == MOE_F32)
+    launch_expand<float, float>(z, d, row_slot, n_rows, n_slots, ret, dev_flags, stream);
+  else if (z_dtype == MOE_F32)
+    launch_expand<float, bf16_t>(z, d, row_slot, n_rows, n_slots, ret, dev_flags, stream);
+  else
+    launch_expand<bf16_t, float>(z, d, row_slot, n_rows, n_slots, ret, dev_flags, stream);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
 
 MOE_API int moe_unpermute_combine(const void* z, int32_t z_dtype, int32_t d, const int32_t* idx, int64_t lo,
                                   int64_t hi, const float* gates, int64_t T, int32_t k, float* y,

@@ -5,25 +5,35 @@
 // reads each row's local expert id from the header row of its pool and groups
 // the rows into static [n_local, cap, d] expert arrays, dropping rows above
 // the receiver capacity; 04: the capacity is per local expert per wave; 07:
-// rows keep a fixed source order and overflow does not look at router scores.
+// rows keep a fixed source order and overflow does not look at router scores;
+// the rotation of that order per receiver (the fairness fix 07 proposes) is
+// the src_rotation argument: sources are visited from src_rotation onwards,
+// wrapping round.  A pool has H = max(1, ceil(pool_rows / d)) header rows.
 // "M6.6 - MoE Runtime Systems", 0x03C2: this is the second, receive-side
 // stable permutation into local-expert order.
 //
 // Launches: the shared bucket-rank passes over rows in (source, row) order
 // with bucket = header id (pass 3 writes row_slot), then a row copy that
-// moves every accepted row to its slot and marks header rows -1.
+// moves every accepted row to its slot and marks the header rows -1.
 #include "bucket_rank.h"
 
 namespace moe {
 namespace {
 
+// Rows are ranked in visiting order i = v * P + r, where v is the visit
+// number of source s = (v + rot) mod S.
+__device__ __forceinline__ int64_t visit_source(int64_t v, int64_t rot, int64_t S) {
+  const int64_t s = v + rot;
+  return s >= S ? s - S : s;
+}
+
 struct HeaderBucket {
   const bf16_t* pools;
-  int64_t P, P1, d;
+  int64_t P, P1, d, rot, S;
   int32_t L;
   __device__ uint32_t load(int64_t i) const {
-    const int64_t s = i / P, r = i - s * P;
-    return pools[s * P1 * d + r];
+    const int64_t v = i / P, r = i - v * P;
+    return pools[visit_source(v, rot, S) * P1 * d + r];   // id of data row r: element r of the header rows
   }
   __device__ int classify(uint32_t h, uint32_t* flags) const {
     if (h < static_cast<uint32_t>(L)) return static_cast<int>(h);
@@ -33,24 +43,24 @@ struct HeaderBucket {
 };
 
 struct CompactEmit {
-  int64_t P, P1, cap;
+  int64_t P, P1, H, rot, S, cap;
   int32_t* row_slot;
   __device__ void operator()(int64_t i, int h, int32_t q) const {
-    const int64_t s = i / P, r = i - s * P;
+    const int64_t v = i / P, r = i - v * P;
     const int32_t slot = (h >= 0 && q < cap) ? static_cast<int32_t>(h * cap + q) : -1;
-    row_slot[s * P1 + 1 + r] = slot;
+    row_slot[visit_source(v, rot, S) * P1 + H + r] = slot;
   }
 };
 
 constexpr int kRowsPerBlock = 4;   // one wavefront per incoming row
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_rows_kernel(
-    const vec16* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t row_vecs, int32_t* __restrict__ row_slot,
-    vec16* __restrict__ compact) {
+    const vec16* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t H, int64_t row_vecs,
+    int32_t* __restrict__ row_slot, vec16* __restrict__ compact) {
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= n_rows) return;
-  if (row % P1 == 0) {
+  if (row % P1 < H) {
     if (lane == 0) row_slot[row] = -1;
     return;
   }
@@ -72,14 +82,15 @@ MOE_API size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int3
 }
 
 MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d, int32_t n_local,
-                             int32_t cap, void* compact, int32_t* counts, int32_t* arrived, int32_t* row_slot,
-                             int32_t* recv_dropped, void* ws, size_t ws_bytes, uint32_t* dev_flags,
-                             hipStream_t stream) {
+                             int32_t cap, int32_t src_rotation, void* compact, int32_t* counts, int32_t* arrived,
+                             int32_t* row_slot, int32_t* recv_dropped, void* ws, size_t ws_bytes,
+                             uint32_t* dev_flags, hipStream_t stream) {
   using namespace moe;
   MOE_CHECK(n_src >= 0 && pool_rows >= 0 && n_local >= 1 && n_local <= MOE_MAX_EXPERTS && cap >= 0, MOE_EINVAL);
   MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
-  MOE_CHECK(pool_rows <= d, MOE_EUNSUPPORTED);
-  const int64_t P1 = static_cast<int64_t>(pool_rows) + 1;
+  MOE_CHECK(src_rotation >= 0 && src_rotation < (n_src > 0 ? n_src : 1), MOE_EINVAL);
+  const int64_t H = pool_rows > d ? (static_cast<int64_t>(pool_rows) + d - 1) / d : 1;
+  const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
   const int64_t n_rows = static_cast<int64_t>(n_src) * P1;
   MOE_CHECK(n_rows <= INT32_MAX && static_cast<int64_t>(n_local) * cap <= INT32_MAX, MOE_EUNSUPPORTED);
   MOE_CHECK(counts && recv_dropped, MOE_EINVAL);
@@ -96,13 +107,14 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_r
                                                    align_up((n_local + 1) * sizeof(int32_t), 256));
   RankScanOut out{arrived ? arrived : arrived_ws, counts, offsets, recv_dropped, 0};
   const bf16_t* pb = static_cast<const bf16_t*>(pools_in);
-  int st = bucket_rank(g, HeaderBucket{pb, pool_rows, P1, d, n_local}, CompactEmit{pool_rows, P1, cap, row_slot},
-                       cap, out, table, dev_flags, stream);
+  int st = bucket_rank(g, HeaderBucket{pb, pool_rows, P1, d, src_rotation, n_src, n_local},
+                       CompactEmit{pool_rows, P1, H, src_rotation, n_src, cap, row_slot}, cap, out, table, dev_flags,
+                       stream);
   if (st != MOE_OK) return st;
   if (n_rows > 0) {
     const unsigned blocks = static_cast<unsigned>((n_rows + kRowsPerBlock - 1) / kRowsPerBlock);
     hipLaunchKernelGGL(compact_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
-                       static_cast<const vec16*>(pools_in), n_rows, P1, static_cast<int64_t>(d) / 8, row_slot,
+                       static_cast<const vec16*>(pools_in), n_rows, P1, H, static_cast<int64_t>(d) / 8, row_slot,
                        static_cast<vec16*>(compact));
     MOE_LAUNCH_CHECK();
   }

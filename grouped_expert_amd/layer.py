@@ -37,20 +37,24 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, w_gate: torch.Tensor, w_up:
 
 def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: torch.Tensor, gates: torch.Tensor,
                   T: int, k: int, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, cap: int,
-                  y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None):
+                  y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None,
+                  rotation: int = 0, ret_dtype: torch.dtype = torch.float32):
     """One wave of the receiver path; adds the wave's contributions into ``y``.
 
-    ``pools_w`` is ``[n_src, pool_rows + 1, d]`` (one wave's pools).  ``bufs``
-    may hold preallocated ``compact``/``z``/``ret`` tensors to reuse."""
+    ``pools_w`` is ``[n_src, pool_height, d]`` (one wave's pools, header rows
+    included).  ``bufs`` may hold preallocated ``compact``/``z``/``ret``
+    tensors to reuse; ``rotation`` is the receiver's first source.  With
+    ``ret_dtype`` bf16 the expert rows leave the GEMM as bf16 and the return
+    buffer is bf16 ("M6.6 - MoE Runtime Systems", 0x0AE); the combine still
+    accumulates in FP32."""
     S, P1, d = pools_w.shape
     L = w_gate.shape[0]
     bufs = {} if bufs is None else bufs
-    rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags)
+    rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags, rotation=rotation)
     starts = torch.arange(L, dtype=torch.int32, device=pools_w.device) * cap
     z = B.grouped_swiglu(rc["compact"].view(L * cap, d), starts, rc["counts"], w_gate, w_up, w_down,
-                         z_dtype=torch.float32, z=bufs.get("z"), flags=flags)
-    ret = B.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, y=bufs.get("ret"), accumulate=False,
-                              flags=flags)
+                         z_dtype=ret_dtype, z=bufs.get("z"), flags=flags)
+    ret = B.expand_rows(z, rc["row_slot"], ret_dtype=ret_dtype, ret=bufs.get("ret"), flags=flags)
     lo = wave * S * P1
     B.unpermute_combine(ret, route_loc, gates, T, k, lo=lo, hi=lo + S * P1, y=y, accumulate=True, flags=flags)
     return rc, z, ret

@@ -87,7 +87,7 @@ typedef enum {
 #define MOE_FLAG_BAD_EXPERT      1u  /* expert id < -1 or >= E (route dropped) */
 #define MOE_FLAG_NONFINITE_LOGIT 2u  /* token with a NaN/Inf logit (all slots id -1) */
 #define MOE_FLAG_BAD_HEADER      4u  /* header id neither < n_local nor 0xFFFF (row ignored) */
-#define MOE_FLAG_BAD_INDEX       8u  /* combine index < -1 (route ignored) */
+#define MOE_FLAG_BAD_INDEX       8u  /* combine index < -1 or expand slot out of range (ignored) */
 #define MOE_FLAG_BAD_SEGMENT    16u  /* expert segment outside [0, rows) (expert skipped) */
 
 /* Limits of this build. */
@@ -251,25 +251,50 @@ int moe_unpermute_combine(const void* z, int32_t z_dtype, int32_t d,
                           float* y, int32_t accumulate, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_expand_rows -- receiver expansion of static-array results to pool rows.
+ *
+ * "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 03 (the receiver
+ * expands its expert rows back to the pool layout for the reverse exchange);
+ * "M6.6 - MoE Runtime Systems", 0x04B (padding and dropped rows never reach
+ * the combine) and 0x0AE (the returned row is BF16).  For i in [0, n_rows):
+ *   ret[i] = z[row_slot[i]]   converted to ret_dtype, if 0 <= row_slot[i] < n_slots
+ *   ret[i] = 0                otherwise (header, empty, receiver-dropped rows)
+ * f32 -> bf16 rounds to nearest even; bf16 -> f32 is exact; same dtype is a
+ * copy.  row_slot < -1 or >= n_slots sets MOE_FLAG_BAD_INDEX (row zeroed).
+ *
+ *   z          device [n_slots, d] of z_dtype (MOE_F32 or MOE_BF16)
+ *   d % 8 == 0
+ *   row_slot   device int32 [n_rows] (e.g. moe_recv_compact's row_slot)
+ *   ret        device [n_rows, d] of ret_dtype, every row written
+ * ------------------------------------------------------------------------- */
+int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* row_slot,
+                    int64_t n_rows, int64_t n_slots, void* ret, int32_t ret_dtype,
+                    uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_pool_pack -- pooled-wave sender pack into fixed destination pools.
  *
- * For route r = t*k + j with valid expert e = topk_ids[r] (pooled wave 02-04):
+ * A pool has H = max(1, ceil(pool_rows / d)) full-width header rows (one at
+ * the pages' sizes) followed by pool_rows data rows; PH = pool_rows + H.
+ * Header element i (row i / d, column i % d) holds data row i's local id.
+ *
+ * For route r = t*k + j with valid expert e = topk_ids[r] (pooled wave 02-05):
  *   dest = e / experts_per_dest,  local = e % experts_per_dest
  *   o_r  = #{r' < r : dest_r' = dest_r}     (the route's destination rank)
  *   wave = o_r % n_waves,  row = o_r / n_waves,  accepted iff row < pool_rows
- *   pools[wave][dest][1 + row][:] = x[t]
- *   pools[wave][dest][0][row]     = local   (header row, uint16)
- *   route_loc[r] = (wave*n_dest + dest)*(pool_rows + 1) + 1 + row, else -1
+ *   pools[wave][dest][H + row][:] = x[t]
+ *   header element row of pools[wave][dest] = local   (uint16)
+ *   route_loc[r] = (wave*n_dest + dest)*PH + H + row, else -1
  * Every other header element is 0xFFFF and every data row without a route
  * is zero.  dest_counts[dest] = routes to dest before the cap;
  * sender_dropped = T*k - accepted (routes above the cap plus routes whose id
  * is -1 or invalid; invalid ids set MOE_FLAG_BAD_EXPERT).
  *
- *   x_bf16     device bf16 [T, d], d % 8 == 0, pool_rows <= d
+ *   x_bf16     device bf16 [T, d], d % 8 == 0
  *   E <= n_dest * experts_per_dest, n_dest <= MOE_MAX_EXPERTS, 1 <= n_waves
- *   wave       -1: pools is [n_waves][n_dest][pool_rows + 1][d] (all waves);
- *              w >= 0: pools is [n_dest][pool_rows + 1][d], only wave w's rows
- *              and headers are written (route_loc keeps the all-wave index)
+ *   wave       -1: pools is [n_waves][n_dest][PH][d] (all waves);
+ *              w >= 0: pools is [n_dest][PH][d], only wave w's rows and
+ *              headers are written (route_loc keeps the all-wave index)
  *   route_loc  device int32 [T*k]; dest_counts int32 [n_dest]; sender_dropped int32 [1]
  *   ws         device workspace of moe_pool_pack_workspace(T, k, n_dest)
  * ------------------------------------------------------------------------- */
@@ -283,28 +308,32 @@ int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_
 /* ---------------------------------------------------------------------------
  * moe_recv_compact -- receiver compaction into static per-expert arrays.
  *
- * Over one wave's incoming pools, visited in fixed source order s = 0..n_src-1,
- * then i = 0..pool_rows-1 (pooled wave 02-04, 07):
- *   h = header[s][i] (uint16 at pools_in[s][0][i]); 0xFFFF = empty row
- *   q = number of earlier rows with the same h
- *   accepted iff q < cap:  compact[h][q][:] = pools_in[s][1 + i][:]
- *   row_slot[s*(pool_rows+1) + 1 + i] = h*cap + q, else -1
+ * Pools have the layout of moe_pool_pack: H = max(1, ceil(pool_rows / d))
+ * header rows, then pool_rows data rows; PH = pool_rows + H.  Over one
+ * wave's incoming pools, visiting sources s = (src_rotation + v) % n_src for
+ * v = 0..n_src-1 (src_rotation = 0: the fixed source order of pooled wave
+ * 07; another value is the per-receiver rotation proposed there), then
+ * i = 0..pool_rows-1 (pooled wave 02-04, 07):
+ *   h = header element i of source s (uint16); 0xFFFF = empty row
+ *   q = number of earlier visited rows with the same h
+ *   accepted iff q < cap:  compact[h][q][:] = pools_in[s][H + i][:]
+ *   row_slot[s*PH + H + i] = h*cap + q, else -1
  *   row_slot of header rows and empty rows = -1
  *   arrived[h] = rows with id h, counts[h] = min(arrived[h], cap),
  *   recv_dropped = sum_h arrived[h] - counts[h]
  * Header ids >= n_local other than 0xFFFF set MOE_FLAG_BAD_HEADER and the
  * row is ignored.  compact rows at or past counts[h] are not written.
  *
- *   pools_in   device bf16 [n_src][pool_rows + 1][d], d % 8 == 0, pool_rows <= d
- *   1 <= n_local <= MOE_MAX_EXPERTS, cap >= 0
+ *   pools_in   device bf16 [n_src][PH][d], d % 8 == 0
+ *   1 <= n_local <= MOE_MAX_EXPERTS, cap >= 0, 0 <= src_rotation < max(n_src, 1)
  *   compact    device bf16 [n_local][cap][d]
  *   counts int32 [n_local]; arrived int32 [n_local] or NULL;
- *   row_slot int32 [n_src*(pool_rows + 1)]; recv_dropped int32 [1]
+ *   row_slot int32 [n_src*PH]; recv_dropped int32 [1]
  *   ws         device workspace of moe_recv_compact_workspace(n_src, pool_rows, n_local)
  * ------------------------------------------------------------------------- */
 size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int32_t n_local);
 int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d,
-                     int32_t n_local, int32_t cap, void* compact, int32_t* counts,
+                     int32_t n_local, int32_t cap, int32_t src_rotation, void* compact, int32_t* counts,
                      int32_t* arrived, int32_t* row_slot, int32_t* recv_dropped,
                      void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
 

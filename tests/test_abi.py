@@ -14,7 +14,7 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 def test_exports_every_header_symbol():
     names = B.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
@@ -125,8 +125,10 @@ def test_pool_pack_validation():
     args = [p, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
     bad = list(args); bad[5] = 385                                  # E > n_dest * epd
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[9] = 4000                                 # header row cannot hold the ids
+    bad = list(args); bad[9] = 1 << 30                              # pool rows past the int32 route locations
     assert lib.moe_pool_pack(*bad) == EUNSUP
+    bad = list(args); bad[9] = -1                                   # negative pool rows
+    assert lib.moe_pool_pack(*bad) == EINVAL
     bad = list(args); bad[10] = 3                                   # wave out of range
     assert lib.moe_pool_pack(*bad) == EINVAL
     bad = list(args); bad[16] = 8                                   # workspace too small
@@ -136,15 +138,35 @@ def test_pool_pack_validation():
 def test_recv_compact_validation():
     p, _keep = _fake()
     ws = lib.moe_recv_compact_workspace(64, 3004, 6)
-    args = [p, 64, 3004, 3072, 6, 33497, p, p, p, p, p, p, ws, NULL, NULL]
+    args = [p, 64, 3004, 3072, 6, 33497, 0, p, p, p, p, p, p, ws, NULL, NULL]
     bad = list(args); bad[5] = -1                                   # negative capacity
     assert lib.moe_recv_compact(*bad) == EINVAL
     bad = list(args); bad[4] = 0                                    # no local experts
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[12] = 0                                   # workspace
+    bad = list(args); bad[6] = 64                                   # rotation past the last source
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[6] = -1                                   # negative rotation
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[13] = 0                                   # workspace
     assert lib.moe_recv_compact(*bad) == EWS
-    bad = list(args); bad[3] = 1000                                 # header row too narrow
+    bad = list(args); bad[2] = 1 << 26                              # pool rows past int32 row indexes
     assert lib.moe_recv_compact(*bad) == EUNSUP
+
+
+def test_expand_rows_validation():
+    p, _keep = _fake()
+    args = [p, 1, 3072, p, 100, 50, p, 0, NULL, NULL]
+    bad = list(args); bad[1] = 2                                    # unknown z dtype
+    assert lib.moe_expand_rows(*bad) == EINVAL
+    bad = list(args); bad[7] = 5                                    # unknown return dtype
+    assert lib.moe_expand_rows(*bad) == EINVAL
+    bad = list(args); bad[2] = 12                                   # d not a multiple of 8
+    assert lib.moe_expand_rows(*bad) == EINVAL
+    bad = list(args); bad[4] = 1 << 40                              # more rows than one launch holds
+    assert lib.moe_expand_rows(*bad) == EUNSUP
+    bad = list(args); bad[6] = NULL                                 # no output
+    assert lib.moe_expand_rows(*bad) == EINVAL
+    assert lib.moe_expand_rows(NULL, 0, 64, NULL, 0, 0, NULL, 1, NULL, NULL) == 0   # nothing to do
 
 
 def test_workspace_queries_reject_bad_sizes():

@@ -274,6 +274,37 @@ def test_unpermute_combine(ge, T, k, d, zdt, window, acc):
     assert int(to_np(flags)[0]) == 0
 
 
+@pytest.mark.parametrize("zdt,rdt", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("n,nz,d", [(1000, 300, 3072), (77, 5, 8), (3, 0, 64), (0, 4, 16)])
+def test_expand_rows(ge, zdt, rdt, n, nz, d):
+    """Expansion of static-array rows to pool rows: a copy (exact), a widening
+    (exact) or a rounding to bf16 (nearest even, bit-exact)."""
+    rng = np.random.default_rng(n + nz + d)
+    z32 = rng.standard_normal((max(nz, 1), d)).astype(np.float32)[:nz]
+    z = z32 if zdt == "f32" else _bf16(z32)
+    slot = rng.integers(-1, max(nz, 1), size=n).astype(np.int32) if nz else np.full(n, -1, np.int32)
+    flags = ge.new_flags("cuda")
+    zt = to_gpu(z) if nz else torch.empty((0, d), dtype=torch.float32 if zdt == "f32" else torch.bfloat16,
+                                          device="cuda")
+    st = to_gpu(slot) if n else torch.empty(0, dtype=torch.int32, device="cuda")
+    ret = ge.expand_rows(zt, st, ret_dtype=torch.float32 if rdt == "f32" else torch.bfloat16, flags=flags)
+    want = O.expand_rows(z if nz else np.zeros((0, d), np.float32), slot.astype(np.int64))
+    got = to_np(ret)
+    assert got.shape == (n, d) and int(to_np(flags)[0]) == 0
+    if rdt == "bf16":
+        assert np.array_equal(got, _bf16(want.astype(np.float32)))      # nearest-even of an exact value
+    else:
+        assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_expand_rows_bad_slot_flag(ge):
+    z = to_gpu(np.ones((4, 8), np.float32))
+    flags = ge.new_flags("cuda")
+    ret = ge.expand_rows(z, to_gpu(np.array([0, -5, 4, 3, -1], np.int32)), ret_dtype=torch.bfloat16, flags=flags)
+    assert int(to_np(flags)[0]) == 8
+    assert (as_f64(ret) == np.array([[1.0] * 8, [0.0] * 8, [0.0] * 8, [1.0] * 8, [0.0] * 8])).all()
+
+
 def test_combine_bad_index_flag(ge):
     z = to_gpu(np.ones((4, 8), np.float32))
     idx = to_gpu(np.array([0, -5, 1, 2], np.int32))
@@ -292,7 +323,10 @@ def test_combine_bad_index_flag(ge):
                                                   (500, 8, 3, 16, 2, 100, 128, 1),
                                                   (64, 2, 1, 4, 1, 0, 8, -1),
                                                   (0, 2, 2, 3, 3, 5, 8, -1),
-                                                  (3000, 8, 6, 64, 3, 30, 64, 2)])
+                                                  (3000, 8, 6, 64, 3, 30, 64, 2),
+                                                  (400, 4, 3, 8, 2, 30, 8, -1),      # four header rows
+                                                  (3000, 8, 6, 16, 2, 150, 64, 1),   # three header rows
+                                                  (900, 8, 2, 8, 2, 129, 128, -1)])  # two, second one 1 id
 def test_pool_pack(ge, T, k, epd, D, W, P, d, wave):
     rng = np.random.default_rng(T + D + P)
     E = D * epd
@@ -316,22 +350,28 @@ def test_pool_pack(ge, T, k, epd, D, W, P, d, wave):
     assert (int(to_np(flags)[0]) & 1 != 0) == bool(pk["bad"].any())
 
 
-@pytest.mark.parametrize("S,P,d,L,cap", [(8, 40, 64, 6, 30), (64, 100, 128, 6, 700), (5, 6, 8, 3, 0),
-                                         (3, 0, 8, 2, 4), (40, 200, 256, 17, 100)])
-def test_recv_compact(ge, S, P, d, L, cap):
-    rng = np.random.default_rng(S * P + L)
-    pools = rng.integers(0, 2 ** 16, size=(S, P + 1, d)).astype(np.uint16)
+@pytest.mark.parametrize("S,P,d,L,cap,rot", [(8, 40, 64, 6, 30, 0), (64, 100, 128, 6, 700, 0), (5, 6, 8, 3, 0, 0),
+                                             (3, 0, 8, 2, 4, 0), (40, 200, 256, 17, 100, 0),
+                                             (8, 40, 64, 6, 30, 5),             # rotated source order
+                                             (7, 30, 8, 3, 25, 6),              # four header rows, rotated
+                                             (33, 129, 128, 6, 300, 1),         # two header rows
+                                             (1, 20, 8, 2, 3, 0)])
+def test_recv_compact(ge, S, P, d, L, cap, rot):
+    rng = np.random.default_rng(S * P + L + rot)
+    H = O.header_rows(P, d)
+    pools = rng.integers(0, 2 ** 16, size=(S, P + H, d)).astype(np.uint16)
     p = (np.arange(1, L + 1) ** -1.1)
     hdr = rng.choice(L, size=(S, P), p=p / p.sum()).astype(np.uint16)
     if P > 3:
-        hdr[1, 2] = 0xFFFF
+        hdr[1 % S, 2] = 0xFFFF
         hdr[0, 3] = L + 1                         # bad id
-    pools[:, 0, :] = 0xFFFF
-    pools[:, 0, :P] = hdr
+    flat = np.full((S, H * d), 0xFFFF, dtype=np.uint16)
+    flat[:, :P] = hdr
+    pools[:, :H, :] = flat.reshape(S, H, d)
     flags = ge.new_flags("cuda")
     compact0 = torch.zeros((L, cap, d), dtype=torch.bfloat16, device="cuda")
-    out = ge.recv_compact(to_gpu(pools), L, cap, compact=compact0, flags=flags)
-    rc = O.recv_compact(pools, L, cap)
+    out = ge.recv_compact(to_gpu(pools), L, cap, compact=compact0, flags=flags, rotation=rot)
+    rc = O.recv_compact(pools, L, cap, rotation=rot)
     assert np.array_equal(to_np(out["compact"]), rc["compact"])
     assert to_np(out["counts"]).tolist() == rc["counts"].tolist()
     assert to_np(out["arrived"]).tolist() == rc["arrived"].tolist()

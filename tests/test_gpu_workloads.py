@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, through the same library calls
+"""GPU parity at the workloads' full sizes, through the same library calls
 (and so the same launch configurations) that bench.py times.
 
 Integer outputs (ids, plans, pools, headers, compaction maps, drop counts) are
@@ -107,11 +107,12 @@ def test_decode_bf16(ge):
     assert (plan.counts == 0).sum() > 50 and plan.counts.max() <= 8
 
 
-@pytest.fixture(scope="module")
-def send_case():
-    """Inputs and the oracle's routing and pack of the sender-pack workload
-    (computed once for the tests that use them)."""
-    w = W.SEND
+@pytest.fixture(scope="module", params=["sender_pack_bf16", "sender_pack_2w_bf16"])
+def send_case(request):
+    """Inputs and the oracle's routing and pack of a sender-pack workload, three
+    waves of 3004-row pools or two waves of 4506-row pools with two header
+    rows (computed once for the tests that use them)."""
+    w = W.WORKLOADS[request.param]
     logits = W.router_logits(w)
     x = W.tokens(w)
     ids, gates, _ = O.route_topk(logits, w.k)
@@ -121,7 +122,8 @@ def send_case():
 
 def test_sender_pack_full(ge, send_case):
     """Sender pack of 65,536 tokens x top-8 over 384 experts into three waves of
-    [64, 3005, 3072] pools: every byte of every pool, every route location."""
+    [64, 3005, 3072] pools (or two of [64, 4508, 3072]): every byte of every
+    pool, every route location."""
     c = send_case
     w, pk = c["w"], c["pk"]
     flags = ge.new_flags("cuda")
@@ -142,15 +144,19 @@ def test_sender_pack_full(ge, send_case):
     assert 0.0 < rate < 0.1
 
 
-def test_recv_share(ge):
+@pytest.mark.parametrize("name,rotation", [("recv_share_bf16", 0), ("recv_share_2w_bf16", 17)])
+def test_recv_share(ge, name, rotation):
     """Receiver share: three waves of 64 x 3004 incoming rows, six local
-    experts, capacity 33,497.  Wave 0's compaction in full; all waves'
+    experts, capacity 33,497, sources in the fixed order; or the two-wave
+    profile (64 x 4506 rows behind two header rows, capacity 50,245) with the
+    sources visited from source 17.  Wave 0's compaction in full; all waves'
     counters; expert outputs and the fp32 expansion on sampled rows."""
-    w = W.RECV
+    w = W.WORKLOADS[name]
     wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
     bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
     gw = [to_gpu(a) for a in (wg, wu, wd)]
-    L, cap, d, S, P1 = w.n_local, w.recv_cap, w.d, w.n_src, w.pool_rows + 1
+    L, cap, d, S = w.n_local, w.recv_cap, w.d, w.n_src
+    P1 = O.header_rows(w.pool_rows, d) + w.pool_rows
     compact = torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda")
     z = torch.empty((L * cap, d), dtype=torch.float32, device="cuda")
     starts = torch.arange(L, dtype=torch.int32, device="cuda") * cap
@@ -159,12 +165,13 @@ def test_recv_share(ge):
     for wave in range(w.n_waves):
         pools = W.recv_pools(w, wave)
         flags = ge.new_flags("cuda")
-        rc = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags)
+        assert pools.shape == (S, P1, d)
+        rc = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags, rotation=rotation)
         ge.grouped_swiglu(compact.view(L * cap, d), starts, rc["counts"], *gw, z=z, flags=flags)
         ret = ge.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, flags=flags)
         torch.cuda.synchronize()
         assert int(to_np(flags)[0]) == 0
-        orc = O.recv_compact(pools, L, cap, with_rows=(wave == 0))
+        orc = O.recv_compact(pools, L, cap, with_rows=(wave == 0), rotation=rotation)
         counts = to_np(rc["counts"])
         assert np.array_equal(counts, orc["counts"])
         assert np.array_equal(to_np(rc["arrived"]), orc["arrived"])
@@ -198,16 +205,20 @@ def test_recv_share(ge):
     assert total_drop > 0
 
 
-@pytest.mark.parametrize("cap", [33497, 28400])
-def test_loopback_sender_to_receiver(ge, send_case, cap):
-    """Sender pools of the sender-pack workload fed back to a receiver with
-    six local experts (the receiver workload's weights): for sampled tokens
-    the FP32 accumulation over the three waves equals the sum of gated
-    outputs of the routes that both capacities kept.  The receiver capacity
-    is the page's 33,497 (no receiver drop with a single sender's traffic)
-    and a lower 28,400 that makes the receiver drop rows."""
+@pytest.mark.parametrize("cap_kind,ret", [("page", "f32"), ("low", "f32"), ("low", "bf16")])
+def test_loopback_sender_to_receiver(ge, send_case, cap_kind, ret):
+    """Sender pools of a sender-pack workload fed back to a receiver with six
+    local experts (the receiver workload's weights): for sampled tokens the
+    FP32 accumulation over the waves equals the sum of gated outputs of the
+    routes that both capacities kept.  The receiver capacity is the page's
+    (33,497 at three waves, 50,245 at two: no receiver drop with a single
+    sender's traffic) or 85% of it, which makes the receiver drop rows.  The
+    return rows are FP32 or bf16 (rounded once, as they leave the GEMM); the
+    receiver visits the sources from source 5 when the rows are bf16."""
     c = send_case
-    ws, wr = c["w"], W.RECV
+    ws = c["w"]
+    wr = W.RECV if ws.n_waves == 3 else W.RECV_2W
+    cap = wr.recv_cap if cap_kind == "page" else int(0.85 * wr.recv_cap)
     ids, gates, pk, x = c["ids"], c["gates"], c["pk"], c["x"]
     wg, wu, wd = W.all_expert_weights(wr, n_experts=wr.n_local)
     gw = [to_gpu(a) for a in (wg, wu, wd)]
@@ -216,30 +227,32 @@ def test_loopback_sender_to_receiver(ge, send_case, cap):
     pk_g = ge.pool_pack(to_gpu(x), ids_g, ws.E, ws.experts_per_dest, ws.n_dest, ws.n_waves, ws.pool_rows,
                         flags=flags)
     y = torch.zeros((ws.T, ws.d), dtype=torch.float32, device="cuda")
+    rdt = torch.bfloat16 if ret == "bf16" else torch.float32
+    rot = 5 if ret == "bf16" else 0
     bufs = dict(compact=torch.empty((wr.n_local, cap, ws.d), dtype=torch.bfloat16, device="cuda"),
-                z=torch.empty((wr.n_local * cap, ws.d), dtype=torch.float32, device="cuda"))
+                z=torch.empty((wr.n_local * cap, ws.d), dtype=rdt, device="cuda"))
     slots, drops = [], 0
     for wave in range(ws.n_waves):
         rc, _, _ = ge.loopback_wave(pk_g["pools"][wave], wave, ws.n_waves, pk_g["route_loc"], gates_g, ws.T, ws.k,
-                                    *gw, cap, y, flags=flags, bufs=bufs)
+                                    *gw, cap, y, flags=flags, bufs=bufs, rotation=rot, ret_dtype=rdt)
         slots.append(to_np(rc["row_slot"]))
         drops += int(to_np(rc["recv_dropped"])[0])
     torch.cuda.synchronize()
     assert int(to_np(flags)[0]) == 0
 
-    P1 = ws.pool_rows + 1
+    P1 = O.header_rows(ws.pool_rows, ws.d) + ws.pool_rows
     loc = pk["route_loc"]
     kept = np.zeros(loc.size, dtype=bool)
     want_drops = 0
     for wave in range(ws.n_waves):
-        rc = O.recv_compact(pk["pools"][wave], wr.n_local, cap, with_rows=False)
+        rc = O.recv_compact(pk["pools"][wave], wr.n_local, cap, with_rows=False, rotation=rot)
         assert np.array_equal(slots[wave], rc["row_slot"])
         want_drops += rc["recv_dropped"]
         lo = wave * ws.n_dest * P1
         inw = (loc >= lo) & (loc < lo + ws.n_dest * P1)
         kept[inw] = rc["row_slot"][loc[inw] - lo] >= 0
     assert drops == want_drops
-    assert (want_drops > 0) == (cap < 33497)
+    assert (want_drops > 0) == (cap < wr.recv_cap)
     rng = np.random.default_rng(2)
     tok = np.unique(np.concatenate([rng.choice(ws.T, size=40, replace=False),
                                     np.nonzero(~kept.reshape(ws.T, ws.k).all(axis=1))[0][:8]]))

@@ -76,6 +76,7 @@ class Workload:
     n_local: int = 0
     recv_cap: int = 0
     recv_zipf: float = 0.0
+    ret_dtype: str = "f32"     # receiver return rows: "f32" or "bf16"
     # group-restricted router (gating variants)
     gating: int = 0            # 0 softmax-renorm, 1 V1, 2 V2, 3 V3 (the library's moe_gating ids)
     n_group: int = 0
@@ -98,6 +99,18 @@ RECV = Workload(name="recv_share_bf16", seed=2, dtype="bf16", d=3072, d_ff=1536,
 SEND = Workload(name="sender_pack_bf16", seed=3, dtype="bf16", T=65536, d=3072,
                 E=384, k=8, logits="normal", zipf_bias=1.1, x_std=1.0,
                 experts_per_dest=6, n_dest=64, n_waves=3, pool_rows=3004)
+# The two-wave profile (pooled wave 05): the same incoming rows per receiver in
+# two waves, so each pool holds ceil(1.10 * 524288 / 128) rows (two header
+# rows at d = 3072) and each receiver array ceil(1.15 * 524288 / 12) rows.
+RECV_2W = Workload(name="recv_share_2w_bf16", seed=2, dtype="bf16", d=3072, d_ff=1536,
+                   E=6, n_src=64, pool_rows=4506, n_waves=2, n_local=6, recv_cap=50245,
+                   recv_zipf=1.1, x_std=1.0, w_std=0.02)
+# The receiver share with bf16 return rows ("M6.6", 0x0AE: the returned row is
+# BF16): the expert GEMM stores bf16 and the return buffer is bf16.
+RECV_RET16 = dataclasses.replace(RECV, name="recv_share_ret_bf16", ret_dtype="bf16")
+SEND_2W = Workload(name="sender_pack_2w_bf16", seed=3, dtype="bf16", T=65536, d=3072,
+                   E=384, k=8, logits="normal", zipf_bias=1.1, x_std=1.0,
+                   experts_per_dest=6, n_dest=64, n_waves=2, pool_rows=4506)
 DECODE = Workload(name="decode_bf16", seed=4, dtype="bf16", T=64, d=3072, E=384,
                   k=8, d_ff=1536, logits="normal", x_std=1.0, w_std=0.02)
 
@@ -106,7 +119,7 @@ DECODE = Workload(name="decode_bf16", seed=4, dtype="bf16", T=64, d=3072, E=384,
 ROUTER_V3 = Workload(name="router_v3_f32", seed=5, dtype="f32", T=65536, E=256, k=8, logits="normal",
                      gating=3, n_group=8, topk_group=4, route_scale=2.5, bias_std=0.05)
 
-WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3)}
+WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3, RECV_2W, SEND_2W, RECV_RET16)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
@@ -222,27 +235,34 @@ def recv_local_ids(w: Workload, wave: int) -> np.ndarray:
     return rng.choice(w.n_local, size=(w.n_src, w.pool_rows), p=p).astype(np.uint16)
 
 
-def recv_pools(w: Workload, wave: int, ids: Optional[np.ndarray] = None) -> np.ndarray:
-    """Incoming bf16 pools ``[n_src, pool_rows + 1, d]`` for one wave.
+def recv_header_rows(w: Workload) -> int:
+    """Header rows per incoming pool: ``d`` 16-bit ids per row, at least one."""
+    return max(1, -(-w.pool_rows // w.d))
 
-    Row 0 of each pool is the header: element ``i`` holds the 16-bit local
-    expert id of data row ``i`` (stored at pool row ``1 + i``); elements past
-    ``pool_rows`` hold 0xFFFF.  Every data row of this workload is occupied.
-    ``ids`` may override the drawn ids (0xFFFF marks an empty row).
+
+def recv_pools(w: Workload, wave: int, ids: Optional[np.ndarray] = None) -> np.ndarray:
+    """Incoming bf16 pools ``[n_src, H + pool_rows, d]`` for one wave.
+
+    The first ``H = recv_header_rows(w)`` rows of each pool are the header:
+    element ``i`` of the flattened header holds the 16-bit local expert id of
+    data row ``i`` (stored at pool row ``H + i``); elements past ``pool_rows``
+    hold 0xFFFF.  Every data row of this workload is occupied.  ``ids`` may
+    override the drawn ids (0xFFFF marks an empty row).
     """
     if ids is None:
         ids = recv_local_ids(w, wave)
-    if w.pool_rows > w.d:
-        raise ValueError("one header row holds at most d ids")
-    pools = np.empty((w.n_src, w.pool_rows + 1, w.d), dtype=np.uint16)
-    pools[:, 0, :] = HEADER_EMPTY
-    pools[:, 0, : w.pool_rows] = ids
+    H = recv_header_rows(w)
+    pools = np.empty((w.n_src, H + w.pool_rows, w.d), dtype=np.uint16)
+    hdr = pools[:, :H, :].reshape(w.n_src, H * w.d)
+    hdr[:] = HEADER_EMPTY
+    hdr[:, : w.pool_rows] = ids
+    pools[:, :H, :] = hdr.reshape(w.n_src, H, w.d)
     base = _rng(w.seed, _TAG_RECV_ROWS, wave)
     seeds = base.integers(0, 2**63 - 1, size=w.n_src)
 
     def one(s):
         r = np.random.Generator(np.random.PCG64(int(seeds[s])))
-        pools[s, 1:, :] = f32_to_bf16_bits(_normal(r, (w.pool_rows, w.d), w.x_std))
+        pools[s, H:, :] = f32_to_bf16_bits(_normal(r, (w.pool_rows, w.d), w.x_std))
 
     with _cf.ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(one, range(w.n_src)))
