@@ -15,7 +15,8 @@ Sources (page title, then section):
   capacity, §0x03B count / prefix / permute, §0x03C forward transpose,
   §0x03G executable logical transpose and its rejection list, §0x04D the two
   layouts (token-major repeat vs expert-major sort), §0x06L1 family table
-  (Mixtral row: FP32 softmax, top-k, renormalise to one).
+  (Mixtral row: FP32 softmax, top-k, renormalise to one),
+  §0x03D backward as the reverse semantic transpose.
 * "Fixed pooled-wave all-to-all for the 8-of-384 MoE" (cited as *pooled
   wave*): §02 pools and stripe rule, §03 one wave, §04 capacities, §05 drop
   metrics, §07 fixed source order on the receiver.
@@ -61,6 +62,8 @@ __all__ = [
     "DispatchPlan", "dispatch_plan", "check_dispatch",
     "gather_rows", "silu", "swiglu_expert", "swiglu_bank", "scalar_bank", "run_segments",
     "combine", "moe_layer_token_major", "moe_layer_expert_major",
+    "combine_backward", "silu_grad", "swiglu_expert_backward", "swiglu_bank_backward",
+    "scalar_bank_backward", "run_segments_backward", "moe_layer_backward",
     "header_rows", "pool_rows_of", "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
     "capacity_ceil", "drop_rates", "swiglu_flops", "padded_exec_rows",
     "block_exec_rows",
@@ -499,6 +502,122 @@ def moe_layer_expert_major(x: np.ndarray, ids: np.ndarray, gates: np.ndarray,
     z = run_segments(xp, plan.offsets[:-1], plan.counts, expert)
     y = combine(z, plan.inv, gates, T, k)
     return y, plan
+
+
+# ----------------------------------------------------------------------------
+# backward of the transpose (M6.2 §0x03D)
+# ----------------------------------------------------------------------------
+
+ExpertBwd = Callable[[int, np.ndarray, np.ndarray], Tuple[np.ndarray, tuple]]
+"""Expert backward: ``f(e, rows_f64, dz_f64) -> (dx_f64, parameter_grads)``."""
+
+
+def combine_backward(dy: np.ndarray, z_rows: np.ndarray, idx: np.ndarray, gates: np.ndarray,
+                     T: int, k: int):
+    """Reverse of :func:`combine` (M6.2 §0x03D): an accepted route ``r`` of
+    token ``t`` whose row is ``p = idx[r]`` receives ``Zbar_p = g_r Ybar_t``
+    and the gate gradient ``gbar_r = <Ybar_t, Z_p>``.  Routes without a row
+    (``idx = -1``) get ``gbar = 0`` and write nothing.
+
+    Returns ``(dz [rows, d] float64, zero where no route points, dgates
+    [T, k] float64)``.
+    """
+    dyf = np.asarray(dy, dtype=np.float64)
+    z = to_f64(z_rows)
+    idx = np.asarray(idx, dtype=np.int64).reshape(T, k)
+    g = np.asarray(gates, dtype=np.float64).reshape(T, k)
+    dz = np.zeros_like(z)
+    dg = np.zeros((T, k))
+    for j in range(k):
+        t = np.nonzero(idx[:, j] >= 0)[0]
+        p = idx[t, j]
+        dz[p] = g[t, j, None] * dyf[t]
+        dg[t, j] = np.einsum("ij,ij->i", dyf[t], z[p])
+    return dz, dg
+
+
+def silu_grad(v: np.ndarray) -> np.ndarray:
+    """d SiLU / dv = sigma(v) (1 + v (1 - sigma(v)))."""
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-v))
+    return s * (1.0 + v * (1.0 - s))
+
+
+def swiglu_expert_backward(x: np.ndarray, dz: np.ndarray, wg: np.ndarray, wu: np.ndarray,
+                           wd: np.ndarray):
+    """Reverse of :func:`swiglu_expert` (chain rule through M6.6 §0x04A):
+    with ``G = X W_g^T``, ``U = X W_u^T``, ``H = SiLU(G) (.) U``,
+    ``Z = H W_d^T``:  ``Hbar = Zbar W_d``, ``W_d bar = Zbar^T H``,
+    ``Gbar = Hbar (.) U (.) SiLU'(G)``, ``Ubar = Hbar (.) SiLU(G)``,
+    ``Xbar = Gbar W_g + Ubar W_u``, ``W_g bar = Gbar^T X``,
+    ``W_u bar = Ubar^T X``.  Returns ``(dx, (dwg, dwu, dwd))``."""
+    g = x @ wg.T
+    u = x @ wu.T
+    h = silu(g) * u
+    dh = dz @ wd
+    dwd = dz.T @ h
+    dg = dh * u * silu_grad(g)
+    du = dh * silu(g)
+    dx = dg @ wg + du @ wu
+    return dx, (dg.T @ x, du.T @ x, dwd)
+
+
+def swiglu_bank_backward(weights: Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]) -> ExpertBwd:
+    """Backward of :func:`swiglu_bank` with the same stored weights."""
+    def run(e: int, x: np.ndarray, dz: np.ndarray):
+        wg, wu, wd = (to_f64(w) for w in weights(e))
+        return swiglu_expert_backward(x, dz, wg, wu, wd)
+    return run
+
+
+def scalar_bank_backward(scales) -> ExpertBwd:
+    """Backward of :func:`scalar_bank`: ``Xbar = s_e Zbar`` and
+    ``s_e bar = sum <Zbar, X>`` over the expert's rows (M6.2 §0x03D toy)."""
+    s = [float(v) for v in scales]
+    return lambda e, x, dz: (s[e] * dz, (float((dz * x).sum()),))
+
+
+def run_segments_backward(rows: np.ndarray, dz: np.ndarray, seg_start: np.ndarray,
+                          seg_count: np.ndarray, expert_bwd: ExpertBwd):
+    """Expert backward per non-empty segment (the segmentation is backward
+    state, M6.2 §0x03D).  Returns ``(dx_rows, grads)`` with ``grads[e]`` the
+    expert's parameter gradients, or None for a zero-row expert."""
+    x = to_f64(rows)
+    dzf = np.asarray(dz, dtype=np.float64)
+    dx = np.zeros_like(x)
+    grads = []
+    for e in range(len(seg_count)):
+        n = int(seg_count[e])
+        if n == 0:
+            grads.append(None)
+            continue
+        s0 = int(seg_start[e])
+        dx[s0:s0 + n], ge = expert_bwd(e, x[s0:s0 + n], dzf[s0:s0 + n])
+        grads.append(ge)
+    return dx, grads
+
+
+def moe_layer_backward(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert: ExpertFn,
+                       expert_bwd: ExpertBwd, E: int, dy: np.ndarray, capacity: int = -1):
+    """Backward of the layer, expert-major (M6.2 §0x03D): the forward state
+    (permutation, origin record through the inverse map, gates, segments and
+    the expert outputs ``Z``) is rematerialised; the route gradients and gate
+    gradients come from :func:`combine_backward`; each segment runs its
+    expert backward; the route-input gradients are summed by origin token
+    through the inverse map (:func:`combine` with unit weights).
+
+    Returns a dict with ``dx [T, d]``, ``dgates [T, k]`` (0 for dropped
+    routes), ``grads`` (per expert, None when it has no rows) and the
+    intermediate ``plan``, ``z``, ``dz``, ``dx_rows``.
+    """
+    T, k = ids.shape
+    plan = dispatch_plan(ids, E, capacity)
+    xp = gather_rows(x, plan.src, k, plan.accepted)
+    z = run_segments(xp, plan.offsets[:-1], plan.counts, expert)
+    dz, dg = combine_backward(dy, z, plan.inv, gates, T, k)
+    dx_rows, grads = run_segments_backward(xp, dz, plan.offsets[:-1], plan.counts, expert_bwd)
+    dx = combine(dx_rows, plan.inv, None, T, k)
+    return dict(dx=dx, dgates=dg, grads=grads, plan=plan, z=z, dz=dz, dx_rows=dx_rows)
 
 
 # ----------------------------------------------------------------------------
