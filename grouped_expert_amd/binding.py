@@ -48,6 +48,10 @@ _SIGS = {
     "moe_grouped_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _i32, _p,
                                           _sz, _p, _p]),
     "moe_unpermute_combine": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p]),
+    "moe_combine_backward": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i64, _p, _p, _i32, _p, _i32, _p, _p, _p]),
+    "moe_grouped_swiglu_backward_workspace": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_grouped_swiglu_backward": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _i32,
+                                                   _p, _p, _p, _p, _sz, _p, _p]),
     "moe_pool_pack_workspace": (_sz, [_i64, _i32, _i32]),
     "moe_pool_pack": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
                                      _p, _p, _sz, _p, _p]),
@@ -231,6 +235,46 @@ def pool_rows_of_height(height: int, d: int) -> int:
         if header_rows(height - h, d) == h:
             return int(height) - h
     raise ValueError(f"no pool of row width {d} is {height} rows tall")
+
+
+def combine_backward(dy: torch.Tensor, z: torch.Tensor, idx: torch.Tensor, gates: torch.Tensor, k: int,
+                     dz_dtype: torch.dtype = torch.bfloat16, dz: Optional[torch.Tensor] = None,
+                     flags: Optional[torch.Tensor] = None):
+    """Route gradients ``dz[idx[r]] = g_r dy[t]`` and gate gradients
+    ``<dy[t], z[idx[r]]>``; returns ``(dz, dgates [T, k])``."""
+    _need_gpu(dy, z, idx, gates, dz, flags)
+    T, d = dy.shape
+    rows = z.shape[0]
+    if dz is None:
+        dz = torch.empty((rows, d), dtype=dz_dtype, device=dy.device)
+    dg = torch.empty((T, k), dtype=torch.float32, device=dy.device)
+    _check("moe_combine_backward", lib.moe_combine_backward(
+        _ptr(dy), T, d, _ptr(z), _dtype_code(z), rows, _ptr(idx), _ptr(gates), k, _ptr(dz), _dtype_code(dz),
+        _ptr(dg), _ptr(flags), _stream(dy.device)))
+    return dz, dg
+
+
+def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor,
+                            w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                            dx_dtype: torch.dtype = torch.float32, dx: Optional[torch.Tensor] = None,
+                            flags: Optional[torch.Tensor] = None):
+    """Expert backward over the segments; returns a dict with dx (route-input
+    gradients, rows of x), dw_gate, dw_up, dw_down (fp32)."""
+    _need_gpu(x, dz, seg_start, seg_count, w_gate, w_up, w_down, dx, flags)
+    rows, d = x.shape
+    E, d_ff, _ = w_gate.shape
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((rows, d), dtype=dx_dtype, device=dev)
+    dwg = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
+    dwu = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
+    dwd = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+    ws = _ws(lib.moe_grouped_swiglu_backward_workspace(rows, E, d, d_ff), dev)
+    _check("moe_grouped_swiglu_backward", lib.moe_grouped_swiglu_backward(
+        _ptr(x), d, d_ff, E, _ptr(seg_start), _ptr(seg_count), rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(dz), _ptr(dx), _dtype_code(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(ws), ws.numel(), _ptr(flags),
+        _stream(dev)))
+    return dict(dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd)
 
 
 def expand_rows(z: torch.Tensor, row_slot: torch.Tensor, ret_dtype: torch.dtype = torch.float32,

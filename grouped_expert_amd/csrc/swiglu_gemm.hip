@@ -24,606 +24,10 @@
 //
 // The fp32 variant (dtype MOE_F32) runs the same three steps with an LDS-tiled
 // FMA kernel in fp32.
-#include <type_traits>
-
-#include "common.h"
+#include "gemm_core.h"
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// One M-tile of one expert segment.  first / ntile locate the expert's run of
-// tiles in the table (used by the expert-blocked workgroup order).
-struct TileEntry {
-  int32_t expert, row0, row_end, first, ntile, pad0, pad1, pad2;
-};
-
-// ---------------------------------------------------------------------------
-// 1. tile table
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ seg_start,
-                                                           const int32_t* __restrict__ seg_count, int32_t E,
-                                                           int64_t rows, int32_t BM, int32_t max_tiles,
-                                                           TileEntry* __restrict__ tiles,
-                                                           int32_t* __restrict__ n_tiles, uint32_t* flags) {
-  __shared__ int32_t sh16[17];
-  const int t = threadIdx.x;
-  int32_t s = 0, c = 0;
-  if (t < E) {
-    s = seg_start[t];
-    c = seg_count[t];
-    const bool ok = s >= 0 && c >= 0 && static_cast<int64_t>(s) + c <= rows;
-    if (!ok) {
-      flag_or(flags, MOE_FLAG_BAD_SEGMENT);
-      c = 0;
-    }
-  }
-  const int32_t cnt = (c + BM - 1) / BM;
-  int32_t total = 0;
-  const int32_t pre = block_exclusive_scan_1024(cnt, sh16, &total);
-  // an expert whose tiles would run past the table (only with overlapping
-  // segments) keeps the tiles that fit, so its run stays self-consistent
-  const int32_t keep = pre >= max_tiles ? 0 : (cnt < max_tiles - pre ? cnt : max_tiles - pre);
-  for (int32_t i = 0; i < keep; ++i)
-    tiles[pre + i] = TileEntry{t, s + i * BM, s + c, pre, keep, 0, 0, 0};
-  if (t == 0) {
-    n_tiles[0] = total < max_tiles ? total : max_tiles;
-    if (total > max_tiles) flag_or(flags, MOE_FLAG_BAD_SEGMENT);   // overlapping segments
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2./3. bf16 MFMA GEMM:  C[m, n] = sum_k A[m, k] * B[n, k]
-// ---------------------------------------------------------------------------
-// One workgroup (4 wavefronts) owns a BM x BN_OUT output tile.  The K loop
-// runs over BK = 64 slices held in an LDS ring of STAGES slices; each slice
-// holds the BM rows of A followed by the BNB rows of B, 128 bytes per row.
-// Slices are filled by direct global -> LDS loads (global_load_lds_dwordx4:
-// 16 bytes per lane, no staging registers), so STAGES - 1 slices are in
-// flight while one is consumed.  Each load instruction of a wavefront fills
-// 1 KB = 8 consecutive LDS rows; a lane picks the global 16-byte chunk that
-// must land at its LDS position, which realises the XOR swizzle below.
-//
-// LDS row r, 16-byte chunk c is stored at r * 128 + ((c ^ ((r >> 1) & 7)) * 16):
-// the 16 lanes of one 256-byte LDS phase (16 rows, one chunk, two rows per
-// bank line) then hit 16 different bank groups on fragment reads.
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-
-// Byte offset of logical 16-byte chunk c of LDS row r in a slice whose rows
-// are RB bytes long (RB = 2 * BK): rows sharing a 256-byte bank line are
-// told apart by their position in the line, the XOR separates rows that
-// share a position.
-template <int RB>
-__device__ __forceinline__ int swz_off(int r, int c) {
-  constexpr int RPL = 256 / RB, CPR = RB / 16;
-  return r * RB + ((c ^ ((r / RPL) % CPR)) << 4);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier without a memory fence: a fence would wait for every
-// outstanding LDS DMA, including the slices still meant to be in flight.
-// The empty asm statements keep the compiler from moving LDS accesses across.
-__device__ __forceinline__ void barrier_nofence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-
-// SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
-__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
-
-template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
-          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false>
-struct Cfg {
-  static constexpr int NW = NW_;                          // wavefronts per workgroup
-  // RS: the weight (B) rows of a slice travel HBM -> registers -> LDS through
-  // two register stages, so two B slices are in flight with a two-stage LDS
-  // ring; the A rows keep the direct LDS DMA (else: everything by DMA)
-  static constexpr bool RS = RS_;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
-  static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
-  static constexpr int OCC = OCC_;                        // workgroups per CU the registers must allow
-  static constexpr int RB = BK * 2;                       // bytes per LDS row
-  static constexpr int CPR = BK / 8;                      // 16-byte chunks per row
-  static constexpr int RPI = 1024 / RB;                   // rows filled by one wave-wide DMA load
-  static constexpr bool GATEUP = GATEUP_, OUT_F32 = OUT_F32_, EXPERT_BLOCKED = EB_;
-  static constexpr int WTM = BM / WM;                     // rows per wavefront
-  static constexpr int TM = WTM / 32;                     // 32-row MFMA tiles per wavefront
-  // GATEUP: B holds BNB/2 gate rows then BNB/2 up rows and the output tile has
-  // BNB/2 columns of H.  Otherwise BNB output columns.
-  static constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
-  static constexpr int WTN = BN_OUT / WN;                 // output columns per wavefront
-  static constexpr int TN = WTN / 32;
-  static constexpr int NB = GATEUP ? 2 : 1;
-  static constexpr int ROWS = BM + BNB;                   // LDS rows per slice
-  static constexpr int SLICE = ROWS * BK;                 // bf16 elements per slice
-  static constexpr int LOADS = ROWS / RPI / NW;           // load instructions per wavefront per slice
-  static_assert(BK == 32 || BK == 64, "slice depth");
-  static_assert(ROWS % (RPI * NW) == 0 && BM % RPI == 0 && (BNB / 2) % RPI == 0, "slice rows vs DMA blocks");
-  static_assert(WM * WN == NW, "wavefront grid");
-  static_assert(TM >= 1 && TN >= 1, "wavefront tile too small");
-  static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
-  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
-  static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
-  // with RS every wavefront issues LA loads of A blocks and LB of B blocks
-  static constexpr int LA = RS ? BM / RPI / NW : LOADS;
-  static constexpr int LB = RS ? BNB / RPI / NW : 0;
-  static_assert(!RS || (BM % (RPI * NW) == 0 && BNB % (RPI * NW) == 0 && LA + LB == LOADS && LB > 0),
-                "register staging splits every wavefront's loads between A and B");
-  static_assert(!RS || !GATEUP || (BNB / 2) % (LB * RPI) == 0,
-                "with register staging all B rows of a wavefront come from one matrix");
-  // 8-row block of the slice filled by load i of wavefront w
-  static __device__ __forceinline__ int block(int w, int i) {
-    return !RS ? w * LOADS + i : (i < LA ? w * LA + i : BM / RPI + w * LB + (i - LA));
-  }
-};
-
-// Issue the loads of one K slice into an LDS stage.  Load i of a wavefront
-// reads from a wave-uniform base (A, or the expert's gate / up / down
-// matrix) plus a per-lane 32-bit element offset; ko is the slice's K offset.
-template <class C>
-__device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* base, const uint32_t* off,
-                                            uint32_t ko, int wave) {
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + ko)),
-                                     (lds_ptr_t)(stage + C::block(wave, i) * 512), 16, 0, 0);
-}
-
-// Consume one K slice.  Fragments are software-pipelined: the LDS read of the
-// next B fragment (and, at the last group of a k-step, of the next k-step's A
-// fragments) is issued before the MFMA group that uses the current one, so
-// LDS latency hides behind matrix-core work.  sched_barrier keeps the
-// compiler from regrouping the reads behind the MFMAs.
-// A rows of the slice sit at a_stage (row r at r * RB bytes), B rows at
-// b_stage (B row r likewise); the swizzle repeats every 16 rows and BM is a
-// multiple of 16, so both halves use their local row index.
-template <class C>
-__device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_t* b_stage,
-                                              f32x16 (&acc)[C::NB][C::TM][C::TN], int wm, int wn, int lane) {
-  constexpr int KS = C::BK / 16;               // MFMA k-steps per slice
-  constexpr int NF = C::NB * C::TN;            // B fragments per k-step
-  const int lr = lane % 32, lk = lane / 32;
-  const char* abase = reinterpret_cast<const char*>(a_stage);
-  const char* bbase = reinterpret_cast<const char*>(b_stage);
-  auto a_frag = [&](int kk, int i) {
-    return *reinterpret_cast<const bf16x8*>(abase + swz_off<C::RB>(wm * C::WTM + i * 32 + lr, kk * 2 + lk));
-  };
-  auto b_frag = [&](int kk, int f) {
-    const int h = f / C::TN, j = f % C::TN;
-    const int brow = h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
-    return *reinterpret_cast<const bf16x8*>(bbase + swz_off<C::RB>(brow, kk * 2 + lk));
-  };
-  bf16x8 a_cur[C::TM], a_nxt[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) a_cur[i] = a_frag(0, i);
-  bf16x8 b_cur = b_frag(0, 0), b_nxt;
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + 1 < NF) {
-        b_nxt = b_frag(kk, f + 1);
-      } else if (kk + 1 < KS) {
-        b_nxt = b_frag(kk + 1, 0);
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) a_nxt[i] = a_frag(kk + 1, i);
-      }
-      const int h = f / C::TN, j = f % C::TN;
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i], b_cur, acc[h][i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      b_cur = b_nxt;
-    }
-    if (kk + 1 < KS) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) a_cur[i] = a_nxt[i];
-    }
-  }
-}
-
-template <class C>
-__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
-  // The K-slice ring.  With register staging the A rows of the two stages
-  // come first and the B rows of the two stages follow.  (One LDS array only:
-  // with several, the compiler tracks the LDS DMA per array and waits for it
-  // before every LDS read of that array.)
-  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
-
-  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
-  if (blockIdx.x >= total) return;
-  const uint32_t logical = xcd_remap(blockIdx.x, total);
-  int mt, nt;
-  if (C::EXPERT_BLOCKED) {
-    // all N-tiles of one expert form a block; inside it the M-tiles of one
-    // N-tile are adjacent, so they run together and share that weight slice
-    const TileEntry tq = tiles[logical / n_tiles_n];
-    const int local = static_cast<int>(logical) - tq.first * n_tiles_n;
-    nt = local / tq.ntile;
-    mt = tq.first + local % tq.ntile;
-  } else if (C::GROUP_M > 1) {
-    // bands of GROUP_M M-tiles: inside a band the M-tiles of one N-tile are
-    // adjacent, so the workgroups running together on an XCD share both the
-    // A rows of the band and the weight slices of a few N-tiles
-    const int n_mt = static_cast<int>(total / n_tiles_n);
-    const int band = static_cast<int>(logical) / (C::GROUP_M * n_tiles_n);
-    const int idx = static_cast<int>(logical) - band * C::GROUP_M * n_tiles_n;
-    const int gm = n_mt - band * C::GROUP_M < C::GROUP_M ? n_mt - band * C::GROUP_M : C::GROUP_M;
-    nt = idx / gm;
-    mt = band * C::GROUP_M + idx % gm;
-  } else {
-    mt = static_cast<int>(logical / n_tiles_n);
-    nt = static_cast<int>(logical % n_tiles_n);
-  }
-  const TileEntry te = tiles[mt];
-  const int64_t e = te.expert;
-  const int32_t row0 = te.row0, row_end = te.row_end;
-  const int32_t n0 = nt * C::BN_OUT;
-
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / C::WN, wn = wave % C::WN;
-
-  // Source of every load instruction: LDS row rr of the slice; the lane's
-  // physical chunk p = lane % CPR holds logical chunk p ^ swizzle(rr).  Rows
-  // past the segment (A) or past N (B) read a valid row instead; their
-  // results are never stored.  All offsets fit 32 bits (checked on the host).
-  const bf16_t* base[C::LOADS];
-  uint32_t off[C::LOADS];
-  const bf16_t* Bexp0 = B0 + e * N * static_cast<int64_t>(K);
-  const bf16_t* Bexp1 = C::GATEUP ? B1 + e * N * static_cast<int64_t>(K) : Bexp0;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int blk = C::block(wave, i);                     // 8-row block (wave-uniform)
-    const int rr = blk * C::RPI + lane / C::CPR;
-    const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
-    if (blk * C::RPI < C::BM) {
-      int32_t row = row0 + rr;
-      row = row < row_end ? row : row_end - 1;
-      base[i] = A;
-      off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + c * 8;
-    } else {
-      const int r = rr - C::BM;
-      const bool up = C::GATEUP && r >= C::BNB / 2;
-      int n = n0 + (up ? r - C::BNB / 2 : r);
-      n = n < N ? n : N - 1;
-      base[i] = up ? Bexp1 : Bexp0;
-      off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8;
-    }
-  }
-
-  f32x16 acc[C::NB][C::TM][C::TN];
-#pragma unroll
-  for (int h = 0; h < C::NB; ++h)
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
-
-  auto issue_group = [&](int slice) {
-    issue_slice<C>(ring + (slice % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(slice * C::BK), wave);
-  };
-
-  // K loop over an LDS ring of STAGES slices: wait for slice kt (the loads of
-  // the STAGES - 2 younger slices may stay in flight), barrier (every wave's
-  // part of slice kt has landed and everyone is done with slice kt - 1),
-  // refill the freed stage with slice kt + STAGES - 1, consume slice kt.
-  const int KT = K / C::BK;
-  if constexpr (C::RS) {
-    // Two-stage LDS ring; A rows by LDS DMA one slice ahead, B rows through
-    // register stages rb0 / rb1: B of slice s is loaded at step s - 3 (or in
-    // the prologue), written to LDS at step s - 1 and consumed at step s, so
-    // during the compute of slice kt the B loads of slices kt + 2 and kt + 3
-    // are in flight.  Step kt: wait for this wave's DMA of slice kt (exactly
-    // the LB loads of B(kt + 2) are younger) and for its LDS writes, then the
-    // barrier publishes slice kt and frees the other stage, which takes the
-    // register copy of B(kt + 1) and the DMA of A(kt + 1).  Loads past the
-    // last slice re-read the last slice into the stage that is free at that
-    // step (never consumed), so every step issues the same instructions and
-    // the compiler's own waits for the register loads stay exact.  Inside a
-    // step the LDS writes come before the DMA (an LDS write behind an
-    // outstanding LDS DMA would make the compiler wait for it) and the DMA
-    // before the B loads (the vmcnt count above).
-    vec16 rb0[C::LB], rb1[C::LB];
-    auto clamp = [&](int slice) { return slice < KT ? slice : KT - 1; };
-    // A rows by LDS DMA.  (The global form: the compiler does not track it
-    // as an LDS write, so it adds no waits of its own before LDS accesses.)
-    auto dma_a = [&](int stage, int slice) {
-      bf16_t* st = ring + stage * (C::BM * C::BK);
-#pragma unroll
-      for (int i = 0; i < C::LA; ++i)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + static_cast<uint32_t>(slice * C::BK))),
-                                         (lds_ptr_t)(st + C::block(wave, i) * 512), 16, 0, 0);
-    };
-    // B loads are buffer loads over the wave's weight matrix (all B rows of a
-    // wavefront come from one of gate / up): a per-lane byte offset fixed for
-    // the tile plus the slice's K offset in a scalar register, so no address
-    // arithmetic or 64-bit address registers per slice.  The matrix is
-    // N * K * 2 bytes (< 2^32, checked on the host).
-    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t*>(base[C::LA]), 0, static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 2u),
-        0x00020000);
-    uint32_t boff[C::LB];
-#pragma unroll
-    for (int i = 0; i < C::LB; ++i) boff[i] = off[C::LA + i] * 2u;
-    auto gload_b = [&](vec16 (&r)[C::LB], int slice) {
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i)
-        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, static_cast<int>(boff[i]), slice * C::BK * 2, 0);
-    };
-    bf16_t* const ring_b = ring + 2 * C::BM * C::BK;
-    auto lstore_b = [&](int stage, const vec16 (&r)[C::LB]) {
-      bf16_t* st = ring_b + stage * (C::BNB * C::BK) + lane * 8;
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i)
-        *reinterpret_cast<vec16*>(st + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) = r[i];
-    };
-    auto step_sync = [&]() {
-      wait_vmcnt<C::LB>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
-      barrier_nofence();
-    };
-    const bf16_t* const a0 = ring;
-    const bf16_t* const a1 = ring + C::BM * C::BK;
-    const bf16_t* const b0 = ring_b;
-    const bf16_t* const b1 = ring_b + C::BNB * C::BK;
-    dma_a(0, 0);
-    gload_b(rb0, 0);
-    lstore_b(0, rb0);
-    asm volatile("" ::: "memory");
-    gload_b(rb1, clamp(1));
-    asm volatile("" ::: "memory");           // B(1) strictly older than B(2)
-    gload_b(rb0, clamp(2));
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {             // an even and an odd step; no early exit
-      step_sync();
-      lstore_b(1, rb1);                        // B(kt + 1)
-      asm volatile("" ::: "memory");
-      dma_a(1, kt + 1);
-      asm volatile("" ::: "memory");
-      gload_b(rb1, clamp(kt + 3));
-      compute_slice<C>(a0, b0, acc, wm, wn, lane);
-      step_sync();
-      lstore_b(0, rb0);                        // B(kt + 2), or a repeat past the end
-      asm volatile("" ::: "memory");
-      dma_a(0, clamp(kt + 2));
-      asm volatile("" ::: "memory");
-      gload_b(rb0, clamp(kt + 4));
-      compute_slice<C>(a1, b1, acc, wm, wn, lane);
-    }
-    if (kt < KT) {                             // odd slice count: the last slice is in stage 0
-      step_sync();
-      compute_slice<C>(a0, b0, acc, wm, wn, lane);
-    }
-    wait_vmcnt<0>();                           // no DMA may still land in the ring
-  } else {
-#pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < KT) issue_group(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + C::STAGES - 2 < KT)
-      wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
-    else
-      wait_vmcnt<0>();
-    barrier_nofence();
-    const int nk = kt + C::STAGES - 1;
-    if (nk < KT) issue_group(nk);
-    compute_slice<C>(ring + (kt % C::STAGES) * C::SLICE, ring + (kt % C::STAGES) * C::SLICE + C::BM * C::BK, acc, wm, wn,
-                     lane);
-  }
-  }
-
-  // epilogue: acc[q] holds C[m = 8*(q/4) + 4*(lane/32) + q%4][n = lane%32]
-  const int lr = lane % 32, lk = lane / 32;
-  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
-  constexpr int OUT_ROW = C::BN_OUT * static_cast<int>(sizeof(OutT));          // bytes per tile row
-  constexpr bool STAGED = C::BM * OUT_ROW <= static_cast<int>(sizeof(ring));  // tile fits the ring
-  auto value = [&](int i, int j, int q) -> OutT {
-    if constexpr (C::GATEUP) {
-      return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
-    } else if constexpr (C::OUT_F32) {
-      return acc[0][i][j][q];
-    } else {
-      return f32_to_bf16(acc[0][i][j][q]);
-    }
-  };
-  if constexpr (STAGED) {
-    // Transpose through LDS: every wave writes its fragments into a row-major
-    // BM x BN_OUT tile, then all threads store whole rows with 16-byte writes.
-    char* tile = reinterpret_cast<char*>(ring);
-    barrier_nofence();                                   // every wave is done reading the ring
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-          const int cc = wn * C::WTN + j * 32 + lr;
-          *reinterpret_cast<OutT*>(tile + r * OUT_ROW + cc * sizeof(OutT)) = value(i, j, q);
-        }
-    __syncthreads();
-    constexpr int VPR = OUT_ROW / 16;                    // 16-byte vectors per tile row
-    const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
-    const int cols_here = N - n0 < C::BN_OUT ? N - n0 : C::BN_OUT;
-    const int vec_cols = cols_here * static_cast<int>(sizeof(OutT)) / 16;   // N is a multiple of 64
-    for (int v = threadIdx.x; v < C::BM * VPR; v += C::THREADS) {
-      const int r = v / VPR, cv = v % VPR;
-      if (r >= rows_here || cv >= vec_cols) continue;
-      const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
-      char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(row0 + r) * N + n0) * sizeof(OutT) + cv * 16;
-      *reinterpret_cast<vec16*>(dst) = val;
-    }
-  } else {
-    const bool full_rows = row0 + C::BM <= row_end;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int col = n0 + wn * C::WTN + j * 32 + lr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int32_t row = row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-          if (!full_rows && row >= row_end) continue;
-          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = value(i, j, q);
-        }
-      }
-    }
-  }
-}
-
-// Dynamic wait for the oldest in-flight slice: `after` younger slices (0 ..
-// STAGES-2) may stay in flight.
-template <class C, int N = C::STAGES - 2>
-__device__ __forceinline__ void wait_slice(int after) {
-  if constexpr (N <= 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (after >= N)
-      wait_vmcnt<N * C::LOADS>();
-    else
-      wait_slice<C, N - 1>(after);
-  }
-}
-
-// Persistent form: gridDim.x workgroups walk the tile list with a static
-// stride (round r takes tiles r*G + remap(b)), and the K-slice ring runs on
-// across tile boundaries: the first slices of the next tile are already in
-// flight while the current tile finishes and writes its outputs (direct
-// stores), so neither the pipeline fill nor the epilogue leaves the CU idle.
-template <class C>
-__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persistent(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
-  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
-
-  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
-  const uint32_t G = gridDim.x;
-  const uint32_t slot = xcd_remap(blockIdx.x, G);
-  if (slot >= total) return;
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int KT = K / C::BK;
-
-  struct Coords { int64_t e; int32_t row0, row_end, n0; };
-  auto coords = [&](uint32_t logical) {
-    const int mt = static_cast<int>(logical / n_tiles_n), nt = static_cast<int>(logical % n_tiles_n);
-    const TileEntry te = tiles[mt];
-    return Coords{te.expert, te.row0, te.row_end, nt * C::BN_OUT};
-  };
-
-  // loader state: tile being loaded and its per-lane sources
-  const bf16_t* base[C::LOADS];
-  uint32_t off[C::LOADS];
-  auto set_sources = [&](const Coords& t) {
-    const bf16_t* Bexp0 = B0 + t.e * N * static_cast<int64_t>(K);
-    const bf16_t* Bexp1 = C::GATEUP ? B1 + t.e * N * static_cast<int64_t>(K) : Bexp0;
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int blk = C::block(wave, i);
-      const int rr = blk * C::RPI + lane / C::CPR;
-      const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
-      if (blk * C::RPI < C::BM) {
-        int32_t row = t.row0 + rr;
-        row = row < t.row_end ? row : t.row_end - 1;
-        base[i] = A;
-        off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + c * 8;
-      } else {
-        const int r = rr - C::BM;
-        const bool up = C::GATEUP && r >= C::BNB / 2;
-        int n = t.n0 + (up ? r - C::BNB / 2 : r);
-        n = n < N ? n : N - 1;
-        base[i] = up ? Bexp1 : Bexp0;
-        off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8;
-      }
-    }
-  };
-  uint32_t ld_tile = slot;
-  int ld_k = 0;
-  bool ld_live = true;
-  set_sources(coords(ld_tile));
-  int issued = 0, consumed = 0;
-  auto issue_next = [&]() {
-    if (!ld_live) return;
-    issue_slice<C>(ring + (issued % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(ld_k * C::BK), wave);
-    ++issued;
-    if (++ld_k == KT) {
-      ld_k = 0;
-      ld_tile += G;
-      ld_live = ld_tile < total;
-      if (ld_live) set_sources(coords(ld_tile));
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s) issue_next();
-
-  f32x16 acc[C::NB][C::TM][C::TN];
-  const int lr = lane % 32, lk = lane / 32;
-  for (uint32_t tile = slot; tile < total; tile += G) {
-    const Coords t = coords(tile);
-#pragma unroll
-    for (int h = 0; h < C::NB; ++h)
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_slice<C>(issued - consumed - 1);
-      barrier_nofence();
-      issue_next();
-      compute_slice<C>(ring + (consumed % C::STAGES) * C::SLICE, ring + (consumed % C::STAGES) * C::SLICE + C::BM * C::BK,
-                         acc, wm, wn, lane);
-      ++consumed;
-    }
-    const bool full_rows = t.row0 + C::BM <= t.row_end;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int col = t.n0 + wn * C::WTN + j * 32 + lr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int32_t row = t.row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-          if (!full_rows && row >= t.row_end) continue;
-          OutT v;
-          if constexpr (C::GATEUP)
-            v = f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
-          else if constexpr (C::OUT_F32)
-            v = acc[0][i][j][q];
-          else
-            v = f32_to_bf16(acc[0][i][j][q]);
-          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = v;
-        }
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // fp32 path: LDS-tiled FMA GEMM, 64 x 64 output tile, 4 x 4 per thread
@@ -696,38 +100,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Three tile shapes, chosen from the mean rows per expert (rows / E), which the
-// host knows without reading the device counts:
-//   large  (mean >= 768 rows): 256 x 256 tiles, 8 wavefronts (two per SIMD, so
-//          one wave's MFMAs cover the other's waits), 2-slice ring (128 KB)
-//          with the weight rows register-staged two slices ahead, bands of 4
-//          M-tiles for L2 reuse -- long MFMA-bound segments (static receiver
-//          arrays);
-//   medium (mean >= 48 rows):  128 x 256 tiles, 8 wavefronts, 3-slice ring
-//          (144 KB), bands of 2 M-tiles -- prefill-like weight streaming;
-//   small  (otherwise):        32 x 256 tiles, 4 wavefronts, 4-slice ring
-//          (144 KB), persistent -- decode-like segments of a few rows.
-// Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
-// hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true>;
-using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true>;
-using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true>;
-using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
-using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
-using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
-using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
-using CfgSmDF = Cfg<32, 256, 1, 4, 4, false, true>;
-using CfgSmDB = Cfg<32, 256, 1, 4, 4, false, false>;
-
-constexpr bool kPersistLg = false, kPersistMd = false, kPersistSm = true;
-
-enum TileKind { kLarge = 0, kMedium = 1, kSmall = 2 };
-
-inline TileKind pick_tiles(int64_t rows, int32_t E) {
-  const int64_t mean = rows / E;
-  return mean >= 768 ? kLarge : (mean >= 48 ? kMedium : kSmall);
-}
-
 inline int32_t tile_bm(int32_t dtype, TileKind t) {
   if (dtype == MOE_F32) return kF32BM;
   return t == kLarge ? CfgLgGU::BM : (t == kMedium ? CfgMdGU::BM : CfgSmGU::BM);
@@ -752,54 +124,6 @@ inline WsLayout ws_layout(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype) 
   w.ntiles_off = w.tiles_off + align_up(static_cast<size_t>(w.max_tiles) * sizeof(TileEntry), 256);
   w.total = w.ntiles_off + 256;
   return w;
-}
-
-// Compute units of the current device (cached per device; the library keeps
-// no other state).
-inline int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-template <class C>
-void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
-                const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream) {
-  const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
-  if (persistent) {
-    const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
-    const int64_t g = upper < slots ? upper : slots;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
-                       dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                       static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
-  } else {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(upper)),
-                       dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                       static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
-  }
-}
-
-template <class GU, class DF, class DB, bool PERSIST>
-int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
-                void* z, int32_t z_dtype, const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles,
-                hipStream_t stream) {
-  const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
-  const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
-  MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
-  launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
-  MOE_LAUNCH_CHECK();
-  if (z_dtype == MOE_F32)
-    launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
-  else
-    launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
 }
 
 }  // namespace

@@ -35,6 +35,27 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, w_gate: torch.Tensor, w_up:
     return y, dict(ids=ids, gates=gates, plan=plan, z=z)
 
 
+def moe_layer_backward(dy: torch.Tensor, x: torch.Tensor, state: dict, w_gate: torch.Tensor, w_up: torch.Tensor,
+                       w_down: torch.Tensor, flags: Optional[torch.Tensor] = None):
+    """Backward of :func:`moe_layer` from its saved state ("M6.2 - Expert
+    Parallelism and DeepSeek MoE", 0x03D: the permutation, the inverse map,
+    the gates, the segments and the expert outputs are backward state):
+    route and gate gradients, the expert backward over the segments, then the
+    route-input gradients summed by origin token through the inverse map.
+
+    Returns ``(dx fp32 [T, d], grads)`` with ``grads`` holding ``dgates``
+    ``[T, k]``, ``dw_gate``, ``dw_up``, ``dw_down`` (fp32) and the
+    intermediate ``dz`` / ``dx_rows``."""
+    plan = state["plan"]
+    T, k = state["ids"].shape
+    dz, dg = B.combine_backward(dy, state["z"], plan["inv"], state["gates"], k, dz_dtype=x.dtype, flags=flags)
+    bw = B.grouped_swiglu_backward(plan["x_perm"], dz, plan["offsets"], plan["counts"], w_gate, w_up, w_down,
+                                   flags=flags)
+    dx = B.unpermute_combine(bw["dx"], plan["inv"], None, T, k, flags=flags)
+    return dx, dict(dgates=dg, dw_gate=bw["dw_gate"], dw_up=bw["dw_up"], dw_down=bw["dw_down"], dz=dz,
+                    dx_rows=bw["dx"])
+
+
 def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: torch.Tensor, gates: torch.Tensor,
                   T: int, k: int, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, cap: int,
                   y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None,

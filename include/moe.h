@@ -251,6 +251,57 @@ int moe_unpermute_combine(const void* z, int32_t z_dtype, int32_t d,
                           float* y, int32_t accumulate, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_combine_backward -- reverse of the combine (route and gate gradients).
+ *
+ * "M6.2 - Expert Parallelism and DeepSeek MoE", 0x03D: with upstream
+ * gradient dy, route r = t*k + j with row p = idx[r] (0 <= p < rows) gets
+ *   dz[p]     = gates[r] * dy[t]            (converted to dz_dtype, nearest even)
+ *   dgates[r] = sum_i dy[t, i] * z[p, i]    (fp32 accumulation)
+ * Routes with idx = -1 get dgates = 0 and write nothing; idx < -1 or >= rows
+ * also sets MOE_FLAG_BAD_INDEX.  Rows of dz that no route points to are not
+ * written.
+ *
+ *   dy         device fp32 [T, d]; d % 8 == 0
+ *   z          device [rows, d] of z_dtype: the forward's expert outputs
+ *   idx        device int32 [T*k] (moe_permute's inv); gates fp32 [T*k]
+ *   dz         device [rows, d] of dz_dtype (MOE_F32 or MOE_BF16)
+ *   dgates     device fp32 [T*k]
+ * ------------------------------------------------------------------------- */
+int moe_combine_backward(const float* dy, int64_t T, int32_t d, const void* z, int32_t z_dtype,
+                         int64_t rows, const int32_t* idx, const float* gates, int32_t k,
+                         void* dz, int32_t dz_dtype, float* dgates, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu_backward -- expert backward over ragged row segments.
+ *
+ * "M6.2 - Expert Parallelism and DeepSeek MoE", 0x03D (expert backward gives
+ * route-input and parameter gradients; the segments are backward state),
+ * through the SwiGLU of "M6.6 - MoE Runtime Systems", 0x04A.  For every
+ * expert e with rows X_e = x[seg_start[e] .. + seg_count[e]) and route
+ * gradients dZ_e (same rows of dz), with G, U, H recomputed from X_e:
+ *   dH = dZ_e W_d[e],  dG = dH * U * SiLU'(G),  dU = dH * SiLU(G)
+ *   dx rows   = dG W_g[e] + dU W_u[e]                 (dx_dtype)
+ *   dw_down[e] = dZ_e^T H,  dw_gate[e] = dG^T X_e,  dw_up[e] = dU^T X_e   (fp32)
+ * with SiLU'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)).  bf16 operands
+ * on MFMA with fp32 accumulation; dH, dG, dU and H are rounded to bf16
+ * between the products.  Every expert's weight gradients are written (zero
+ * for an expert without rows).  Segments as in moe_grouped_swiglu.
+ *
+ *   x, dz      device bf16 [rows, d]; d % 64 == 0, d_ff % 64 == 0
+ *   w_gate, w_up  device bf16 [E, d_ff, d]; w_down device bf16 [E, d, d_ff]
+ *   dx         device [rows, d] of dx_dtype (rows outside every segment not written)
+ *   dw_gate, dw_up  device fp32 [E, d_ff, d]; dw_down device fp32 [E, d, d_ff]
+ *   ws         device workspace of moe_grouped_swiglu_backward_workspace(rows, E, d, d_ff)
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_backward_workspace(int64_t rows, int32_t E, int32_t d, int32_t d_ff);
+int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, int32_t E,
+                                const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const void* dz, void* dx, int32_t dx_dtype,
+                                float* dw_gate, float* dw_up, float* dw_down,
+                                void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_expand_rows -- receiver expansion of static-array results to pool rows.
  *
  * "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 03 (the receiver
