@@ -69,9 +69,10 @@ def parse():
 
 # kernel sources of each call (plus the shared header and the C ABI)
 _CALL_SOURCES = {"route": ["route_topk.hip"], "permute": ["permute.hip", "bucket_rank.h"],
-                 "swiglu": ["swiglu_gemm.hip"], "combine": ["combine.hip"], "expand": ["combine.hip"],
-                 "pool_pack": ["pool_pack.hip", "bucket_rank.h"],
-                 "recv_compact": ["recv_compact.hip", "bucket_rank.h"]}
+                 "swiglu": ["swiglu_gemm.hip", "gemm_core.h"], "combine": ["combine.hip"],
+                 "expand": ["combine.hip"], "pool_pack": ["pool_pack.hip", "bucket_rank.h"],
+                 "recv_compact": ["recv_compact.hip", "bucket_rank.h"], "combine_bwd": ["combine.hip"],
+                 "swiglu_bwd": ["swiglu_backward.hip", "gemm_core.h"], "dx_combine": ["combine.hip"]}
 
 
 def sources_digest(call):
@@ -171,6 +172,8 @@ def recorded_traffic(w, call):
 
 
 def workload_kind(w):
+    if w.train:
+        return "train"
     if w.name.startswith("router"):
         return "router"
     return "recv" if w.name.startswith("recv") else "pack" if w.name.startswith("sender") else "layer"
@@ -242,7 +245,7 @@ def layer_step(ge, timer, w, bank, flags):
     z = timer.run("swiglu", ge.grouped_swiglu, plan["x_perm"], plan["offsets"], plan["counts"], bank["wg"],
                   bank["wu"], bank["wd"], z_dtype=zdt, flags=flags)
     y = timer.run("combine", ge.unpermute_combine, z, plan["inv"], gates, T, w.k, flags=flags)
-    return dict(y=y, ids=ids, gates=gates, plan=plan)
+    return dict(y=y, ids=ids, gates=gates, plan=plan, z=z)
 
 
 def layer_ledger(w, counts):
@@ -274,6 +277,61 @@ def layer_cpu_baseline(w, host, sample):
     return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
                 sample=f"first {s} of {w.T} tokens of {w.name}, full layer (route, dispatch plan, "
                        f"fp64 SwiGLU of every routed row, combine); {dt:.2f} s")
+
+
+def train_setup(torch, w, banks):
+    host, bank_list = layer_setup(torch, w, banks)
+    host["dy"] = W.upstream_grad(w)
+    bank_list[0]["dy"] = to_dev(torch, host["dy"])
+    for b in bank_list[1:]:
+        b["dy"] = bank_list[0]["dy"].clone()
+    return host, bank_list
+
+
+def train_step(ge, timer, w, bank, flags):
+    """Forward of the layer, then its backward: route and gate gradients, the
+    expert backward (route-input and weight gradients), and the token
+    gradients through the inverse map."""
+    out = layer_step(ge, timer, w, bank, flags)
+    plan, T, k = out["plan"], w.T, w.k
+    dz, dg = timer.run("combine_bwd", ge.combine_backward, bank["dy"], out["z"], plan["inv"], out["gates"], k,
+                       flags=flags)
+    bw = timer.run("swiglu_bwd", ge.grouped_swiglu_backward, plan["x_perm"], dz, plan["offsets"], plan["counts"],
+                   bank["wg"], bank["wu"], bank["wd"], flags=flags)
+    dx = timer.run("dx_combine", ge.unpermute_combine, bw["dx"], plan["inv"], None, T, k, flags=flags)
+    out.update(dx=dx, dgates=dg, grads=bw)
+    return out
+
+
+def train_ledger(w, counts):
+    """The forward ledger plus the backward calls.  The expert backward does
+    16 A d d_ff flops (dH, the recomputed gate/up, dX, dW_d, dW_g and dW_u)
+    and moves x and dZ rows in, dX rows out (fp32), the active experts'
+    weights in and every expert's fp32 weight gradients out."""
+    led = layer_ledger(w, counts)
+    A = int(counts.sum())
+    E_act = int((counts > 0).sum())
+    T, k, d, dff, E = w.T, w.k, w.d, w.d_ff, w.E
+    led["combine_bwd"] = dict(bytes=4 * T * d + A * d * 2 + A * d * 2 + 12 * T * k, flops=2 * A * d)
+    led["swiglu_bwd"] = dict(bytes=2 * A * d * 2 + E_act * 3 * d * dff * 2 + A * d * 4 + E * 3 * d * dff * 4,
+                             flops=16 * A * d * dff)
+    led["dx_combine"] = dict(bytes=A * d * 4 + 4 * T * k + 4 * T * d, flops=A * d)
+    return led
+
+
+def train_cpu_baseline(w, host, sample):
+    """The oracle layer forward and backward on the first ``sample`` tokens."""
+    import oracle as O
+    s = min(sample, w.T)
+    t0 = time.perf_counter()
+    ids, gates, _ = O.route_topk(host["logits"][:s], w.k)
+    wts = lambda e: (host["wg"][e], host["wu"][e], host["wd"][e])
+    O.moe_layer_backward(host["x"][:s], ids, gates.astype(np.float64), O.swiglu_bank(wts), O.swiglu_bank_backward(wts),
+                         w.E, host["dy"][:s].astype(np.float64), w.capacity)
+    dt = time.perf_counter() - t0
+    return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"first {s} of {w.T} tokens of {w.name}: route, fp64 forward and backward of the layer "
+                       f"(route, gate, token and weight gradients); {dt:.2f} s")
 
 
 def recv_setup(torch, w, banks):
@@ -436,6 +494,9 @@ def main():
     if kind == "layer":
         host, bank_list = layer_setup(torch, w, banks)
         step = lambda tm, b: layer_step(ge, tm, w, b, flags)
+    elif kind == "train":
+        host, bank_list = train_setup(torch, w, banks)
+        step = lambda tm, b: train_step(ge, tm, w, b, flags)
     elif kind == "recv":
         host, bank_list = recv_setup(torch, w, banks)
         L, cap, d = w.n_local, w.recv_cap, w.d
@@ -486,9 +547,9 @@ def main():
         print(f"[bench] warning: dev_flags = {int(flags.item())}", file=sys.stderr)
 
     # ledger and dominant call
-    if kind == "layer":
+    if kind in ("layer", "train"):
         counts = last["plan"]["counts"].cpu().numpy()
-        led = layer_ledger(w, counts)
+        led = layer_ledger(w, counts) if kind == "layer" else train_ledger(w, counts)
         units, unit = w.T, "tokens/s"
         per_step_calls = 1
     elif kind == "recv":
@@ -536,6 +597,8 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         if kind == "layer":
             cpu = layer_cpu_baseline(w, host, args.cpu_sample or min(w.T, 2048))
+        elif kind == "train":
+            cpu = train_cpu_baseline(w, host, args.cpu_sample or min(w.T, 512))
         elif kind == "recv":
             cpu = recv_cpu_baseline(w, host, args.cpu_sample or 4096)
         elif kind == "router":

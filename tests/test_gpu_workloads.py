@@ -107,6 +107,51 @@ def test_decode_bf16(ge):
     assert (plan.counts == 0).sum() > 50 and plan.counts.max() <= 8
 
 
+def test_mid_bf16_backward(ge):
+    """Training step of the mid layer at full size: forward, then the backward
+    of the transpose with an N(0, 1) upstream gradient.  Token and gate
+    gradients on sampled tokens (each route's expert backward evaluated row
+    by row in fp64), weight gradients of the largest, a middle and the
+    smallest expert in full."""
+    w = W.MID_TRAIN
+    logits = W.router_logits(w)
+    x = W.tokens(w)
+    wg, wu, wd = W.all_expert_weights(w)
+    dy = W.upstream_grad(w)
+    flags = ge.new_flags("cuda")
+    gw = [to_gpu(a) for a in (wg, wu, wd)]
+    y, st = ge.moe_layer(to_gpu(x), to_gpu(logits), *gw, w.k, w.capacity, flags=flags)
+    dx, gr = ge.moe_layer_backward(to_gpu(dy), to_gpu(x), st, *gw, flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+    ids, gates, _ = O.route_topk(logits, w.k)
+    assert np.array_equal(to_np(st["ids"]), ids)
+    plan = O.dispatch_plan(ids, w.E, w.capacity)
+    W64 = lambda e: (O.to_f64(wg[e]), O.to_f64(wu[e]), O.to_f64(wd[e]))
+    xf, dyf, g64 = O.to_f64(x), dy.astype(np.float64), gates.astype(np.float64)
+    rng = np.random.default_rng(5)
+    tok = np.sort(rng.choice(w.T, size=48, replace=False))
+    want_dx = np.zeros((tok.size, w.d))
+    want_dg = np.zeros((tok.size, w.k))
+    bound = np.zeros((tok.size, w.k))
+    for i, t in enumerate(tok):
+        for j in range(w.k):
+            e = ids[t, j]
+            z = O.swiglu_expert(xf[t:t + 1], *W64(e))[0]
+            want_dg[i, j] = float(np.dot(dyf[t], z))
+            bound[i, j] = float(np.abs(dyf[t] * z).sum())
+            want_dx[i] += O.swiglu_expert_backward(xf[t:t + 1], g64[t, j] * dyf[t:t + 1], *W64(e))[0][0]
+    assert_rows_close(to_np(dx)[tok], want_dx, what="token gradient")
+    assert np.all(np.abs(to_np(gr["dgates"])[tok].astype(np.float64) - want_dg) <= 4e-3 * bound)
+    order = np.argsort(plan.counts, kind="stable")
+    for e in (int(order[-1]), int(order[len(order) // 2]), int(order[np.nonzero(plan.counts[order])[0][0]])):
+        routes = plan.src[plan.offsets[e]:plan.offsets[e + 1]]
+        t, j = routes // w.k, routes % w.k
+        _, (dwg, dwu, dwd) = O.swiglu_expert_backward(xf[t], g64[t, j, None] * dyf[t], *W64(e))
+        for name, want in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
+            assert_rows_close(to_np(gr[name][e]).astype(np.float64), want, what=f"{name}[{e}]")
+
+
 @pytest.fixture(scope="module", params=["sender_pack_bf16", "sender_pack_2w_bf16"])
 def send_case(request):
     """Inputs and the oracle's routing and pack of a sender-pack workload, three

@@ -46,6 +46,7 @@ _TAG_WEIGHTS = 3
 _TAG_RECV_IDS = 4
 _TAG_RECV_ROWS = 5
 _TAG_BIAS = 6
+_TAG_DY = 7
 
 HEADER_EMPTY = 0xFFFF
 
@@ -77,6 +78,7 @@ class Workload:
     recv_cap: int = 0
     recv_zipf: float = 0.0
     ret_dtype: str = "f32"     # receiver return rows: "f32" or "bf16"
+    train: bool = False        # a step is the layer forward plus its backward (upstream gradient ~ N(0, 1))
     # group-restricted router (gating variants)
     gating: int = 0            # 0 softmax-renorm, 1 V1, 2 V2, 3 V3 (the library's moe_gating ids)
     n_group: int = 0
@@ -105,6 +107,10 @@ SEND = Workload(name="sender_pack_bf16", seed=3, dtype="bf16", T=65536, d=3072,
 RECV_2W = Workload(name="recv_share_2w_bf16", seed=2, dtype="bf16", d=3072, d_ff=1536,
                    E=6, n_src=64, pool_rows=4506, n_waves=2, n_local=6, recv_cap=50245,
                    recv_zipf=1.1, x_std=1.0, w_std=0.02)
+# The mid layer as a training step: forward, then the backward of the
+# transpose ("M6.2", 0x03D) with an N(0, 1) fp32 upstream gradient.
+MID_TRAIN = dataclasses.replace(MID, name="mid_bf16_train", train=True)
+
 # The receiver share with bf16 return rows ("M6.6", 0x0AE: the returned row is
 # BF16): the expert GEMM stores bf16 and the return buffer is bf16.
 RECV_RET16 = dataclasses.replace(RECV, name="recv_share_ret_bf16", ret_dtype="bf16")
@@ -119,7 +125,8 @@ DECODE = Workload(name="decode_bf16", seed=4, dtype="bf16", T=64, d=3072, E=384,
 ROUTER_V3 = Workload(name="router_v3_f32", seed=5, dtype="f32", T=65536, E=256, k=8, logits="normal",
                      gating=3, n_group=8, topk_group=4, route_scale=2.5, bias_std=0.05)
 
-WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3, RECV_2W, SEND_2W, RECV_RET16)}
+WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3, RECV_2W, SEND_2W, RECV_RET16,
+                                 MID_TRAIN)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
@@ -196,6 +203,11 @@ def tokens(w: Workload) -> np.ndarray:
     with _cf.ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(one, range((w.T + chunk - 1) // chunk)))
     return out
+
+
+def upstream_grad(w: Workload) -> np.ndarray:
+    """fp32 upstream gradient ``[T, d]`` of the layer output ~ N(0, 1)."""
+    return _normal(_rng(w.seed, _TAG_DY), (w.T, w.d), 1.0)
 
 
 def expert_weights(w: Workload, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
