@@ -64,7 +64,10 @@ __all__ = [
     "combine", "moe_layer_token_major", "moe_layer_expert_major",
     "combine_backward", "silu_grad", "swiglu_expert_backward", "swiglu_bank_backward",
     "scalar_bank_backward", "run_segments_backward", "moe_layer_backward",
-    "header_rows", "pool_rows_of", "pool_pack", "recv_compact", "expand_rows", "loopback_layer",
+    "header_rows", "header_rows_bytes", "pool_rows_of", "pool_rows_of_bytes", "pool_pack", "recv_compact",
+    "expand_rows", "loopback_layer",
+    "FP8_E4M3_MAX", "FP8_MODES", "fp8_e4m3_decode", "fp8_e4m3_encode", "fp8_record_layout", "fp8_payload_bytes",
+    "quantize_fp8_rows", "dequantize_fp8_rows", "f32_to_bf16_rne",
     "capacity_ceil", "drop_rates", "swiglu_flops", "padded_exec_rows",
     "block_exec_rows",
 ]
@@ -621,25 +624,161 @@ def moe_layer_backward(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert
 
 
 # ----------------------------------------------------------------------------
+# FP8 dispatch payload (M6.2 §0x0AA-§0x0AC)
+# ----------------------------------------------------------------------------
+
+FP8_E4M3_MAX = 448.0
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the 127 non-negative finite E4M3 codes 0x00..0x7E (4-bit
+    exponent with bias 7, 3-bit mantissa, exponent field 0 subnormal; code
+    0x7F is NaN and there are no infinities), in code order (increasing)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes to float32 (exact)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    v = np.where(mag == 0x7F, np.nan, _e4m3_magnitudes()[np.minimum(mag, 126)])
+    return np.where(c & 0x80, -v, v).astype(np.float32)
+
+
+def fp8_e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """float32 to E4M3 by round to nearest, ties to the even code, saturating
+    at +-448 (the format has no infinity); NaN gives 0x7F with the sign.  The
+    sign bit is copied from the input, zeros and underflow included."""
+    a32 = np.asarray(v, dtype=np.float32)
+    a = np.abs(a32.astype(np.float64))
+    mags = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, 126)      # mags[hi-1] < a <= mags[hi]
+    lo = hi - 1
+    dlo, dhi = a - mags[lo], mags[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= FP8_E4M3_MAX, 126, code)
+    code = np.where(a <= 0.0, 0, code)
+    code = np.where(np.isnan(a), 0x7F, code)
+    return (code | np.where(np.signbit(a32), 0x80, 0)).astype(np.uint8)
+
+
+FP8_MODES = ("row", "b128")
+
+
+def fp8_record_layout(d: int, mode: str) -> Tuple[int, int]:
+    """``(G, W)``: scales per row (one, or one per 128 values, M6.2 §0x0AB)
+    and the record width in bytes: ``d`` fp8 bytes, then ``G`` fp32 scales,
+    zero padding to a multiple of 16 bytes."""
+    if mode not in FP8_MODES:
+        raise ValueError(mode)
+    G = 1 if mode == "row" else -(-int(d) // 128)
+    return G, -(-(int(d) + 4 * G) // 16) * 16
+
+
+def fp8_payload_bytes(R: int, d: int, mode: Optional[str]) -> int:
+    """Logical payload bytes of ``R`` rows (M6.2 §0x0AB): bf16 data
+    ``2 R d``; fp8 data plus fp32 scales ``R d + 4 R G``.  No padding,
+    alignment or transport metadata."""
+    if mode is None:
+        return 2 * R * d
+    G = fp8_record_layout(d, mode)[0]
+    return R * d + 4 * R * G
+
+
+def quantize_fp8_rows(x: np.ndarray, mode: str) -> np.ndarray:
+    """Rows (exact fp32 values, e.g. bf16 inputs) to fp8 records.
+
+    M6.2 §0x0AC: quantization yields data plus its scales, owned by the same
+    row.  Per scale group (the row, or 128 consecutive values): ``a`` = the
+    largest magnitude; ``scale = fp32(a / 448)``, ``inv = fp32(448 / a)``,
+    code ``= E4M3(fp32(x * inv))``; a group with ``a = 0`` gets scale 0 and
+    zero codes.  (The pages fix no scale rule: this max-to-448 rule, with
+    every step one correctly rounded fp32 operation, is the reading.)
+    Returns uint8 ``[n, W]``.
+    """
+    xf = np.asarray(x, dtype=np.float32)
+    n, d = xf.shape
+    G, Wb = fp8_record_layout(d, mode)
+    width = d if mode == "row" else 128
+    rec = np.zeros((n, Wb), dtype=np.uint8)
+    scales = np.zeros((n, G), dtype=np.float32)
+    for g in range(G):
+        c0, c1 = g * width, min(d, (g + 1) * width)
+        blk = xf[:, c0:c1]
+        amax = np.abs(blk).max(axis=1) if n else np.zeros(0, np.float32)
+        live = amax > 0
+        safe = np.where(live, amax, np.float32(1.0)).astype(np.float32)
+        scale = np.where(live, safe / np.float32(FP8_E4M3_MAX), np.float32(0.0)).astype(np.float32)
+        inv = (np.float32(FP8_E4M3_MAX) / safe).astype(np.float32)
+        q = fp8_e4m3_encode((blk * inv[:, None]).astype(np.float32))
+        rec[:, c0:c1] = np.where(live[:, None], q, 0)
+        scales[:, g] = scale
+    rec[:, d:d + 4 * G] = scales.view(np.uint8).reshape(n, 4 * G)
+    return rec
+
+
+def dequantize_fp8_rows(rec: np.ndarray, d: int, mode: str) -> np.ndarray:
+    """fp8 records to fp32 rows: ``fp32(decode(code) * scale)`` with the scale
+    of the value's group read from the same record (M6.2 §0x0AC)."""
+    r = np.ascontiguousarray(rec, dtype=np.uint8)
+    G, Wb = fp8_record_layout(d, mode)
+    if r.shape[-1] != Wb:
+        raise ValueError("record width")
+    r = r.reshape(-1, Wb)
+    scales = np.ascontiguousarray(r[:, d:d + 4 * G]).view(np.float32)
+    width = d if mode == "row" else 128
+    per_col = scales[:, np.arange(d) // width]
+    return (fp8_e4m3_decode(r[:, :d]) * per_col).astype(np.float32)
+
+
+def f32_to_bf16_rne(a: np.ndarray) -> np.ndarray:
+    """float32 to bf16 bits, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
 # a7: pooled-wave sender pack
 # ----------------------------------------------------------------------------
 
+def header_rows_bytes(pool_rows: int, row_bytes: int) -> int:
+    """Full-width header rows of a pool whose rows are ``row_bytes`` wide:
+    one 16-bit id per data row, ``row_bytes / 2`` ids per header row, at
+    least one (pooled wave §02 uses one row for 3004 ids in 6144-byte bf16
+    rows; more rows are the configurable-header variant)."""
+    return max(1, -(-2 * int(pool_rows) // int(row_bytes)))
+
+
 def header_rows(pool_rows: int, d: int) -> int:
-    """Full-width header rows of a pool: one 16-bit id per data row, ``d``
-    per header row (pooled wave §02 uses one row for 3004 ids at d = 3072;
-    more rows are the configurable-header variant, e.g. the two-wave profile
-    of §05 needs 4506 ids per pool).  At least one."""
-    return max(1, -(-int(pool_rows) // int(d)))
+    """Header rows of a pool of bf16 rows ``d`` values wide (the two-wave
+    profile of §05 needs 4506 ids per pool: two rows at d = 3072)."""
+    return header_rows_bytes(pool_rows, 2 * int(d))
 
 
-def pool_rows_of(pool_height: int, d: int) -> int:
+def pool_rows_of_bytes(pool_height: int, row_bytes: int) -> int:
     """The ``pool_rows`` whose pool has ``pool_height`` rows (data rows plus
     their header rows); unique because the height grows with pool_rows."""
     for h in range(1, pool_height + 1):
         p = pool_height - h
-        if header_rows(p, d) == h:
+        if header_rows_bytes(p, row_bytes) == h:
             return p
     raise ValueError("no pool_rows gives this pool height")
+
+
+def pool_rows_of(pool_height: int, d: int) -> int:
+    """:func:`pool_rows_of_bytes` for bf16 rows ``d`` values wide."""
+    return pool_rows_of_bytes(pool_height, 2 * int(d))
+
+
+def _row_bytes(a: np.ndarray) -> np.ndarray:
+    """Rows of bf16 bits (uint16) or of fp8 records (uint8) as bytes."""
+    a = np.ascontiguousarray(a)
+    if a.dtype not in (np.uint16, np.uint8):
+        raise TypeError("rows are bf16 bits (uint16) or fp8 records (uint8)")
+    return a.view(np.uint8).reshape(a.shape[:-1] + (a.shape[-1] * a.itemsize,))
 
 
 def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest: int,
@@ -675,20 +814,24 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
     wave = np.where(valid, rank % n_waves, -1)
     row = np.where(valid, rank // n_waves, -1)
     acc = valid & (row < pool_rows)
-    d = np.asarray(x_bits).shape[1]
-    H = header_rows(pool_rows, d)
+    xa = np.asarray(x_bits)
+    x8 = _row_bytes(xa)
+    rb = x8.shape[1]
+    H = header_rows_bytes(pool_rows, rb)
     P1 = pool_rows + H
     route_loc = np.where(acc, (wave * n_dest + dest) * P1 + H + row, -1)
     pools = None
     if with_pools:
-        x = np.asarray(x_bits, dtype=np.uint16)
-        pools = np.zeros((n_waves, n_dest, P1, d), dtype=np.uint16)
-        pools[:, :, :H, :] = HEADER_EMPTY
+        n_pools = n_waves * n_dest
+        p8 = np.zeros((n_pools, P1, rb), dtype=np.uint8)
+        p8[:, :H, :] = 0xFF                              # 0xFFFF ids: empty
         r = np.nonzero(acc)[0]
-        flat = pools.reshape(-1, d)                      # rows indexed like route_loc
-        flat[route_loc[r]] = x[r // k]
-        header = (wave[r] * n_dest + dest[r]) * P1       # first header row of the route's pool
-        flat[header + row[r] // d, row[r] % d] = local[r].astype(np.uint16)
+        p8.reshape(-1, rb)[route_loc[r]] = x8[r // k]    # rows indexed like route_loc
+        hdr = p8.reshape(n_pools, P1 * rb)[:, :H * rb].view(np.uint16)   # little-endian 16-bit ids
+        hdr[wave[r] * n_dest + dest[r], row[r]] = local[r].astype(np.uint16)
+        pools = p8.reshape(n_waves, n_dest, P1, rb)
+        if xa.dtype == np.uint16:
+            pools = pools.view(np.uint16)
     return dict(pools=pools, route_loc=route_loc, dest_counts=plan.sel,
                 sender_dropped=int(e.size - acc.sum()), wave=wave, row=row,
                 dest=dest, local=local, accepted=acc, bad=(e < -1) | (e >= n_exp))
@@ -698,7 +841,8 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
 # a8: receiver compaction into static per-expert arrays
 # ----------------------------------------------------------------------------
 
-def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool = True, rotation: int = 0):
+def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool = True, rotation: int = 0,
+                 record: Optional[Tuple[int, str]] = None):
     """Group one wave's incoming rows into ``[n_local, cap, d]`` arrays.
 
     Pooled wave §02/§03: the receiver reads each row's local expert id from
@@ -709,6 +853,10 @@ def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool =
     visited in the order ``rotation, rotation+1, ..., n_src-1, 0, ...`` so
     that overflow does not always fall on the same last source (0 = the
     fixed order).  The pool height is ``pool_rows + header_rows(pool_rows, d)``.
+    ``record = (d, mode)`` says that the pools hold fp8 records (uint8 rows,
+    see :func:`quantize_fp8_rows`); the compaction then dequantizes the
+    accepted rows with the scales stored in the same record (M6.2 §0x0AC)
+    and the compact arrays hold bf16 bits.
 
     Returns a dict with ``compact`` (uint16 ``[n_local, cap, d]``, rows past
     ``counts[h]`` zero; None when ``with_rows`` is False), ``counts``,
@@ -716,15 +864,18 @@ def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool =
     or -1; header rows -1), ``recv_dropped`` and ``bad_header`` (count of
     header ids that are neither a local id nor 0xFFFF).
     """
-    pools = np.asarray(pools, dtype=np.uint16)
-    S, P1, d = pools.shape
-    P = pool_rows_of(P1, d)
+    pools = np.asarray(pools)
+    p8 = _row_bytes(pools)
+    S, P1, rb = p8.shape
+    P = pool_rows_of_bytes(P1, rb)
     H = P1 - P
+    d = pools.shape[2] if record is None else int(record[0])
     if not 0 <= rotation < max(S, 1):
         raise ValueError("rotation must be in [0, n_src)")
     order = (np.arange(S) + rotation) % S if S else np.arange(0)
     # ids in visiting order: source order[v], then data row i
-    h = pools[order, :H, :].reshape(S, H * d)[:, :P].astype(np.int64).reshape(-1)
+    h = np.ascontiguousarray(p8[order, :H, :]).reshape(S, H * rb).view(np.uint16)[:, :P]
+    h = h.astype(np.int64).reshape(-1)
     valid = h < n_local
     bad = (h != HEADER_EMPTY) & ~valid
     plan = dispatch_plan(np.where(valid, h, -1), n_local, capacity=cap)
@@ -738,7 +889,11 @@ def recv_compact(pools: np.ndarray, n_local: int, cap: int, *, with_rows: bool =
     if with_rows:
         compact = np.zeros((n_local, cap, d), dtype=np.uint16)
         r = np.nonzero(acc)[0]
-        compact[h[r], q[r]] = pools[s_idx[r], H + i_idx[r]]
+        if record is None:
+            compact[h[r], q[r]] = pools[s_idx[r], H + i_idx[r]]
+        else:
+            rows = dequantize_fp8_rows(p8[s_idx[r], H + i_idx[r]], d, record[1])
+            compact[h[r], q[r]] = f32_to_bf16_rne(rows)
     return dict(compact=compact, counts=plan.counts, arrived=plan.sel, row_slot=row_slot,
                 recv_dropped=int(plan.sel.sum() - plan.counts.sum()),
                 bad_header=int(bad.sum()))
@@ -755,7 +910,7 @@ def expand_rows(z_static: np.ndarray, row_slot: np.ndarray) -> np.ndarray:
 
 def loopback_layer(x_bits: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert: ExpertFn,
                    experts_per_dest: int, n_dest: int, n_waves: int, pool_rows: int,
-                   recv_cap: int):
+                   recv_cap: int, payload: Optional[str] = None):
     """One sender's pools fed back as one receiver's incoming pools.
 
     A single-GPU stand-in for the fixed exchange: the sender's wave-``w``
@@ -766,16 +921,21 @@ def loopback_layer(x_bits: np.ndarray, ids: np.ndarray, gates: np.ndarray, exper
     accumulator through the sender's route locations.  The result equals the
     layer in which expert ``e`` uses local expert ``e mod experts_per_dest``'s
     weights and routes dropped by the sender or the receiver add nothing.
+    ``payload`` "row" / "b128" sends fp8 records (M6.2 §0x0AB-§0x0AC): each
+    token row is quantized once, the records travel in the pools and the
+    receiver dequantizes them into its bf16 arrays.
     Returns ``(y [T,d] float64, details)``.
     """
     T, k = ids.shape
-    pk = pool_pack(x_bits, ids, experts_per_dest, n_dest, n_waves, pool_rows)
     d = np.asarray(x_bits).shape[1]
-    P1 = pool_rows + header_rows(pool_rows, d)
+    rows = x_bits if payload is None else quantize_fp8_rows(to_f64(x_bits).astype(np.float32), payload)
+    pk = pool_pack(rows, ids, experts_per_dest, n_dest, n_waves, pool_rows)
+    P1 = pool_rows + header_rows_bytes(pool_rows, _row_bytes(np.asarray(rows[:1])).shape[1])
     y = np.zeros((T, d))
     waves = []
     for w in range(n_waves):
-        rc = recv_compact(pk["pools"][w], experts_per_dest, recv_cap)
+        rc = recv_compact(pk["pools"][w], experts_per_dest, recv_cap,
+                          record=None if payload is None else (d, payload))
         starts = np.arange(experts_per_dest) * recv_cap
         z = run_segments(rc["compact"].reshape(-1, d), starts, rc["counts"], expert)
         ret = expand_rows(z, rc["row_slot"])
