@@ -19,12 +19,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgrouped_expert_amd.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_ROW, MOE_FP8_B128 = 0, 1, 2, 3
+FP8_CODES = {"row": MOE_FP8_ROW, "b128": MOE_FP8_B128}
 MOE_GATING_SOFTMAX_TOPK_RENORM = 0
 MOE_GATING_SOFTMAX_TOPK = 1                 # V1
 MOE_GATING_SOFTMAX_GROUP_LIMITED = 2        # V2
 MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 = 3      # V3
 FLAG_BAD_EXPERT, FLAG_NONFINITE_LOGIT, FLAG_BAD_HEADER, FLAG_BAD_INDEX, FLAG_BAD_SEGMENT = 1, 2, 4, 8, 16
+FLAG_NONFINITE_INPUT = 32
 
 
 class MoEError(RuntimeError):
@@ -53,12 +55,15 @@ _SIGS = {
     "moe_grouped_swiglu_backward": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _i32,
                                                    _p, _p, _p, _p, _sz, _p, _p]),
     "moe_pool_pack_workspace": (_sz, [_i64, _i32, _i32]),
-    "moe_pool_pack": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
-                                     _p, _p, _sz, _p, _p]),
+    "moe_pool_pack": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
+                                     _p, _p, _p, _sz, _p, _p]),
+    "moe_row_bytes": (_sz, [_i32, _i32]),
+    "moe_quantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _i32, _p, _p, _p]),
+    "moe_dequantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p]),
     "moe_recv_compact_workspace": (_sz, [_i32, _i32, _i32]),
     "moe_expand_rows": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i32, _p, _p]),
-    "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p,
-                                        _p]),
+    "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                                        _sz, _p, _p]),
 }
 
 
@@ -66,7 +71,7 @@ def header_functions(path: str = HEADER):
     """Names of the functions declared in ``include/moe.h``."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -154,17 +159,19 @@ def route_topk_grouped(logits: torch.Tensor, k: int, gating: int, n_group: int, 
 
 
 def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity: int = -1,
-            materialize: bool = True, flags: Optional[torch.Tensor] = None):
+            materialize: bool = True, flags: Optional[torch.Tensor] = None, payload: Optional[str] = None,
+            d: Optional[int] = None):
     """``topk_ids`` is ``[T, k]``.  Returns a dict with x_perm (None when not
-    materialised), src, inv, sel, counts, offsets, dropped."""
+    materialised), src, inv, sel, counts, offsets, dropped.  With ``payload``
+    "row" / "b128", ``x`` holds fp8 records of rows ``d`` wide and x_perm
+    receives whole records."""
     _need_gpu(x, topk_ids, flags)
     T, k = topk_ids.shape
     dev = topk_ids.device
     R = T * k
     xp = None
     if materialize:
-        d = x.shape[1]
-        xp = torch.empty((R, d), dtype=x.dtype, device=dev)
+        xp = torch.empty((R, x.shape[1]), dtype=x.dtype, device=dev)
     src = torch.empty(R, dtype=torch.int32, device=dev)
     inv = torch.empty(R, dtype=torch.int32, device=dev)
     sel = torch.empty(E, dtype=torch.int32, device=dev)
@@ -173,8 +180,12 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity:
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
     nbytes = lib.moe_permute_workspace(T, k, E)
     ws = _ws(nbytes, dev)
-    dt = _dtype_code(x) if x is not None else MOE_BF16
-    _check("moe_permute", lib.moe_permute(_ptr(x), dt, T, 0 if x is None else x.shape[1], _ptr(topk_ids), k, E,
+    if payload is not None:
+        dt, dd = FP8_CODES[payload], d
+        assert x.dtype == torch.uint8 and x.shape[1] == row_bytes(d, payload), "fp8 payload: x holds records"
+    else:
+        dt, dd = (_dtype_code(x), x.shape[1]) if x is not None else (MOE_BF16, 0)
+    _check("moe_permute", lib.moe_permute(_ptr(x), dt, T, dd, _ptr(topk_ids), k, E,
                                           capacity, _ptr(xp), _ptr(src), _ptr(inv), _ptr(sel), _ptr(counts),
                                           _ptr(offsets), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags),
                                           _stream(dev)))
@@ -218,23 +229,53 @@ def unpermute_combine(z: torch.Tensor, idx: torch.Tensor, gates: Optional[torch.
     return y
 
 
-def header_rows(pool_rows: int, d: int) -> int:
+def row_bytes(d: int, payload: Optional[str] = None) -> int:
+    """Bytes of one dispatched row: bf16 (payload None) or an fp8 record
+    ("row": one fp32 scale per row, "b128": one per 128 values)."""
+    return int(lib.moe_row_bytes(MOE_BF16 if payload is None else FP8_CODES[payload], d))
+
+
+def header_rows(pool_rows: int, d: int, payload: Optional[str] = None) -> int:
     """Header rows of a pool as the library lays it out: one 16-bit id per
-    data row, ``d`` ids per row, at least one row."""
-    return max(1, -(-int(pool_rows) // int(d)))
+    data row, ``row_bytes / 2`` ids per row, at least one row."""
+    return max(1, -(-2 * int(pool_rows) // row_bytes(d, payload)))
 
 
-def pool_height(pool_rows: int, d: int) -> int:
+def pool_height(pool_rows: int, d: int, payload: Optional[str] = None) -> int:
     """Rows of one pool: data rows plus header rows."""
-    return int(pool_rows) + header_rows(pool_rows, d)
+    return int(pool_rows) + header_rows(pool_rows, d, payload)
 
 
-def pool_rows_of_height(height: int, d: int) -> int:
+def pool_rows_of_height(height: int, d: int, payload: Optional[str] = None) -> int:
     """Data rows of a pool that is ``height`` rows tall."""
     for h in range(1, int(height) + 1):
-        if header_rows(height - h, d) == h:
+        if header_rows(height - h, d, payload) == h:
             return int(height) - h
     raise ValueError(f"no pool of row width {d} is {height} rows tall")
+
+
+def quantize_fp8(x: torch.Tensor, payload: str = "b128", rec: Optional[torch.Tensor] = None,
+                 flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows ``[n, d]`` (bf16 or fp32) to fp8 records ``uint8 [n, row_bytes]``."""
+    _need_gpu(x, rec, flags)
+    n, d = x.shape
+    if rec is None:
+        rec = torch.empty((n, row_bytes(d, payload)), dtype=torch.uint8, device=x.device)
+    _check("moe_quantize_fp8", lib.moe_quantize_fp8(_ptr(x), _dtype_code(x), n, d, FP8_CODES[payload], _ptr(rec),
+                                                     _ptr(flags), _stream(x.device)))
+    return rec
+
+
+def dequantize_fp8(rec: torch.Tensor, d: int, payload: str = "b128", out_dtype: torch.dtype = torch.bfloat16,
+                   out: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp8 records back to ``[n, d]`` rows of ``out_dtype``."""
+    _need_gpu(rec, out, flags)
+    n = rec.shape[0]
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=rec.device)
+    _check("moe_dequantize_fp8", lib.moe_dequantize_fp8(_ptr(rec), FP8_CODES[payload], n, d, _ptr(out),
+                                                         _dtype_code(out), _ptr(flags), _stream(rec.device)))
+    return out
 
 
 def combine_backward(dy: torch.Tensor, z: torch.Tensor, idx: torch.Tensor, gates: torch.Tensor, k: int,
@@ -294,35 +335,54 @@ def expand_rows(z: torch.Tensor, row_slot: torch.Tensor, ret_dtype: torch.dtype 
 
 def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest: int, n_dest: int, n_waves: int,
               pool_rows: int, wave: int = -1, pools: Optional[torch.Tensor] = None,
-              flags: Optional[torch.Tensor] = None):
-    """Returns a dict with pools (bf16), route_loc, dest_counts, sender_dropped."""
+              flags: Optional[torch.Tensor] = None, payload: Optional[str] = None, d: Optional[int] = None):
+    """Returns a dict with pools, route_loc, dest_counts, sender_dropped.
+
+    ``x`` is bf16 ``[T, d]`` (pools bf16 ``[..., PH, d]``) or, with
+    ``payload`` "row" / "b128", fp8 records ``uint8 [T, row_bytes]`` of rows
+    ``d`` wide (pools uint8 ``[..., PH, row_bytes]``)."""
     _need_gpu(x, topk_ids, pools, flags)
-    T, d = x.shape
+    T = x.shape[0]
+    if payload is None:
+        d = x.shape[1]
+        code, last, pdt = MOE_BF16, d, torch.bfloat16
+    else:
+        code, last, pdt = FP8_CODES[payload], row_bytes(d, payload), torch.uint8
+        assert x.dtype == torch.uint8 and x.shape[1] == last, "fp8 payload: x holds records"
     k = topk_ids.shape[-1]
     dev = x.device
-    PH = pool_height(pool_rows, d)
-    shape = (n_waves, n_dest, PH, d) if wave < 0 else (n_dest, PH, d)
+    PH = pool_height(pool_rows, d, payload)
+    shape = (n_waves, n_dest, PH, last) if wave < 0 else (n_dest, PH, last)
     if pools is None:
-        pools = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        pools = torch.empty(shape, dtype=pdt, device=dev)
     route_loc = torch.empty(T * k, dtype=torch.int32, device=dev)
     dest_counts = torch.empty(n_dest, dtype=torch.int32, device=dev)
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
     ws = _ws(lib.moe_pool_pack_workspace(T, k, n_dest), dev)
     _check("moe_pool_pack", lib.moe_pool_pack(
-        _ptr(x), T, d, _ptr(topk_ids), k, E, experts_per_dest, n_dest, n_waves, pool_rows, wave, _ptr(pools),
+        _ptr(x), code, T, d, _ptr(topk_ids), k, E, experts_per_dest, n_dest, n_waves, pool_rows, wave, _ptr(pools),
         _ptr(route_loc), _ptr(dest_counts), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
     return dict(pools=pools, route_loc=route_loc, dest_counts=dest_counts, sender_dropped=dropped)
 
 
 def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Optional[torch.Tensor] = None,
-                 flags: Optional[torch.Tensor] = None, rotation: int = 0):
-    """Returns a dict with compact [n_local, cap, d], counts, arrived, row_slot, recv_dropped.
+                 flags: Optional[torch.Tensor] = None, rotation: int = 0, payload: Optional[str] = None,
+                 d: Optional[int] = None):
+    """Returns a dict with compact [n_local, cap, d] (bf16), counts, arrived, row_slot, recv_dropped.
 
-    ``pools_in`` is ``[n_src, pool_height, d]``; sources are visited from
+    ``pools_in`` is ``[n_src, pool_height, d]`` bf16, or with ``payload``
+    "row" / "b128" fp8 records ``uint8 [n_src, pool_height, row_bytes]`` of
+    rows ``d`` wide (dequantized into ``compact``); sources are visited from
     ``rotation`` onwards."""
     _need_gpu(pools_in, compact, flags)
-    S, P1, d = pools_in.shape
-    P = pool_rows_of_height(P1, d)
+    S, P1 = pools_in.shape[0], pools_in.shape[1]
+    if payload is None:
+        d = pools_in.shape[2]
+        code = MOE_BF16
+    else:
+        code = FP8_CODES[payload]
+        assert pools_in.dtype == torch.uint8 and pools_in.shape[2] == row_bytes(d, payload)
+    P = pool_rows_of_height(P1, d, payload)
     dev = pools_in.device
     if compact is None:
         compact = torch.empty((n_local, cap, d), dtype=torch.bfloat16, device=dev)
@@ -332,6 +392,6 @@ def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Option
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
     ws = _ws(lib.moe_recv_compact_workspace(S, P, n_local), dev)
     _check("moe_recv_compact", lib.moe_recv_compact(
-        _ptr(pools_in), S, P, d, n_local, cap, rotation, _ptr(compact), _ptr(counts), _ptr(arrived),
+        _ptr(pools_in), code, S, P, d, n_local, cap, rotation, _ptr(compact), _ptr(counts), _ptr(arrived),
         _ptr(row_slot), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
     return dict(compact=compact, counts=counts, arrived=arrived, row_slot=row_slot, recv_dropped=dropped)

@@ -9,6 +9,7 @@
 // gathered from the hidden states (one copy per route); 0x0CD: accepted plus
 // dropped routes equal T*k and the counts sum to the accepted total.
 #include "bucket_rank.h"
+#include "fp8.h"
 
 namespace moe {
 namespace {
@@ -102,12 +103,13 @@ MOE_API int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d, co
   MOE_CHECK(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL);
   MOE_CHECK(T <= INT32_MAX / k, MOE_EUNSUPPORTED);
   MOE_CHECK(capacity >= -1, MOE_EINVAL);
-  MOE_CHECK(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_EINVAL);
-  const int elt = x_dtype == MOE_F32 ? 4 : 2;
+  MOE_CHECK(x_dtype == MOE_F32 || x_dtype == MOE_BF16 || is_fp8(x_dtype), MOE_EINVAL);
+  // fp8 records move whole: codes and scales together (M6.2 0x0AC)
+  const int64_t rb = row_bytes(x_dtype, d);
   MOE_CHECK(counts && offsets && n_dropped, MOE_EINVAL);
   MOE_CHECK(T == 0 || (topk_ids && src && inv), MOE_EINVAL);
   if (x_perm) {
-    MOE_CHECK(x && d >= 1 && (static_cast<int64_t>(d) * elt) % 16 == 0, MOE_EINVAL);
+    MOE_CHECK(x && d >= 1 && rb % 16 == 0 && (!is_fp8(x_dtype) || d % 8 == 0), MOE_EINVAL);
     MOE_CHECK(aligned16(x) && aligned16(x_perm), MOE_EINVAL);
   }
   const RankGeom g = rank_geom(T * k, E);
@@ -119,7 +121,7 @@ MOE_API int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d, co
                        table, dev_flags, stream);
   if (st != MOE_OK) return st;
   if (R > 0) {
-    const int64_t row_vecs = x_perm ? static_cast<int64_t>(d) * elt / 16 : 0;
+    const int64_t row_vecs = x_perm ? rb / 16 : 0;
     const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
     hipLaunchKernelGGL(scatter_rows_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream,
                        static_cast<const vec16*>(x), T, row_vecs, k, offsets + E, inv, src,

@@ -7,8 +7,11 @@
 // destination (the only reading that fits the pool shape [64, 3005, 3072]
 // per wave and the per-destination, per-wave capacity of 04); extra rows are
 // dropped; the first full-width row of a pool carries the packed local expert
-// ids so that no count exchange is needed (reading: ceil(pool_rows / d) such
-// rows when one row cannot hold the ids, e.g. the two-wave profile of 05).
+// ids so that no count exchange is needed (reading: as many such rows as the
+// 16-bit ids need, e.g. two for the two-wave profile of 05).  Rows are bf16
+// or fp8 records ("M6.2 - Expert Parallelism and DeepSeek MoE", 0x0AB-0x0AC:
+// the scales travel inside the row); the kernels move rows as 16-byte
+// vectors and never look inside them.
 // 03: every wave has the same static shape.
 //
 // Launches: the shared bucket-rank passes with bucket = destination (pass 3
@@ -17,6 +20,7 @@
 // its placed copies) or fill the unused rows (zero data, 0xFFFF header tail)
 // so that the pools are fully defined.
 #include "bucket_rank.h"
+#include "fp8.h"
 
 namespace moe {
 namespace {
@@ -35,7 +39,7 @@ struct DestBucket {
 
 struct PackEmit {
   const int32_t* ids;
-  int32_t epd, n_dest, n_waves, pool_rows, d, wave_sel, H;
+  int32_t epd, n_dest, n_waves, pool_rows, re, wave_sel, H;    // re: 16-bit elements per row
   int32_t* route_loc;
   bf16_t* pools;
   __device__ void operator()(int64_t r, int dest, int32_t o) const {
@@ -52,7 +56,7 @@ struct PackEmit {
     route_loc[r] = static_cast<int32_t>((static_cast<int64_t>(w) * n_dest + dest) * P1 + H + row);
     if (wave_sel < 0 || wave_sel == w) {
       const int64_t slab = wave_sel < 0 ? w : 0;
-      pools[((slab * n_dest + dest) * P1) * d + row] = static_cast<bf16_t>(ids[r] % epd);
+      pools[((slab * n_dest + dest) * P1) * re + row] = static_cast<bf16_t>(ids[r] % epd);
     }
   }
 };
@@ -103,7 +107,7 @@ __device__ __forceinline__ void pack_token_rows(const vec16* __restrict__ x, int
 constexpr int kFillRows = 16;
 
 __device__ __forceinline__ void pack_fill_rows(const int32_t* __restrict__ dest_counts, int32_t n_dest,
-                                               int32_t n_waves, int32_t pool_rows, int32_t d, int32_t H,
+                                               int32_t n_waves, int32_t pool_rows, int32_t re, int32_t H,
                                                int32_t wave_sel, bf16_t* __restrict__ pools, int64_t pool,
                                                int32_t rblk) {
   const int32_t dest = static_cast<int32_t>(pool % n_dest);
@@ -113,19 +117,19 @@ __device__ __forceinline__ void pack_fill_rows(const int32_t* __restrict__ dest_
   const int64_t m = n < cap_all ? n : cap_all;
   const int32_t filled = m > w ? static_cast<int32_t>((m - w + n_waves - 1) / n_waves) : 0;
   const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
-  bf16_t* base = pools + pool * P1 * d;
+  bf16_t* base = pools + pool * P1 * re;
   if (rblk == 0) {
-    const int64_t hdr = static_cast<int64_t>(H) * d;     // header elements of the pool
+    const int64_t hdr = static_cast<int64_t>(H) * re;    // 16-bit header elements of the pool
     for (int64_t i = filled + threadIdx.x; i < hdr; i += blockDim.x) base[i] = 0xFFFF;
   }
   const int32_t r0 = rblk * kFillRows;
   if (r0 + kFillRows <= filled) return;
-  const int64_t row_vecs = static_cast<int64_t>(d) / 8;
+  const int64_t row_vecs = static_cast<int64_t>(re) / 8;
   const vec16 zero = {0u, 0u, 0u, 0u};
   for (int32_t rr = 0; rr < kFillRows; ++rr) {
     const int32_t row = r0 + rr;
     if (row < filled || row >= pool_rows) continue;
-    vec16* out = reinterpret_cast<vec16*>(base + (H + static_cast<int64_t>(row)) * d);
+    vec16* out = reinterpret_cast<vec16*>(base + (H + static_cast<int64_t>(row)) * re);
     for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) st_stream(zero, out + c);
   }
 }
@@ -136,14 +140,14 @@ __device__ __forceinline__ void pack_fill_rows(const int32_t* __restrict__ dest_
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ route_loc,
     int64_t slab_lo, int64_t slab_hi, int64_t tok_blocks, const int32_t* __restrict__ dest_counts, int32_t n_dest,
-    int32_t n_waves, int32_t pool_rows, int32_t d, int32_t H, int32_t wave_sel, int32_t fill_blocks_per_pool,
+    int32_t n_waves, int32_t pool_rows, int32_t re, int32_t H, int32_t wave_sel, int32_t fill_blocks_per_pool,
     bf16_t* __restrict__ pools) {
   const int64_t b = blockIdx.x;
   if (b < tok_blocks) {
     pack_token_rows(x, T, row_vecs, k, route_loc, slab_lo, slab_hi, reinterpret_cast<vec16*>(pools), b);
   } else {
     const int64_t f = b - tok_blocks;
-    pack_fill_rows(dest_counts, n_dest, n_waves, pool_rows, d, H, wave_sel, pools, f / fill_blocks_per_pool,
+    pack_fill_rows(dest_counts, n_dest, n_waves, pool_rows, re, H, wave_sel, pools, f / fill_blocks_per_pool,
                    static_cast<int32_t>(f % fill_blocks_per_pool));
   }
 }
@@ -157,7 +161,8 @@ MOE_API size_t moe_pool_pack_workspace(int64_t T, int32_t k, int32_t n_dest) {
   return rank_table_bytes(rank_geom(T * k, n_dest)) + align_up((n_dest + 1) * sizeof(int32_t), 256);
 }
 
-MOE_API int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k, int32_t E,
+MOE_API int moe_pool_pack(const void* x, int32_t x_dtype, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k,
+                          int32_t E,
                           int32_t experts_per_dest, int32_t n_dest, int32_t n_waves, int32_t pool_rows,
                           int32_t wave, void* pools, int32_t* route_loc, int32_t* dest_counts,
                           int32_t* sender_dropped, void* ws, size_t ws_bytes, uint32_t* dev_flags,
@@ -170,12 +175,16 @@ MOE_API int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_
   MOE_CHECK(E <= static_cast<int64_t>(n_dest) * experts_per_dest, MOE_EINVAL);
   MOE_CHECK(wave >= -1 && wave < n_waves, MOE_EINVAL);
   MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
-  const int32_t H = pool_rows > d ? (pool_rows + d - 1) / d : 1;   // header rows: one 16-bit id per data row
+  MOE_CHECK(x_dtype == MOE_BF16 || is_fp8(x_dtype), MOE_EINVAL);
+  const int64_t rb = row_bytes(x_dtype, d);                       // a multiple of 16
+  MOE_CHECK(rb <= INT32_MAX, MOE_EUNSUPPORTED);
+  const int32_t re = static_cast<int32_t>(rb / 2);                // 16-bit elements per row
+  const int32_t H = pool_rows > re ? (pool_rows + re - 1) / re : 1;   // header rows: one 16-bit id per data row
   const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
   MOE_CHECK(static_cast<int64_t>(n_waves) * n_dest * P1 <= INT32_MAX, MOE_EUNSUPPORTED);
   MOE_CHECK(pools && dest_counts && sender_dropped, MOE_EINVAL);
-  MOE_CHECK(T == 0 || (x_bf16 && topk_ids && route_loc), MOE_EINVAL);
-  MOE_CHECK(aligned16(pools) && (T == 0 || aligned16(x_bf16)), MOE_EINVAL);
+  MOE_CHECK(T == 0 || (x && topk_ids && route_loc), MOE_EINVAL);
+  MOE_CHECK(aligned16(pools) && (T == 0 || aligned16(x)), MOE_EINVAL);
   const RankGeom g = rank_geom(T * k, n_dest);
   const size_t tb = rank_table_bytes(g);
   MOE_CHECK(ws && ws_bytes >= moe_pool_pack_workspace(T, k, n_dest), MOE_EWORKSPACE);
@@ -185,22 +194,22 @@ MOE_API int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_
   RankScanOut out{dest_counts, nullptr, offsets, sender_dropped, 1};
   bf16_t* pb = static_cast<bf16_t*>(pools);
   int st = bucket_rank(g, DestBucket{topk_ids, E, experts_per_dest},
-                       PackEmit{topk_ids, experts_per_dest, n_dest, n_waves, pool_rows, d, wave, H, route_loc, pb},
+                       PackEmit{topk_ids, experts_per_dest, n_dest, n_waves, pool_rows, re, wave, H, route_loc, pb},
                        cap_all, out, table, dev_flags, stream);
   if (st != MOE_OK) return st;
-  const int64_t row_vecs = d / 8;
+  const int64_t row_vecs = rb / 16;
   const int64_t slab_rows = static_cast<int64_t>(n_dest) * P1;
   const int64_t lo = wave < 0 ? 0 : wave * slab_rows;
   const int64_t hi = wave < 0 ? n_waves * slab_rows : lo + slab_rows;
   const int64_t tok_blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
   const int64_t n_pools = static_cast<int64_t>(wave < 0 ? n_waves : 1) * n_dest;
-  const int32_t rb = (pool_rows + kFillRows - 1) / kFillRows;
-  const int32_t fill_per_pool = rb > 0 ? rb : 1;
+  const int32_t fill_blocks = (pool_rows + kFillRows - 1) / kFillRows;
+  const int32_t fill_per_pool = fill_blocks > 0 ? fill_blocks : 1;
   const int64_t blocks = tok_blocks + n_pools * fill_per_pool;
   MOE_CHECK(blocks <= INT32_MAX, MOE_EUNSUPPORTED);
   hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPackThreads), 0, stream,
-                     static_cast<const vec16*>(x_bf16), T, row_vecs, k, route_loc, lo, hi, tok_blocks, dest_counts,
-                     n_dest, n_waves, pool_rows, d, H, wave, fill_per_pool, pb);
+                     static_cast<const vec16*>(x), T, row_vecs, k, route_loc, lo, hi, tok_blocks, dest_counts,
+                     n_dest, n_waves, pool_rows, re, H, wave, fill_per_pool, pb);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -14,8 +14,12 @@
 //
 // Launches: the shared bucket-rank passes over rows in (source, row) order
 // with bucket = header id (pass 3 writes row_slot), then a row copy that
-// moves every accepted row to its slot and marks the header rows -1.
+// moves every accepted row to its slot and marks the header rows -1.  With
+// fp8 records in the pools ("M6.2 - Expert Parallelism and DeepSeek MoE",
+// 0x0AC) the copy dequantizes each accepted row with its own scales into the
+// bf16 arrays, so the expert GEMM reads bf16 as before.
 #include "bucket_rank.h"
+#include "fp8.h"
 
 namespace moe {
 namespace {
@@ -29,11 +33,11 @@ __device__ __forceinline__ int64_t visit_source(int64_t v, int64_t rot, int64_t 
 
 struct HeaderBucket {
   const bf16_t* pools;
-  int64_t P, P1, d, rot, S;
+  int64_t P, P1, re, rot, S;                              // re: 16-bit elements per pool row
   int32_t L;
   __device__ uint32_t load(int64_t i) const {
     const int64_t v = i / P, r = i - v * P;
-    return pools[visit_source(v, rot, S) * P1 * d + r];   // id of data row r: element r of the header rows
+    return pools[visit_source(v, rot, S) * P1 * re + r];  // id of data row r: element r of the header rows
   }
   __device__ int classify(uint32_t h, uint32_t* flags) const {
     if (h < static_cast<uint32_t>(L)) return static_cast<int>(h);
@@ -53,6 +57,31 @@ struct CompactEmit {
 };
 
 constexpr int kRowsPerBlock = 4;   // one wavefront per incoming row
+
+// fp8 records: one wavefront per incoming row; every lane dequantizes 8
+// values at a time (codes and the group's scale from the same record) and
+// stores them as 16 bytes of bf16.
+template <bool ROW>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_fp8_rows_kernel(
+    const uint8_t* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t H, int64_t rb, int32_t d,
+    int32_t* __restrict__ row_slot, bf16_t* __restrict__ compact) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= n_rows) return;
+  if (row % P1 < H) {
+    if (lane == 0) row_slot[row] = -1;
+    return;
+  }
+  const int32_t slot = row_slot[row];
+  if (slot < 0) return;
+  const uint8_t* in = pools + row * rb;
+  bf16_t* out = compact + static_cast<int64_t>(slot) * d;
+  for (int32_t c = lane * 8; c < d; c += kWave * 8) {
+    float v[8];
+    fp8_dequant8<ROW>(in, c, d, v);
+    st_stream(pack_bf16x8(v), reinterpret_cast<vec16*>(out + c));
+  }
+}
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_rows_kernel(
     const vec16* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t H, int64_t row_vecs,
@@ -81,7 +110,8 @@ MOE_API size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int3
   return rank_table_bytes(rank_geom(n, n_local)) + 2 * align_up((n_local + 1) * sizeof(int32_t), 256);
 }
 
-MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d, int32_t n_local,
+MOE_API int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n_src, int32_t pool_rows, int32_t d,
+                             int32_t n_local,
                              int32_t cap, int32_t src_rotation, void* compact, int32_t* counts, int32_t* arrived,
                              int32_t* row_slot, int32_t* recv_dropped, void* ws, size_t ws_bytes,
                              uint32_t* dev_flags, hipStream_t stream) {
@@ -89,7 +119,10 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_r
   MOE_CHECK(n_src >= 0 && pool_rows >= 0 && n_local >= 1 && n_local <= MOE_MAX_EXPERTS && cap >= 0, MOE_EINVAL);
   MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
   MOE_CHECK(src_rotation >= 0 && src_rotation < (n_src > 0 ? n_src : 1), MOE_EINVAL);
-  const int64_t H = pool_rows > d ? (static_cast<int64_t>(pool_rows) + d - 1) / d : 1;
+  MOE_CHECK(pool_dtype == MOE_BF16 || is_fp8(pool_dtype), MOE_EINVAL);
+  const int64_t rb = row_bytes(pool_dtype, d);                      // bytes per pool row
+  const int64_t re = rb / 2;                                        // 16-bit elements per pool row
+  const int64_t H = pool_rows > re ? (static_cast<int64_t>(pool_rows) + re - 1) / re : 1;
   const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
   const int64_t n_rows = static_cast<int64_t>(n_src) * P1;
   MOE_CHECK(n_rows <= INT32_MAX && static_cast<int64_t>(n_local) * cap <= INT32_MAX, MOE_EUNSUPPORTED);
@@ -107,15 +140,24 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_r
                                                    align_up((n_local + 1) * sizeof(int32_t), 256));
   RankScanOut out{arrived ? arrived : arrived_ws, counts, offsets, recv_dropped, 0};
   const bf16_t* pb = static_cast<const bf16_t*>(pools_in);
-  int st = bucket_rank(g, HeaderBucket{pb, pool_rows, P1, d, src_rotation, n_src, n_local},
+  int st = bucket_rank(g, HeaderBucket{pb, pool_rows, P1, re, src_rotation, n_src, n_local},
                        CompactEmit{pool_rows, P1, H, src_rotation, n_src, cap, row_slot}, cap, out, table, dev_flags,
                        stream);
   if (st != MOE_OK) return st;
   if (n_rows > 0) {
     const unsigned blocks = static_cast<unsigned>((n_rows + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL(compact_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
-                       static_cast<const vec16*>(pools_in), n_rows, P1, H, static_cast<int64_t>(d) / 8, row_slot,
-                       static_cast<vec16*>(compact));
+    if (pool_dtype == MOE_BF16)
+      hipLaunchKernelGGL(compact_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
+                         static_cast<const vec16*>(pools_in), n_rows, P1, H, static_cast<int64_t>(d) / 8, row_slot,
+                         static_cast<vec16*>(compact));
+    else if (pool_dtype == MOE_FP8_ROW)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(compact_fp8_rows_kernel<true>), dim3(blocks), dim3(kRowsPerBlock * kWave),
+                         0, stream, static_cast<const uint8_t*>(pools_in), n_rows, P1, H, rb, d, row_slot,
+                         static_cast<bf16_t*>(compact));
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(compact_fp8_rows_kernel<false>), dim3(blocks), dim3(kRowsPerBlock * kWave),
+                         0, stream, static_cast<const uint8_t*>(pools_in), n_rows, P1, H, rb, d, row_slot,
+                         static_cast<bf16_t*>(compact));
     MOE_LAUNCH_CHECK();
   }
   return MOE_OK;

@@ -60,7 +60,14 @@ typedef enum {
   MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Row storage.  MOE_FP8_ROW / MOE_FP8_B128 are fp8 dispatch records
+ * ("M6.2 - Expert Parallelism and DeepSeek MoE", 0x0AB-0x0AC: fp8 data plus
+ * fp32 scales that travel with their row): d OCP E4M3 codes (bias 7, 3
+ * mantissa bits, max 448, 0x7F NaN, no infinity), then G fp32 scales (G = 1,
+ * or ceil(d / 128) for one scale per 128 values), then zero bytes up to a
+ * multiple of 16 (moe_row_bytes).  Value i of a record is
+ * decode(code_i) * scale[i / group width]. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_ROW = 2, MOE_FP8_B128 = 3 } moe_dtype;
 
 /* Gating families ("M6.2 - Expert Parallelism and DeepSeek MoE").
  *   SOFTMAX_TOPK_RENORM   0x06L1, Mixtral row: FP32 softmax over all experts,
@@ -89,10 +96,48 @@ typedef enum {
 #define MOE_FLAG_BAD_HEADER      4u  /* header id neither < n_local nor 0xFFFF (row ignored) */
 #define MOE_FLAG_BAD_INDEX       8u  /* combine index < -1 or expand slot out of range (ignored) */
 #define MOE_FLAG_BAD_SEGMENT    16u  /* expert segment outside [0, rows) (expert skipped) */
+#define MOE_FLAG_NONFINITE_INPUT 32u  /* NaN/Inf in a quantized group (group stored as zeros) */
 
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 1024   /* E, n_dest, n_local */
 #define MOE_MAX_TOPK    16
+
+/* Bytes of one row of d values stored as dtype (records padded to 16 bytes);
+ * 0 for an unknown dtype or d < 1. */
+size_t moe_row_bytes(int32_t dtype, int32_t d);
+
+/* ---------------------------------------------------------------------------
+ * moe_quantize_fp8 -- rows to fp8 dispatch records.
+ *
+ * "M6.2 - Expert Parallelism and DeepSeek MoE", 0x0AB-0x0AC: quantization
+ * yields fp8 data and its fp32 scales, owned by the same row.  For every
+ * scale group of row t (the row, or 128 consecutive values; the pages fix no
+ * scale rule, this is the library's): a = largest |x| of the group,
+ *   scale = a / 448, inv = 448 / a   (each one correctly rounded fp32 op)
+ *   code_i = E4M3(x_i * inv)         (fp32 product; nearest, ties to even,
+ *                                     saturating at +-448, sign kept)
+ * A group with a = 0 stores scale 0 and zero codes; a group holding NaN or
+ * Inf stores the same and sets MOE_FLAG_NONFINITE_INPUT.
+ *
+ *   x          device [n, d] of x_dtype (MOE_BF16 or MOE_F32); d % 8 == 0
+ *   rec_dtype  MOE_FP8_ROW or MOE_FP8_B128
+ *   rec        device [n, moe_row_bytes(rec_dtype, d)] bytes, 16-byte aligned
+ * ------------------------------------------------------------------------- */
+int moe_quantize_fp8(const void* x, int32_t x_dtype, int64_t n, int32_t d, int32_t rec_dtype, void* rec,
+                     uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_dequantize_fp8 -- fp8 dispatch records back to rows.
+ *
+ * out[t][i] = decode(code_i) * scale[group of i] (fp32 product), stored as
+ * out_dtype (bf16: nearest even) -- the scale read from the same record
+ * (M6.2 0x0AC).
+ *
+ *   rec        device records [n, moe_row_bytes(rec_dtype, d)]; d % 8 == 0
+ *   out        device [n, d] of out_dtype (MOE_BF16 or MOE_F32)
+ * ------------------------------------------------------------------------- */
+int moe_dequantize_fp8(const void* rec, int32_t rec_dtype, int64_t n, int32_t d, void* out, int32_t out_dtype,
+                       uint32_t* dev_flags, hipStream_t stream);
 
 /* Human-readable name of a moe_status value.  Never NULL. */
 const char* moe_strerror(int status);
@@ -172,13 +217,15 @@ int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k,
  *   offsets    exclusive prefix of counts, offsets[E] = A (accepted total)
  *   inv[r]     = offsets[e_r] + pos_r, or -1 if dropped
  *   src[p]     = r with inv[r] = p for p < A; -1 for A <= p < T*k
- *   x_perm[p]  = x[src[p] / k] for p < A (rows p >= A are not written)
+ *   x_perm[p]  = x[src[p] / k] for p < A (rows p >= A are not written); fp8
+ *                records move whole, codes and scales together (M6.2 0x0AC)
  *   n_dropped  = T*k - A
  * Expert id -1 means "no route" (dropped, not flagged); ids < -1 or >= E
  * are dropped and set MOE_FLAG_BAD_EXPERT.
  *
  *   x          device, [T, d] of x_dtype; may be NULL when x_perm is NULL
- *   x_dtype    MOE_F32 (d % 4 == 0) or MOE_BF16 (d % 8 == 0)
+ *   x_dtype    MOE_F32 (d % 4 == 0), MOE_BF16 (d % 8 == 0) or an fp8 record
+ *              dtype (d % 8 == 0; rows of moe_row_bytes(x_dtype, d) bytes)
  *   topk_ids   device int32 [T*k]
  *   capacity   -1 (dropless) or >= 0
  *   x_perm     device [T*k, d] of x_dtype, or NULL (metadata only)
@@ -325,9 +372,12 @@ int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* ro
 /* ---------------------------------------------------------------------------
  * moe_pool_pack -- pooled-wave sender pack into fixed destination pools.
  *
- * A pool has H = max(1, ceil(pool_rows / d)) full-width header rows (one at
- * the pages' sizes) followed by pool_rows data rows; PH = pool_rows + H.
- * Header element i (row i / d, column i % d) holds data row i's local id.
+ * Rows are RB = moe_row_bytes(x_dtype, d) bytes: bf16 rows, or fp8 records
+ * (M6.2 0x0AB-0x0AC: the scales travel inside the row).  A pool has
+ * H = max(1, ceil(2 * pool_rows / RB)) full-width header rows (one for bf16
+ * rows at the pages' sizes) followed by pool_rows data rows;
+ * PH = pool_rows + H.  The header rows hold little-endian uint16 ids: id i
+ * (bytes 2i, 2i+1 of the flattened header) is data row i's local id.
  *
  * For route r = t*k + j with valid expert e = topk_ids[r] (pooled wave 02-05):
  *   dest = e / experts_per_dest,  local = e % experts_per_dest
@@ -341,16 +391,16 @@ int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* ro
  * sender_dropped = T*k - accepted (routes above the cap plus routes whose id
  * is -1 or invalid; invalid ids set MOE_FLAG_BAD_EXPERT).
  *
- *   x_bf16     device bf16 [T, d], d % 8 == 0
+ *   x          device [T] rows of x_dtype (MOE_BF16, MOE_FP8_ROW, MOE_FP8_B128), d % 8 == 0
  *   E <= n_dest * experts_per_dest, n_dest <= MOE_MAX_EXPERTS, 1 <= n_waves
- *   wave       -1: pools is [n_waves][n_dest][PH][d] (all waves);
- *              w >= 0: pools is [n_dest][PH][d], only wave w's rows and
+ *   wave       -1: pools is [n_waves][n_dest][PH] rows of RB bytes (all waves);
+ *              w >= 0: pools is [n_dest][PH] rows, only wave w's rows and
  *              headers are written (route_loc keeps the all-wave index)
  *   route_loc  device int32 [T*k]; dest_counts int32 [n_dest]; sender_dropped int32 [1]
  *   ws         device workspace of moe_pool_pack_workspace(T, k, n_dest)
  * ------------------------------------------------------------------------- */
 size_t moe_pool_pack_workspace(int64_t T, int32_t k, int32_t n_dest);
-int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k,
+int moe_pool_pack(const void* x, int32_t x_dtype, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k,
                   int32_t E, int32_t experts_per_dest, int32_t n_dest, int32_t n_waves,
                   int32_t pool_rows, int32_t wave, void* pools, int32_t* route_loc,
                   int32_t* dest_counts, int32_t* sender_dropped, void* ws, size_t ws_bytes,
@@ -359,8 +409,8 @@ int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_
 /* ---------------------------------------------------------------------------
  * moe_recv_compact -- receiver compaction into static per-expert arrays.
  *
- * Pools have the layout of moe_pool_pack: H = max(1, ceil(pool_rows / d))
- * header rows, then pool_rows data rows; PH = pool_rows + H.  Over one
+ * Pools have the layout of moe_pool_pack for rows of pool_dtype: H header
+ * rows, then pool_rows data rows; PH = pool_rows + H.  Over one
  * wave's incoming pools, visiting sources s = (src_rotation + v) % n_src for
  * v = 0..n_src-1 (src_rotation = 0: the fixed source order of pooled wave
  * 07; another value is the per-receiver rotation proposed there), then
@@ -368,6 +418,8 @@ int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_
  *   h = header element i of source s (uint16); 0xFFFF = empty row
  *   q = number of earlier visited rows with the same h
  *   accepted iff q < cap:  compact[h][q][:] = pools_in[s][H + i][:]
+ *                          (fp8 records: dequantized to bf16 as in
+ *                          moe_dequantize_fp8, with the record's own scales)
  *   row_slot[s*PH + H + i] = h*cap + q, else -1
  *   row_slot of header rows and empty rows = -1
  *   arrived[h] = rows with id h, counts[h] = min(arrived[h], cap),
@@ -375,7 +427,8 @@ int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_
  * Header ids >= n_local other than 0xFFFF set MOE_FLAG_BAD_HEADER and the
  * row is ignored.  compact rows at or past counts[h] are not written.
  *
- *   pools_in   device bf16 [n_src][PH][d], d % 8 == 0
+ *   pools_in   device [n_src][PH] rows of pool_dtype (MOE_BF16, MOE_FP8_ROW,
+ *              MOE_FP8_B128), d % 8 == 0
  *   1 <= n_local <= MOE_MAX_EXPERTS, cap >= 0, 0 <= src_rotation < max(n_src, 1)
  *   compact    device bf16 [n_local][cap][d]
  *   counts int32 [n_local]; arrived int32 [n_local] or NULL;
@@ -383,7 +436,7 @@ int moe_pool_pack(const void* x_bf16, int64_t T, int32_t d, const int32_t* topk_
  *   ws         device workspace of moe_recv_compact_workspace(n_src, pool_rows, n_local)
  * ------------------------------------------------------------------------- */
 size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int32_t n_local);
-int moe_recv_compact(const void* pools_in, int32_t n_src, int32_t pool_rows, int32_t d,
+int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n_src, int32_t pool_rows, int32_t d,
                      int32_t n_local, int32_t cap, int32_t src_rotation, void* compact, int32_t* counts,
                      int32_t* arrived, int32_t* row_slot, int32_t* recv_dropped,
                      void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);

@@ -695,7 +695,8 @@ def quantize_fp8_rows(x: np.ndarray, mode: str) -> np.ndarray:
     largest magnitude; ``scale = fp32(a / 448)``, ``inv = fp32(448 / a)``,
     code ``= E4M3(fp32(x * inv))``; a group with ``a = 0`` gets scale 0 and
     zero codes.  (The pages fix no scale rule: this max-to-448 rule, with
-    every step one correctly rounded fp32 operation, is the reading.)
+    every step one correctly rounded fp32 operation, is the reading; a group
+    holding NaN or infinity is stored like an all-zero group.)
     Returns uint8 ``[n, W]``.
     """
     xf = np.asarray(x, dtype=np.float32)
@@ -708,7 +709,7 @@ def quantize_fp8_rows(x: np.ndarray, mode: str) -> np.ndarray:
         c0, c1 = g * width, min(d, (g + 1) * width)
         blk = xf[:, c0:c1]
         amax = np.abs(blk).max(axis=1) if n else np.zeros(0, np.float32)
-        live = amax > 0
+        live = np.isfinite(amax) & (amax > 0)         # zero or non-finite groups store zeros
         safe = np.where(live, amax, np.float32(1.0)).astype(np.float32)
         scale = np.where(live, safe / np.float32(FP8_E4M3_MAX), np.float32(0.0)).astype(np.float32)
         inv = (np.float32(FP8_E4M3_MAX) / safe).astype(np.float32)

@@ -14,7 +14,7 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 def test_exports_every_header_symbol():
     names = B.header_functions()
-    assert len(names) == 17
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
@@ -122,35 +122,57 @@ def test_combine_validation():
 def test_pool_pack_validation():
     p, _keep = _fake()
     ws = lib.moe_pool_pack_workspace(100, 8, 64)
-    args = [p, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
-    bad = list(args); bad[5] = 385                                  # E > n_dest * epd
+    args = [p, 1, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[6] = 385                                  # E > n_dest * epd
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[9] = 1 << 30                              # pool rows past the int32 route locations
+    bad = list(args); bad[10] = 1 << 30                             # pool rows past the int32 route locations
     assert lib.moe_pool_pack(*bad) == EUNSUP
-    bad = list(args); bad[9] = -1                                   # negative pool rows
+    bad = list(args); bad[10] = -1                                  # negative pool rows
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[10] = 3                                   # wave out of range
+    bad = list(args); bad[11] = 3                                   # wave out of range
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[16] = 8                                   # workspace too small
+    bad = list(args); bad[17] = 8                                   # workspace too small
     assert lib.moe_pool_pack(*bad) == EWS
+    bad = list(args); bad[1] = 0                                    # fp32 rows are not a dispatch payload
+    assert lib.moe_pool_pack(*bad) == EINVAL
+    bad = list(args); bad[1] = 3; bad[10] = 1 << 30                 # fp8 records are accepted (then: too many rows)
+    assert lib.moe_pool_pack(*bad) == EUNSUP
 
 
 def test_recv_compact_validation():
     p, _keep = _fake()
     ws = lib.moe_recv_compact_workspace(64, 3004, 6)
-    args = [p, 64, 3004, 3072, 6, 33497, 0, p, p, p, p, p, p, ws, NULL, NULL]
-    bad = list(args); bad[5] = -1                                   # negative capacity
+    args = [p, 1, 64, 3004, 3072, 6, 33497, 0, p, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[6] = -1                                   # negative capacity
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[4] = 0                                    # no local experts
+    bad = list(args); bad[5] = 0                                    # no local experts
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[6] = 64                                   # rotation past the last source
+    bad = list(args); bad[7] = 64                                   # rotation past the last source
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[6] = -1                                   # negative rotation
+    bad = list(args); bad[7] = -1                                   # negative rotation
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[13] = 0                                   # workspace
+    bad = list(args); bad[14] = 0                                   # workspace
     assert lib.moe_recv_compact(*bad) == EWS
-    bad = list(args); bad[2] = 1 << 26                              # pool rows past int32 row indexes
+    bad = list(args); bad[3] = 1 << 26                              # pool rows past int32 row indexes
     assert lib.moe_recv_compact(*bad) == EUNSUP
+    bad = list(args); bad[1] = 7                                    # unknown pool dtype
+    assert lib.moe_recv_compact(*bad) == EINVAL
+
+
+def test_fp8_record_widths_and_validation():
+    assert lib.moe_row_bytes(1, 3072) == 6144 and lib.moe_row_bytes(0, 3) == 12
+    assert lib.moe_row_bytes(2, 3072) == 3088            # 3072 codes + 4 + 12 padding
+    assert lib.moe_row_bytes(3, 3072) == 3168            # 3072 codes + 24 scales
+    assert lib.moe_row_bytes(3, 7168) == 7168 + 4 * 56
+    assert lib.moe_row_bytes(9, 64) == 0 and lib.moe_row_bytes(1, 0) == 0
+    p, _keep = _fake()
+    assert lib.moe_quantize_fp8(p, 1, 10, 64, 1, p, NULL, NULL) == EINVAL      # record dtype must be fp8
+    assert lib.moe_quantize_fp8(p, 2, 10, 64, 2, p, NULL, NULL) == EINVAL      # input must be bf16 / fp32
+    assert lib.moe_quantize_fp8(p, 1, 10, 12, 2, p, NULL, NULL) == EINVAL      # d % 8
+    assert lib.moe_quantize_fp8(NULL, 1, 0, 64, 3, NULL, NULL, NULL) == 0      # nothing to do
+    assert lib.moe_dequantize_fp8(p, 1, 10, 64, p, 1, NULL, NULL) == EINVAL    # records must be fp8
+    assert lib.moe_dequantize_fp8(p, 3, 10, 64, p, 2, NULL, NULL) == EINVAL    # output bf16 / fp32
+    assert lib.moe_dequantize_fp8(NULL, 3, 0, 64, NULL, 1, NULL, NULL) == 0
 
 
 def test_expand_rows_validation():
