@@ -68,10 +68,11 @@ def parse():
 # ---------------------------------------------------------------------------
 
 # kernel sources of each call (plus the shared header and the C ABI)
-_CALL_SOURCES = {"route": ["route_topk.hip"], "permute": ["permute.hip", "bucket_rank.h"],
+_CALL_SOURCES = {"route": ["route_topk.hip"], "permute": ["permute.hip", "bucket_rank.h", "fp8.h"],
                  "swiglu": ["swiglu_gemm.hip", "gemm_core.h"], "combine": ["combine.hip"],
-                 "expand": ["combine.hip"], "pool_pack": ["pool_pack.hip", "bucket_rank.h"],
-                 "recv_compact": ["recv_compact.hip", "bucket_rank.h"], "combine_bwd": ["combine.hip"],
+                 "expand": ["combine.hip"], "pool_pack": ["pool_pack.hip", "bucket_rank.h", "fp8.h"],
+                 "recv_compact": ["recv_compact.hip", "bucket_rank.h", "fp8.h"], "combine_bwd": ["combine.hip"],
+                 "quantize": ["fp8.hip", "fp8.h"],
                  "swiglu_bwd": ["swiglu_backward.hip", "gemm_core.h"], "dx_combine": ["combine.hip"]}
 
 
@@ -95,7 +96,8 @@ def _call_of(kernel):
     of the next dispatch, by the caller of this function."""
     table = (("route_topk_kernel", "route"), ("build_tiles_kernel", "swiglu"), ("grouped_gemm_", "swiglu"),
              ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
-             ("compact_rows_kernel", "recv_compact"), ("expand_rows_kernel", "expand"),
+             ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
+             ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),
              ("combine_kernel", "combine"), ("rank_", "rank"))
     for pat, call in table:
         if pat in kernel:
@@ -106,7 +108,7 @@ def _call_of(kernel):
 # one dispatch per call instance: counts the launches of each call
 _ANCHORS = {"route": "route_topk_kernel", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
             "combine": "combine_kernel", "expand": "expand_rows_kernel", "pool_pack": "pack_kernel",
-            "recv_compact": "compact_rows_kernel"}
+            "recv_compact": "compact_", "quantize": "quantize_kernel"}
 
 
 def record_traffic(args):
@@ -334,12 +336,34 @@ def train_cpu_baseline(w, host, sample):
                        f"(route, gate, token and weight gradients); {dt:.2f} s")
 
 
+def fp8_pools(torch, ge, w, wave, pools16):
+    """The wave's incoming pools as fp8 records (untimed set-up): the bf16
+    data rows quantized by the library, the same local ids in the record
+    pools' header rows (16-bit little-endian, 0xFFFF past the last row)."""
+    S, P, d = w.n_src, w.pool_rows, w.d
+    H16 = W.recv_header_rows(w)
+    rows = pools16[:, H16:, :].reshape(S * P, d).contiguous()
+    rec = ge.quantize_fp8(rows, w.payload)
+    Wb = rec.shape[1]
+    H8 = ge.header_rows(P, d, w.payload)
+    out = torch.empty((S, H8 + P, Wb), dtype=torch.uint8, device=rows.device)
+    hdr = out[:, :H8, :].reshape(S, H8 * Wb).view(torch.int16)
+    hdr.fill_(-1)
+    hdr[:, :P] = to_dev(torch, W.recv_local_ids(w, wave).view(np.int16))
+    out[:, H8:, :] = rec.view(S, P, Wb)
+    return out
+
+
 def recv_setup(torch, w, banks):
     pools = [W.recv_pools(w, wave) for wave in range(w.n_waves)]
     wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
     host = dict(pools=pools, wg=wg, wu=wu, wd=wd)
-    b0 = dict(pools=[to_dev(torch, p) for p in pools], wg=to_dev(torch, wg), wu=to_dev(torch, wu),
-              wd=to_dev(torch, wd))
+    dev_pools = [to_dev(torch, p) for p in pools]
+    if w.payload is not None:
+        import grouped_expert_amd as ge
+        dev_pools = [fp8_pools(torch, ge, w, wave, p) for wave, p in enumerate(dev_pools)]
+        torch.cuda.synchronize()
+    b0 = dict(pools=dev_pools, wg=to_dev(torch, wg), wu=to_dev(torch, wu), wd=to_dev(torch, wd))
     bank_list = [b0]
     for _ in range(banks - 1):
         bank_list.append(dict(pools=[p.clone() for p in b0["pools"]], wg=b0["wg"].clone(), wu=b0["wu"].clone(),
@@ -349,12 +373,12 @@ def recv_setup(torch, w, banks):
 
 def recv_step(ge, timer, w, bank, flags, bufs):
     import torch
-    S, P1, L, cap, d = w.n_src, ge.pool_height(w.pool_rows, w.d), w.n_local, w.recv_cap, w.d
+    S, P1, L, cap, d = w.n_src, ge.pool_height(w.pool_rows, w.d, w.payload), w.n_local, w.recv_cap, w.d
     starts = bufs["starts"]
     outs = []
     for wave in range(w.n_waves):
         rc = timer.run("recv_compact", ge.recv_compact, bank["pools"][wave], L, cap, compact=bufs["compact"],
-                       flags=flags)
+                       flags=flags, payload=w.payload, d=d)
         z = timer.run("swiglu", ge.grouped_swiglu, bufs["compact"].view(L * cap, d), starts, rc["counts"],
                       bank["wg"], bank["wu"], bank["wd"], z=bufs["z"], flags=flags)
         ret = timer.run("expand", ge.expand_rows, z, rc["row_slot"], ret=bufs["ret"][wave], flags=flags)
@@ -363,15 +387,18 @@ def recv_step(ge, timer, w, bank, flags, bufs):
 
 
 def recv_ledger(w, counts_per_wave):
-    S, P, P1, d, dff = w.n_src, w.pool_rows, W.recv_header_rows(w) + w.pool_rows, w.d, w.d_ff
+    import grouped_expert_amd as ge
+    S, P, d, dff = w.n_src, w.pool_rows, w.d, w.d_ff
+    P1 = ge.pool_height(P, d, w.payload)
+    rb = ge.row_bytes(d, w.payload)             # bytes of one incoming row (bf16 or fp8 record)
     zb = 2 if w.ret_dtype == "bf16" else 4      # bytes per expert-output / return element
     led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0),
            "expand": dict(bytes=0, flops=0)}
     for counts in counts_per_wave:
         A = int(counts.sum())
         E_act = int((counts > 0).sum())
-        # header ids, accepted rows read and written (receiver-dropped rows are never read), row_slot
-        led["recv_compact"]["bytes"] += S * P * 2 + 2 * A * d * 2 + 4 * S * P1
+        # header ids, accepted rows read and written as bf16 (receiver-dropped rows are never read), row_slot
+        led["recv_compact"]["bytes"] += S * P * 2 + A * rb + A * d * 2 + 4 * S * P1
         led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * zb
         led["swiglu"]["flops"] += 6 * A * d * dff
         led["expand"]["bytes"] += A * d * zb + 4 * S * P1 + S * P1 * d * zb
@@ -385,6 +412,11 @@ def recv_cpu_baseline(w, host, sample):
     t0 = time.perf_counter()
     rc = O.recv_compact(host["pools"][0], w.n_local, w.recv_cap)
     comp = rc["compact"]
+    if w.payload is not None:                   # the records of the sampled rows: quantize and dequantize
+        flat = comp.reshape(-1, w.d)[:sample]
+        rec = O.quantize_fp8_rows(O.to_f64(flat).astype(np.float32), w.payload)
+        comp = comp.copy()
+        comp.reshape(-1, w.d)[:sample] = O.f32_to_bf16_rne(O.dequantize_fp8_rows(rec, w.d, w.payload))
     n = 0
     for e in range(w.n_local):
         take = min(int(rc["counts"][e]), max(0, sample - n))
@@ -396,7 +428,9 @@ def recv_cpu_baseline(w, host, sample):
     dt = time.perf_counter() - t0
     return dict(value=w.n_src * w.pool_rows / dt if n >= int(rc["counts"].sum()) else n / dt,
                 unit="incoming rows/s", cores=cpu_threads(), kind="oracle",
-                sample=f"wave 0 compaction of {w.n_src}x{w.pool_rows} rows plus fp64 SwiGLU of {n} accepted rows; "
+                sample=f"wave 0 compaction of {w.n_src}x{w.pool_rows} rows"
+                       + (f", fp8 quantize + dequantize of {sample} rows" if w.payload else "")
+                       + f" plus fp64 SwiGLU of {n} accepted rows; "
                        f"rate = SwiGLU rows / {dt:.2f} s")
 
 
@@ -410,16 +444,24 @@ def pack_setup(torch, w, banks):
 
 def pack_step(ge, timer, w, bank, flags, bufs):
     ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, flags=flags)
-    out = timer.run("pool_pack", ge.pool_pack, bank["x"], ids, w.E, w.experts_per_dest, w.n_dest, w.n_waves,
-                    w.pool_rows, pools=bufs["pools"], flags=flags)
+    rows = bank["x"]
+    if w.payload is not None:
+        rows = timer.run("quantize", ge.quantize_fp8, rows, w.payload, rec=bufs["rec"], flags=flags)
+    out = timer.run("pool_pack", ge.pool_pack, rows, ids, w.E, w.experts_per_dest, w.n_dest, w.n_waves,
+                    w.pool_rows, pools=bufs["pools"], flags=flags, payload=w.payload, d=w.d)
     return dict(ids=ids, gates=gates, pack=out)
 
 
 def pack_ledger(w):
+    import grouped_expert_amd as ge
     T, k, d, E = w.T, w.k, w.d, w.E
-    return {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
-            "pool_pack": dict(bytes=8 * T * k + T * d * 2 + w.n_waves * w.n_dest * (W.recv_header_rows(w) + w.pool_rows) * d * 2,
-                              flops=0)}
+    rb = ge.row_bytes(d, w.payload)
+    P1 = ge.pool_height(w.pool_rows, d, w.payload)
+    led = {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
+           "pool_pack": dict(bytes=8 * T * k + T * rb + w.n_waves * w.n_dest * P1 * rb, flops=0)}
+    if w.payload is not None:
+        led["quantize"] = dict(bytes=T * d * 2 + T * rb, flops=0)
+    return led
 
 
 def pack_cpu_baseline(w, host, sample):
@@ -427,10 +469,14 @@ def pack_cpu_baseline(w, host, sample):
     s = min(sample, w.T)
     t0 = time.perf_counter()
     ids, _, _ = O.route_topk(host["logits"][:s], w.k)
-    O.pool_pack(host["x"][:s], ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
+    rows = host["x"][:s]
+    if w.payload is not None:
+        rows = O.quantize_fp8_rows(O.to_f64(rows).astype(np.float32), w.payload)
+    O.pool_pack(rows, ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
     dt = time.perf_counter() - t0
     return dict(value=s / dt, unit="tokens/s", cores=cpu_threads(), kind="oracle",
-                sample=f"first {s} of {w.T} tokens of {w.name}: route + pack of all waves; {dt:.2f} s")
+                sample=f"first {s} of {w.T} tokens of {w.name}: route + "
+                       + ("fp8 quantize + " if w.payload else "") + f"pack of all waves; {dt:.2f} s")
 
 
 def router_setup(torch, w, banks):
@@ -503,7 +549,8 @@ def main():
         rdt = torch.bfloat16 if w.ret_dtype == "bf16" else torch.float32
         bufs = dict(compact=torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda"),
                     z=torch.empty((L * cap, d), dtype=rdt, device="cuda"),
-                    ret=[torch.empty((w.n_src * ge.pool_height(w.pool_rows, d), d), dtype=rdt, device="cuda")
+                    ret=[torch.empty((w.n_src * ge.pool_height(w.pool_rows, d, w.payload), d), dtype=rdt,
+                                     device="cuda")
                          for _ in range(w.n_waves)],
                     starts=torch.arange(L, dtype=torch.int32, device="cuda") * cap)
         step = lambda tm, b: recv_step(ge, tm, w, b, flags, bufs)
@@ -512,8 +559,14 @@ def main():
         step = lambda tm, b: router_step(ge, tm, w, b, flags)
     else:
         host, bank_list = pack_setup(torch, w, banks)
-        bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, ge.pool_height(w.pool_rows, w.d), w.d), dtype=torch.bfloat16,
-                                      device="cuda"))
+        if w.payload is None:
+            bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, ge.pool_height(w.pool_rows, w.d), w.d),
+                                          dtype=torch.bfloat16, device="cuda"))
+        else:
+            rb = ge.row_bytes(w.d, w.payload)
+            bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, ge.pool_height(w.pool_rows, w.d, w.payload), rb),
+                                          dtype=torch.uint8, device="cuda"),
+                        rec=torch.empty((w.T, rb), dtype=torch.uint8, device="cuda"))
         step = lambda tm, b: pack_step(ge, tm, w, b, flags, bufs)
     # one plain device copy of known size (untimed): under rocprofv3 --pmc its
     # FETCH_SIZE / WRITE_SIZE readings calibrate the counters to bytes

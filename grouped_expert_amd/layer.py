@@ -59,7 +59,7 @@ def moe_layer_backward(dy: torch.Tensor, x: torch.Tensor, state: dict, w_gate: t
 def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: torch.Tensor, gates: torch.Tensor,
                   T: int, k: int, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, cap: int,
                   y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None,
-                  rotation: int = 0, ret_dtype: torch.dtype = torch.float32):
+                  rotation: int = 0, ret_dtype: torch.dtype = torch.float32, payload: Optional[str] = None):
     """One wave of the receiver path; adds the wave's contributions into ``y``.
 
     ``pools_w`` is ``[n_src, pool_height, d]`` (one wave's pools, header rows
@@ -67,11 +67,14 @@ def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: tor
     tensors to reuse; ``rotation`` is the receiver's first source.  With
     ``ret_dtype`` bf16 the expert rows leave the GEMM as bf16 and the return
     buffer is bf16 ("M6.6 - MoE Runtime Systems", 0x0AE); the combine still
-    accumulates in FP32."""
-    S, P1, d = pools_w.shape
+    accumulates in FP32.  With ``payload`` "row" / "b128" the pools hold fp8
+    records and the compaction dequantizes them ("M6.2", 0x0AC)."""
+    S, P1 = pools_w.shape[0], pools_w.shape[1]
     L = w_gate.shape[0]
+    d = w_down.shape[1]
     bufs = {} if bufs is None else bufs
-    rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags, rotation=rotation)
+    rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags, rotation=rotation,
+                        payload=payload, d=d)
     starts = torch.arange(L, dtype=torch.int32, device=pools_w.device) * cap
     z = B.grouped_swiglu(rc["compact"].view(L * cap, d), starts, rc["counts"], w_gate, w_up, w_down,
                          z_dtype=ret_dtype, z=bufs.get("z"), flags=flags)

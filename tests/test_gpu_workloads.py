@@ -152,17 +152,19 @@ def test_mid_bf16_backward(ge):
             assert_rows_close(to_np(gr[name][e]).astype(np.float64), want, what=f"{name}[{e}]")
 
 
-@pytest.fixture(scope="module", params=["sender_pack_bf16", "sender_pack_2w_bf16"])
+@pytest.fixture(scope="module", params=["sender_pack_bf16", "sender_pack_2w_bf16", "sender_pack_fp8"])
 def send_case(request):
     """Inputs and the oracle's routing and pack of a sender-pack workload, three
-    waves of 3004-row pools or two waves of 4506-row pools with two header
-    rows (computed once for the tests that use them)."""
+    waves of 3004-row pools, two waves of 4506-row pools with two header rows,
+    or three waves of fp8 records (computed once for the tests that use
+    them)."""
     w = W.WORKLOADS[request.param]
     logits = W.router_logits(w)
     x = W.tokens(w)
     ids, gates, _ = O.route_topk(logits, w.k)
-    pk = O.pool_pack(x, ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
-    return dict(w=w, logits=logits, x=x, ids=ids, gates=gates, pk=pk)
+    rec = None if w.payload is None else O.quantize_fp8_rows(O.to_f64(x).astype(np.float32), w.payload)
+    pk = O.pool_pack(x if rec is None else rec, ids, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows)
+    return dict(w=w, logits=logits, x=x, ids=ids, gates=gates, pk=pk, rec=rec)
 
 
 def test_sender_pack_full(ge, send_case):
@@ -173,8 +175,12 @@ def test_sender_pack_full(ge, send_case):
     w, pk = c["w"], c["pk"]
     flags = ge.new_flags("cuda")
     ids_g, gates_g = ge.route_topk(to_gpu(c["logits"]), w.k, flags=flags)
-    out = ge.pool_pack(to_gpu(c["x"]), ids_g, w.E, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows,
-                       flags=flags)
+    rows = to_gpu(c["x"])
+    if w.payload is not None:
+        rows = ge.quantize_fp8(rows, w.payload, flags=flags)
+        assert np.array_equal(to_np(rows), c["rec"])                   # codes and scales, every token
+    out = ge.pool_pack(rows, ids_g, w.E, w.experts_per_dest, w.n_dest, w.n_waves, w.pool_rows,
+                       flags=flags, payload=w.payload, d=w.d)
     torch.cuda.synchronize()
     assert int(to_np(flags)[0]) == 0
     assert np.array_equal(to_np(ids_g), c["ids"])
@@ -269,8 +275,9 @@ def test_loopback_sender_to_receiver(ge, send_case, cap_kind, ret):
     gw = [to_gpu(a) for a in (wg, wu, wd)]
     flags = ge.new_flags("cuda")
     ids_g, gates_g = ge.route_topk(to_gpu(c["logits"]), ws.k, flags=flags)
-    pk_g = ge.pool_pack(to_gpu(x), ids_g, ws.E, ws.experts_per_dest, ws.n_dest, ws.n_waves, ws.pool_rows,
-                        flags=flags)
+    rows = to_gpu(x) if ws.payload is None else ge.quantize_fp8(to_gpu(x), ws.payload, flags=flags)
+    pk_g = ge.pool_pack(rows, ids_g, ws.E, ws.experts_per_dest, ws.n_dest, ws.n_waves, ws.pool_rows,
+                        flags=flags, payload=ws.payload, d=ws.d)
     y = torch.zeros((ws.T, ws.d), dtype=torch.float32, device="cuda")
     rdt = torch.bfloat16 if ret == "bf16" else torch.float32
     rot = 5 if ret == "bf16" else 0
@@ -279,18 +286,20 @@ def test_loopback_sender_to_receiver(ge, send_case, cap_kind, ret):
     slots, drops = [], 0
     for wave in range(ws.n_waves):
         rc, _, _ = ge.loopback_wave(pk_g["pools"][wave], wave, ws.n_waves, pk_g["route_loc"], gates_g, ws.T, ws.k,
-                                    *gw, cap, y, flags=flags, bufs=bufs, rotation=rot, ret_dtype=rdt)
+                                    *gw, cap, y, flags=flags, bufs=bufs, rotation=rot, ret_dtype=rdt,
+                                    payload=ws.payload)
         slots.append(to_np(rc["row_slot"]))
         drops += int(to_np(rc["recv_dropped"])[0])
     torch.cuda.synchronize()
     assert int(to_np(flags)[0]) == 0
 
-    P1 = O.header_rows(ws.pool_rows, ws.d) + ws.pool_rows
+    P1 = pk["pools"].shape[2]
     loc = pk["route_loc"]
     kept = np.zeros(loc.size, dtype=bool)
     want_drops = 0
     for wave in range(ws.n_waves):
-        rc = O.recv_compact(pk["pools"][wave], wr.n_local, cap, with_rows=False, rotation=rot)
+        rc = O.recv_compact(pk["pools"][wave], wr.n_local, cap, with_rows=False, rotation=rot,
+                            record=None if ws.payload is None else (ws.d, ws.payload))
         assert np.array_equal(slots[wave], rc["row_slot"])
         want_drops += rc["recv_dropped"]
         lo = wave * ws.n_dest * P1
@@ -302,7 +311,10 @@ def test_loopback_sender_to_receiver(ge, send_case, cap_kind, ret):
     tok = np.unique(np.concatenate([rng.choice(ws.T, size=40, replace=False),
                                     np.nonzero(~kept.reshape(ws.T, ws.k).all(axis=1))[0][:8]]))
     bank = O.swiglu_bank(lambda l: (wg[l], wu[l], wd[l]))
-    xf = O.to_f64(x[tok])
+    if ws.payload is None:
+        xf = O.to_f64(x[tok])
+    else:                                       # the rows the receiver computes on: dequantized, in bf16
+        xf = O.to_f64(O.f32_to_bf16_rne(O.dequantize_fp8_rows(c["rec"][tok], ws.d, ws.payload)))
     out = {}                                    # (sample index, slot) -> expert output
     for l in range(ws.experts_per_dest):
         pairs = [(i, j) for i, t in enumerate(tok) for j in range(ws.k)

@@ -79,6 +79,7 @@ class Workload:
     recv_zipf: float = 0.0
     ret_dtype: str = "f32"     # receiver return rows: "f32" or "bf16"
     train: bool = False        # a step is the layer forward plus its backward (upstream gradient ~ N(0, 1))
+    payload: Optional[str] = None   # dispatched rows: None = bf16, "row" / "b128" = fp8 records
     # group-restricted router (gating variants)
     gating: int = 0            # 0 softmax-renorm, 1 V1, 2 V2, 3 V3 (the library's moe_gating ids)
     n_group: int = 0
@@ -114,6 +115,11 @@ MID_TRAIN = dataclasses.replace(MID, name="mid_bf16_train", train=True)
 # The receiver share with bf16 return rows ("M6.6", 0x0AE: the returned row is
 # BF16): the expert GEMM stores bf16 and the return buffer is bf16.
 RECV_RET16 = dataclasses.replace(RECV, name="recv_share_ret_bf16", ret_dtype="bf16")
+# fp8 dispatch records with one fp32 scale per 128 values ("M6.2", 0x0AB):
+# the sender quantizes each token row once and packs records; the receiver
+# compacts records and dequantizes them into its bf16 arrays.
+SEND_FP8 = dataclasses.replace(SEND, name="sender_pack_fp8", payload="b128")
+RECV_FP8 = dataclasses.replace(RECV, name="recv_share_fp8", payload="b128")
 SEND_2W = Workload(name="sender_pack_2w_bf16", seed=3, dtype="bf16", T=65536, d=3072,
                    E=384, k=8, logits="normal", zipf_bias=1.1, x_std=1.0,
                    experts_per_dest=6, n_dest=64, n_waves=2, pool_rows=4506)
@@ -126,7 +132,7 @@ ROUTER_V3 = Workload(name="router_v3_f32", seed=5, dtype="f32", T=65536, E=256, 
                      gating=3, n_group=8, topk_group=4, route_scale=2.5, bias_std=0.05)
 
 WORKLOADS = {w.name: w for w in (TINY, MID, RECV, SEND, DECODE, ROUTER_V3, RECV_2W, SEND_2W, RECV_RET16,
-                                 MID_TRAIN)}
+                                 MID_TRAIN, SEND_FP8, RECV_FP8)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
