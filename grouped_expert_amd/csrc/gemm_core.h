@@ -120,9 +120,18 @@ __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgc
 constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
-          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore>
+          int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore,
+          bool BT_ = false>
 struct Cfg {
   static constexpr int EPI = EPI_;
+  // BT: B is stored K-major, [K][N] per expert with N contiguous (a weight
+  // used transposed, as in the data-gradient products of the backward).  The
+  // slice's B region then holds BK rows of BNB values, filled by LDS DMA, and
+  // MFMA B fragments are read with the gfx950 transposing LDS read: in each
+  // 16-lane group, lane j receives value i of the 8-byte row addressed by
+  // lane 4i + j/4, element j%4, so 16 lanes that address 4 k-rows x 16
+  // consecutive n get 4 consecutive k of one n each.
+  static constexpr bool BT = BT_;
   static constexpr int NW = NW_;                          // wavefronts per workgroup
   // RS: the weight (B) rows of a slice travel HBM -> registers -> LDS through
   // two register stages, so two B slices are in flight with a two-stage LDS
@@ -155,6 +164,13 @@ struct Cfg {
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
   static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
   static_assert(EPI == kEpiStore || GATEUP, "the SwiGLU backward epilogue needs gate/up tiles");
+  static_assert(!BT || (!GATEUP && !RS_ && BK == 64 && (BNB == 128 || BNB == 256)), "K-major B tiles");
+  static constexpr int BRB = BNB * 2;                     // BT: bytes per k-row of the B region
+  static constexpr int BCPR = BNB / 8;                    // BT: 16-byte chunks per k-row
+  static constexpr int BRPI = 1024 / BRB;                 // BT: k-rows filled by one wave-wide DMA load
+  // BT swizzle: logical chunk c of k-row r sits at c ^ bt_sw(r), so the 4
+  // k-rows x 2 chunks of one transposing read land in 8 distinct positions
+  static __device__ __forceinline__ int bt_sw(int r) { return ((r % 8) * 2) % BCPR; }
   // with RS every wavefront issues LA loads of A blocks and LB of B blocks
   static constexpr int LA = RS ? BM / RPI / NW : LOADS;
   static constexpr int LB = RS ? BNB / RPI / NW : 0;
@@ -171,14 +187,22 @@ struct Cfg {
 // Issue the loads of one K slice into an LDS stage.  Load i of a wavefront
 // reads from a wave-uniform base (A, or the expert's gate / up / down
 // matrix) plus a per-lane 32-bit element offset; ko is the slice's K offset.
+// With K-major B (BT) the B loads read from bsel, the slice's first k-row of
+// the right matrix, plus their offset.
 template <class C>
 __device__ __forceinline__ void issue_slice(bf16_t* stage, const bf16_t* const* base, const uint32_t* off,
-                                            uint32_t ko, int wave) {
+                                            uint32_t ko, int wave, const bf16_t* bsel = nullptr) {
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + ko)),
-                                     (lds_ptr_t)(stage + C::block(wave, i) * 512), 16, 0, 0);
+  for (int i = 0; i < C::LOADS; ++i) {
+    const bool b_row = C::BT && C::block(wave, i) >= C::BM / C::RPI;
+    const bf16_t* src = b_row ? bsel + off[i] : base[i] + (off[i] + ko);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::block(wave, i) * 512), 16, 0, 0);
+  }
 }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
 // Consume one K slice.  Fragments are software-pipelined: the LDS read of the
 // next B fragment (and, at the last group of a k-step, of the next k-step's A
@@ -201,8 +225,24 @@ __device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_
   };
   auto b_frag = [&](int kk, int f) {
     const int h = f / C::TN, j = f % C::TN;
-    const int brow = h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
-    return *reinterpret_cast<const bf16x8*>(bbase + swz_off<C::RB>(brow, kk * 2 + lk));
+    if constexpr (C::BT) {
+      // two transposing reads give k = 8*(lane/32) + 0..3 and + 4..7 of
+      // n = lane%32 of the fragment's 32 columns
+      const int g = lane / 16, r = lane % 16;
+      const int n = wn * C::WTN + j * 32 + 16 * (g % 2) + 4 * (r % 4);
+      v4s part[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kr = kk * 16 + 8 * (g / 2) + 4 * q + r / 4;
+        const int byte = kr * C::BRB + (((n / 8) ^ C::bt_sw(kr)) * 16) + (n % 8) * 2;
+        part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(const_cast<char*>(bbase) + byte));
+      }
+      const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, both);
+    } else {
+      const int brow = h * (C::BNB / 2) + wn * C::WTN + j * 32 + lr;
+      return *reinterpret_cast<const bf16x8*>(bbase + swz_off<C::RB>(brow, kk * 2 + lk));
+    }
   };
   bf16x8 a_cur[C::TM], a_nxt[C::TM];
 #pragma unroll
@@ -238,7 +278,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const bf16_t* __restrict__ aux_in,
-    bf16_t* __restrict__ aux_out) {
+    bf16_t* __restrict__ aux_out, int32_t kb1) {
   // The K-slice ring.  With register staging the A rows of the two stages
   // come first and the B rows of the two stages follow.  (One LDS array only:
   // with several, the compiler tracks the LDS DMA per array and waits for it
@@ -285,14 +325,27 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
   // results are never stored.  All offsets fit 32 bits (checked on the host).
   const bf16_t* base[C::LOADS];
   uint32_t off[C::LOADS];
-  const bf16_t* Bexp0 = B0 + e * N * static_cast<int64_t>(K);
-  const bf16_t* Bexp1 = C::GATEUP ? B1 + e * N * static_cast<int64_t>(K) : Bexp0;
+  // K-major B (BT): the expert's matrix is [K1][N], or, with a split K, k < K1
+  // from B0 and k >= K1 from B1 (both [K1][N] per expert)
+  const int32_t K1 = kb1 > 0 ? kb1 : K;
+  const bf16_t* Bexp0 = B0 + e * N * static_cast<int64_t>(C::BT ? K1 : K);
+  const bf16_t* Bexp1 = C::GATEUP ? B1 + e * N * static_cast<int64_t>(K)
+                                  : (C::BT && B1 ? B1 + e * N * static_cast<int64_t>(K1) : Bexp0);
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int blk = C::block(wave, i);                     // 8-row block (wave-uniform)
     const int rr = blk * C::RPI + lane / C::CPR;
     const int c = (lane % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
-    if (blk * C::RPI < C::BM) {
+    if (C::BT && blk * C::RPI >= C::BM) {
+      // k-row kr of the B region, logical chunk cb; columns past N read a
+      // valid chunk instead (never stored)
+      const int kr = (blk - C::BM / C::RPI) * C::BRPI + lane / C::BCPR;
+      const int cb = (lane % C::BCPR) ^ C::bt_sw(kr);
+      int n = n0 + cb * 8;
+      n = n <= N - 8 ? n : N - 8;
+      base[i] = Bexp0;
+      off[i] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(N) + static_cast<uint32_t>(n);
+    } else if (blk * C::RPI < C::BM) {
       int32_t row = row0 + rr;
       row = row < row_end ? row : row_end - 1;
       base[i] = A;
@@ -318,7 +371,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
         for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
 
   auto issue_group = [&](int slice) {
-    issue_slice<C>(ring + (slice % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(slice * C::BK), wave);
+    const int ko = slice * C::BK;
+    const bf16_t* bsel = nullptr;
+    if constexpr (C::BT)
+      bsel = ko < K1 ? Bexp0 + static_cast<int64_t>(ko) * N : Bexp1 + static_cast<int64_t>(ko - K1) * N;
+    issue_slice<C>(ring + (slice % C::STAGES) * C::SLICE, base, off, static_cast<uint32_t>(ko), wave, bsel);
   };
 
   // K loop over an LDS ring of STAGES slices: wait for slice kt (the loads of
@@ -731,13 +788,13 @@ inline int device_cus() {
 template <class C>
 void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
                 const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream,
-                const void* aux_in = nullptr, void* aux_out = nullptr) {
+                const void* aux_in = nullptr, void* aux_out = nullptr, int32_t kb1 = 0) {
   const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
   // the persistent form has the plain store epilogue only
-  if (C::EPI == kEpiStore && persistent) {
+  if (C::EPI == kEpiStore && !C::BT && persistent) {
     const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
     const int64_t g = upper < slots ? upper : slots;
-    if constexpr (C::EPI == kEpiStore)
+    if constexpr (C::EPI == kEpiStore && !C::BT)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                          static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
@@ -745,7 +802,7 @@ void launch_one(bool persistent, const void* a, const void* b0, const void* b1, 
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(upper)),
                        dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn,
-                       static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out));
+                       static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1);
   }
 }
 

@@ -12,16 +12,16 @@
 // Launch sequence (no host synchronisation):
 //   1. tile tables: the M-tiles of the GEMM tiling, and 64-row K-tiles with
 //      each expert's run of them (the padded K layout of step 6).
-//   2. weight transposes into the workspace: W_d^T [E, d_ff, d] and
-//      [W_g; W_u]^T [E, d, 2 d_ff], so that both data-gradient products keep
-//      K contiguous in both operands (experts without rows are skipped).
-//   3. dH = dZ (W_d^T)^T: GEMM with K = d, N = d_ff, bf16 out.
-//   4. the gate/up GEMM recomputed from X with the SwiGLU backward epilogue:
+//   2. dH = dZ W_d: GEMM with K = d, N = d_ff, bf16 out.  W_d [d, d_ff] is
+//      K-major here, so its tiles are read with the transposing LDS read (no
+//      transposed copy of the weights).
+//   3. the gate/up GEMM recomputed from X with the SwiGLU backward epilogue:
 //      dGU = [dG | dU] [rows, 2 d_ff] and H [rows, d_ff], bf16.
-//   5. dX = dGU ([W_g; W_u]^T)^T: GEMM with K = 2 d_ff, N = d.
-//   6. segment-padded transposes of dZ, H, dGU and X to [C, Kp]: expert e's
+//   4. dX = dGU [W_g; W_u]: GEMM with K = 2 d_ff, N = d; K-major B, k < d_ff
+//      from W_g and the rest from W_u.
+//   5. segment-padded transposes of dZ, H, dGU and X to [C, Kp]: expert e's
 //      rows become columns starting at 64 * (its first K-tile), zero padded.
-//   7. weight gradients (fp32): dW_d[e] = dZ_e^T H_e and
+//   6. weight gradients (fp32): dW_d[e] = dZ_e^T H_e and
 //      [dW_g; dW_u][e] = dGU_e^T X_e, with K = the expert's padded rows.
 #include "gemm_core.h"
 
@@ -60,19 +60,6 @@ __device__ __forceinline__ void transpose_tile(const bf16_t* __restrict__ src, i
   }
 }
 
-// dst[e][c][col_off + r] = src[e][r][c] for src [E, R, C]; dst rows have
-// dst_ld elements and an expert's block is C * dst_ld.  Grid (C/64, R/64, E).
-__global__ __launch_bounds__(kTpThreads) void transpose_weights_kernel(const bf16_t* __restrict__ src, int32_t R,
-                                                                       int32_t Cc, bf16_t* __restrict__ dst,
-                                                                       int32_t dst_ld, int32_t col_off,
-                                                                       const int32_t* __restrict__ seg_count) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[kTp * kTpPitch];
-  const int64_t e = blockIdx.z;
-  if (seg_count[e] <= 0) return;                   // an expert without rows needs no transposed weights
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTp, r0 = static_cast<int64_t>(blockIdx.y) * kTp;
-  transpose_tile(src + (e * R + r0) * Cc + c0, Cc, kTp, dst + (e * Cc + c0) * dst_ld + col_off + r0, dst_ld, tile);
-}
-
 // Segment-padded transpose of row-major src [rows, C]: K-tile t (64 rows of
 // one expert, zero past the segment end) becomes columns [64 t, 64 t + 64) of
 // dst [C, Kp].  Grid (max K-tiles, C/64); tiles past the table leave.
@@ -108,7 +95,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(
   const int per_e = n_mt * n_nt;
   const int e = static_cast<int>(logical) / per_e;
   const int rem = static_cast<int>(logical) - e * per_e;
-  const int nt = rem / n_mt, mt = rem - nt * n_mt;         // M-tiles of one N-tile are adjacent
+  const int mt = rem / n_nt, nt = rem - mt * n_nt;         // N-tiles of one M-tile are adjacent
   const int m0 = mt * C::BM, n0 = nt * C::BN_OUT;
   const int KT = exp_ntile[e];
   const uint32_t kbase = static_cast<uint32_t>(exp_first[e]) * C::BK;
@@ -185,19 +172,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(
   }
 }
 
-// Backward tile configurations: the forward's tilings for the two data
-// gradients (step 3 with bf16 out, step 5 with the caller's dtype) and the
-// gate/up tiling with the SwiGLU backward epilogue (step 4, never persistent).
+// Backward tile configurations, with the forward's M tilings: K-major-B tiles
+// for the two data gradients (step 2 with bf16 out, step 4 with the caller's
+// dtype; DMA ring, one tile per workgroup) and the gate/up tiling with the
+// SwiGLU backward epilogue (step 3, never persistent).
+template <bool F>
+using CfgLgBT = Cfg<256, 128, 4, 2, 3, false, F, false, 64, 1, 4, 8, false, kEpiStore, true>;
+template <bool F>
+using CfgMdBT = Cfg<128, 256, 2, 4, 3, false, F, false, 64, 1, 2, 8, false, kEpiStore, true>;
+template <bool F>
+using CfgSmBT = Cfg<32, 256, 1, 4, 4, false, F, false, 64, 1, 1, 4, false, kEpiStore, true>;
 using CfgLgGB = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiSwigluBwd>;
 using CfgMdGB = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8, false, kEpiSwigluBwd>;
 using CfgSmGB = Cfg<32, 256, 1, 4, 4, true, false, false, 64, 1, 1, 4, false, kEpiSwigluBwd>;
-static_assert(CfgLgGB::BM == CfgLgGU::BM && CfgMdGB::BM == CfgMdGU::BM && CfgSmGB::BM == CfgSmGU::BM,
+static_assert(CfgLgGB::BM == CfgLgGU::BM && CfgMdGB::BM == CfgMdGU::BM && CfgSmGB::BM == CfgSmGU::BM &&
+                  CfgLgBT<true>::BM == CfgLgGU::BM && CfgMdBT<true>::BM == CfgMdGU::BM &&
+                  CfgSmBT<true>::BM == CfgSmGU::BM,
               "one M tiling per kind");
 // weight gradients: 128 x 256 fp32 tiles, 8 wavefronts, 3-slice ring
 using CfgWg = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 1, 8>;
 
 struct BwdLayout {
-  size_t tiles, ntiles, ktiles, nktiles, efirst, entile, wdT, wguT, dH, dGU, H, dZT, HT, GUT, XT, total;
+  size_t tiles, ntiles, ktiles, nktiles, efirst, entile, dH, dGU, H, dZT, HT, GUT, XT, total;
   int32_t max_tiles, max_ktiles, bm;
   int64_t Kp;
 };
@@ -222,8 +218,6 @@ inline BwdLayout bwd_layout(int64_t rows, int32_t E, int32_t d, int32_t d_ff) {
   w.nktiles = take(4);
   w.efirst = take(e * 4);
   w.entile = take(e * 4);
-  w.wdT = take(e * F * D * 2);
-  w.wguT = take(e * D * 2 * F * 2);
   w.dH = take(r * F * 2);
   w.dGU = take(r * 2 * F * 2);
   w.H = take(r * F * 2);
@@ -237,21 +231,25 @@ inline BwdLayout bwd_layout(int64_t rows, int32_t E, int32_t d, int32_t d_ff) {
 
 template <class GB, class DB, class DF>
 int launch_bwd_gemms(const void* x, const void* dz, int32_t d, int32_t d_ff, const void* wg, const void* wu,
-                     const void* wdT, const void* wguT, void* dH, void* dGU, void* H, void* dx, int32_t dx_dtype,
+                     const void* wd, void* dH, void* dGU, void* H, void* dx, int32_t dx_dtype,
                      const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, hipStream_t stream) {
   const int nt_f = (d_ff + DB::BN_OUT - 1) / DB::BN_OUT;
   const int nt_g = (d_ff + GB::BN_OUT - 1) / GB::BN_OUT;
   const int nt_d = (d + DF::BN_OUT - 1) / DF::BN_OUT;
   const int nmax = nt_f > nt_g ? (nt_f > nt_d ? nt_f : nt_d) : (nt_g > nt_d ? nt_g : nt_d);
   MOE_CHECK(static_cast<int64_t>(max_tiles) * nmax <= INT32_MAX, MOE_EUNSUPPORTED);
-  launch_one<DB>(false, dz, wdT, nullptr, dH, d, d_ff, tiles, n_tiles, max_tiles, nt_f, stream);
+  // dH = dZ W_d: W_d[e] is [d (K)][d_ff (N)]
+  launch_one<DB>(false, dz, wd, nullptr, dH, d, d_ff, tiles, n_tiles, max_tiles, nt_f, stream);
   MOE_LAUNCH_CHECK();
   launch_one<GB>(false, x, wg, wu, dGU, d, d_ff, tiles, n_tiles, max_tiles, nt_g, stream, dH, H);
   MOE_LAUNCH_CHECK();
+  // dX = [dG | dU] [W_g; W_u]: W_g[e], W_u[e] are [d_ff (K)][d (N)], split at K = d_ff
   if (dx_dtype == MOE_F32)
-    launch_one<DF>(false, dGU, wguT, nullptr, dx, 2 * d_ff, d, tiles, n_tiles, max_tiles, nt_d, stream);
+    launch_one<DF>(false, dGU, wg, wu, dx, 2 * d_ff, d, tiles, n_tiles, max_tiles, nt_d, stream, nullptr, nullptr,
+                   d_ff);
   else
-    launch_one<DB>(false, dGU, wguT, nullptr, dx, 2 * d_ff, d, tiles, n_tiles, max_tiles, nt_d, stream);
+    launch_one<DB>(false, dGU, wg, wu, dx, 2 * d_ff, d, tiles, n_tiles, max_tiles, nt_d, stream, nullptr, nullptr,
+                   d_ff);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -295,8 +293,6 @@ MOE_API int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, 
   int32_t* n_ktiles = reinterpret_cast<int32_t*>(w + L.nktiles);
   int32_t* efirst = reinterpret_cast<int32_t*>(w + L.efirst);
   int32_t* entile = reinterpret_cast<int32_t*>(w + L.entile);
-  bf16_t* wdT = reinterpret_cast<bf16_t*>(w + L.wdT);
-  bf16_t* wguT = reinterpret_cast<bf16_t*>(w + L.wguT);
   bf16_t* dH = reinterpret_cast<bf16_t*>(w + L.dH);
   bf16_t* dGU = reinterpret_cast<bf16_t*>(w + L.dGU);
   bf16_t* H = reinterpret_cast<bf16_t*>(w + L.H);
@@ -313,36 +309,26 @@ MOE_API int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, 
                      L.max_ktiles, ktiles, n_ktiles, nullptr, efirst, entile);
   MOE_LAUNCH_CHECK();
   if (rows > 0) {
-    // 2. weight transposes (experts with rows)
-    const bf16_t* wgp = static_cast<const bf16_t*>(w_gate);
-    const bf16_t* wup = static_cast<const bf16_t*>(w_up);
-    const bf16_t* wdp = static_cast<const bf16_t*>(w_down);
-    hipLaunchKernelGGL(transpose_weights_kernel, dim3(d_ff / kTp, d / kTp, E), dim3(kTpThreads), 0, stream, wdp, d,
-                       d_ff, wdT, d, 0, seg_count);
-    MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(transpose_weights_kernel, dim3(d / kTp, d_ff / kTp, E), dim3(kTpThreads), 0, stream, wgp,
-                       d_ff, d, wguT, 2 * d_ff, 0, seg_count);
-    MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(transpose_weights_kernel, dim3(d / kTp, d_ff / kTp, E), dim3(kTpThreads), 0, stream, wup,
-                       d_ff, d, wguT, 2 * d_ff, d_ff, seg_count);
-    MOE_LAUNCH_CHECK();
-    // 3.-5. data gradients
+    // 2.-4. data gradients
     int st;
     switch (pick_tiles(rows, E)) {
       case kLarge:
-        st = launch_bwd_gemms<CfgLgGB, CfgLgDB, CfgLgDF>(x, dz, d, d_ff, w_gate, w_up, wdT, wguT, dH, dGU, H, dx,
-                                                         dx_dtype, tiles, n_tiles, L.max_tiles, stream);
+        st = launch_bwd_gemms<CfgLgGB, CfgLgBT<false>, CfgLgBT<true>>(x, dz, d, d_ff, w_gate, w_up, w_down, dH,
+                                                                      dGU, H, dx, dx_dtype, tiles, n_tiles,
+                                                                      L.max_tiles, stream);
         break;
       case kMedium:
-        st = launch_bwd_gemms<CfgMdGB, CfgMdDB, CfgMdDF>(x, dz, d, d_ff, w_gate, w_up, wdT, wguT, dH, dGU, H, dx,
-                                                         dx_dtype, tiles, n_tiles, L.max_tiles, stream);
+        st = launch_bwd_gemms<CfgMdGB, CfgMdBT<false>, CfgMdBT<true>>(x, dz, d, d_ff, w_gate, w_up, w_down, dH,
+                                                                      dGU, H, dx, dx_dtype, tiles, n_tiles,
+                                                                      L.max_tiles, stream);
         break;
       default:
-        st = launch_bwd_gemms<CfgSmGB, CfgSmDB, CfgSmDF>(x, dz, d, d_ff, w_gate, w_up, wdT, wguT, dH, dGU, H, dx,
-                                                         dx_dtype, tiles, n_tiles, L.max_tiles, stream);
+        st = launch_bwd_gemms<CfgSmGB, CfgSmBT<false>, CfgSmBT<true>>(x, dz, d, d_ff, w_gate, w_up, w_down, dH,
+                                                                      dGU, H, dx, dx_dtype, tiles, n_tiles,
+                                                                      L.max_tiles, stream);
     }
     if (st != MOE_OK) return st;
-    // 6. segment-padded transposes
+    // 5. segment-padded transposes
     const bf16_t* zsrc = static_cast<const bf16_t*>(dz);
     const bf16_t* xsrc = static_cast<const bf16_t*>(x);
     const unsigned kt = static_cast<unsigned>(L.max_ktiles);
@@ -359,7 +345,7 @@ MOE_API int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, 
                        n_ktiles, XT, L.Kp);
     MOE_LAUNCH_CHECK();
   }
-  // 7. weight gradients (every expert: zero where it has no rows)
+  // 6. weight gradients (every expert: zero where it has no rows)
   using C = CfgWg;
   {
     const int n_mt = (d + C::BM - 1) / C::BM, n_nt = (d_ff + C::BN_OUT - 1) / C::BN_OUT;
