@@ -444,10 +444,8 @@ def pack_setup(torch, w, banks):
 
 def pack_step(ge, timer, w, bank, flags, bufs):
     ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, flags=flags)
-    rows = bank["x"]
-    if w.payload is not None:
-        rows = timer.run("quantize", ge.quantize_fp8, rows, w.payload, rec=bufs["rec"], flags=flags)
-    out = timer.run("pool_pack", ge.pool_pack, rows, ids, w.E, w.experts_per_dest, w.n_dest, w.n_waves,
+    # with an fp8 payload the pack quantizes each bf16 token row itself
+    out = timer.run("pool_pack", ge.pool_pack, bank["x"], ids, w.E, w.experts_per_dest, w.n_dest, w.n_waves,
                     w.pool_rows, pools=bufs["pools"], flags=flags, payload=w.payload, d=w.d)
     return dict(ids=ids, gates=gates, pack=out)
 
@@ -457,11 +455,9 @@ def pack_ledger(w):
     T, k, d, E = w.T, w.k, w.d, w.E
     rb = ge.row_bytes(d, w.payload)
     P1 = ge.pool_height(w.pool_rows, d, w.payload)
-    led = {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
-           "pool_pack": dict(bytes=8 * T * k + T * rb + w.n_waves * w.n_dest * P1 * rb, flops=0)}
-    if w.payload is not None:
-        led["quantize"] = dict(bytes=T * d * 2 + T * rb, flops=0)
-    return led
+    # token rows are read once as bf16 (quantized inside the pack for an fp8 payload)
+    return {"route": dict(bytes=4 * T * E + 8 * T * k, flops=0),
+            "pool_pack": dict(bytes=8 * T * k + T * d * 2 + w.n_waves * w.n_dest * P1 * rb, flops=0)}
 
 
 def pack_cpu_baseline(w, host, sample):
@@ -565,8 +561,7 @@ def main():
         else:
             rb = ge.row_bytes(w.d, w.payload)
             bufs = dict(pools=torch.empty((w.n_waves, w.n_dest, ge.pool_height(w.pool_rows, w.d, w.payload), rb),
-                                          dtype=torch.uint8, device="cuda"),
-                        rec=torch.empty((w.T, rb), dtype=torch.uint8, device="cuda"))
+                                          dtype=torch.uint8, device="cuda"))
         step = lambda tm, b: pack_step(ge, tm, w, b, flags, bufs)
     # one plain device copy of known size (untimed): under rocprofv3 --pmc its
     # FETCH_SIZE / WRITE_SIZE readings calibrate the counters to bytes

@@ -55,8 +55,8 @@ _SIGS = {
     "moe_grouped_swiglu_backward": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _i32,
                                                    _p, _p, _p, _p, _sz, _p, _p]),
     "moe_pool_pack_workspace": (_sz, [_i64, _i32, _i32]),
-    "moe_pool_pack": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
-                                     _p, _p, _p, _sz, _p, _p]),
+    "moe_pool_pack": (ctypes.c_int, [_p, _i32, _i32, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p,
+                                     _p, _p, _p, _p, _sz, _p, _p]),
     "moe_row_bytes": (_sz, [_i32, _i32]),
     "moe_quantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _i32, _p, _p, _p]),
     "moe_dequantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p]),
@@ -338,9 +338,10 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
               flags: Optional[torch.Tensor] = None, payload: Optional[str] = None, d: Optional[int] = None):
     """Returns a dict with pools, route_loc, dest_counts, sender_dropped.
 
-    ``x`` is bf16 ``[T, d]`` (pools bf16 ``[..., PH, d]``) or, with
-    ``payload`` "row" / "b128", fp8 records ``uint8 [T, row_bytes]`` of rows
-    ``d`` wide (pools uint8 ``[..., PH, row_bytes]``)."""
+    ``x`` is bf16 ``[T, d]`` (pools bf16 ``[..., PH, d]``).  With ``payload``
+    "row" / "b128" the pools hold fp8 records (uint8 ``[..., PH, row_bytes]``)
+    and ``x`` is either those records (``uint8 [T, row_bytes]`` of rows ``d``
+    wide) or bf16 rows that the pack quantizes on the way."""
     _need_gpu(x, topk_ids, pools, flags)
     T = x.shape[0]
     if payload is None:
@@ -348,7 +349,12 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
         code, last, pdt = MOE_BF16, d, torch.bfloat16
     else:
         code, last, pdt = FP8_CODES[payload], row_bytes(d, payload), torch.uint8
-        assert x.dtype == torch.uint8 and x.shape[1] == last, "fp8 payload: x holds records"
+        if x.dtype == torch.bfloat16:
+            d = x.shape[1] if d is None else d
+            assert x.shape[1] == d
+        else:
+            assert x.dtype == torch.uint8 and x.shape[1] == last, "fp8 payload: x holds records or bf16 rows"
+    xcode = MOE_BF16 if x.dtype == torch.bfloat16 else code
     k = topk_ids.shape[-1]
     dev = x.device
     PH = pool_height(pool_rows, d, payload)
@@ -360,7 +366,7 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
     ws = _ws(lib.moe_pool_pack_workspace(T, k, n_dest), dev)
     _check("moe_pool_pack", lib.moe_pool_pack(
-        _ptr(x), code, T, d, _ptr(topk_ids), k, E, experts_per_dest, n_dest, n_waves, pool_rows, wave, _ptr(pools),
+        _ptr(x), xcode, code, T, d, _ptr(topk_ids), k, E, experts_per_dest, n_dest, n_waves, pool_rows, wave, _ptr(pools),
         _ptr(route_loc), _ptr(dest_counts), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
     return dict(pools=pools, route_loc=route_loc, dest_counts=dest_counts, sender_dropped=dropped)
 

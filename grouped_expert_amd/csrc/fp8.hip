@@ -17,51 +17,6 @@ namespace {
 
 constexpr int kQRows = 4;              // rows (wavefronts) per workgroup
 
-template <typename XT>
-__device__ __forceinline__ void load_row8(const XT* p, float (&v)[8]);
-
-template <>
-__device__ __forceinline__ void load_row8<bf16_t>(const bf16_t* p, float (&v)[8]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load_row8<float>(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// Largest magnitude of 8 values; *bad set when one is NaN or infinite.
-__device__ __forceinline__ float amax8(const float (&v)[8], bool* bad) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = fabsf(v[i]);
-    if (!(a <= 3.402823466e38f)) *bad = true;
-    m = fmaxf(m, a);
-  }
-  return m;
-}
-
-// The 8 codes of one piece, as two words.  With amax = 0 or a bad group every
-// code is 0.  x * inv is one fp32 product.
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], float inv, bool zero) {
-  uint2 q = {0u, 0u};
-  if (zero) return q;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q.x |= e4m3_encode(v[i] * inv) << (8 * i);
-    q.y |= e4m3_encode(v[4 + i] * inv) << (8 * i);
-  }
-  return q;
-}
-
 template <typename XT, bool ROW>
 __global__ __launch_bounds__(kQRows * kWave) void quantize_kernel(const XT* __restrict__ x, int64_t n, int32_t d,
                                                                   uint8_t* __restrict__ rec, int64_t W,

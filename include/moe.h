@@ -372,8 +372,12 @@ int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* ro
 /* ---------------------------------------------------------------------------
  * moe_pool_pack -- pooled-wave sender pack into fixed destination pools.
  *
- * Rows are RB = moe_row_bytes(x_dtype, d) bytes: bf16 rows, or fp8 records
- * (M6.2 0x0AB-0x0AC: the scales travel inside the row).  A pool has
+ * Pool rows are RB = moe_row_bytes(pool_dtype, d) bytes: bf16 rows, or fp8
+ * records (M6.2 0x0AB-0x0AC: the scales travel inside the row).  Rows are
+ * moved as they are (pool_dtype == x_dtype) or bf16 rows are quantized into
+ * records on the way (x_dtype bf16, pool_dtype fp8: every token row is
+ * quantized once, exactly as moe_quantize_fp8 does, and its record written to
+ * each placed slot).  A pool has
  * H = max(1, ceil(2 * pool_rows / RB)) full-width header rows (one for bf16
  * rows at the pages' sizes) followed by pool_rows data rows;
  * PH = pool_rows + H.  The header rows hold little-endian uint16 ids: id i
@@ -392,6 +396,7 @@ int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* ro
  * is -1 or invalid; invalid ids set MOE_FLAG_BAD_EXPERT).
  *
  *   x          device [T] rows of x_dtype (MOE_BF16, MOE_FP8_ROW, MOE_FP8_B128), d % 8 == 0
+ *   pool_dtype x_dtype, or an fp8 record dtype when x_dtype is MOE_BF16
  *   E <= n_dest * experts_per_dest, n_dest <= MOE_MAX_EXPERTS, 1 <= n_waves
  *   wave       -1: pools is [n_waves][n_dest][PH] rows of RB bytes (all waves);
  *              w >= 0: pools is [n_dest][PH] rows, only wave w's rows and
@@ -400,7 +405,8 @@ int moe_expand_rows(const void* z, int32_t z_dtype, int32_t d, const int32_t* ro
  *   ws         device workspace of moe_pool_pack_workspace(T, k, n_dest)
  * ------------------------------------------------------------------------- */
 size_t moe_pool_pack_workspace(int64_t T, int32_t k, int32_t n_dest);
-int moe_pool_pack(const void* x, int32_t x_dtype, int64_t T, int32_t d, const int32_t* topk_ids, int32_t k,
+int moe_pool_pack(const void* x, int32_t x_dtype, int32_t pool_dtype, int64_t T, int32_t d,
+                  const int32_t* topk_ids, int32_t k,
                   int32_t E, int32_t experts_per_dest, int32_t n_dest, int32_t n_waves,
                   int32_t pool_rows, int32_t wave, void* pools, int32_t* route_loc,
                   int32_t* dest_counts, int32_t* sender_dropped, void* ws, size_t ws_bytes,

@@ -122,21 +122,26 @@ def test_combine_validation():
 def test_pool_pack_validation():
     p, _keep = _fake()
     ws = lib.moe_pool_pack_workspace(100, 8, 64)
-    args = [p, 1, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
-    bad = list(args); bad[6] = 385                                  # E > n_dest * epd
+    args = [p, 1, 1, 100, 3072, p, 8, 384, 6, 64, 3, 3004, -1, p, p, p, p, p, ws, NULL, NULL]
+    bad = list(args); bad[7] = 385                                  # E > n_dest * epd
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[10] = 1 << 30                             # pool rows past the int32 route locations
+    bad = list(args); bad[11] = 1 << 30                             # pool rows past the int32 route locations
     assert lib.moe_pool_pack(*bad) == EUNSUP
-    bad = list(args); bad[10] = -1                                  # negative pool rows
+    bad = list(args); bad[11] = -1                                  # negative pool rows
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[11] = 3                                   # wave out of range
+    bad = list(args); bad[12] = 3                                   # wave out of range
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[17] = 8                                   # workspace too small
+    bad = list(args); bad[18] = 8                                   # workspace too small
     assert lib.moe_pool_pack(*bad) == EWS
-    bad = list(args); bad[1] = 0                                    # fp32 rows are not a dispatch payload
+    bad = list(args); bad[1] = 0; bad[2] = 0                        # fp32 rows are not a dispatch payload
     assert lib.moe_pool_pack(*bad) == EINVAL
-    bad = list(args); bad[1] = 3; bad[10] = 1 << 30                 # fp8 records are accepted (then: too many rows)
-    assert lib.moe_pool_pack(*bad) == EUNSUP
+    bad = list(args); bad[1] = 3; bad[2] = 1                        # records cannot be widened back to bf16
+    assert lib.moe_pool_pack(*bad) == EINVAL
+    bad = list(args); bad[1] = 3; bad[2] = 2                        # nor turned into the other record kind
+    assert lib.moe_pool_pack(*bad) == EINVAL
+    for xd, pd in ((3, 3), (1, 2), (1, 3)):                         # accepted pairs (then: too many rows)
+        bad = list(args); bad[1] = xd; bad[2] = pd; bad[11] = 1 << 30
+        assert lib.moe_pool_pack(*bad) == EUNSUP
 
 
 def test_recv_compact_validation():

@@ -102,18 +102,26 @@ def test_permute_moves_whole_records(ge, mode):
     assert np.array_equal(to_np(plan["x_perm"])[:A], rec[want.src[:A] // k])
 
 
-@pytest.mark.parametrize("T,k,epd,D,Wv,P,d,mode", [(400, 4, 3, 8, 2, 30, 128, "row"),
-                                                   (3000, 8, 6, 64, 3, 30, 256, "b128"),
-                                                   (900, 8, 2, 8, 2, 200, 64, "b128")])   # several header rows
-def test_pool_pack_and_compact_fp8(ge, T, k, epd, D, Wv, P, d, mode):
+@pytest.mark.parametrize("T,k,epd,D,Wv,P,d,mode,fused", [(400, 4, 3, 8, 2, 30, 128, "row", False),
+                                                         (400, 4, 3, 8, 2, 30, 128, "row", True),
+                                                         (3000, 8, 6, 64, 3, 30, 256, "b128", False),
+                                                         (3000, 8, 6, 64, 3, 30, 256, "b128", True),
+                                                         (900, 8, 2, 8, 2, 200, 200, "b128", True),
+                                                         (900, 8, 2, 8, 2, 200, 64, "b128", False)])
+def test_pool_pack_and_compact_fp8(ge, T, k, epd, D, Wv, P, d, mode, fused):
+    """Records packed as they are, or bf16 rows quantized by the pack itself
+    (fused): the same pools either way.  d = 200 has a short last group and
+    d = 64 needs several header rows."""
     rng = np.random.default_rng(T + P)
     E = D * epd
     z = rng.standard_normal((T, E)).astype(np.float32)
     z[:, :epd] += 1.5
     ids, _, _ = O.route_topk(z, k)
-    rec = O.quantize_fp8_rows(_rows(rng, T, d), mode)
+    x16 = W.f32_to_bf16_bits(_rows(rng, T, d))
+    rec = O.quantize_fp8_rows(O.to_f64(x16).astype(np.float32), mode)
     flags = ge.new_flags("cuda")
-    out = ge.pool_pack(to_gpu(rec), to_gpu(ids), E, epd, D, Wv, P, flags=flags, payload=mode, d=d)
+    out = ge.pool_pack(to_gpu(x16 if fused else rec), to_gpu(ids), E, epd, D, Wv, P, flags=flags, payload=mode,
+                       d=d)
     pk = O.pool_pack(rec, ids, epd, D, Wv, P)
     assert np.array_equal(to_np(out["pools"]), pk["pools"])
     assert np.array_equal(to_np(out["route_loc"]), pk["route_loc"])
