@@ -94,7 +94,8 @@ def _call_of(kernel):
     """The library call a dispatched kernel belongs to (None: not ours).
     Bucket-rank kernels are shared by three calls and are given to the call
     of the next dispatch, by the caller of this function."""
-    table = (("route_topk_kernel", "route"), ("build_tiles_kernel", "swiglu"), ("grouped_gemm_", "swiglu"),
+    table = (("route_topk_kernel", "route"), ("route_grouped_kernel", "route"), ("build_tiles_kernel", "swiglu"),
+             ("grouped_gemm_", "swiglu"),
              ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
              ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
              ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),
@@ -106,7 +107,7 @@ def _call_of(kernel):
 
 
 # one dispatch per call instance: counts the launches of each call
-_ANCHORS = {"route": "route_topk_kernel", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
+_ANCHORS = {"route": "route_", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
             "combine": "combine_kernel", "expand": "expand_rows_kernel", "pool_pack": "pack_kernel",
             "recv_compact": "compact_", "quantize": "quantize_kernel"}
 
@@ -120,7 +121,9 @@ def record_traffic(args):
                 if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         names = [r["Kernel_Name"] for r in rows]
-        first_ours = next(i for i, n in enumerate(names) if _call_of(n))
+        # the step's first call (library kernels of the untimed set-up come earlier)
+        lead = "recv_compact" if workload_kind(w) == "recv" else "route"
+        first_ours = next(i for i, n in enumerate(names) if _call_of(n) == lead)
         # the calibration copy is the last plain device copy before the first library kernel
         calib = max(i for i in range(first_ours) if "copyBuffer" in names[i])
         factor = COPY_CALIB_BYTES / (float(rows[calib]["Counter_Value"]) * 1024.0)
