@@ -48,8 +48,8 @@ CSRC_DIR = os.path.join(ROOT, "grouped_expert_amd", "csrc")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mid_bf16", choices=sorted(W.WORKLOADS))
     ap.add_argument("--banks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,13 +189,19 @@ def workload_kind(w):
 # ---------------------------------------------------------------------------
 
 class OpTimer:
-    """Per-call HIP event pairs recorded on the current stream."""
+    """Per-call HIP event pairs recorded on the current stream, around every
+    call or only around the calls named in ``only``.  Each timing event costs
+    the stream a few microseconds, so the timed steps bracket only the call
+    whose launch duration the roofline needs."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, only=None):
         self.torch = torch
+        self.only = only
         self.marks = []          # (name, start_event, end_event)
 
     def run(self, name, fn, *a, **kw):
+        if self.only is not None and name not in self.only:
+            return fn(*a, **kw)
         t = self.torch
         s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         s.record()
@@ -579,7 +585,21 @@ def main():
         last = step(OpTimer(torch), bank_list[i % banks])
     torch.cuda.synchronize()
 
-    timer = OpTimer(torch)
+    # per-call durations from an untimed pass with events around every call;
+    # it also names the dominant call (the largest time per step)
+    n_probe = max(2, min(args.steps, 5))
+    print(f"[bench] per-call pass {n_probe} steps", file=sys.stderr, flush=True)
+    probe = OpTimer(torch)
+    for i in range(n_probe):
+        last = step(probe, bank_list[i % banks])
+    torch.cuda.synchronize()
+    per_op = {k: float(np.mean(v)) for k, v in probe.totals_ms().items()}
+    n_calls = {k: len(v) // n_probe for k, v in probe.totals_ms().items()}
+    dom = max(per_op, key=lambda k: per_op[k] * n_calls[k])
+
+    # timed steps: events around the dominant call only (its launch duration,
+    # live over the timed region, on the stream it runs on)
+    timer = OpTimer(torch, only={dom})
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -592,8 +612,7 @@ def main():
     wall_s = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / max(1, args.steps)
-    per_op = {k: float(np.mean(v)) for k, v in timer.totals_ms().items()}
-    n_calls = {k: len(v) for k, v in timer.totals_ms().items()}
+    dom_launches = timer.totals_ms()[dom]
     if int(flags.item()) != 0:
         print(f"[bench] warning: dev_flags = {int(flags.item())}", file=sys.stderr)
 
@@ -617,9 +636,7 @@ def main():
         units, unit = w.T, "tokens/s"
         per_step_calls = 1
     value = units / (ms_per_step / 1e3)
-    # dominant = the call with the largest time per step
-    dom = max(per_op, key=lambda k: per_op[k] * n_calls[k])
-    dom_ms = per_op[dom]                                  # average duration of one launch of that call
+    dom_ms = float(np.mean(dom_launches))                 # average duration of one launch, timed region
     per_launch_bytes = led[dom]["bytes"] / per_step_calls if dom in ("recv_compact", "swiglu", "expand") and \
         kind == "recv" else led[dom]["bytes"]
     per_launch_flops = led[dom]["flops"] / per_step_calls if kind == "recv" else led[dom]["flops"]
@@ -640,6 +657,7 @@ def main():
         roof["traffic_over_alg"] = round(traffic / max(1, per_launch_bytes), 3)
     roof["kernel"] = dom
     roof["launch_ms"] = round(dom_ms, 4)
+    roof["launches_timed"] = len(dom_launches)
     roof["alg_bytes_per_launch"] = int(per_launch_bytes)
     roof["alg_flops_per_launch"] = int(per_launch_flops)
 
@@ -664,7 +682,7 @@ def main():
         if v:
             cfg[key] = v
     cfg["banks"] = banks
-    ops = {k: dict(ms=round(per_op[k], 4), calls_per_step=n_calls[k] // max(1, args.steps),
+    ops = {k: dict(ms=round(per_op[k], 4), calls_per_step=n_calls[k],
                    alg_GBps=round(led[k]["bytes"] / (per_step_calls if kind == "recv" else 1) / (per_op[k] / 1e3)
                                   / 1e9, 1) if k in led else None)
            for k in per_op}
@@ -673,6 +691,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu, "ops": ops,
+        "ops_note": f"per-call ms from {n_probe} untimed steps with events around every call",
         "wall_s": round(wall_s, 3),
     }
     print(json.dumps(line), flush=True)
