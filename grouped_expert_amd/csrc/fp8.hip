@@ -77,8 +77,10 @@ __global__ __launch_bounds__(kQRows * kWave) void quantize_kernel(const XT* __re
       }
     }
   }
-  const int32_t tail = static_cast<int32_t>(W) - d - 4 * G;   // zero padding bytes
-  if (lane < tail) rr[d + 4 * G + lane] = 0;
+  // zero padding: fewer than 128 bytes from a 4-byte boundary (d % 8 == 0),
+  // one word per lane
+  const int32_t tail_words = (static_cast<int32_t>(W) - d - 4 * G) / 4;
+  if (lane < tail_words) reinterpret_cast<uint32_t*>(rr + d + 4 * G)[lane] = 0u;
 }
 
 template <typename OT, bool ROW>

@@ -197,11 +197,12 @@ __device__ __forceinline__ void pack_token_rows_fp8(const bf16_t* __restrict__ x
       }
     }
   }
-  const int32_t tail = static_cast<int32_t>(rb) - d - 4 * G;     // zero padding bytes
+  // zero padding: fewer than 128 bytes from a 4-byte boundary, one word per lane
+  const int32_t tail_words = (static_cast<int32_t>(rb) - d - 4 * G) / 4;
   for (int j = 0; j < live; ++j) {
     uint8_t* out = pools + static_cast<int64_t>(loc[j]) * rb;
     if (ROW && lane == 0) *reinterpret_cast<float*>(out + d) = row_scale;
-    if (lane < tail) out[d + 4 * G + lane] = 0;
+    if (lane < tail_words) reinterpret_cast<uint32_t*>(out + d + 4 * G)[lane] = 0u;
   }
   if (bad_any && lane == 0) flag_or(flags, MOE_FLAG_NONFINITE_INPUT);
 }

@@ -102,8 +102,9 @@ typedef enum {
 #define MOE_MAX_EXPERTS 1024   /* E, n_dest, n_local */
 #define MOE_MAX_TOPK    16
 
-/* Bytes of one row of d values stored as dtype (records padded to 16 bytes);
- * 0 for an unknown dtype or d < 1. */
+/* Bytes of one row of d values stored as dtype (fp8 records: d code bytes,
+ * the fp32 scales, zero bytes up to a multiple of 128, a whole number of
+ * cache lines); 0 for an unknown dtype or d < 1. */
 size_t moe_row_bytes(int32_t dtype, int32_t d);
 
 /* ---------------------------------------------------------------------------

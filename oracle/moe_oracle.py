@@ -670,11 +670,13 @@ FP8_MODES = ("row", "b128")
 def fp8_record_layout(d: int, mode: str) -> Tuple[int, int]:
     """``(G, W)``: scales per row (one, or one per 128 values, M6.2 §0x0AB)
     and the record width in bytes: ``d`` fp8 bytes, then ``G`` fp32 scales,
-    zero padding to a multiple of 16 bytes."""
+    zero padding to a multiple of 128 bytes (whole cache lines: the layout is
+    the library's choice, the pages fix only that scales travel with their
+    row)."""
     if mode not in FP8_MODES:
         raise ValueError(mode)
     G = 1 if mode == "row" else -(-int(d) // 128)
-    return G, -(-(int(d) + 4 * G) // 16) * 16
+    return G, -(-(int(d) + 4 * G) // 128) * 128
 
 
 def fp8_payload_bytes(R: int, d: int, mode: Optional[str]) -> int:

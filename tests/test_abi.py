@@ -166,9 +166,10 @@ def test_recv_compact_validation():
 
 def test_fp8_record_widths_and_validation():
     assert lib.moe_row_bytes(1, 3072) == 6144 and lib.moe_row_bytes(0, 3) == 12
-    assert lib.moe_row_bytes(2, 3072) == 3088            # 3072 codes + 4 + 12 padding
-    assert lib.moe_row_bytes(3, 3072) == 3168            # 3072 codes + 24 scales
-    assert lib.moe_row_bytes(3, 7168) == 7168 + 4 * 56
+    assert lib.moe_row_bytes(2, 3072) == 3200            # 3072 codes + 4 + 124 padding
+    assert lib.moe_row_bytes(3, 3072) == 3200            # 3072 codes + 24 scales + 104 padding
+    assert lib.moe_row_bytes(3, 7168) == 7424            # 7168 + 4 * 56 = 7392, to whole 128-byte lines
+    assert lib.moe_row_bytes(2, 124) == 128 and lib.moe_row_bytes(2, 125) == 256
     assert lib.moe_row_bytes(9, 64) == 0 and lib.moe_row_bytes(1, 0) == 0
     p, _keep = _fake()
     assert lib.moe_quantize_fp8(p, 1, 10, 64, 1, p, NULL, NULL) == EINVAL      # record dtype must be fp8
