@@ -22,6 +22,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import re
 import json
 import os
 import sys
@@ -90,26 +91,37 @@ def sources_digest(call):
     return h.hexdigest()
 
 
-def _call_of(kernel):
+def _call_of(kernel, train=False):
     """The library call a dispatched kernel belongs to (None: not ours).
-    Bucket-rank kernels are shared by three calls and are given to the call
-    of the next dispatch, by the caller of this function."""
-    table = (("route_topk_kernel", "route"), ("route_grouped_kernel", "route"), ("build_tiles_kernel", "swiglu"),
-             ("grouped_gemm_", "swiglu"),
+    Bucket-rank and tile-table kernels serve several calls and are given to
+    the call of the next dispatch, by the caller of this function ("rank").
+    The expert backward's GEMMs carry the SwiGLU-backward epilogue or K-major
+    B tiles (the last two tile parameters); in a training step the fp32
+    combine is the token-gradient pass."""
+    if "grouped_gemm_" in kernel:
+        m = re.search(r"Cfg<[^<>]*, (\d+), (true|false)>", kernel)
+        return "swiglu_bwd" if m and (m.group(1) != "0" or m.group(2) == "true") else "swiglu"
+    table = (("route_topk_kernel", "route"), ("route_grouped_kernel", "route"), ("build_tiles_kernel", "rank"),
+             ("transpose_rows_kernel", "swiglu_bwd"), ("grouped_wgrad_kernel", "swiglu_bwd"),
              ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
              ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
              ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),
-             ("combine_kernel", "combine"), ("rank_", "rank"))
+             ("combine_backward_kernel", "combine_bwd"), ("rank_", "rank"))
     for pat, call in table:
         if pat in kernel:
             return call
+    if "combine_kernel" in kernel:
+        return "dx_combine" if train and "combine_kernel<float>" in kernel else "combine"
     return None
 
 
 # one dispatch per call instance: counts the launches of each call
-_ANCHORS = {"route": "route_", "swiglu": "build_tiles_kernel", "permute": "scatter_rows_kernel",
+_ANCHORS = {"route": "route_", "swiglu": "grouped_gemm_", "permute": "scatter_rows_kernel",
             "combine": "combine_kernel", "expand": "expand_rows_kernel", "pool_pack": "pack_kernel",
-            "recv_compact": "compact_", "quantize": "quantize_kernel"}
+            "recv_compact": "compact_", "quantize": "quantize_kernel", "combine_bwd": "combine_backward_kernel",
+            "swiglu_bwd": ", 1, false>", "dx_combine": "combine_kernel"}
+# calls whose anchor kernel is dispatched more than once per call
+_ANCHOR_PER_CALL = {"swiglu": 2}
 
 
 def record_traffic(args):
@@ -127,7 +139,7 @@ def record_traffic(args):
         # the calibration copy is the last plain device copy before the first library kernel
         calib = max(i for i in range(first_ours) if "copyBuffer" in names[i])
         factor = COPY_CALIB_BYTES / (float(rows[calib]["Counter_Value"]) * 1024.0)
-        calls = [_call_of(n) for n in names]
+        calls = [_call_of(n, train=w.train) for n in names]
         nxt = None
         for i in range(len(calls) - 1, first_ours - 1, -1):    # rank kernels -> call of the next dispatch
             if calls[i] == "rank":
@@ -142,6 +154,7 @@ def record_traffic(args):
             kib[c] = kib.get(c, 0.0) + float(rows[i]["Counter_Value"])
             if _ANCHORS[c] in names[i]:
                 launches[c] = launches.get(c, 0) + 1
+        launches = {c: v // _ANCHOR_PER_CALL.get(c, 1) for c, v in launches.items()}
         per[counter] = dict(factor=factor, bytes={c: kib[c] * 1024.0 * factor / launches[c] for c in kib},
                             launches=launches)
     entry = dict(command=args.pmc_command,

@@ -67,3 +67,46 @@ def test_record_traffic_attributes_kernels_to_calls(tmp_path, monkeypatch):
     data["mid_bf16"]["calls"]["swiglu"]["sources_sha256"] = "0" * 64
     json.dump(data, open(out, "w"))
     assert bench.recorded_traffic(w, "swiglu") is None
+
+
+def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
+    """Forward and backward kernels share names (tile tables, GEMMs, the
+    combine): the backward GEMMs are told apart by their last two tile
+    parameters (SwiGLU-backward epilogue, K-major B), tile tables go to the
+    call of the next dispatch, and the fp32 combine is the token-gradient pass."""
+    calib_kib = bench.COPY_CALIB_BYTES / 1024
+    ns = "moe::(anonymous namespace)::"
+    gemm = "void " + ns + "grouped_gemm_bf16_kernel<" + ns + "Cfg<128, 256, 2, 4, 3, {}, {}, false, 64, 1, 2, 8, false, {}, {}> >(x)"
+    step = [("void " + ns + "route_topk_kernel<2>(float const*)", 1.0),
+            ("void " + ns + "rank_count_kernel<ExpertBucket>(x)", 1.0),
+            (ns + "scatter_rows_kernel(x)", 10.0),
+            (ns + "build_tiles_kernel(x)", 0.5),
+            (gemm.format("true", "false", 0, "false"), 100.0),
+            (gemm.format("false", "false", 0, "false"), 50.0),
+            ("void " + ns + "combine_kernel<unsigned short>(x)", 5.0),
+            ("void " + ns + "combine_backward_kernel<unsigned short, unsigned short>(x)", 7.0),
+            (ns + "build_tiles_kernel(x)", 0.25),
+            (ns + "build_tiles_kernel(x)", 0.25),
+            (gemm.format("false", "false", 0, "true"), 40.0),
+            (gemm.format("true", "false", 1, "false"), 60.0),
+            (gemm.format("false", "true", 0, "true"), 80.0)]
+    step += [(ns + "transpose_rows_kernel(x)", 3.0)] * 4
+    step += [("void " + ns + "grouped_wgrad_kernel<" + ns + "Cfg<128, 256> >(x)", 200.0)] * 2
+    step += [("void " + ns + "combine_kernel<float>(x)", 9.0)]
+    head = [("__amd_rocclr_copyBuffer", 99.0)]
+    fetch = head + [("__amd_rocclr_copyBuffer", calib_kib / 2)] + step * 3
+    write = head + [("__amd_rocclr_copyBuffer", calib_kib)] + step * 3
+    _write_counters(tmp_path / "f", "FETCH_SIZE", fetch)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "mid_bf16_train", "--record-traffic",
+                                      str(tmp_path / "f"), str(tmp_path / "w")])
+    bench.record_traffic(bench.parse())
+    c = json.load(open(out))["mid_bf16_train"]["calls"]
+    assert set(c) == {"route", "permute", "swiglu", "combine", "combine_bwd", "swiglu_bwd", "dx_combine"}
+    assert all(v["launches"] == 3 for v in c.values())
+    assert c["swiglu"]["write_bytes"] == int(150.5 * 1024)
+    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 180.0 + 12.0 + 400.0) * 1024)
+    assert c["combine"]["write_bytes"] == int(5.0 * 1024) and c["dx_combine"]["write_bytes"] == int(9.0 * 1024)
+    assert c["combine_bwd"]["read_bytes"] == int(7.0 * 1024 * 2)
