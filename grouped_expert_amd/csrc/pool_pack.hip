@@ -291,7 +291,7 @@ MOE_API int moe_pool_pack(const void* x, int32_t x_dtype, int32_t pool_dtype, in
   MOE_CHECK(x_dtype == MOE_BF16 || is_fp8(x_dtype), MOE_EINVAL);
   // rows are moved as they are, or bf16 rows are quantized into fp8 records
   MOE_CHECK(pool_dtype == x_dtype || (x_dtype == MOE_BF16 && is_fp8(pool_dtype)), MOE_EINVAL);
-  const int64_t rb = row_bytes(pool_dtype, d);                    // pool row bytes, a multiple of 16
+  const int64_t rb = row_bytes(pool_dtype, d);                    // pool row bytes, a multiple of 16 (of 128 for records)
   MOE_CHECK(rb <= INT32_MAX, MOE_EUNSUPPORTED);
   const int32_t re = static_cast<int32_t>(rb / 2);                // 16-bit elements per row
   const int32_t H = pool_rows > re ? (pool_rows + re - 1) / re : 1;   // header rows: one 16-bit id per data row

@@ -65,7 +65,7 @@ typedef enum {
  * fp32 scales that travel with their row): d OCP E4M3 codes (bias 7, 3
  * mantissa bits, max 448, 0x7F NaN, no infinity), then G fp32 scales (G = 1,
  * or ceil(d / 128) for one scale per 128 values), then zero bytes up to a
- * multiple of 16 (moe_row_bytes).  Value i of a record is
+ * multiple of 128, whole cache lines (moe_row_bytes).  Value i of a record is
  * decode(code_i) * scale[i / group width]. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_ROW = 2, MOE_FP8_B128 = 3 } moe_dtype;
 
