@@ -617,11 +617,16 @@ __device__ __forceinline__ void wait_slice(int after) {
   }
 }
 
-// Persistent form: gridDim.x workgroups walk the tile list with a static
-// stride (round r takes tiles r*G + remap(b)), and the K-slice ring runs on
-// across tile boundaries: the first slices of the next tile are already in
-// flight while the current tile finishes and writes its outputs (direct
-// stores), so neither the pipeline fill nor the epilogue leaves the CU idle.
+// Persistent form: G workgroups walk the tile list with a static stride
+// (round r takes tiles r*G + slot), and the K-slice ring runs on across tile
+// boundaries: the first slices of the next tile are already in flight while
+// the current tile finishes and writes its outputs (direct stores), so
+// neither the pipeline fill nor the epilogue leaves the CU idle.  G is chosen
+// on the device from the tile count: of the gridDim.x launched workgroups,
+// as many stay (the same number on every XCD) as make the rounds even, so
+// the last round is not a handful of tiles run while the rest of the chip
+// waits (mid layer gate/up: 1032 tiles run as 208 x 5 instead of 256 x 4 + 8;
+// about 2 % faster).
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
@@ -631,8 +636,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
-  const uint32_t G = gridDim.x;
-  const uint32_t slot = xcd_remap(blockIdx.x, G);
+  const uint32_t G0 = gridDim.x;
+  const uint32_t rounds = (total + G0 - 1) / G0;
+  uint32_t G = rounds > 0 ? (total + rounds - 1) / rounds : G0;
+  uint32_t slot;
+  if (G0 % kXcds == 0) {
+    // `per` workgroups on each XCD (<= G0 / 8); consecutive slots share an XCD
+    const uint32_t per = (G + kXcds - 1) / kXcds;
+    G = per * kXcds;
+    const uint32_t x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+    if (l >= per) return;
+    slot = x * per + l;
+  } else {
+    G = G0;
+    slot = xcd_remap(blockIdx.x, G0);
+  }
   if (slot >= total) return;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
