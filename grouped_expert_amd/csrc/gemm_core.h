@@ -273,21 +273,41 @@ __device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_
   }
 }
 
-template <class C>
-__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const bf16_t* __restrict__ aux_in,
-    bf16_t* __restrict__ aux_out, int32_t kb1) {
-  // The K-slice ring.  With register staging the A rows of the two stages
-  // come first and the B rows of the two stages follow.  (One LDS array only:
-  // with several, the compiler tracks the LDS DMA per array and waits for it
-  // before every LDS read of that array.)
-  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
+// Even rounds for a grid of gridDim.x = G0 workgroups that walks `total`
+// tiles with a static stride: of the launched workgroups, as many stay (the
+// same number on every XCD) as make the rounds even, so the last round is
+// not a handful of tiles run while the rest of the chip waits (mid layer
+// gate/up: 1032 tiles run as 208 x 5 instead of 256 x 4 + 8).  Returns false
+// for a workgroup with no tile; else its first tile `slot` and the stride G.
+// Consecutive slots share an XCD (the hardware deals workgroups round-robin
+// over the XCDs).
+__device__ __forceinline__ bool even_rounds(uint32_t total, uint32_t* slot, uint32_t* G) {
+  const uint32_t G0 = gridDim.x;
+  const uint32_t rounds = (total + G0 - 1) / G0;
+  uint32_t g = rounds > 0 ? (total + rounds - 1) / rounds : G0;
+  uint32_t s;
+  if (G0 % kXcds == 0) {
+    const uint32_t per = (g + kXcds - 1) / kXcds;      // <= G0 / kXcds
+    g = per * kXcds;
+    const uint32_t x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+    if (l >= per) return false;
+    s = x * per + l;
+  } else {
+    g = G0;
+    s = xcd_remap(blockIdx.x, G0);
+  }
+  *slot = s;
+  *G = g;
+  return s < total;
+}
 
-  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
-  if (blockIdx.x >= total) return;
-  const uint32_t logical = xcd_remap(blockIdx.x, total);
+// One output tile (logical tile index `logical` of `total`).
+template <class C>
+__device__ __forceinline__ void gemm_tile(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles, uint32_t total,
+    int32_t n_tiles_n, const bf16_t* __restrict__ aux_in, bf16_t* __restrict__ aux_out, int32_t kb1,
+    bf16_t (&ring)[C::STAGES * C::SLICE], uint32_t logical) {
   int mt, nt;
   if (C::EXPERT_BLOCKED) {
     // all N-tiles of one expert form a block; inside it the M-tiles of one
@@ -603,6 +623,37 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
   }
 }
 
+// Workgroups walk the tile list with even rounds (one tile at a time: the
+// ring drains at the end of each tile, whose epilogue may stage through it;
+// backward data-gradient GEMMs about 5 % faster than one tile per
+// workgroup).  Register-staged tiles keep one tile per workgroup (the loop
+// costs them spilled registers).
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const bf16_t* __restrict__ aux_in,
+    bf16_t* __restrict__ aux_out, int32_t kb1) {
+  // The K-slice ring.  With register staging the A rows of the two stages
+  // come first and the B rows of the two stages follow.  (One LDS array only:
+  // with several, the compiler tracks the LDS DMA per array and waits for it
+  // before every LDS read of that array.)
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
+  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
+  if constexpr (C::RS) {
+    if (blockIdx.x < total)
+      gemm_tile<C>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, ring,
+                   xcd_remap(blockIdx.x, total));
+    return;
+  }
+  uint32_t slot, G;
+  if (!even_rounds(total, &slot, &G)) return;
+  for (uint32_t logical = slot; logical < total; logical += G) {
+    gemm_tile<C>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, ring, logical);
+    barrier_nofence();                       // every wave is done with the ring before the next tile's loads
+  }
+}
+
 // Dynamic wait for the oldest in-flight slice: `after` younger slices (0 ..
 // STAGES-2) may stay in flight.
 template <class C, int N = C::STAGES - 2>
@@ -621,12 +672,8 @@ __device__ __forceinline__ void wait_slice(int after) {
 // (round r takes tiles r*G + slot), and the K-slice ring runs on across tile
 // boundaries: the first slices of the next tile are already in flight while
 // the current tile finishes and writes its outputs (direct stores), so
-// neither the pipeline fill nor the epilogue leaves the CU idle.  G is chosen
-// on the device from the tile count: of the gridDim.x launched workgroups,
-// as many stay (the same number on every XCD) as make the rounds even, so
-// the last round is not a handful of tiles run while the rest of the chip
-// waits (mid layer gate/up: 1032 tiles run as 208 x 5 instead of 256 x 4 + 8;
-// about 2 % faster).
+// neither the pipeline fill nor the epilogue leaves the CU idle.  The rounds
+// are even (even_rounds).
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
@@ -636,22 +683,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
-  const uint32_t G0 = gridDim.x;
-  const uint32_t rounds = (total + G0 - 1) / G0;
-  uint32_t G = rounds > 0 ? (total + rounds - 1) / rounds : G0;
-  uint32_t slot;
-  if (G0 % kXcds == 0) {
-    // `per` workgroups on each XCD (<= G0 / 8); consecutive slots share an XCD
-    const uint32_t per = (G + kXcds - 1) / kXcds;
-    G = per * kXcds;
-    const uint32_t x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
-    if (l >= per) return;
-    slot = x * per + l;
-  } else {
-    G = G0;
-    slot = xcd_remap(blockIdx.x, G0);
-  }
-  if (slot >= total) return;
+  uint32_t slot, G;
+  if (!even_rounds(total, &slot, &G)) return;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -819,7 +852,11 @@ void launch_one(bool persistent, const void* a, const void* b0, const void* b1, 
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                          static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
   } else {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(upper)),
+    // at most one workgroup per CU slot; each walks its tiles (even rounds);
+    // register-staged tiles: one workgroup per tile
+    const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
+    const int64_t g = C::RS || upper < slots ? upper : slots;
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(g)),
                        dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn,
                        static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1);
