@@ -122,6 +122,41 @@ def _need_gpu(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape=None, dtype=None, numel: Optional[int] = None) -> None:
+    """Host-side check of a tensor the kernels will index by the sizes they
+    were given: a wrong shape or dtype would make them read or write outside
+    it.  ``shape`` entries of None are free."""
+    if t is None:
+        return
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(a) for a in allowed)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and int(a) != int(s) for a, s in zip(t.shape, shape)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+
+
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def _segments_ok(seg_start: torch.Tensor, seg_count: torch.Tensor, E: int) -> None:
+    """int32 vectors of at least E entries (the kernels read the first E; an
+    offsets vector with its sentinel serves as seg_start)."""
+    for name, t in (("seg_start", seg_start), ("seg_count", seg_count)):
+        _expect(name, t, (None,), torch.int32)
+        if t.numel() < E:
+            raise ValueError(f"{name}: {t.numel()} entries, expected at least {E}")
+
+
+def _flags_ok(flags: Optional[torch.Tensor]) -> None:
+    _expect("flags", flags, dtype=(torch.int32,))
+    if flags is not None and flags.numel() < 1:
+        raise ValueError("flags: needs one element")
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -135,6 +170,8 @@ def new_flags(device) -> torch.Tensor:
 def route_topk(logits: torch.Tensor, k: int, gating: int = MOE_GATING_SOFTMAX_TOPK_RENORM,
                flags: Optional[torch.Tensor] = None):
     """Returns ``(topk_ids int32 [T,k], topk_w fp32 [T,k])``."""
+    _expect("logits", logits, (None, None), torch.float32)
+    _flags_ok(flags)
     _need_gpu(logits, flags)
     T, E = logits.shape
     ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
@@ -148,6 +185,9 @@ def route_topk_grouped(logits: torch.Tensor, k: int, gating: int, n_group: int, 
                        route_scale: float, bias: Optional[torch.Tensor] = None,
                        flags: Optional[torch.Tensor] = None):
     """Group-restricted router (V2 / V3).  Returns ``(topk_ids, topk_w)``."""
+    _expect("logits", logits, (None, None), torch.float32)
+    _expect("bias", bias, (logits.shape[1],), torch.float32)
+    _flags_ok(flags)
     _need_gpu(logits, bias, flags)
     T, E = logits.shape
     ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
@@ -165,6 +205,12 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity:
     materialised), src, inv, sel, counts, offsets, dropped.  With ``payload``
     "row" / "b128", ``x`` holds fp8 records of rows ``d`` wide and x_perm
     receives whole records."""
+    _expect("topk_ids", topk_ids, (None, None), torch.int32)
+    _flags_ok(flags)
+    if materialize or x is not None:
+        if x is None:
+            raise ValueError("x: required to materialise x_perm")
+        _expect("x", x, (topk_ids.shape[0], None), _FLOATS if payload is None else torch.uint8)
     _need_gpu(x, topk_ids, flags)
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -197,9 +243,16 @@ def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Te
                    z: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None):
     """Runs expert ``e`` on rows ``[seg_start[e], seg_start[e]+seg_count[e])``
     of ``x``; returns ``z`` (rows outside every segment are left as allocated)."""
-    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags)
+    _expect("x", x, (None, None), _FLOATS)
     rows, d = x.shape
+    _expect("w_gate", w_gate, (None, None, d), x.dtype)
     E, d_ff, _ = w_gate.shape
+    _expect("w_up", w_up, (E, d_ff, d), x.dtype)
+    _expect("w_down", w_down, (E, d, d_ff), x.dtype)
+    _segments_ok(seg_start, seg_count, E)
+    _expect("z", z, (rows, d), _FLOATS)
+    _flags_ok(flags)
+    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags)
     dev = x.device
     if z is None:
         z = torch.empty((rows, d), dtype=z_dtype, device=dev)
@@ -215,10 +268,17 @@ def unpermute_combine(z: torch.Tensor, idx: torch.Tensor, gates: Optional[torch.
                       lo: int = 0, hi: Optional[int] = None, y: Optional[torch.Tensor] = None,
                       accumulate: bool = False, flags: Optional[torch.Tensor] = None):
     """``y[t] (+)= sum_j g[t,j] z[idx[t,j] - lo]`` over routes inside ``[lo, hi)``."""
-    _need_gpu(z, idx, gates, y, flags)
+    _expect("z", z, (None, None), _FLOATS)
     d = z.shape[-1]
     if hi is None:
         hi = lo + z.shape[0]
+    if hi - lo > z.shape[0]:
+        raise ValueError(f"z: {z.shape[0]} rows, window [lo, hi) needs {hi - lo}")
+    _expect("idx", idx, None, torch.int32, T * k)
+    _expect("gates", gates, None, torch.float32, T * k)
+    _expect("y", y, (T, d), torch.float32)
+    _flags_ok(flags)
+    _need_gpu(z, idx, gates, y, flags)
     dev = idx.device
     if y is None:
         y = torch.empty((T, d), dtype=torch.float32, device=dev)
@@ -257,8 +317,11 @@ def pool_rows_of_height(height: int, d: int, payload: Optional[str] = None) -> i
 def quantize_fp8(x: torch.Tensor, payload: str = "b128", rec: Optional[torch.Tensor] = None,
                  flags: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Rows ``[n, d]`` (bf16 or fp32) to fp8 records ``uint8 [n, row_bytes]``."""
-    _need_gpu(x, rec, flags)
+    _expect("x", x, (None, None), _FLOATS)
     n, d = x.shape
+    _expect("rec", rec, (n, row_bytes(d, payload)), torch.uint8)
+    _flags_ok(flags)
+    _need_gpu(x, rec, flags)
     if rec is None:
         rec = torch.empty((n, row_bytes(d, payload)), dtype=torch.uint8, device=x.device)
     _check("moe_quantize_fp8", lib.moe_quantize_fp8(_ptr(x), _dtype_code(x), n, d, FP8_CODES[payload], _ptr(rec),
@@ -269,8 +332,11 @@ def quantize_fp8(x: torch.Tensor, payload: str = "b128", rec: Optional[torch.Ten
 def dequantize_fp8(rec: torch.Tensor, d: int, payload: str = "b128", out_dtype: torch.dtype = torch.bfloat16,
                    out: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp8 records back to ``[n, d]`` rows of ``out_dtype``."""
-    _need_gpu(rec, out, flags)
+    _expect("rec", rec, (None, row_bytes(d, payload)), torch.uint8)
     n = rec.shape[0]
+    _expect("out", out, (n, d), _FLOATS)
+    _flags_ok(flags)
+    _need_gpu(rec, out, flags)
     if out is None:
         out = torch.empty((n, d), dtype=out_dtype, device=rec.device)
     _check("moe_dequantize_fp8", lib.moe_dequantize_fp8(_ptr(rec), FP8_CODES[payload], n, d, _ptr(out),
@@ -283,9 +349,15 @@ def combine_backward(dy: torch.Tensor, z: torch.Tensor, idx: torch.Tensor, gates
                      flags: Optional[torch.Tensor] = None):
     """Route gradients ``dz[idx[r]] = g_r dy[t]`` and gate gradients
     ``<dy[t], z[idx[r]]>``; returns ``(dz, dgates [T, k])``."""
-    _need_gpu(dy, z, idx, gates, dz, flags)
+    _expect("dy", dy, (None, None), torch.float32)
     T, d = dy.shape
+    _expect("z", z, (None, d), _FLOATS)
     rows = z.shape[0]
+    _expect("idx", idx, None, torch.int32, T * k)
+    _expect("gates", gates, None, torch.float32, T * k)
+    _expect("dz", dz, (rows, d), _FLOATS)
+    _flags_ok(flags)
+    _need_gpu(dy, z, idx, gates, dz, flags)
     if dz is None:
         dz = torch.empty((rows, d), dtype=dz_dtype, device=dy.device)
     dg = torch.empty((T, k), dtype=torch.float32, device=dy.device)
@@ -301,9 +373,17 @@ def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.
                             flags: Optional[torch.Tensor] = None):
     """Expert backward over the segments; returns a dict with dx (route-input
     gradients, rows of x), dw_gate, dw_up, dw_down (fp32)."""
-    _need_gpu(x, dz, seg_start, seg_count, w_gate, w_up, w_down, dx, flags)
+    _expect("x", x, (None, None), torch.bfloat16)
     rows, d = x.shape
+    _expect("dz", dz, (rows, d), torch.bfloat16)
+    _expect("w_gate", w_gate, (None, None, d), torch.bfloat16)
     E, d_ff, _ = w_gate.shape
+    _expect("w_up", w_up, (E, d_ff, d), torch.bfloat16)
+    _expect("w_down", w_down, (E, d, d_ff), torch.bfloat16)
+    _segments_ok(seg_start, seg_count, E)
+    _expect("dx", dx, (rows, d), _FLOATS)
+    _flags_ok(flags)
+    _need_gpu(x, dz, seg_start, seg_count, w_gate, w_up, w_down, dx, flags)
     dev = x.device
     if dx is None:
         dx = torch.empty((rows, d), dtype=dx_dtype, device=dev)
@@ -321,10 +401,14 @@ def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.
 def expand_rows(z: torch.Tensor, row_slot: torch.Tensor, ret_dtype: torch.dtype = torch.float32,
                 ret: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None):
     """``ret[i] = z[row_slot[i]]`` (converted) or a zero row; returns ``ret``."""
-    _need_gpu(z, row_slot, ret, flags)
+    _expect("z", z, None, _FLOATS)
+    _expect("row_slot", row_slot, None, torch.int32)
     d = z.shape[-1]
     n_slots = z.numel() // d
     n = row_slot.numel()
+    _expect("ret", ret, None, _FLOATS, n * d)
+    _flags_ok(flags)
+    _need_gpu(z, row_slot, ret, flags)
     if ret is None:
         ret = torch.empty((n, d), dtype=ret_dtype, device=row_slot.device)
     _check("moe_expand_rows", lib.moe_expand_rows(
@@ -342,6 +426,9 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
     "row" / "b128" the pools hold fp8 records (uint8 ``[..., PH, row_bytes]``)
     and ``x`` is either those records (``uint8 [T, row_bytes]`` of rows ``d``
     wide) or bf16 rows that the pack quantizes on the way."""
+    _expect("x", x, (None, None), (torch.bfloat16, torch.uint8))
+    _expect("topk_ids", topk_ids, (x.shape[0], None), torch.int32)
+    _flags_ok(flags)
     _need_gpu(x, topk_ids, pools, flags)
     T = x.shape[0]
     if payload is None:
@@ -361,6 +448,7 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
     shape = (n_waves, n_dest, PH, last) if wave < 0 else (n_dest, PH, last)
     if pools is None:
         pools = torch.empty(shape, dtype=pdt, device=dev)
+    _expect("pools", pools, shape, pdt)
     route_loc = torch.empty(T * k, dtype=torch.int32, device=dev)
     dest_counts = torch.empty(n_dest, dtype=torch.int32, device=dev)
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
@@ -380,6 +468,8 @@ def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Option
     "row" / "b128" fp8 records ``uint8 [n_src, pool_height, row_bytes]`` of
     rows ``d`` wide (dequantized into ``compact``); sources are visited from
     ``rotation`` onwards."""
+    _expect("pools_in", pools_in, (None, None, None), torch.bfloat16 if payload is None else torch.uint8)
+    _flags_ok(flags)
     _need_gpu(pools_in, compact, flags)
     S, P1 = pools_in.shape[0], pools_in.shape[1]
     if payload is None:
@@ -392,6 +482,7 @@ def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Option
     dev = pools_in.device
     if compact is None:
         compact = torch.empty((n_local, cap, d), dtype=torch.bfloat16, device=dev)
+    _expect("compact", compact, None, torch.bfloat16, n_local * cap * d)
     counts = torch.empty(n_local, dtype=torch.int32, device=dev)
     arrived = torch.empty(n_local, dtype=torch.int32, device=dev)
     row_slot = torch.empty(S * P1, dtype=torch.int32, device=dev)
