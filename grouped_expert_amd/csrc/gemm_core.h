@@ -7,6 +7,7 @@
 // expert segments, B rows from the segment's expert matrices.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -827,15 +828,15 @@ inline TileKind pick_tiles(int64_t rows, int32_t E) {
 // Compute units of the current device (cached per device; the library keeps
 // no other state).
 inline int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];       // zero-initialised; a race only repeats the query
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <class C>
