@@ -12,6 +12,7 @@ torch = pytest.importorskip("torch")
 import oracle as O
 import workloads as W
 from tests.helpers import as_f64, assert_rows_close, to_gpu, to_np
+from tests.test_gpu_ops import _gates_close, _v3_agree
 
 pytestmark = pytest.mark.gpu
 
@@ -128,4 +129,76 @@ def test_grouped_swiglu_sweep(ge, seed):
     for s, c in zip(starts, counts):
         covered[s:s + c] = True
     assert np.all(as_f64(z)[~covered] == 0), case                   # rows outside every segment untouched
+    assert int(to_np(flags)[0]) == 0, case
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_grouped_swiglu_backward_sweep(ge, seed):
+    rng = np.random.default_rng(4000 + seed)
+    E = int(rng.choice([1, 3, 12]))
+    d = int(rng.choice([64, 192, 256]))
+    d_ff = int(rng.choice([64, 128, 320]))
+    top = min(int(rng.choice([2, 70, 500, 1100])), 3000 // E + 1)
+    counts = rng.integers(0, top, size=E).astype(np.int32)
+    gaps = rng.integers(0, 4, size=E).astype(np.int32)
+    starts = (np.cumsum(counts + gaps) - counts).astype(np.int32)
+    rows = int(starts[-1] + counts[-1] + rng.integers(0, 5))
+    dxdt = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    case = dict(seed=seed, E=E, d=d, d_ff=d_ff, rows=rows, counts=counts.tolist(), dx=str(dxdt))
+    x = W.f32_to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    dz = W.f32_to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    ws = [W.f32_to_bf16_bits((0.05 * rng.standard_normal(s)).astype(np.float32))
+          for s in [(E, d_ff, d), (E, d_ff, d), (E, d, d_ff)]]
+    flags = ge.new_flags("cuda")
+    dx0 = torch.zeros((rows, d), dtype=dxdt, device="cuda")
+    out = ge.grouped_swiglu_backward(to_gpu(x), to_gpu(dz), to_gpu(starts), to_gpu(counts),
+                                     *[to_gpu(w) for w in ws], dx=dx0, flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0, case
+    want_dx, grads = O.run_segments_backward(x, O.to_f64(dz), starts, counts,
+                                             O.swiglu_bank_backward(lambda e: (ws[0][e], ws[1][e], ws[2][e])))
+    covered = np.zeros(rows, bool)
+    for s, c in zip(starts, counts):
+        covered[s:s + c] = True
+    got_dx = as_f64(out["dx"])
+    if covered.any():
+        assert_rows_close(got_dx[covered], want_dx[covered], what=f"dx {case}")
+    assert np.all(got_dx[~covered] == 0), case
+    for e in range(E):
+        for name, i in (("dw_gate", 0), ("dw_up", 1), ("dw_down", 2)):
+            got = to_np(out[name][e]).astype(np.float64)
+            if grads[e] is None:
+                assert np.all(got == 0), (case, e, name)
+            else:
+                assert_rows_close(got, grads[e][i], what=f"{name}[{e}] {case}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_grouped_router_sweep(ge, seed):
+    """V2 (group-limited softmax) and V3 (sigmoid + bias, top-two group
+    scores) on random group geometries."""
+    rng = np.random.default_rng(5000 + seed)
+    n_group = int(rng.choice([1, 2, 4, 8]))
+    per = int(rng.choice([2, 4, 16, 32]))
+    E = n_group * per
+    topk_group = int(rng.integers(1, n_group + 1))
+    k = int(rng.integers(1, min(topk_group * per, 16) + 1))
+    T = int(rng.integers(1, 400))
+    scale = float(rng.choice([1.0, 2.5, 16.0]))
+    case = dict(seed=seed, E=E, n_group=n_group, topk_group=topk_group, k=k, T=T, scale=scale)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    flags = ge.new_flags("cuda")
+    ids2, g2 = ge.route_topk_grouped(to_gpu(z), k, ge.MOE_GATING_SOFTMAX_GROUP_LIMITED, n_group, topk_group, scale,
+                                     flags=flags)
+    want2 = O.route_v2(z, k, n_group, topk_group, scale)
+    assert np.array_equal(to_np(ids2), want2[0]), case
+    assert np.all(np.abs(to_np(g2).astype(np.float64) - want2[1]) <= 1e-5 * np.abs(want2[1]) + 1e-7), case
+    ids3, g3 = ge.route_topk_grouped(to_gpu(z), k, ge.MOE_GATING_SIGMOID_BIAS_GROUP_TOP2, n_group, topk_group,
+                                     scale, bias=to_gpu(bias), flags=flags)
+    want3 = O.route_v3(z, bias, k, n_group, topk_group, scale)
+    got3 = to_np(ids3)
+    _v3_agree(z, bias, got3, want3[0], k, n_group, topk_group)
+    same = (got3 == want3[0]).all(axis=1)
+    assert _gates_close(to_np(g3)[same], want3[1][same]), case
     assert int(to_np(flags)[0]) == 0, case
