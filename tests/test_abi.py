@@ -203,3 +203,13 @@ def test_workspace_queries_reject_bad_sizes():
     assert lib.moe_grouped_swiglu_workspace(10, 8, 64, 7) == 0
     assert lib.moe_pool_pack_workspace(10, 0, 8) == 0
     assert lib.moe_recv_compact_workspace(4, 4, 0) == 0
+
+
+def test_record_widths_agree_with_the_oracle_layout():
+    """The library's record width and the oracle's record layout are written
+    independently; they must agree for every width and scale layout."""
+    import oracle as O
+    for d in list(range(8, 1025, 8)) + [2048, 3072, 4096, 7168, 8192]:
+        for code, mode in ((2, "row"), (3, "b128")):
+            assert lib.moe_row_bytes(code, d) == O.fp8_record_layout(d, mode)[1], (d, mode)
+        assert lib.moe_row_bytes(1, d) == 2 * d and lib.moe_row_bytes(0, d) == 4 * d
