@@ -58,7 +58,8 @@ import numpy as np
 
 __all__ = [
     "HEADER_EMPTY", "bf16_to_f64", "to_f64",
-    "route_topk", "route_v1", "group_limited_select", "route_v2", "sigmoid_f32", "route_v3",
+    "route_topk", "route_v1", "group_limited_select", "route_v2", "sigmoid_f32", "sigmoid_f32_ambiguous",
+    "route_v3",
     "DispatchPlan", "dispatch_plan", "check_dispatch",
     "gather_rows", "silu", "swiglu_expert", "swiglu_bank", "scalar_bank", "run_segments",
     "combine", "moe_layer_token_major", "moe_layer_expert_major",
@@ -223,28 +224,55 @@ def route_v2(logits: np.ndarray, k: int, n_group: int, topk_group: int,
 
 
 def sigmoid_f32(z: np.ndarray) -> np.ndarray:
-    """Sigmoid evaluated in fp32, 1 / (1 + exp(-z)): the precision in which
-    V3 makes its selection decisions (M6.2 §0x06I: sigmoid scores plus an FP32
-    correction bias)."""
-    z32 = np.asarray(z, dtype=np.float32)
+    """The V3 affinity as a decision key: the sigmoid ``1 / (1 + exp(-z))``
+    evaluated in fp64 and rounded once to fp32 (nearest, ties to even).
+
+    M6.2 §0x06I makes the selection from sigmoid scores plus an FP32
+    correction bias, so the corrected score is an fp32 value; the pages leave
+    open how the fp32 affinity itself is obtained.  Reading: the fp32 value
+    nearest to the sigmoid.  Evaluated in fp64 (relative error near 2^-52),
+    that rounding is exact unless the sigmoid lies within about 2^-45 of an
+    fp32 rounding midpoint (``sigmoid_f32_ambiguous``)."""
+    z64 = np.asarray(z, dtype=np.float32).astype(np.float64)
     with np.errstate(over="ignore"):
-        return (np.float32(1.0) / (np.float32(1.0) + np.exp(-z32))).astype(np.float32)
+        return (1.0 / (1.0 + np.exp(-z64))).astype(np.float32)
+
+
+def sigmoid_f32_ambiguous(z: np.ndarray, rel: float = 2.0 ** -45) -> Tuple[np.ndarray, np.ndarray]:
+    """Where rounding the fp64 sigmoid to fp32 is not determined by an fp64
+    evaluation: the value lies within ``rel`` (relative) of the midpoint
+    between two adjacent fp32 values.  Returns ``(mask, other)``: ``other``
+    holds the fp32 neighbour on the far side of that midpoint (equal to
+    ``sigmoid_f32`` where ``mask`` is false)."""
+    z64 = np.asarray(z, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        s64 = 1.0 / (1.0 + np.exp(-z64))
+    s32 = s64.astype(np.float32)
+    up = np.nextafter(s32, np.float32(np.inf))
+    dn = np.nextafter(s32, np.float32(-np.inf))
+    other = np.where(s64 >= s32.astype(np.float64), up, dn).astype(np.float32)
+    mid = (s32.astype(np.float64) + other.astype(np.float64)) / 2.0     # exact in fp64
+    mask = np.abs(s64 - mid) <= rel * np.abs(s64)
+    return mask, np.where(mask, other, s32)
 
 
 def route_v3(logits: np.ndarray, bias: Optional[np.ndarray], k: int, n_group: int, topk_group: int,
-             route_scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             route_scale: float, affinity32: Optional[np.ndarray] = None
+             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """V3: sigmoid affinity ``s``, corrected score ``s + b`` (fp32) decides
     groups (sum of each group's two largest corrected scores) and experts;
     the gates return to the original affinities of the selected experts,
     renormalised and scaled by ``route_scale`` (M6.2 §0x06A-§0x06D, §0x06I:
     8 groups of 32, keep 4, top-8, scale 2.5).
 
-    Decisions use fp32 scores; gates use the fp64 sigmoid of the logits.
+    Decisions use the fp32 affinity of ``sigmoid_f32`` (or ``affinity32``
+    when given, e.g. the other rounding of an ambiguous value) plus the fp32
+    bias, added in fp32; gates use the fp64 sigmoid of the logits.
     """
     z = np.asarray(logits, dtype=np.float32)
     T, E = z.shape
     b = np.zeros(E, np.float32) if bias is None else np.asarray(bias, dtype=np.float32)
-    s32 = sigmoid_f32(z)
+    s32 = sigmoid_f32(z) if affinity32 is None else np.asarray(affinity32, dtype=np.float32)
     corrected = (s32 + b[None, :]).astype(np.float32)
     invalid = ~(np.isfinite(z).all(axis=1) & np.isfinite(corrected).all(axis=1))
     corrected = np.where(invalid[:, None], np.float32(0), corrected)
@@ -789,7 +817,8 @@ def pool_pack(x_bits: np.ndarray, ids: np.ndarray, experts_per_dest: int, n_dest
     """Pack one sender's routes into fixed destination pools.
 
     Pooled wave §02: expert id gives a destination and a local expert id;
-    "wave = rank mod 3, pool row = rank / 3" with rank read as the route's
+    the stripe rule takes the page's rank modulo three as the wave and the
+    rank divided by three as the pool row, with the rank read as the route's
     ordinal among this sender's routes to that destination (generalised to
     ``n_waves``: the two-wave profile of §05); each destination gets
     ``pool_rows`` rows per wave and extra rows are dropped; the first

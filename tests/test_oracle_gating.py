@@ -16,7 +16,7 @@ def _logit(s):
 def test_v3_page_token_t0(golden):
     f = golden("m62_gating_fixtures.json")["v3_t0"]
     z = _logit(f["affinity"])[None, :]
-    # the fp32 sigmoid of these logits reproduces the tabulated affinities
+    # the fp32 affinity of these logits reproduces the tabulated affinities
     assert np.allclose(O.sigmoid_f32(z)[0], f["affinity"], atol=2e-7)
     ids, gates, inv = O.route_v3(z, np.array(f["bias"], np.float32), f["k"], f["n_group"], f["topk_group"],
                                  f["route_scale"])
@@ -58,6 +58,59 @@ def test_v3_group_statistic_is_top2_sum(golden):
     ids, _, _ = O.route_v3(_logit(sc[0])[None, :], None, f["k"], f["n_group"], f["topk_group"], 2.5)
     assert 0 not in ids[0].tolist()
     assert int(np.argmax(sc[0])) == 0
+
+
+def _nearest_f32(x):
+    """The fp32 value nearest to the Decimal ``x`` (ties to the even code),
+    found among the neighbours of a first guess by exact comparison."""
+    from decimal import Decimal
+    guess = np.float32(float(x))
+    cands = [np.nextafter(guess, np.float32(-np.inf)), guess, np.nextafter(guess, np.float32(np.inf))]
+    def key(c):
+        return (abs(Decimal(float(c)) - x), int(np.array(c, np.float32).view(np.uint32)) & 1)
+    return min(cands, key=key)
+
+
+def test_v3_affinity_is_the_nearest_fp32_sigmoid():
+    """The V3 decision key rounds the exact sigmoid once to fp32: checked
+    against a 60-digit decimal evaluation of 1 / (1 + exp(-z)), except where
+    the oracle itself reports the rounding as too close to call."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    rng = np.random.default_rng(11)
+    z = np.concatenate([rng.standard_normal(3000) * 4, [0.0, -0.0, 1e-30, -1e-30, 20.0, -20.0, 88.0, -88.0,
+                                                        -103.0, 17.0, -17.0]]).astype(np.float32)
+    got = O.sigmoid_f32(z)
+    amb, other = O.sigmoid_f32_ambiguous(z)
+    assert amb.sum() <= 2
+    for zi, g, a in zip(z, got, amb):
+        x = Decimal(1) / (Decimal(1) + (-Decimal(float(zi))).exp())
+        want = _nearest_f32(x)
+        if not a:
+            assert g == want, (float(zi), float(g), float(want))
+    assert got[z == 0.0].tolist() == [0.5, 0.5]
+    assert float(got[z == 20.0][0]) == 1.0                   # 1 - 2e-9 rounds to one in fp32
+    # a planted single-rounding mistake (fp32 exp, as a float32 evaluation
+    # would do) is caught by the same comparison on some input
+    with np.errstate(over="ignore"):
+        bad = (np.float32(1) / (np.float32(1) + np.exp(-z))).astype(np.float32)
+    assert np.any(bad != got)
+
+
+def test_v3_ambiguity_report_is_consistent():
+    rng = np.random.default_rng(12)
+    z = (rng.standard_normal(200000) * 3).astype(np.float32)
+    amb, other = O.sigmoid_f32_ambiguous(z)
+    s = O.sigmoid_f32(z)
+    assert np.array_equal(other[~amb], s[~amb])
+    # an ambiguous value's alternative is the adjacent fp32 value
+    step = np.abs(other[amb].view(np.int32).astype(np.int64) - s[amb].view(np.int32).astype(np.int64))
+    assert np.all(step == 1)
+    # a wide window flags more values, a zero window none
+    wide, _ = O.sigmoid_f32_ambiguous(z, rel=2.0 ** -30)
+    none, _ = O.sigmoid_f32_ambiguous(z, rel=0.0)
+    assert wide.sum() > amb.sum() and none.sum() <= amb.sum()
+    assert np.all(wide[amb])
 
 
 # ---- V2 -----------------------------------------------------------------
