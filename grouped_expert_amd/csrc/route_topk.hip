@@ -184,7 +184,7 @@ void launch(const float* logits, int64_t T, int32_t E, int32_t k, int32_t full_m
 
 // Group-restricted router (V2 when sigmoid_bias = 0, V3 when 1).  One
 // wavefront per token.  Each lane turns its logits into selection keys (V2:
-// the logit; V3: sigmoid + bias in fp32) and stores them in the wavefront's
+// the logit; V3: the fp32-rounded fp64 sigmoid plus the bias in fp32) and stores them in the wavefront's
 // LDS row; lane g < n_group then scans group g's G contiguous keys for the
 // group score (V2: largest key; V3: fp32 sum of the two largest corrected
 // scores).  topk_group rounds of max / lowest-index pick the groups, the
@@ -214,7 +214,11 @@ __global__ __launch_bounds__(kTokensPerBlock * kWave) void route_grouped_kernel(
       const float z = row[e];
       bad |= !isfinite(z);
       if (sigmoid_bias) {
-        const float sg = 1.0f / (1.0f + expf(-z));
+        // the affinity as a decision key: the sigmoid evaluated in fp64 and
+        // rounded once to fp32, so that it is the fp32 value nearest to the
+        // sigmoid (any other fp32 evaluation depends on the exp used); the
+        // corrected score is one fp32 addition
+        const float sg = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(z))));
         const float c = sg + (bias ? bias[e] : 0.0f);
         bad |= !isfinite(c);
         key[v] = order_key(c);

@@ -107,6 +107,21 @@ typedef enum {
  * cache lines); 0 for an unknown dtype or d < 1. */
 size_t moe_row_bytes(int32_t dtype, int32_t d);
 
+/* Pool geometry of the pooled-wave pack and the receiver's compaction
+ * ("Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02-05: a pool is one
+ * packed full-width header row of local expert ids followed by its data
+ * rows).  With RB = moe_row_bytes(row_dtype, d), a pool of pool_rows data
+ * rows has H = max(1, ceil(2 * pool_rows / RB)) header rows (one 16-bit id
+ * per data row) and is PH = pool_rows + H rows tall.
+ *   moe_pool_geometry        writes H and PH for pool_rows >= 0.
+ *   moe_pool_rows_of_height  writes the data-row count of a pool PH rows tall
+ *                            (the inverse); MOE_EINVAL if no count fits.
+ * row_dtype MOE_BF16 or an fp8 record dtype, d >= 8 and d % 8 == 0; output
+ * pointers are host pointers.  Host-only: nothing is launched.  Returns
+ * MOE_OK or MOE_EINVAL. */
+int moe_pool_geometry(int32_t row_dtype, int32_t d, int64_t pool_rows, int64_t* header_rows, int64_t* pool_height);
+int moe_pool_rows_of_height(int32_t row_dtype, int32_t d, int64_t pool_height, int64_t* pool_rows);
+
 /* ---------------------------------------------------------------------------
  * moe_quantize_fp8 -- rows to fp8 dispatch records.
  *
@@ -183,7 +198,8 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
  *     probability does); keep topk_group groups; the k largest logits among
  *     the kept groups' experts, descending; topk_w = softmax probability over
  *     all E experts times route_scale (no renormalisation).  bias must be NULL.
- *   MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 (V3): s_e = 1 / (1 + exp(-z_e)) and
+ *   MOE_GATING_SIGMOID_BIAS_GROUP_TOP2 (V3): s_e = 1 / (1 + exp(-z_e))
+ *     evaluated in fp64 and rounded once to fp32 (nearest even), and
  *     c_e = s_e + bias[e] in fp32 (bias NULL = 0); group score = sum of the
  *     group's two largest c; keep topk_group groups; the k largest c among the
  *     kept groups' experts, descending; topk_w = route_scale * s_j / sum over

@@ -92,17 +92,37 @@ def test_route_grouped_v2(ge, T, E, k, ng, tg, scale):
     assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
 
 
-def _v3_agree(z, bias, gids, rid, k, ng, tg):
-    """Expert ids must match; a differing token is accepted only when its
-    decision was a tie within fp32 rounding of the sigmoid (the kernel's expf
-    and numpy's exp may differ by an ulp)."""
-    if np.array_equal(gids, rid):
-        return
-    c = (O.sigmoid_f32(z) + bias[None, :]).astype(np.float32)
-    for t in np.nonzero((gids != rid).any(axis=1))[0]:
-        diff = set(gids[t].tolist()) ^ set(rid[t].tolist())
-        ref = float(c[t, rid[t, -1]])
-        assert all(abs(float(c[t, e]) - ref) <= 4 * np.spacing(np.float32(abs(ref) + 1)) for e in diff), t
+def _v3_exact(z, bias, gids, gw, k, ng, tg, scale):
+    """V3 ids must equal the oracle's exactly, token by token.  The one
+    exception is a token holding a logit whose fp64 sigmoid lies within
+    2^-45 of an fp32 rounding midpoint (the oracle names these): there the
+    ids (and gates) must equal the oracle's under one of the two roundings of
+    each such value.  Returns the excepted tokens."""
+    z = np.asarray(z, np.float32)
+    rid, rg, inv = O.route_v3(z, bias, k, ng, tg, scale)
+    amb, other = O.sigmoid_f32_ambiguous(z)
+    amb &= np.isfinite(z)
+    named = np.nonzero(amb.any(axis=1))[0]
+    plain = np.ones(z.shape[0], dtype=bool)
+    plain[named] = False
+    assert np.array_equal(gids[plain], rid[plain])
+    assert _gates_close(gw[plain], rg[plain])
+    base = O.sigmoid_f32(z)
+    for t in named:
+        cols = np.nonzero(amb[t])[0]
+        assert cols.size <= 4, (t, cols)
+        ok = False
+        for m in range(1 << cols.size):
+            s32 = base[t:t + 1].copy()
+            for i, c in enumerate(cols):
+                if (m >> i) & 1:
+                    s32[0, c] = other[t, c]
+            ids_t, g_t, _ = O.route_v3(z[t:t + 1], bias, k, ng, tg, scale, affinity32=s32)
+            if np.array_equal(gids[t], ids_t[0]) and _gates_close(gw[t:t + 1], g_t):
+                ok = True
+                break
+        assert ok, f"token {t}: ids {gids[t].tolist()} match neither rounding of logits {cols.tolist()}"
+    return inv, named.tolist()
 
 
 @pytest.mark.parametrize("T,E,k,ng,tg,scale", [(300, 256, 8, 8, 4, 2.5), (200, 64, 6, 8, 3, 1.0),
@@ -113,12 +133,10 @@ def test_route_grouped_v3(ge, T, E, k, ng, tg, scale):
     flags = ge.new_flags("cuda")
     ids, w = ge.route_topk_grouped(to_gpu(z), k, ge.binding.MOE_GATING_SIGMOID_BIAS_GROUP_TOP2, ng, tg, scale,
                                    bias=to_gpu(bias), flags=flags)
-    rid, rg, inv = O.route_v3(z, bias, k, ng, tg, scale)
-    gids = to_np(ids)
-    _v3_agree(z, bias, gids, rid, k, ng, tg)
-    same = (gids == rid).all(axis=1)
-    assert _gates_close(to_np(w)[same], rg[same])
+    inv, named = _v3_exact(z, bias, to_np(ids), to_np(w), k, ng, tg, scale)
     assert (int(to_np(flags)[0]) & 2 != 0) == bool(inv.any())
+    if named:
+        print(f"V3 tokens with an ambiguous fp32 affinity (either rounding accepted): {named}")
 
 
 def test_route_grouped_page_tokens(ge, golden):

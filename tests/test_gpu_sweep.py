@@ -12,7 +12,7 @@ torch = pytest.importorskip("torch")
 import oracle as O
 import workloads as W
 from tests.helpers import as_f64, assert_rows_close, to_gpu, to_np
-from tests.test_gpu_ops import _gates_close, _v3_agree
+from tests.test_gpu_ops import _gates_close, _v3_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -196,9 +196,5 @@ def test_grouped_router_sweep(ge, seed):
     assert np.all(np.abs(to_np(g2).astype(np.float64) - want2[1]) <= 1e-5 * np.abs(want2[1]) + 1e-7), case
     ids3, g3 = ge.route_topk_grouped(to_gpu(z), k, ge.MOE_GATING_SIGMOID_BIAS_GROUP_TOP2, n_group, topk_group,
                                      scale, bias=to_gpu(bias), flags=flags)
-    want3 = O.route_v3(z, bias, k, n_group, topk_group, scale)
-    got3 = to_np(ids3)
-    _v3_agree(z, bias, got3, want3[0], k, n_group, topk_group)
-    same = (got3 == want3[0]).all(axis=1)
-    assert _gates_close(to_np(g3)[same], want3[1][same]), case
+    _v3_exact(z, bias, to_np(ids3), to_np(g3), k, n_group, topk_group, scale)
     assert int(to_np(flags)[0]) == 0, case
