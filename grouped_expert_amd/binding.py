@@ -58,6 +58,8 @@ _SIGS = {
     "moe_pool_pack": (ctypes.c_int, [_p, _i32, _i32, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p,
                                      _p, _p, _p, _p, _sz, _p, _p]),
     "moe_row_bytes": (_sz, [_i32, _i32]),
+    "moe_pool_geometry": (ctypes.c_int, [_i32, _i32, _i64, _p, _p]),
+    "moe_pool_rows_of_height": (ctypes.c_int, [_i32, _i32, _i64, _p]),
     "moe_quantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _i32, _p, _p, _p]),
     "moe_dequantize_fp8": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p]),
     "moe_recv_compact_workspace": (_sz, [_i32, _i32, _i32]),
@@ -295,23 +297,35 @@ def row_bytes(d: int, payload: Optional[str] = None) -> int:
     return int(lib.moe_row_bytes(MOE_BF16 if payload is None else FP8_CODES[payload], d))
 
 
+def _row_code(payload: Optional[str]) -> int:
+    return MOE_BF16 if payload is None else FP8_CODES[payload]
+
+
+def pool_geometry(pool_rows: int, d: int, payload: Optional[str] = None):
+    """``(header_rows, pool_height)`` of a pool as the library lays it out."""
+    h, ph = ctypes.c_int64(), ctypes.c_int64()
+    _check("moe_pool_geometry", lib.moe_pool_geometry(_row_code(payload), d, int(pool_rows), ctypes.byref(h),
+                                                      ctypes.byref(ph)))
+    return int(h.value), int(ph.value)
+
+
 def header_rows(pool_rows: int, d: int, payload: Optional[str] = None) -> int:
-    """Header rows of a pool as the library lays it out: one 16-bit id per
-    data row, ``row_bytes / 2`` ids per row, at least one row."""
-    return max(1, -(-2 * int(pool_rows) // row_bytes(d, payload)))
+    """Header rows of a pool (the library's geometry query)."""
+    return pool_geometry(pool_rows, d, payload)[0]
 
 
 def pool_height(pool_rows: int, d: int, payload: Optional[str] = None) -> int:
-    """Rows of one pool: data rows plus header rows."""
-    return int(pool_rows) + header_rows(pool_rows, d, payload)
+    """Rows of one pool: data rows plus header rows (the library's query)."""
+    return pool_geometry(pool_rows, d, payload)[1]
 
 
 def pool_rows_of_height(height: int, d: int, payload: Optional[str] = None) -> int:
-    """Data rows of a pool that is ``height`` rows tall."""
-    for h in range(1, int(height) + 1):
-        if header_rows(height - h, d, payload) == h:
-            return int(height) - h
-    raise ValueError(f"no pool of row width {d} is {height} rows tall")
+    """Data rows of a pool that is ``height`` rows tall (the library's query)."""
+    p = ctypes.c_int64()
+    st = lib.moe_pool_rows_of_height(_row_code(payload), d, int(height), ctypes.byref(p))
+    if st != 0:
+        raise ValueError(f"no pool of row width {d} is {height} rows tall")
+    return int(p.value)
 
 
 def quantize_fp8(x: torch.Tensor, payload: str = "b128", rec: Optional[torch.Tensor] = None,

@@ -35,6 +35,17 @@ inline int64_t row_bytes(int32_t dtype, int64_t d) {
   }
 }
 
+// Header rows of a pool whose rows are rb bytes and which holds pool_rows
+// data rows: one 16-bit local id per data row, rb / 2 ids per header row, at
+// least one row ("Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02 and
+// 05: one packed full-width row at the page's sizes).  0 for rb < 2 or a
+// negative row count.
+inline int64_t pool_header_rows(int64_t rb, int64_t pool_rows) {
+  if (rb < 2 || pool_rows < 0) return 0;
+  const int64_t per_row = rb / 2;
+  return pool_rows > per_row ? (pool_rows + per_row - 1) / per_row : 1;
+}
+
 // float -> E4M3 (bias 7, 3 mantissa bits, largest finite 448, 0x7F NaN, no
 // infinity): nearest, ties to even, saturating at +-448, sign bit kept.
 // Normal results: round the fp32 pattern at bit 20 (half to even), which

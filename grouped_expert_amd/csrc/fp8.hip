@@ -110,6 +110,34 @@ MOE_API size_t moe_row_bytes(int32_t dtype, int32_t d) {
   return static_cast<size_t>(moe::row_bytes(dtype, d));
 }
 
+MOE_API int moe_pool_geometry(int32_t row_dtype, int32_t d, int64_t pool_rows, int64_t* header_rows,
+                              int64_t* pool_height) {
+  using namespace moe;
+  const int64_t rb = row_bytes(row_dtype, d);
+  MOE_CHECK(rb > 0 && d % 8 == 0 && pool_rows >= 0 && header_rows && pool_height, MOE_EINVAL);
+  const int64_t H = pool_header_rows(rb, pool_rows);
+  *header_rows = H;
+  *pool_height = pool_rows + H;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_rows_of_height(int32_t row_dtype, int32_t d, int64_t pool_height, int64_t* pool_rows) {
+  using namespace moe;
+  const int64_t rb = row_bytes(row_dtype, d);
+  MOE_CHECK(rb > 0 && d % 8 == 0 && pool_height >= 1 && pool_rows, MOE_EINVAL);
+  // the header grows by one row per rb / 2 data rows, so at most one data-row
+  // count fits a height; search the few header counts that can
+  const int64_t per_row = rb / 2;
+  for (int64_t h = 1; h <= pool_height && h <= pool_height / per_row + 2; ++h) {
+    const int64_t p = pool_height - h;
+    if (pool_header_rows(rb, p) == h) {
+      *pool_rows = p;
+      return MOE_OK;
+    }
+  }
+  return MOE_EINVAL;
+}
+
 MOE_API int moe_quantize_fp8(const void* x, int32_t x_dtype, int64_t n, int32_t d, int32_t rec_dtype, void* rec,
                              uint32_t* dev_flags, hipStream_t stream) {
   using namespace moe;

@@ -2,10 +2,11 @@
 //
 // "Fixed pooled-wave all-to-all for the 8-of-384 MoE", 02: the sender keeps
 // one pool per destination GPU and wave; an expert id gives a destination and
-// a local expert id; "wave = rank mod 3, pool row = rank / 3", where the rank
-// is read as the route's ordinal among this sender's routes to that
-// destination (the only reading that fits the pool shape [64, 3005, 3072]
-// per wave and the per-destination, per-wave capacity of 04); extra rows are
+// a local expert id; a route's ordinal among this sender's routes to its
+// destination picks the wave (ordinal mod n_waves) and the pool row (ordinal
+// div n_waves) -- the ordinal is the page's "rank" (the only reading that fits
+// the pool shape [64, 3005, 3072] per wave and the per-destination, per-wave
+// capacity of 04); extra rows are
 // dropped; the first full-width row of a pool carries the packed local expert
 // ids so that no count exchange is needed (reading: as many such rows as the
 // 16-bit ids need, e.g. two for the two-wave profile of 05).  Rows are bf16
@@ -294,7 +295,7 @@ MOE_API int moe_pool_pack(const void* x, int32_t x_dtype, int32_t pool_dtype, in
   const int64_t rb = row_bytes(pool_dtype, d);                    // pool row bytes, a multiple of 16 (of 128 for records)
   MOE_CHECK(rb <= INT32_MAX, MOE_EUNSUPPORTED);
   const int32_t re = static_cast<int32_t>(rb / 2);                // 16-bit elements per row
-  const int32_t H = pool_rows > re ? (pool_rows + re - 1) / re : 1;   // header rows: one 16-bit id per data row
+  const int32_t H = static_cast<int32_t>(pool_header_rows(rb, pool_rows));   // one 16-bit id per data row
   const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
   MOE_CHECK(static_cast<int64_t>(n_waves) * n_dest * P1 <= INT32_MAX, MOE_EUNSUPPORTED);
   MOE_CHECK(pools && dest_counts && sender_dropped, MOE_EINVAL);

@@ -122,7 +122,7 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n
   MOE_CHECK(pool_dtype == MOE_BF16 || is_fp8(pool_dtype), MOE_EINVAL);
   const int64_t rb = row_bytes(pool_dtype, d);                      // bytes per pool row
   const int64_t re = rb / 2;                                        // 16-bit elements per pool row
-  const int64_t H = pool_rows > re ? (static_cast<int64_t>(pool_rows) + re - 1) / re : 1;
+  const int64_t H = pool_header_rows(rb, pool_rows);
   const int64_t P1 = static_cast<int64_t>(pool_rows) + H;
   const int64_t n_rows = static_cast<int64_t>(n_src) * P1;
   MOE_CHECK(n_rows <= INT32_MAX && static_cast<int64_t>(n_local) * cap <= INT32_MAX, MOE_EUNSUPPORTED);

@@ -14,7 +14,7 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 def test_exports_every_header_symbol():
     names = B.header_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
@@ -213,3 +213,26 @@ def test_record_widths_agree_with_the_oracle_layout():
         for code, mode in ((2, "row"), (3, "b128")):
             assert lib.moe_row_bytes(code, d) == O.fp8_record_layout(d, mode)[1], (d, mode)
         assert lib.moe_row_bytes(1, d) == 2 * d and lib.moe_row_bytes(0, d) == 4 * d
+
+
+def test_pool_geometry_agrees_with_the_oracle():
+    """The library's pool geometry (header rows, pool height, and its inverse)
+    against the oracle's header-row rule, written independently, for bf16
+    rows and both fp8 record layouts."""
+    import oracle as O
+    for d in (8, 64, 136, 1024, 3072, 7168):
+        for code, payload in ((1, None), (2, "row"), (3, "b128")):
+            rb = lib.moe_row_bytes(code, d)
+            for P in (0, 1, 2, 3, rb // 2 - 1, rb // 2, rb // 2 + 1, 3004, 4506, 24030, 33497):
+                h, ph = B.pool_geometry(P, d, payload)
+                assert h == O.header_rows_bytes(P, rb), (d, payload, P)
+                assert ph == P + h
+                assert B.pool_rows_of_height(ph, d, payload) == P
+    # the pages' sizes: one header row for 3004-row pools, two for 4506 rows
+    assert B.pool_geometry(3004, 3072) == (1, 3005)
+    assert B.pool_geometry(4506, 3072) == (2, 4508)
+    h = ctypes.c_int64()
+    assert lib.moe_pool_geometry(1, 3072, -1, ctypes.byref(h), ctypes.byref(h)) == EINVAL
+    assert lib.moe_pool_geometry(9, 3072, 10, ctypes.byref(h), ctypes.byref(h)) == EINVAL
+    assert lib.moe_pool_geometry(1, 12, 10, ctypes.byref(h), ctypes.byref(h)) == EINVAL
+    assert lib.moe_pool_rows_of_height(1, 3072, 0, ctypes.byref(h)) == EINVAL
