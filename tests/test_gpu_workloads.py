@@ -2,9 +2,10 @@
 (and so the same launch configurations) that bench.py times.
 
 Integer outputs (ids, plans, pools, headers, compaction maps, drop counts) are
-compared in full and bit-exactly.  Floating-point outputs are compared on
-sampled rows that the fp64 oracle computes one by one (each expert's first and
-last row among them), with the 2e-2 per-row relative error rule."""
+compared in full and bit-exactly.  Floating-point outputs are compared with
+the 2e-2 per-row relative error rule: in full for the layer workloads (every
+expert row, every token), and for the receiver share on whole 256-row GEMM
+tiles (each expert's first and last) plus random rows of every wave."""
 import numpy as np
 import pytest
 
@@ -34,7 +35,12 @@ def _sample_rows(rng, offsets, counts, n_random):
     return np.array(sorted(rows))
 
 
-def _layer_case(ge, w, n_tok_sample, n_row_sample):
+def _layer_case(ge, w, n_tok_sample):
+    """The whole layer through the library calls bench.py times.  Integer
+    outputs bit-exactly; every expert row and every token output against the
+    oracle's expert-major evaluation (count, stable permutation, per-segment
+    SwiGLU, combine through the inverse map); a sample of tokens also against
+    the independent token-major evaluation."""
     logits = W.router_logits(w)
     x = W.tokens(w)
     wg, wu, wd = W.all_expert_weights(w)
@@ -53,24 +59,22 @@ def _layer_case(ge, w, n_tok_sample, n_row_sample):
         assert np.array_equal(to_np(gp[key]), getattr(plan, key)), key
     assert int(to_np(gp["dropped"])[0]) == plan.dropped
     A = plan.accepted
-    assert np.array_equal(to_np(gp["x_perm"])[:A], O.gather_rows(x, plan.src, w.k, A))
+    xp = O.gather_rows(x, plan.src, w.k, A)
+    assert np.array_equal(to_np(gp["x_perm"])[:A], xp)
 
     bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
+    # every packed expert row, each expert's segment run in fp64
+    want_z = O.run_segments(xp, plan.offsets[:-1], plan.counts, bank)
+    assert_rows_close(as_f64(st["z"])[:A], want_z, what="expert rows")
+    # every token: the oracle's combine of those rows through the inverse map
+    want_y = O.combine(want_z, plan.inv, gates, w.T, w.k)
+    assert_rows_close(to_np(y), want_y, what="layer output")
+    # sampled tokens against the token-major layout (no permutation at all)
     rng = np.random.default_rng(0)
-    # expert outputs on sampled packed rows
-    rows = _sample_rows(rng, plan.offsets, plan.counts, n_row_sample)
-    seg = np.searchsorted(plan.offsets, rows, side="right") - 1
-    xz = O.to_f64(O.gather_rows(x, plan.src, w.k, A)[rows])
-    want_z = np.zeros((rows.size, w.d))
-    for e in np.unique(seg):
-        m = seg == e
-        want_z[m] = bank(int(e), xz[m])
-    assert_rows_close(as_f64(st["z"])[rows], want_z, what="expert rows")
-    # layer output on sampled tokens
     tok = np.unique(np.concatenate([rng.choice(w.T, size=min(n_tok_sample, w.T), replace=False),
                                     src_tokens_of_extreme_experts(plan, w.k)]))
-    want_y = O.moe_layer_token_major(x[tok], ids[tok], gates[tok], bank, w.E)
-    assert_rows_close(to_np(y)[tok], want_y, what="layer output")
+    want_tm = O.moe_layer_token_major(x[tok], ids[tok], gates[tok], bank, w.E)
+    assert_rows_close(to_np(y)[tok], want_tm, what="layer output (token-major)")
     return plan
 
 
@@ -90,20 +94,22 @@ def test_tiny_fp32_full(ge):
     """Tiny layer: every token and every packed row against the oracle, both
     oracle layouts."""
     w = W.TINY
-    plan = _layer_case(ge, w, n_tok_sample=w.T, n_row_sample=w.R)
+    plan = _layer_case(ge, w, n_tok_sample=w.T)
     assert plan.dropped == 0
 
 
 def test_mid_bf16(ge):
+    """Mid layer: all 2,048 tokens and all 16,384 packed rows."""
     w = W.MID
-    plan = _layer_case(ge, w, n_tok_sample=96, n_row_sample=256)
+    plan = _layer_case(ge, w, n_tok_sample=96)
     assert plan.counts.max() > 3 * plan.counts.mean()          # skewed loads reached the GEMM
 
 
 def test_decode_bf16(ge):
-    """Decode: all 64 tokens; most experts hold 0-2 rows."""
+    """Decode: all 64 tokens and all 512 packed rows; most experts hold 0-2
+    rows."""
     w = W.DECODE
-    plan = _layer_case(ge, w, n_tok_sample=w.T, n_row_sample=64)
+    plan = _layer_case(ge, w, n_tok_sample=16)
     assert (plan.counts == 0).sum() > 50 and plan.counts.max() <= 8
 
 
@@ -150,6 +156,25 @@ def test_mid_bf16_backward(ge):
         _, (dwg, dwu, dwd) = O.swiglu_expert_backward(xf[t], g64[t, j, None] * dyf[t], *W64(e))
         for name, want in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
             assert_rows_close(to_np(gr[name][e]).astype(np.float64), want, what=f"{name}[{e}]")
+
+
+def test_router_v3_full(ge):
+    """The V3 router at its workload's full size (65,536 tokens, 256 experts in
+    8 groups, keep 4, top-8, scale 2.5, an N(0, 0.05) selection bias): every
+    token's ids exactly (a token holding an fp32 affinity too close to a
+    rounding midpoint to call may take either rounding's ids), every gate."""
+    from tests.test_gpu_ops import _v3_exact
+    w = W.ROUTER_V3
+    z = W.router_logits(w)
+    bias = W.router_bias(w)
+    flags = ge.new_flags("cuda")
+    ids, gw = ge.route_topk_grouped(to_gpu(z), w.k, w.gating, w.n_group, w.topk_group, w.route_scale,
+                                    bias=to_gpu(bias), flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+    inv, named = _v3_exact(z, bias, to_np(ids), to_np(gw), w.k, w.n_group, w.topk_group, w.route_scale)
+    assert not inv.any()
+    print(f"router_v3_f32: tokens with an ambiguous fp32 affinity: {named}")
 
 
 @pytest.fixture(scope="module", params=["sender_pack_bf16", "sender_pack_2w_bf16", "sender_pack_fp8"])
@@ -207,8 +232,10 @@ def test_recv_share(ge, name, rotation):
     """Receiver share: three waves of 64 x 3004 incoming rows, six local
     experts, capacity 33,497, sources in the fixed order; or the two-wave
     profile (64 x 4506 rows behind two header rows, capacity 50,245) with the
-    sources visited from source 17.  Wave 0's compaction in full; all waves'
-    counters; expert outputs and the fp32 expansion on sampled rows."""
+    sources visited from source 17.  Every wave: the compaction byte for byte,
+    all counters and row slots; expert outputs on whole 256-row GEMM tiles
+    (each expert's first and last tile) plus random rows; the fp32 expansion
+    of those rows, and zero rows for dropped ones."""
     w = W.WORKLOADS[name]
     wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
     bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
@@ -220,46 +247,52 @@ def test_recv_share(ge, name, rotation):
     starts = torch.arange(L, dtype=torch.int32, device="cuda") * cap
     rng = np.random.default_rng(1)
     total_drop = 0
+    TILE = 256
     for wave in range(w.n_waves):
         pools = W.recv_pools(w, wave)
         flags = ge.new_flags("cuda")
         assert pools.shape == (S, P1, d)
+        print(f"{name} wave {wave}: compact, GEMM, expand", flush=True)
         rc = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags, rotation=rotation)
         ge.grouped_swiglu(compact.view(L * cap, d), starts, rc["counts"], *gw, z=z, flags=flags)
         ret = ge.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, flags=flags)
         torch.cuda.synchronize()
         assert int(to_np(flags)[0]) == 0
-        orc = O.recv_compact(pools, L, cap, with_rows=(wave == 0), rotation=rotation)
+        orc = O.recv_compact(pools, L, cap, with_rows=True, rotation=rotation)
         counts = to_np(rc["counts"])
         assert np.array_equal(counts, orc["counts"])
         assert np.array_equal(to_np(rc["arrived"]), orc["arrived"])
         assert np.array_equal(to_np(rc["row_slot"]), orc["row_slot"])
         assert int(to_np(rc["recv_dropped"])[0]) == orc["recv_dropped"]
         total_drop += orc["recv_dropped"]
-        if wave == 0:
-            for h in range(L):
-                n = int(counts[h])
-                assert np.array_equal(to_np(compact[h, :n]), orc["compact"][h, :n]), h
-        # sampled expert rows (first / last / random per expert) and their expansion
-        slots, srcrows = [], []
-        row_slot = orc["row_slot"]
         for h in range(L):
             n = int(counts[h])
-            pick = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=6)]))
-            for q in pick:
-                slots.append(h * cap + q)
+            assert np.array_equal(to_np(compact[h, :n]), orc["compact"][h, :n]), (wave, h)
+        # whole GEMM tiles (first and last of each expert) and random rows
+        slots = []
+        for h in range(L):
+            n = int(counts[h])
+            last = (n - 1) // TILE * TILE
+            pick = np.unique(np.concatenate([np.arange(0, min(TILE, n)), np.arange(last, n),
+                                             rng.integers(0, n, size=32)]))
+            slots.extend((h * cap + pick).tolist())
         slots = np.array(slots)
-        inv_slot = {int(s): i for i, s in enumerate(row_slot) if s >= 0}
-        srcrows = np.array([inv_slot[int(s)] for s in slots])
-        xin = O.to_f64(pools.reshape(-1, d)[srcrows])
+        row_slot = orc["row_slot"]
+        inv_slot = np.full(L * cap, -1, dtype=np.int64)
+        live = np.nonzero(row_slot >= 0)[0]
+        inv_slot[row_slot[live]] = live
+        srcrows = inv_slot[slots]
+        assert np.all(srcrows >= 0)
         want = np.zeros((slots.size, d))
         for h in range(L):
             m = slots // cap == h
-            want[m] = bank(h, xin[m])
-        assert_rows_close(to_np(z)[slots], want, what=f"wave {wave} expert rows")
-        assert np.array_equal(to_np(ret)[srcrows], to_np(z)[slots])           # expansion is a copy
-        dropped_rows = np.nonzero(row_slot < 0)[0][:64]
-        assert np.all(to_np(ret)[dropped_rows] == 0)
+            want[m] = bank(h, O.to_f64(orc["compact"][h, slots[m] - h * cap]))
+        zs = to_np(z[to_gpu(slots)])
+        assert_rows_close(zs, want, what=f"wave {wave} expert rows")
+        assert np.array_equal(to_np(ret[to_gpu(srcrows)]), zs)                  # expansion is a copy
+        dropped_rows = np.nonzero(row_slot < 0)[0]
+        assert np.all(to_np(ret[to_gpu(dropped_rows)]) == 0)
+        del orc
     assert total_drop > 0
 
 
