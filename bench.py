@@ -4,18 +4,23 @@
 One step is one pass of the layer over one synthetic batch that is already
 resident in HBM:
 
-* layer workloads (mid_bf16 = the default, tiny_fp32, decode_bf16):
+* recv_share_bf16 (the default: the largest workload one GPU holds, one
+  GPU's receiver share of the 8-of-384 design): three waves of receiver
+  compaction -> grouped SwiGLU over the static per-expert arrays ->
+  expansion to pool rows (fp32);
+* layer workloads (mid_bf16, tiny_fp32, decode_bf16):
   route -> permute -> grouped SwiGLU -> un-permute/combine;
-* recv_share_bf16: three waves of receiver compaction -> grouped SwiGLU over
-  the static per-expert arrays -> expansion to pool rows (fp32);
 * sender_pack_bf16: route -> pooled-wave pack of all three waves.
 
 Inputs rotate over ``--banks`` independent copies (distinct HBM addresses) so
 that no step finds the previous step's operands in the 256 MB last-level
 cache.  Every call is timed with HIP events on the stream it runs on; the
-JSON line reports whole-step throughput, the roofline of the dominant call
-(algorithmic bytes or flops per launch over its measured duration) and the
-CPU oracle timed on a bounded sample of the same workload.
+JSON line reports whole-step throughput (mean, and the nearest-rank median
+and 95th percentile of the per-step times), the roofline of the dominant
+call (algorithmic bytes or flops per launch over its measured duration, with
+the HBM traffic and MFMA busy fraction that rocprofv3 counters recorded for
+the same kernel sources) and the CPU oracle timed on a bounded sample of the
+same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -43,6 +48,7 @@ COPY_CALIB_BYTES = 256 << 20   # size of the calibration copy (read and written 
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy.json")
 CSRC_DIR = os.path.join(ROOT, "grouped_expert_amd", "csrc")
 
 
@@ -51,16 +57,22 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="mid_bf16", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="recv_share_bf16", choices=sorted(W.WORKLOADS))
     ap.add_argument("--banks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens/rows of the CPU oracle sample (0 = auto)")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="CPU oracle sample: tokens (layer, pack, router workloads) or waves (receiver workloads); "
+                         "0 = the default")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: read the counter CSVs of two rocprofv3 --pmc runs of this script "
                          "(FETCH_SIZE, then WRITE_SIZE) for --workload and record HBM bytes per call in "
                          "profiles/hbm_traffic.json")
-    ap.add_argument("--pmc-command", default="", help="with --record-traffic: the profiling command, stored "
-                                                      "beside the figures")
+    ap.add_argument("--record-mfma", metavar="PMC_DIR",
+                    help="no benchmark: read the counter CSV of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE run of this script for --workload and record the MFMA busy fraction "
+                         "of each GEMM call in profiles/mfma_busy.json")
+    ap.add_argument("--pmc-command", default="", help="with --record-traffic / --record-mfma: the profiling "
+                                                      "command, stored beside the figures")
     return ap.parse_args()
 
 
@@ -175,6 +187,76 @@ def record_traffic(args):
     print(json.dumps({w.name: entry}, indent=1))
 
 
+def record_mfma(args):
+    """MFMA busy fraction of the GEMM calls of one workload from a rocprofv3
+    --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run of this script.
+
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over every CU and counts each of a
+    CU's four SIMDs; GRBM_GUI_ACTIVE is summed over the XCDs.  Busy fraction
+    of a dispatch = MFMA_BUSY / (GRBM_GUI_ACTIVE / XCDs * CUs * 4), i.e. the
+    share of SIMD cycles the matrix cores were busy, at the clock the GPU ran
+    (not the 2.4 GHz the published peak assumes).  Per call: cycle-weighted
+    over its dispatches after the first library call (the untimed set-up is
+    excluded)."""
+    import csv
+    w = W.WORKLOADS[args.workload]
+    d = args.record_mfma
+    agent = [r for r in csv.DictReader(open(os.path.join(d, "run_agent_info.csv"))) if r["Agent_Type"] == "GPU"][0]
+    cus, xcds, simds = int(agent["Cu_Count"]), int(agent["Num_Xcc"]), int(agent["Simd_Per_Cu"])
+    rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+    by_disp = {}
+    for r in rows:
+        e = by_disp.setdefault(int(r["Dispatch_Id"]), dict(name=r["Kernel_Name"]))
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+        e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    order = sorted(by_disp)
+    lead = "recv_compact" if workload_kind(w) == "recv" else "route"
+    first = next(i for i in order if _call_of(by_disp[i]["name"]) == lead)
+    acc = {}
+    for i in order:
+        if i < first:
+            continue
+        e = by_disp[i]
+        c = _call_of(e["name"], train=w.train)
+        if c not in ("swiglu", "swiglu_bwd") or "grouped_gemm_" not in e["name"]:
+            continue
+        m = re.search(r"Cfg<([^<>]*)>", e["name"])
+        kind = "gate_up" if m and m.group(1).split(", ")[5] == "true" else "down_or_other"
+        for key in (c, f"{c}:{kind}"):
+            a = acc.setdefault(key, dict(busy=0.0, avail=0.0, n=0, ns=0))
+            a["busy"] += e["SQ_VALU_MFMA_BUSY_CYCLES"]
+            a["avail"] += e["GRBM_GUI_ACTIVE"] / xcds * cus * simds
+            a["n"] += 1
+            a["ns"] += e["ns"]
+    entry = dict(command=args.pmc_command, formula="SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * CUs * 4)",
+                 cus=cus, xcds=xcds,
+                 calls={k: dict(sources_sha256=sources_digest(k.split(":")[0]), mfma_busy=round(a["busy"] / a["avail"], 4),
+                                dispatches=a["n"], mean_dispatch_ms=round(a["ns"] / a["n"] / 1e6, 4))
+                        for k, a in sorted(acc.items())})
+    data = {}
+    if os.path.exists(MFMA_FILE):
+        with open(MFMA_FILE) as f:
+            data = json.load(f)
+    data[w.name] = entry
+    with open(MFMA_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({w.name: entry}, indent=1))
+
+
+def recorded_mfma(w, call):
+    """MFMA busy fraction recorded for ``call`` of this workload, or None when
+    nothing is recorded or the kernel sources changed since."""
+    try:
+        with open(MFMA_FILE) as f:
+            c = json.load(f)[w.name]["calls"].get(call)
+    except (OSError, KeyError, ValueError):
+        return None
+    if not c or c.get("sources_sha256") != sources_digest(call):
+        return None
+    return c["mfma_busy"]
+
+
 def recorded_traffic(w, call):
     """HBM bytes per launch of ``call`` recorded for this workload, or None
     when nothing is recorded or the kernel sources changed since."""
@@ -244,6 +326,51 @@ def cpu_threads():
         return int(max(n)) if n else 1
     except Exception:
         return os.cpu_count() or 1
+
+
+def cpu_host_info():
+    """CPU model, host CPU count and the BLAS library numpy runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            p = libs[0]
+            blas = f"{p.get('internal_api')} {p.get('version')} ({os.path.basename(p.get('filepath', ''))}, " \
+                   f"{p.get('threading_layer', 'n/a')} threading, {p.get('num_threads')} threads)"
+    except Exception:
+        pass
+    return dict(cpu_model=model, host_cpus=os.cpu_count(), blas=blas)
+
+
+def input_sha256(host):
+    """SHA-256 over the host input arrays (sorted by name, lists in order):
+    the bytes both the GPU (after one copy) and the oracle consume."""
+    import hashlib
+    h = hashlib.sha256()
+    for k in sorted(host):
+        for a in (host[k] if isinstance(host[k], list) else [host[k]]):
+            a = np.ascontiguousarray(a)
+            h.update(k.encode())
+            h.update(str(a.dtype).encode() + str(a.shape).encode())
+            h.update(memoryview(a.reshape(-1).view(np.uint8)))
+    return h.hexdigest()
+
+
+def nearest_rank(vals, q):
+    """Nearest-rank percentile q (0 < q <= 100) of a list."""
+    v = sorted(vals)
+    i = max(1, int(np.ceil(q / 100.0 * len(v))))
+    return v[i - 1]
 
 
 # ---------------------------------------------------------------------------
@@ -428,32 +555,37 @@ def recv_ledger(w, counts_per_wave):
 
 
 def recv_cpu_baseline(w, host, sample):
-    """Oracle compaction of one wave (integer part in full, rows copied) plus
-    the fp64 SwiGLU of the first ``sample`` accepted rows."""
+    """The oracle's receiver step on the first waves of the batch, in full:
+    compaction of every incoming row, the fp64 SwiGLU of every accepted row
+    (fp8 records quantized and dequantized first), and the expansion back to
+    pool rows.  ``sample`` is the number of waves (about 5 s of CPU each)."""
     import oracle as O
+    n_w = max(1, min(sample, w.n_waves))
     t0 = time.perf_counter()
-    rc = O.recv_compact(host["pools"][0], w.n_local, w.recv_cap)
-    comp = rc["compact"]
-    if w.payload is not None:                   # the records of the sampled rows: quantize and dequantize
-        flat = comp.reshape(-1, w.d)[:sample]
-        rec = O.quantize_fp8_rows(O.to_f64(flat).astype(np.float32), w.payload)
-        comp = comp.copy()
-        comp.reshape(-1, w.d)[:sample] = O.f32_to_bf16_rne(O.dequantize_fp8_rows(rec, w.d, w.payload))
-    n = 0
-    for e in range(w.n_local):
-        take = min(int(rc["counts"][e]), max(0, sample - n))
-        if take == 0:
-            continue
-        O.swiglu_expert(O.to_f64(comp[e, :take]), O.to_f64(host["wg"][e]), O.to_f64(host["wu"][e]),
-                        O.to_f64(host["wd"][e]))
-        n += take
+    acc = 0
+    for wave in range(n_w):
+        rc = O.recv_compact(host["pools"][wave], w.n_local, w.recv_cap)
+        comp = rc["compact"]
+        z = np.zeros((w.n_local * w.recv_cap, w.d))
+        for e in range(w.n_local):
+            c = int(rc["counts"][e])
+            if c == 0:
+                continue
+            xr = comp[e, :c]
+            if w.payload is not None:
+                rec = O.quantize_fp8_rows(O.to_f64(xr).astype(np.float32), w.payload)
+                xr = O.f32_to_bf16_rne(O.dequantize_fp8_rows(rec, w.d, w.payload))
+            z[e * w.recv_cap:e * w.recv_cap + c] = O.swiglu_expert(
+                O.to_f64(xr), O.to_f64(host["wg"][e]), O.to_f64(host["wu"][e]), O.to_f64(host["wd"][e]))
+        O.expand_rows(z, rc["row_slot"])
+        acc += int(rc["counts"].sum())
     dt = time.perf_counter() - t0
-    return dict(value=w.n_src * w.pool_rows / dt if n >= int(rc["counts"].sum()) else n / dt,
-                unit="incoming rows/s", cores=cpu_threads(), kind="oracle",
-                sample=f"wave 0 compaction of {w.n_src}x{w.pool_rows} rows"
-                       + (f", fp8 quantize + dequantize of {sample} rows" if w.payload else "")
-                       + f" plus fp64 SwiGLU of {n} accepted rows; "
-                       f"rate = SwiGLU rows / {dt:.2f} s")
+    return dict(value=n_w * w.n_src * w.pool_rows / dt, unit="incoming rows/s", cores=cpu_threads(), kind="oracle",
+                extrapolated=False,
+                sample=f"waves 0..{n_w - 1} of {w.name} in full: oracle compaction of {n_w}x{w.n_src}x{w.pool_rows} "
+                       f"incoming rows, "
+                       + ("fp8 quantize + dequantize and " if w.payload else "")
+                       + f"fp64 SwiGLU of all {acc} accepted rows, expansion to pool rows; {dt:.2f} s")
 
 
 def pack_setup(torch, w, banks):
@@ -541,6 +673,9 @@ def main():
     if args.record_traffic:
         record_traffic(args)
         return
+    if args.record_mfma:
+        record_mfma(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -612,19 +747,21 @@ def main():
 
     # timed steps: events around the dominant call only (its launch duration,
     # live over the timed region, on the stream it runs on)
+    # an event at every step boundary gives the per-step times (p50 / p95)
     timer = OpTimer(torch, only={dom})
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
+    marks[0].record()
     for i in range(args.steps):
         last = step(timer, bank_list[i % banks])
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
+    total_ms = marks[0].elapsed_time(marks[-1])
     ms_per_step = total_ms / max(1, args.steps)
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     dom_launches = timer.totals_ms()[dom]
     if int(flags.item()) != 0:
         print(f"[bench] warning: dev_flags = {int(flags.item())}", file=sys.stderr)
@@ -666,6 +803,10 @@ def main():
         roof = dict(bound="hbm", achieved=round(bw, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(bw / HBM_PEAK_GBS, 4), traffic=traffic)
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    if dom in ("swiglu", "swiglu_bwd"):
+        roof["mfma_busy"] = recorded_mfma(w, dom)
+        roof["mfma_busy_formula"] = "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * CUs * 4), rocprofv3"
+        roof["mfma_frac_of_peak"] = round(tf / BF16_PEAK_TFLOPS, 4) if w.dtype != "f32" else None
     if traffic:
         roof["traffic_over_alg"] = round(traffic / max(1, per_launch_bytes), 3)
     roof["kernel"] = dom
@@ -682,11 +823,14 @@ def main():
         elif kind == "train":
             cpu = train_cpu_baseline(w, host, args.cpu_sample or min(w.T, 512))
         elif kind == "recv":
-            cpu = recv_cpu_baseline(w, host, args.cpu_sample or 4096)
+            cpu = recv_cpu_baseline(w, host, args.cpu_sample or 2)
         elif kind == "router":
             cpu = router_cpu_baseline(w, host, args.cpu_sample or 32768)
         else:
             cpu = pack_cpu_baseline(w, host, args.cpu_sample or 16384)
+        cpu.setdefault("extrapolated", False)
+        cpu.update(cpu_host_info())
+        cpu["input_sha256"] = input_sha256(host)
 
     cfg = {"workload": w.name, "dtype": w.dtype}
     for key in ("T", "d", "E", "k", "d_ff", "capacity", "experts_per_dest", "n_dest", "n_waves", "pool_rows",
@@ -701,7 +845,9 @@ def main():
            for k in per_op}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_p50": round(nearest_rank(step_ms, 50), 4), "ms_per_step_p95": round(nearest_rank(step_ms, 95), 4),
+        "timed_ms": round(total_ms, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu, "ops": ops,
         "ops_note": f"per-call ms from {n_probe} untimed steps with events around every call",

@@ -110,3 +110,55 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
     assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 180.0 + 12.0 + 400.0) * 1024)
     assert c["combine"]["write_bytes"] == int(5.0 * 1024) and c["dx_combine"]["write_bytes"] == int(9.0 * 1024)
     assert c["combine_bwd"]["read_bytes"] == int(7.0 * 1024 * 2)
+
+
+def test_record_mfma_busy_fraction(tmp_path, monkeypatch):
+    """Busy fraction = MFMA busy cycles over (GUI-active cycles per XCD x CUs x
+    4 SIMDs), cycle-weighted per call, set-up dispatches excluded."""
+    d = tmp_path / "m"
+    os.makedirs(d)
+    with open(d / "run_agent_info.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Agent_Type", "Cu_Count", "Num_Xcc", "Simd_Per_Cu"])
+        wr.writeheader()
+        wr.writerow({"Agent_Type": "CPU", "Cu_Count": 0, "Num_Xcc": 1, "Simd_Per_Cu": 0})
+        wr.writerow({"Agent_Type": "GPU", "Cu_Count": 256, "Num_Xcc": 8, "Simd_Per_Cu": 4})
+    gu = "void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<moe::(anonymous namespace)::Cfg<256, 256, 4, " \
+         "2, 2, true, false, false, 64, 1, 4, 8, true, 0, false> >(x)"
+    dn = gu.replace("2, 2, true, false, false", "2, 2, false, true, false")
+    disp = [(gu, 1e9, 8e6)]                       # set-up call before the first library call: excluded
+    disp += [("moe::(anonymous namespace)::compact_rows_kernel(x)", 0.0, 1e6), (gu, 0.5 * 1e6 * 1024, 8e6),
+             (dn, 0.25 * 1e6 * 1024, 8e6)]
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=fields)
+        wr.writeheader()
+        for i, (name, busy, gui) in enumerate(disp, start=1):
+            for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", gui)):
+                wr.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v,
+                             "Start_Timestamp": 0, "End_Timestamp": 1000})
+    out = tmp_path / "mfma.json"
+    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "recv_share_bf16", "--record-mfma", str(d)])
+    bench.record_mfma(bench.parse())
+    c = json.load(open(out))["recv_share_bf16"]["calls"]
+    # per XCD 1e6 GUI cycles, 1024 SIMDs: busy 0.5 for gate/up, 0.25 for down, 0.375 together
+    assert c["swiglu:gate_up"]["mfma_busy"] == pytest.approx(0.5)
+    assert c["swiglu:down_or_other"]["mfma_busy"] == pytest.approx(0.25)
+    assert c["swiglu"]["mfma_busy"] == pytest.approx(0.375)
+    assert c["swiglu"]["dispatches"] == 2
+    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
+    assert bench.recorded_mfma(bench.W.WORKLOADS["recv_share_bf16"], "swiglu") == pytest.approx(0.375)
+
+
+def test_nearest_rank_and_input_hash():
+    import numpy as np
+    v = [5.0, 1.0, 4.0, 2.0, 3.0]
+    assert bench.nearest_rank(v, 50) == 3.0
+    assert bench.nearest_rank(v, 95) == 5.0
+    assert bench.nearest_rank(list(range(1, 101)), 95) == 95
+    a = {"x": np.arange(6, dtype=np.uint16).reshape(2, 3), "p": [np.zeros(3, np.float32), np.ones(2, np.float32)]}
+    h1 = bench.input_sha256(a)
+    a["p"][1][0] = 2.0
+    assert bench.input_sha256(a) != h1
+    info = bench.cpu_host_info()
+    assert set(info) == {"cpu_model", "host_cpus", "blas"}
