@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(HERE, "libgrouped_expert_amd.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_F32, MOE_BF16, MOE_FP8_ROW, MOE_FP8_B128 = 0, 1, 2, 3
+MOE_ESCRATCH = -5
+PERMUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
 FP8_CODES = {"row": MOE_FP8_ROW, "b128": MOE_FP8_B128}
 MOE_GATING_SOFTMAX_TOPK_RENORM = 0
 MOE_GATING_SOFTMAX_TOPK = 1                 # V1
@@ -46,6 +48,8 @@ _SIGS = {
     "moe_permute_workspace": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p, _p,
                                    _p, _sz, _p, _p]),
+    "moe_permute_noalloc": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p,
+                                           _p, _p, _p]),
     "moe_grouped_swiglu_workspace": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_grouped_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _i32, _p,
                                           _sz, _p, _p]),
@@ -238,6 +242,34 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity:
                                           _ptr(offsets), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags),
                                           _stream(dev)))
     return dict(x_perm=xp, src=src, inv=inv, sel=sel, counts=counts, offsets=offsets, dropped=dropped)
+
+
+def permute_noalloc(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, capacity: int = -1,
+                    out: Optional[dict] = None, flags: Optional[torch.Tensor] = None):
+    """:func:`permute` through the entry point that allocates nothing (its
+    rank table is the library's static per-GPU scratch).  ``out`` may hold
+    preallocated outputs (keys of :func:`permute`'s result); missing ones are
+    allocated here, by torch, before the call."""
+    _expect("topk_ids", topk_ids, (None, None), torch.int32)
+    _flags_ok(flags)
+    _need_gpu(x, topk_ids, flags)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    R = T * k
+    o = dict(out or {})
+    if x is not None:
+        _expect("x", x, (T, None), _FLOATS)
+        o.setdefault("x_perm", torch.empty((R, x.shape[1]), dtype=x.dtype, device=dev))
+        _expect("x_perm", o["x_perm"], (R, x.shape[1]), x.dtype)
+    for name, n in (("src", R), ("inv", R), ("sel", E), ("counts", E), ("offsets", E + 1), ("dropped", 1)):
+        o.setdefault(name, torch.empty(n, dtype=torch.int32, device=dev))
+        _expect(name, o[name], None, torch.int32, n)
+    dt, dd = (_dtype_code(x), x.shape[1]) if x is not None else (MOE_BF16, 0)
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        _ptr(x), dt, T, dd, _ptr(topk_ids), k, E, capacity, _ptr(o.get("x_perm")), _ptr(o["src"]), _ptr(o["inv"]),
+        _ptr(o["sel"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["dropped"]), _ptr(flags), _stream(dev)))
+    o.setdefault("x_perm", None)
+    return o
 
 
 def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor, w_gate: torch.Tensor,

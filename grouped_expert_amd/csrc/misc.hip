@@ -8,6 +8,7 @@ MOE_API const char* moe_strerror(int status) {
     case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_EHIP: return "HIP runtime error";
+    case MOE_ESCRATCH: return "problem needs more scratch than the no-allocation entry point holds (4 MiB)";
     default: return "unknown status";
   }
 }

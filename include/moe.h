@@ -57,7 +57,8 @@ typedef enum {
   MOE_EINVAL = -1,        /* bad argument */
   MOE_EUNSUPPORTED = -2,  /* valid but not supported by this build (shape / dtype) */
   MOE_EWORKSPACE = -3,    /* workspace missing or smaller than the query returns */
-  MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+  MOE_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  MOE_ESCRATCH = -5       /* larger than the static scratch of moe_permute_noalloc */
 } moe_status;
 
 /* Row storage.  MOE_FP8_ROW / MOE_FP8_B128 are fp8 dispatch records
@@ -257,6 +258,32 @@ int moe_permute(const void* x, int32_t x_dtype, int64_t T, int32_t d,
                 void* x_perm, int32_t* src, int32_t* inv,
                 int32_t* sel_counts, int32_t* counts, int32_t* offsets, int32_t* n_dropped,
                 void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute that allocates nothing and takes no
+ * workspace.
+ *
+ * For callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics, outputs and errors as moe_permute, without ws /
+ * ws_bytes.  The bucket-rank table lives in a static device array of
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES bytes that each GPU the library runs on
+ * holds until the process ends; a problem whose moe_permute_workspace(T, k,
+ * E) exceeds it returns MOE_ESCRATCH before anything is enqueued.  The call
+ * never calls hipMalloc / hipFree.  The array's device address is looked up
+ * once per device (hipGetSymbolAddress, with the stream's device current)
+ * on the first call there; MOE_EHIP if that fails.
+ * Every call on one GPU uses that GPU's single array: calls whose work
+ * overlaps in time on one GPU (different streams, or host threads without
+ * ordering) race and give wrong results; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start at zero (every entry a call
+ * reads was written earlier in the same call).
+ * ------------------------------------------------------------------------- */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_permute_noalloc(const void* x, int32_t x_dtype, int64_t T, int32_t d,
+                        const int32_t* topk_ids, int32_t k, int32_t E, int64_t capacity,
+                        void* x_perm, int32_t* src, int32_t* inv, int32_t* sel_counts, int32_t* counts,
+                        int32_t* offsets, int32_t* n_dropped, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_grouped_swiglu -- bias-free SwiGLU experts over ragged row segments.

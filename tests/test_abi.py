@@ -14,7 +14,7 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 def test_exports_every_header_symbol():
     names = B.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
@@ -236,3 +236,18 @@ def test_pool_geometry_agrees_with_the_oracle():
     assert lib.moe_pool_geometry(9, 3072, 10, ctypes.byref(h), ctypes.byref(h)) == EINVAL
     assert lib.moe_pool_geometry(1, 12, 10, ctypes.byref(h), ctypes.byref(h)) == EINVAL
     assert lib.moe_pool_rows_of_height(1, 3072, 0, ctypes.byref(h)) == EINVAL
+
+
+def test_permute_noalloc_validation():
+    """Host checks of the no-allocation permute: the permute's own argument
+    rules, and MOE_ESCRATCH (before any HIP call) when the rank table would
+    not fit the static scratch."""
+    p, _keep = _fake()
+    ESCRATCH = B.MOE_ESCRATCH
+    assert lib.moe_permute_noalloc(p, 1, 10, 8, p, 0, 8, -1, p, p, p, p, p, p, p, NULL, NULL) == EINVAL   # k < 1
+    assert lib.moe_permute_noalloc(p, 1, 10, 8, p, 2, 8, -2, p, p, p, p, p, p, p, NULL, NULL) == EINVAL   # capacity
+    assert lib.moe_permute_noalloc(p, 1, 10, 8, p, 2, 8, -1, p, p, p, p, NULL, p, p, NULL, NULL) == EINVAL
+    big_T, k, E = 1 << 20, 8, 1024
+    assert lib.moe_permute_workspace(big_T, k, E) > B.PERMUTE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_permute_noalloc(p, 1, big_T, 8, p, k, E, -1, NULL, p, p, p, p, p, p, NULL, NULL) == ESCRATCH
+    assert "scratch" in B.strerror(ESCRATCH)
