@@ -122,64 +122,296 @@ __device__ __forceinline__ void select_topk(uint32_t (&key)[V], int k, int lane,
   }
 }
 
-// full_mass = 0: gates renormalised over the k kept experts;
-// full_mass = 1 (V1): gates are the kept full-softmax probabilities.
-template <int V>
-__global__ __launch_bounds__(kTokensPerBlock * kWave) void route_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t full_mass, int32_t* __restrict__ ids,
-    float* __restrict__ weights, uint32_t* flags) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / kWave;
-  if (t >= T) return;                                   // whole wavefront leaves together
-  const float* row = logits + t * E;
+// ---------------------------------------------------------------------------
+// moe_route_topk: L lanes per token (L = 1..16, a power of two), V logits per
+// lane (expert e = 4 (l + L j) + q for value v = 4 j + q with 16-byte loads,
+// or e = l + L v with 4-byte loads), KL = the power of two >= k.
+//
+// 1. Each lane keeps the KL largest of its values as a sorted list: inserting
+//    x into a descending list a is a'_0 = max(a_0, x), a'_i = med3(a_{i-1},
+//    a_i, x) -- one v_med3_f32 per list entry and value, no data-dependent
+//    branch.
+// 2. log2(L) butterfly steps merge the lists of a token's lanes (the partner's
+//    list arrives through a DPP lane permutation): c_i = max(a_i,
+//    b_{KL-1-i}) is a bitonic sequence holding the KL largest of both, and
+//    log2(KL) half-cleaner stages sort it.  Every lane of the token then holds
+//    the token's KL largest values t_0 >= ... >= t_{KL-1}, ties included.
+// 3. With tau = t_{k-1}, every value >= tau is a candidate; each lane writes
+//    its candidates (value, expert) to its LDS slots.  If the token has
+//    exactly k candidates and t_0 > t_1 > ... > t_{k-1}, candidate x takes
+//    slot #{i < k : t_i > x}, which is its rank (no two candidates are equal).
+// 4. Otherwise (equal values among or at the boundary of the k largest) the
+//    token takes k exact rounds over its lanes: the largest remaining value,
+//    then the lowest expert holding it (ties to the lower expert).
+// Values are compared as fp32 numbers (-0 == +0); a token with a NaN or
+// infinite logit gets ids -1 and weights 0.
+constexpr int kRouteThreads = 256;
+// Padding past the last expert: finite (so x * 0 stays 0) and below every
+// finite logit but -FLT_MAX itself, which it ties with; a tie puts the lower
+// (real) expert first, and k <= E real experts always exist.
+constexpr float kPad = -3.402823466e+38f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-  // key[v]: order key of expert lane + 64 v (0 = no expert; a finite or
-  // infinite logit has a key >= 0x007FFFFF); zf[v] the logit itself
-  uint32_t key[V];
-  float zf[V];
-  bool bad = false;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = lane + v * kWave;
-    key[v] = 0;
-    zf[v] = -INFINITY;
-    if (e < E) {
-      const float z = row[e];
-      bad |= !isfinite(z);
-      key[v] = order_key(z);
-      zf[v] = z;
-    }
-  }
-  const bool token_bad = ballot(bad) != 0;
-
-  uint32_t mine_key, top_key;
-  int32_t mine_e;
-  select_topk<V>(key, k, lane, mine_key, mine_e, top_key);
-
-  const float z = key_value(mine_key);
-  const float z0 = key_value(top_key);
-  const float p = lane < k ? expf(z - z0) : 0.0f;
-  float mass = 0.0f;
-  if (full_mass) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) mass += expf(zf[v] - z0);
-  } else {
-    mass = p;
-  }
-  const float s = wave_sum_f32(mass);
-  if (lane < k) {
-    ids[t * k + lane] = token_bad ? -1 : mine_e;
-    weights[t * k + lane] = token_bad ? 0.0f : p / s;
-  }
-  if (token_bad && lane == 0) flag_or(flags, MOE_FLAG_NONFINITE_LOGIT);
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
-template <int V>
-void launch(const float* logits, int64_t T, int32_t E, int32_t k, int32_t full_mass, int32_t* ids, float* w,
-            uint32_t* flags, hipStream_t s) {
-  const unsigned blocks = static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock);
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(route_topk_kernel<V>), dim3(blocks), dim3(kTokensPerBlock * kWave), 0, s,
-                     logits, T, E, k, full_mass, ids, w, flags);
+// Butterfly partner patterns inside a 16-lane row: xor 1, xor 2, then the
+// half-row mirror (i <-> 7 - i) and the row mirror (i <-> 15 - i), which pair
+// the two merged halves of 8- and 16-lane groups.
+template <int STEP>
+struct Partner;
+template <> struct Partner<0> { static constexpr int C = 0xB1; };
+template <> struct Partner<1> { static constexpr int C = 0x4E; };
+template <> struct Partner<2> { static constexpr int C = 0x141; };
+template <> struct Partner<3> { static constexpr int C = 0x140; };
+
+// max / min as one v_med3_f32 each (fmaxf / fminf would first quiet every
+// operand; NaN tokens are detected separately and their selection discarded)
+__device__ __forceinline__ float fmax1(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+__device__ __forceinline__ float fmin1(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
+
+template <int KL, int STEP>
+__device__ __forceinline__ void merge_step(float (&a)[KL]) {
+  constexpr int CT = Partner<STEP>::C;
+  float c[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) c[i] = fmax1(a[i], dppf<CT>(a[KL - 1 - i]));
+#pragma unroll
+  for (int st = KL / 2; st >= 1; st /= 2)
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+      if ((i & st) == 0) {
+        const float hi = fmax1(c[i], c[i + st]), lo = fmin1(c[i], c[i + st]);
+        c[i] = hi;
+        c[i + st] = lo;
+      }
+#pragma unroll
+  for (int i = 0; i < KL; ++i) a[i] = c[i];
+}
+
+template <int STEP>
+__device__ __forceinline__ float group_sum_step(float v) { return v + dppf<Partner<STEP>::C>(v); }
+template <int STEP>
+__device__ __forceinline__ int group_isum_step(int v) { return v + dppi<Partner<STEP>::C>(v); }
+template <int STEP>
+__device__ __forceinline__ float group_max_step(float v) { return fmax1(v, dppf<Partner<STEP>::C>(v)); }
+template <int STEP>
+__device__ __forceinline__ int group_imin_step(int v) {
+  const int o = dppi<Partner<STEP>::C>(v);
+  return o < v ? o : v;
+}
+
+// reductions over the L lanes of a token (L a power of two, 1..16)
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if (L >= 2) v = group_sum_step<0>(v);
+  if (L >= 4) v = group_sum_step<1>(v);
+  if (L >= 8) v = group_sum_step<2>(v);
+  if (L >= 16) v = group_sum_step<3>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ int group_isum(int v) {
+  if (L >= 2) v = group_isum_step<0>(v);
+  if (L >= 4) v = group_isum_step<1>(v);
+  if (L >= 8) v = group_isum_step<2>(v);
+  if (L >= 16) v = group_isum_step<3>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  if (L >= 2) v = group_max_step<0>(v);
+  if (L >= 4) v = group_max_step<1>(v);
+  if (L >= 8) v = group_max_step<2>(v);
+  if (L >= 16) v = group_max_step<3>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ int group_imin(int v) {
+  if (L >= 2) v = group_imin_step<0>(v);
+  if (L >= 4) v = group_imin_step<1>(v);
+  if (L >= 8) v = group_imin_step<2>(v);
+  if (L >= 16) v = group_imin_step<3>(v);
+  return v;
+}
+
+template <int L, int V, int KL, bool VEC>
+__global__ __launch_bounds__(kRouteThreads) void route_list_kernel(
+    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t full_mass,
+    int32_t* __restrict__ ids, float* __restrict__ weights, uint32_t* flags) {
+  __shared__ uint2 cand[kRouteThreads * KL];           // (value bits, expert) candidates, KL per lane
+  const int lane = threadIdx.x % kWave;
+  const int l = lane % L;                               // position inside the token's lanes
+  const int64_t tpb = kRouteThreads / L;                // tokens per block
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * tpb + threadIdx.x / L;
+  const bool live = t < T;                              // lanes of a missing token still join the DPP steps
+  const float* row = logits + (live ? t : 0) * E;
+
+  // values and their expert ids
+  auto expert_of = [&](int v) { return VEC ? 4 * (l + L * (v / 4)) + v % 4 : l + L * v; };
+  auto load_values = [&](float (&val)[V]) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j) {
+        const int e0 = 4 * (l + L * j);
+        f32x4 q = {kPad, kPad, kPad, kPad};
+        if (live && e0 < E) q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0));
+        val[4 * j] = q[0];
+        val[4 * j + 1] = q[1];
+        val[4 * j + 2] = q[2];
+        val[4 * j + 3] = q[3];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = l + L * v;
+        val[v] = live && e < E ? __builtin_nontemporal_load(row + e) : kPad;
+      }
+    }
+  };
+  float val[V];
+  load_values(val);
+
+  // 1. per-lane sorted list of the KL largest; x * 0 is 0 for finite x and NaN otherwise
+  float lst[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) lst[i] = -INFINITY;
+  float nf = 0.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const float x = val[v];
+    nf = fmaf(x, 0.0f, nf);
+#pragma unroll
+    for (int i = KL - 1; i >= 1; --i) lst[i] = __builtin_amdgcn_fmed3f(lst[i - 1], lst[i], x);
+    lst[0] = fmax1(lst[0], x);
+  }
+  // 2. merge the token's lists
+  if (L >= 2) merge_step<KL, 0>(lst);
+  if (L >= 4) merge_step<KL, 1>(lst);
+  if (L >= 8) merge_step<KL, 2>(lst);
+  if (L >= 16) merge_step<KL, 3>(lst);
+  const bool bad = group_sum<L>(nf != 0.0f ? 1.0f : 0.0f) != 0.0f;     // NaN != 0 as well
+  float tau = lst[0];
+#pragma unroll
+  for (int i = 1; i < KL; ++i) tau = i == k - 1 ? lst[i] : tau;
+  const float z0 = lst[0];
+
+  // gate denominator: the k kept values, or (V1) every expert's logit
+  float denom;
+  if (full_mass) {
+    float m = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) m += __expf(val[v] - z0);       // padding adds exp(-FLT_MAX - z0) = 0
+    denom = group_sum<L>(m);
+  } else {
+    denom = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+      if (i < k) denom += __expf(lst[i] - z0);
+  }
+
+  const float rden = 1.0f / denom;
+
+  // 3. candidates
+  uint2* mine = cand + threadIdx.x * KL;
+  int cnt = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if (val[v] >= tau) {
+      // past KL candidates the last slot is overwritten: more than k
+      // candidates send the token to the exact rounds anyway
+      mine[cnt < KL ? cnt : KL - 1] = make_uint2(__float_as_uint(val[v]), static_cast<uint32_t>(expert_of(v)));
+      ++cnt;
+    }
+  }
+  const int n_cand = group_isum<L>(cnt);
+  bool strict = true;
+#pragma unroll
+  for (int i = 0; i + 1 < KL; ++i)
+    if (i + 1 < k) strict = strict && lst[i] > lst[i + 1];
+  const bool fast = n_cand == k && strict;
+  int32_t* out_ids = ids + (live ? t : 0) * k;
+  float* out_w = weights + (live ? t : 0) * k;
+  if (live && bad) {
+    if (l == 0) flag_or(flags, MOE_FLAG_NONFINITE_LOGIT);
+    for (int j = l; j < k; j += L) {
+      out_ids[j] = -1;
+      out_w[j] = 0.0f;
+    }
+  }
+  if (live && !bad && fast) {
+    for (int c = 0; c < cnt && c < KL; ++c) {
+      const uint2 cv = mine[c];
+      const float x = __uint_as_float(cv.x);
+      int slot = 0;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) slot += (i < k && lst[i] > x) ? 1 : 0;
+      out_ids[slot] = static_cast<int32_t>(cv.y);
+      out_w[slot] = __expf(x - z0) * rden;
+    }
+  }
+  // 4. exact rounds for tokens with equal values (every lane of the wave
+  // joins the reductions; only such tokens' lanes write)
+  const bool slow = live && !bad && !fast;
+  if (ballot(slow) != 0) {
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (val[v] > bv) {                              // strict: the first (lowest) expert among equals
+          bv = val[v];
+          be = expert_of(v);
+        }
+      }
+      const float gmax = group_max<L>(bv);
+      const int emin = group_imin<L>(bv == gmax ? be : 0x7fffffff);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (expert_of(v) == emin) val[v] = -INFINITY;   // taken (valid tokens hold finite values only)
+      if (slow && l == 0) {
+        out_ids[r] = emin;
+        out_w[r] = __expf(gmax - z0) * rden;
+      }
+    }
+  }
+}
+
+template <int L, int V, int KL, bool VEC>
+void launch_list(const float* logits, int64_t T, int32_t E, int32_t k, int32_t full, int32_t* ids, float* w,
+                 uint32_t* flags, hipStream_t s) {
+  constexpr int64_t tpb = kRouteThreads / L;
+  const unsigned blocks = static_cast<unsigned>((T + tpb - 1) / tpb);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(route_list_kernel<L, V, KL, VEC>), dim3(blocks), dim3(kRouteThreads), 0, s,
+                     logits, T, E, k, full, ids, w, flags);
+}
+
+template <int L, int KL>
+void launch_list_v(int V, const float* logits, int64_t T, int32_t E, int32_t k, int32_t full, int32_t* ids,
+                   float* w, uint32_t* flags, hipStream_t s) {
+  if (V <= 8) launch_list<L, 8, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+  else if (V <= 16) launch_list<L, 16, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+  else if (V <= 32) launch_list<L, 32, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+  else if (V <= 48) launch_list<L, 48, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+  else launch_list<L, 64, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+}
+
+template <int KL>
+void launch_list_lv(int L, int V, const float* logits, int64_t T, int32_t E, int32_t k, int32_t full,
+                    int32_t* ids, float* w, uint32_t* flags, hipStream_t s) {
+  switch (L) {
+    case 1: launch_list_v<1, KL>(V, logits, T, E, k, full, ids, w, flags, s); break;
+    case 2: launch_list_v<2, KL>(V, logits, T, E, k, full, ids, w, flags, s); break;
+    case 4: launch_list_v<4, KL>(V, logits, T, E, k, full, ids, w, flags, s); break;
+    case 8: launch_list_v<8, KL>(V, logits, T, E, k, full, ids, w, flags, s); break;
+    default: launch_list_v<16, KL>(V, logits, T, E, k, full, ids, w, flags, s); break;
+  }
 }
 
 // Group-restricted router (V2 when sigmoid_bias = 0, V3 when 1).  One
@@ -337,13 +569,26 @@ MOE_API int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
   MOE_CHECK(logits && topk_ids && topk_w, MOE_EINVAL);
   MOE_CHECK(aligned4(logits) && aligned4(topk_ids) && aligned4(topk_w), MOE_EINVAL);
   const int full = gating == MOE_GATING_SOFTMAX_TOPK ? 1 : 0;
-  const int V = (E + kWave - 1) / kWave;
-  if (V <= 1) launch<1>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 2) launch<2>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 4) launch<4>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 6) launch<6>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
-  else if (V <= 8) launch<8>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
-  else launch<16>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  // 16-byte loads when every row starts on a 16-byte boundary
+  const int vec = (E % 4 == 0 && aligned16(logits)) ? 1 : 0;
+  if (!vec) {
+    // rows not on 16-byte boundaries: one general configuration with 4-byte
+    // loads (16 lanes of up to 64 values, lists of 16)
+    launch_list<16, 64, 16, false>(logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  } else {
+    // lanes per token: the fewest (a power of two) that hold at most 64 values
+    // each, then more while the grid would give fewer than 2048 wavefronts
+    auto values_per_lane = [&](int L) { return 4 * ((E + 4 * L - 1) / (4 * L)); };
+    int L = 1;
+    while (L < 16 && values_per_lane(L) > 64) L *= 2;
+    while (L < 16 && T * L < 2048 * static_cast<int64_t>(kWave) && values_per_lane(2 * L) >= 4) L *= 2;
+    const int V = values_per_lane(L);
+    const int KL = k <= 2 ? 2 : (k <= 4 ? 4 : (k <= 8 ? 8 : 16));
+    if (KL == 2) launch_list_lv<2>(L, V, logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+    else if (KL == 4) launch_list_lv<4>(L, V, logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+    else if (KL == 8) launch_list_lv<8>(L, V, logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+    else launch_list_lv<16>(L, V, logits, T, E, k, full, topk_ids, topk_w, dev_flags, stream);
+  }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
