@@ -213,9 +213,18 @@ typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 // A rows of the slice sit at a_stage (row r at r * RB bytes), B rows at
 // b_stage (B row r likewise); the swizzle repeats every 16 rows and BM is a
 // multiple of 16, so both halves use their local row index.
-template <class C>
+// No memory work between MFMA groups.
+struct NoMem {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// mem(g) runs after the g-th group of MFMAs (g = kk * NF + f, one group per
+// B fragment): it lets a caller spread its loads and LDS writes for later
+// slices over the slice's matrix-core work instead of issuing them all at once.
+template <class C, class Mem = NoMem>
 __device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_t* b_stage,
-                                              f32x16 (&acc)[C::NB][C::TM][C::TN], int wm, int wn, int lane) {
+                                              f32x16 (&acc)[C::NB][C::TM][C::TN], int wm, int wn, int lane,
+                                              Mem mem = Mem()) {
   constexpr int KS = C::BK / 16;               // MFMA k-steps per slice
   constexpr int NF = C::NB * C::TN;            // B fragments per k-step
   const int lr = lane % 32, lk = lane / 32;
@@ -264,6 +273,7 @@ __device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
         acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i], b_cur, acc[h][i][j], 0, 0, 0);
+      mem(kk * NF + f);
       __builtin_amdgcn_sched_barrier(0);
       b_cur = b_nxt;
     }
@@ -453,6 +463,29 @@ __device__ __forceinline__ void gemm_tile(
       for (int i = 0; i < C::LB; ++i)
         *reinterpret_cast<vec16*>(st + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) = r[i];
     };
+    // The loads and LDS writes of one step, spread over its MFMA groups: the
+    // register copy of B(s + 1) into the free stage first (no LDS DMA is in
+    // flight then, so the compiler adds no wait before the writes), then the
+    // LDS DMA of A(s + 1), then the loads of B(s + 3) into the registers just
+    // written out.  Issued all at once after the barrier, these left the
+    // matrix cores of the whole CU idle for several hundred cycles per step.
+    auto step_mem = [&](int stage, vec16 (&r)[C::LB], int a_slice, int b_slice) {
+      bf16_t* stw = ring_b + stage * (C::BNB * C::BK) + lane * 8;
+      bf16_t* sta = ring + stage * (C::BM * C::BK);
+      return [&, stw, sta, a_slice, b_slice](int g) {
+        if (g < C::LB) {
+          *reinterpret_cast<vec16*>(stw + (C::block(wave, C::LA + g) - C::BM / C::RPI) * 512) = r[g];
+        } else if (g < C::LB + C::LA) {
+          const int i = g - C::LB;
+          __builtin_amdgcn_global_load_lds(
+              (gbl_ptr_t)(base[i] + (off[i] + static_cast<uint32_t>(a_slice * C::BK))),
+              (lds_ptr_t)(sta + C::block(wave, i) * 512), 16, 0, 0);
+        } else if (g < 2 * C::LB + C::LA) {
+          const int i = g - C::LB - C::LA;
+          r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, static_cast<int>(boff[i]), b_slice * C::BK * 2, 0);
+        }
+      };
+    };
     auto step_sync = [&]() {
       wait_vmcnt<C::LB>();
       __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
@@ -470,21 +503,14 @@ __device__ __forceinline__ void gemm_tile(
     asm volatile("" ::: "memory");           // B(1) strictly older than B(2)
     gload_b(rb0, clamp(2));
     int kt = 0;
+    static_assert(2 * C::LB + C::LA <= (C::BK / 16) * C::NB * C::TN, "one memory instruction per MFMA group");
     for (; kt + 1 < KT; kt += 2) {             // an even and an odd step; no early exit
       step_sync();
-      lstore_b(1, rb1);                        // B(kt + 1)
-      asm volatile("" ::: "memory");
-      dma_a(1, kt + 1);
-      asm volatile("" ::: "memory");
-      gload_b(rb1, clamp(kt + 3));
-      compute_slice<C>(a0, b0, acc, wm, wn, lane);
+      // B(kt + 1) to stage 1, A(kt + 1) to stage 1, B(kt + 3) to registers
+      compute_slice<C>(a0, b0, acc, wm, wn, lane, step_mem(1, rb1, kt + 1, clamp(kt + 3)));
       step_sync();
-      lstore_b(0, rb0);                        // B(kt + 2), or a repeat past the end
-      asm volatile("" ::: "memory");
-      dma_a(0, clamp(kt + 2));
-      asm volatile("" ::: "memory");
-      gload_b(rb0, clamp(kt + 4));
-      compute_slice<C>(a1, b1, acc, wm, wn, lane);
+      // B(kt + 2) to stage 0, A(kt + 2) to stage 0, B(kt + 4) to registers (repeats past the end)
+      compute_slice<C>(a1, b1, acc, wm, wn, lane, step_mem(0, rb0, clamp(kt + 2), clamp(kt + 4)));
     }
     if (kt < KT) {                             // odd slice count: the last slice is in stage 0
       step_sync();
