@@ -526,11 +526,13 @@ def recv_step(ge, timer, w, bank, flags, bufs):
     starts = bufs["starts"]
     outs = []
     for wave in range(w.n_waves):
+        ret = bufs["ret"][wave]
+        # compaction also records each slot's pool row and zeroes the return
+        # rows without a slot; the GEMM then stores straight into pool rows
         rc = timer.run("recv_compact", ge.recv_compact, bank["pools"][wave], L, cap, compact=bufs["compact"],
-                       flags=flags, payload=w.payload, d=d)
-        z = timer.run("swiglu", ge.grouped_swiglu, bufs["compact"].view(L * cap, d), starts, rc["counts"],
-                      bank["wg"], bank["wu"], bank["wd"], z=bufs["z"], flags=flags)
-        ret = timer.run("expand", ge.expand_rows, z, rc["row_slot"], ret=bufs["ret"][wave], flags=flags)
+                       flags=flags, payload=w.payload, d=d, slot_row=bufs["slot_row"], ret=ret)
+        timer.run("swiglu", ge.grouped_swiglu, bufs["compact"].view(L * cap, d), starts, rc["counts"],
+                  bank["wg"], bank["wu"], bank["wd"], z=ret, z_rows=rc["slot_row"], flags=flags)
         outs.append((rc, ret))
     return outs
 
@@ -541,16 +543,16 @@ def recv_ledger(w, counts_per_wave):
     P1 = ge.pool_height(P, d, w.payload)
     rb = ge.row_bytes(d, w.payload)             # bytes of one incoming row (bf16 or fp8 record)
     zb = 2 if w.ret_dtype == "bf16" else 4      # bytes per expert-output / return element
-    led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0),
-           "expand": dict(bytes=0, flops=0)}
+    led = {"recv_compact": dict(bytes=0, flops=0), "swiglu": dict(bytes=0, flops=0)}
     for counts in counts_per_wave:
         A = int(counts.sum())
         E_act = int((counts > 0).sum())
-        # header ids, accepted rows read and written as bf16 (receiver-dropped rows are never read), row_slot
-        led["recv_compact"]["bytes"] += S * P * 2 + A * rb + A * d * 2 + 4 * S * P1
-        led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * zb
+        # header ids, accepted rows read and written as bf16 (receiver-dropped rows are never read), row_slot,
+        # slot_row, and the zero return rows of every row without a slot
+        led["recv_compact"]["bytes"] += S * P * 2 + A * rb + A * d * 2 + 4 * S * P1 + 4 * A + (S * P1 - A) * d * zb
+        # accepted rows in, weights of the active experts, results stored through the row map into pool rows
+        led["swiglu"]["bytes"] += A * d * 2 + E_act * 3 * d * dff * 2 + A * d * zb + 4 * A
         led["swiglu"]["flops"] += 6 * A * d * dff
-        led["expand"]["bytes"] += A * d * zb + 4 * S * P1 + S * P1 * d * zb
     return led
 
 
@@ -701,7 +703,7 @@ def main():
         L, cap, d = w.n_local, w.recv_cap, w.d
         rdt = torch.bfloat16 if w.ret_dtype == "bf16" else torch.float32
         bufs = dict(compact=torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda"),
-                    z=torch.empty((L * cap, d), dtype=rdt, device="cuda"),
+                    slot_row=torch.empty(L * cap, dtype=torch.int32, device="cuda"),
                     ret=[torch.empty((w.n_src * ge.pool_height(w.pool_rows, d, w.payload), d), dtype=rdt,
                                      device="cuda")
                          for _ in range(w.n_waves)],
@@ -787,8 +789,7 @@ def main():
         per_step_calls = 1
     value = units / (ms_per_step / 1e3)
     dom_ms = float(np.mean(dom_launches))                 # average duration of one launch, timed region
-    per_launch_bytes = led[dom]["bytes"] / per_step_calls if dom in ("recv_compact", "swiglu", "expand") and \
-        kind == "recv" else led[dom]["bytes"]
+    per_launch_bytes = led[dom]["bytes"] / per_step_calls if kind == "recv" else led[dom]["bytes"]
     per_launch_flops = led[dom]["flops"] / per_step_calls if kind == "recv" else led[dom]["flops"]
     t_s = dom_ms / 1e3
     peak_f = F32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS

@@ -52,7 +52,7 @@ _SIGS = {
                                            _p, _p, _p]),
     "moe_grouped_swiglu_workspace": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_grouped_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _i32, _p,
-                                          _sz, _p, _p]),
+                                          _i64, _p, _sz, _p, _p]),
     "moe_unpermute_combine": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p]),
     "moe_combine_backward": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i64, _p, _p, _i32, _p, _i32, _p, _p, _p]),
     "moe_grouped_swiglu_backward_workspace": (_sz, [_i64, _i32, _i32, _i32]),
@@ -69,7 +69,7 @@ _SIGS = {
     "moe_recv_compact_workspace": (_sz, [_i32, _i32, _i32]),
     "moe_expand_rows": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i32, _p, _p]),
     "moe_recv_compact": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
-                                        _sz, _p, _p]),
+                                        _p, _i32, _p, _sz, _p, _p]),
 }
 
 
@@ -274,9 +274,14 @@ def permute_noalloc(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, c
 
 def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor, w_gate: torch.Tensor,
                    w_up: torch.Tensor, w_down: torch.Tensor, z_dtype=torch.float32,
-                   z: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None):
+                   z: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None,
+                   z_rows: Optional[torch.Tensor] = None):
     """Runs expert ``e`` on rows ``[seg_start[e], seg_start[e]+seg_count[e])``
-    of ``x``; returns ``z`` (rows outside every segment are left as allocated)."""
+    of ``x``; returns ``z`` (rows outside every segment are left as allocated).
+
+    With ``z_rows`` (int32 ``[rows]``, e.g. ``recv_compact``'s ``slot_row``)
+    row ``i`` of the result is stored as row ``z_rows[i]`` of ``z``, which
+    must then be given (any row count); rows mapped outside it are dropped."""
     _expect("x", x, (None, None), _FLOATS)
     rows, d = x.shape
     _expect("w_gate", w_gate, (None, None, d), x.dtype)
@@ -284,9 +289,15 @@ def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Te
     _expect("w_up", w_up, (E, d_ff, d), x.dtype)
     _expect("w_down", w_down, (E, d, d_ff), x.dtype)
     _segments_ok(seg_start, seg_count, E)
-    _expect("z", z, (rows, d), _FLOATS)
+    if z_rows is not None:
+        if z is None:
+            raise ValueError("z_rows needs the output z")
+        _expect("z_rows", z_rows, (rows,), torch.int32)
+        _expect("z", z, (None, d), _FLOATS)
+    else:
+        _expect("z", z, (rows, d), _FLOATS)
     _flags_ok(flags)
-    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags)
+    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags, z_rows)
     dev = x.device
     if z is None:
         z = torch.empty((rows, d), dtype=z_dtype, device=dev)
@@ -294,7 +305,8 @@ def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Te
     ws = _ws(lib.moe_grouped_swiglu_workspace(rows, E, d_ff, dt), dev)
     _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
         _ptr(x), dt, d, d_ff, E, _ptr(seg_start), _ptr(seg_count), rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-        _ptr(z), _dtype_code(z), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+        _ptr(z), _dtype_code(z), _ptr(z_rows), z.shape[0] if z_rows is not None else 0, _ptr(ws), ws.numel(),
+        _ptr(flags), _stream(dev)))
     return z
 
 
@@ -507,13 +519,19 @@ def pool_pack(x: torch.Tensor, topk_ids: torch.Tensor, E: int, experts_per_dest:
 
 def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Optional[torch.Tensor] = None,
                  flags: Optional[torch.Tensor] = None, rotation: int = 0, payload: Optional[str] = None,
-                 d: Optional[int] = None):
-    """Returns a dict with compact [n_local, cap, d] (bf16), counts, arrived, row_slot, recv_dropped.
+                 d: Optional[int] = None, slot_row: Optional[torch.Tensor] = None,
+                 ret: Optional[torch.Tensor] = None):
+    """Returns a dict with compact [n_local, cap, d] (bf16), counts, arrived, row_slot, recv_dropped
+    (and slot_row when asked for).
 
     ``pools_in`` is ``[n_src, pool_height, d]`` bf16, or with ``payload``
     "row" / "b128" fp8 records ``uint8 [n_src, pool_height, row_bytes]`` of
     rows ``d`` wide (dequantized into ``compact``); sources are visited from
-    ``rotation`` onwards."""
+    ``rotation`` onwards.  ``slot_row`` (int32 ``[n_local*cap]``, or True to
+    allocate it) receives the pool row of every filled slot; ``ret``
+    (``[n_src*pool_height, d]`` fp32 or bf16) gets zero rows wherever
+    ``row_slot`` is -1, for a grouped SwiGLU that stores its results through
+    ``z_rows=slot_row`` into the same ``ret``."""
     _expect("pools_in", pools_in, (None, None, None), torch.bfloat16 if payload is None else torch.uint8)
     _flags_ok(flags)
     _need_gpu(pools_in, compact, flags)
@@ -533,8 +551,17 @@ def recv_compact(pools_in: torch.Tensor, n_local: int, cap: int, compact: Option
     arrived = torch.empty(n_local, dtype=torch.int32, device=dev)
     row_slot = torch.empty(S * P1, dtype=torch.int32, device=dev)
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    if slot_row is True:
+        slot_row = torch.empty(n_local * cap, dtype=torch.int32, device=dev)
+    _expect("slot_row", slot_row, None, torch.int32, n_local * cap)
+    _expect("ret", ret, (S * P1, d), _FLOATS)
+    _need_gpu(slot_row, ret)
     ws = _ws(lib.moe_recv_compact_workspace(S, P, n_local), dev)
     _check("moe_recv_compact", lib.moe_recv_compact(
         _ptr(pools_in), code, S, P, d, n_local, cap, rotation, _ptr(compact), _ptr(counts), _ptr(arrived),
-        _ptr(row_slot), _ptr(dropped), _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
-    return dict(compact=compact, counts=counts, arrived=arrived, row_slot=row_slot, recv_dropped=dropped)
+        _ptr(row_slot), _ptr(dropped), _ptr(slot_row), _ptr(ret), _dtype_code(ret) if ret is not None else 0,
+        _ptr(ws), ws.numel(), _ptr(flags), _stream(dev)))
+    out = dict(compact=compact, counts=counts, arrived=arrived, row_slot=row_slot, recv_dropped=dropped)
+    if slot_row is not None:
+        out["slot_row"] = slot_row
+    return out

@@ -312,13 +312,71 @@ __device__ __forceinline__ bool even_rounds(uint32_t total, uint32_t* slot, uint
   return s < total;
 }
 
-// One output tile (logical tile index `logical` of `total`).
-template <class C>
+// Output row of A row `row`: the row itself, or out_rows[row] when a row map
+// is given (then -1 when the mapped row is outside [0, out_n): not stored).
+__device__ __forceinline__ int32_t dest_row(const int32_t* __restrict__ out_rows, int32_t out_n, int32_t row) {
+  if (!out_rows) return row;
+  const int32_t o = out_rows[row];
+  return o >= 0 && o < out_n ? o : -1;
+}
+
+// Row-map entry of the wave's tile row wm*WTM + lane (lanes past WTM repeat
+// the wave's rows; rows past the segment give -1).  Fetched when the tile
+// starts, so the load's latency hides under the K loop and the epilogue
+// takes every row's entry from this register with a lane shuffle.
+template <class C, bool MAP>
+__device__ __forceinline__ int32_t lane_dest_row(const int32_t* __restrict__ out_rows, int32_t out_n, int32_t row0,
+                                                 int32_t row_end, int wm, int lane) {
+  static_assert(!MAP || C::WTM <= kWave, "one row-map entry per lane covers the wave's rows");
+  if (!MAP) return 0;
+  const int32_t row = row0 + wm * C::WTM + lane % C::WTM;
+  return row < row_end ? dest_row(out_rows, out_n, row) : -1;
+}
+
+// Direct-store epilogue: every lane writes its fragments' values (value(i, j,
+// q) is C[m][n] at m = 8*(q/4) + 4*(lane/32) + q%4, n = lane%32 of the 32x32
+// block (i, j) of the wave's tile) to row m of Cout, or with a row map to the
+// row held by lane_dst of the lane that owns m (lane_dest_row).
+template <class C, bool MAP, class OutT, class Value>
+__device__ __forceinline__ void store_direct(void* __restrict__ Cout, int32_t N, int32_t row0, int32_t row_end,
+                                             int32_t n0, int wm, int wn, int lane, int32_t lane_dst, Value value) {
+  const int lr = lane % 32, lk = lane / 32;
+  const bool full_rows = row0 + C::BM <= row_end;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    int32_t dst[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int local = i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+      const int32_t row = row0 + wm * C::WTM + local;
+      dst[q] = (!full_rows && row >= row_end) ? -1 : row;
+    }
+    if constexpr (MAP) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int32_t m = __shfl(lane_dst, i * 32 + 8 * (q / 4) + 4 * lk + (q % 4));   // every lane takes part
+        dst[q] = dst[q] < 0 ? -1 : m;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = n0 + wn * C::WTN + j * 32 + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (dst[q] >= 0) static_cast<OutT*>(Cout)[static_cast<int64_t>(dst[q]) * N + col] = value(i, j, q);
+    }
+  }
+}
+
+// One output tile (logical tile index `logical` of `total`).  MAP: results
+// are stored through the row map out_rows (dest_row).
+template <class C, bool MAP>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles, uint32_t total,
     int32_t n_tiles_n, const bf16_t* __restrict__ aux_in, bf16_t* __restrict__ aux_out, int32_t kb1,
-    bf16_t (&ring)[C::STAGES * C::SLICE], uint32_t logical) {
+    const int32_t* __restrict__ out_rows, int32_t out_n, bf16_t (&ring)[C::STAGES * C::SLICE], uint32_t logical) {
   int mt, nt;
   if (C::EXPERT_BLOCKED) {
     // all N-tiles of one expert form a block; inside it the M-tiles of one
@@ -349,6 +407,7 @@ __device__ __forceinline__ void gemm_tile(
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WN, wn = wave % C::WN;
+  const int32_t lane_dst = lane_dest_row<C, MAP>(out_rows, out_n, row0, row_end, wm, lane);
 
   // Source of every load instruction: LDS row rr of the slice; the lane's
   // physical chunk p = lane % CPR holds logical chunk p ^ swizzle(rr).  Rows
@@ -606,7 +665,20 @@ __device__ __forceinline__ void gemm_tile(
   };
   if constexpr (STAGED) {
     // Transpose through LDS: every wave writes its fragments into a row-major
-    // BM x BN_OUT tile, then all threads store whole rows with 16-byte writes.
+    // BM x BN_OUT tile, then all threads store whole rows with 16-byte writes
+    // (thread tid stores pieces v = tid + it*THREADS, row v / VPR; with a row
+    // map their destination rows are fetched first, all at once).
+    constexpr int VPR = OUT_ROW / 16;                    // 16-byte vectors per tile row
+    constexpr int ITERS = (C::BM * VPR + C::THREADS - 1) / C::THREADS;
+    const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
+    int32_t orow[MAP ? ITERS : 1];
+    if constexpr (MAP) {
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int r = (static_cast<int>(threadIdx.x) + it * C::THREADS) / VPR;
+        orow[it] = r < rows_here ? dest_row(out_rows, out_n, row0 + r) : -1;
+      }
+    }
     char* tile = reinterpret_cast<char*>(ring);
     barrier_nofence();                                   // every wave is done reading the ring
 #pragma unroll
@@ -620,33 +692,29 @@ __device__ __forceinline__ void gemm_tile(
           *reinterpret_cast<OutT*>(tile + r * OUT_ROW + cc * sizeof(OutT)) = value(i, j, q);
         }
     __syncthreads();
-    constexpr int VPR = OUT_ROW / 16;                    // 16-byte vectors per tile row
-    const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
     const int cols_here = N - n0 < C::BN_OUT ? N - n0 : C::BN_OUT;
     const int vec_cols = cols_here * static_cast<int>(sizeof(OutT)) / 16;   // N is a multiple of 64
-    for (int v = threadIdx.x; v < C::BM * VPR; v += C::THREADS) {
-      const int r = v / VPR, cv = v % VPR;
-      if (r >= rows_here || cv >= vec_cols) continue;
-      const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
-      char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(row0 + r) * N + n0) * sizeof(OutT) + cv * 16;
-      *reinterpret_cast<vec16*>(dst) = val;
-    }
-  } else {
-    const bool full_rows = row0 + C::BM <= row_end;
+    if constexpr (MAP) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int col = n0 + wn * C::WTN + j * 32 + lr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int32_t row = row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-          if (!full_rows && row >= row_end) continue;
-          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = value(i, j, q);
-        }
+      for (int it = 0; it < ITERS; ++it) {
+        const int v = static_cast<int>(threadIdx.x) + it * C::THREADS;
+        const int r = v / VPR, cv = v % VPR;
+        if (orow[it] < 0 || cv >= vec_cols) continue;
+        const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
+        char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(orow[it]) * N + n0) * sizeof(OutT) + cv * 16;
+        *reinterpret_cast<vec16*>(dst) = val;
+      }
+    } else {
+      for (int v = threadIdx.x; v < C::BM * VPR; v += C::THREADS) {
+        const int r = v / VPR, cv = v % VPR;
+        if (r >= rows_here || cv >= vec_cols) continue;
+        const vec16 val = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
+        char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(row0 + r) * N + n0) * sizeof(OutT) + cv * 16;
+        *reinterpret_cast<vec16*>(dst) = val;
       }
     }
+  } else {
+    store_direct<C, MAP, OutT>(Cout, N, row0, row_end, n0, wm, wn, lane, lane_dst, value);
   }
 }
 
@@ -655,12 +723,12 @@ __device__ __forceinline__ void gemm_tile(
 // backward data-gradient GEMMs about 5 % faster than one tile per
 // workgroup).  Register-staged tiles keep one tile per workgroup (the loop
 // costs them spilled registers).
-template <class C>
+template <class C, bool MAP>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const bf16_t* __restrict__ aux_in,
-    bf16_t* __restrict__ aux_out, int32_t kb1) {
+    bf16_t* __restrict__ aux_out, int32_t kb1, const int32_t* __restrict__ out_rows, int32_t out_n) {
   // The K-slice ring.  With register staging the A rows of the two stages
   // come first and the B rows of the two stages follow.  (One LDS array only:
   // with several, the compiler tracks the LDS DMA per array and waits for it
@@ -669,14 +737,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
   if constexpr (C::RS) {
     if (blockIdx.x < total)
-      gemm_tile<C>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, ring,
-                   xcd_remap(blockIdx.x, total));
+      gemm_tile<C, MAP>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, out_rows, out_n,
+                        ring, xcd_remap(blockIdx.x, total));
     return;
   }
   uint32_t slot, G;
   if (!even_rounds(total, &slot, &G)) return;
   for (uint32_t logical = slot; logical < total; logical += G) {
-    gemm_tile<C>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, ring, logical);
+    gemm_tile<C, MAP>(A, B0, B1, Cout, K, N, tiles, total, n_tiles_n, aux_in, aux_out, kb1, out_rows, out_n, ring,
+                      logical);
     barrier_nofence();                       // every wave is done with the ring before the next tile's loads
   }
 }
@@ -701,11 +770,12 @@ __device__ __forceinline__ void wait_slice(int after) {
 // the current tile finishes and writes its outputs (direct stores), so
 // neither the pipeline fill nor the epilogue leaves the CU idle.  The rounds
 // are even (even_rounds).
-template <class C>
+template <class C, bool MAP>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n) {
+    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
+    int32_t out_n) {
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
 
@@ -770,9 +840,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
   for (int s = 0; s < C::STAGES - 1; ++s) issue_next();
 
   f32x16 acc[C::NB][C::TM][C::TN];
-  const int lr = lane % 32, lk = lane / 32;
   for (uint32_t tile = slot; tile < total; tile += G) {
     const Coords t = coords(tile);
+    const int32_t lane_dst = lane_dest_row<C, MAP>(out_rows, out_n, t.row0, t.row_end, wm, lane);
 #pragma unroll
     for (int h = 0; h < C::NB; ++h)
 #pragma unroll
@@ -789,28 +859,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
                          acc, wm, wn, lane);
       ++consumed;
     }
-    const bool full_rows = t.row0 + C::BM <= t.row_end;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int col = t.n0 + wn * C::WTN + j * 32 + lr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int32_t row = t.row0 + wm * C::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-          if (!full_rows && row >= t.row_end) continue;
-          OutT v;
-          if constexpr (C::GATEUP)
-            v = f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
-          else if constexpr (C::OUT_F32)
-            v = acc[0][i][j][q];
-          else
-            v = f32_to_bf16(acc[0][i][j][q]);
-          static_cast<OutT*>(Cout)[static_cast<int64_t>(row) * N + col] = v;
-        }
-      }
-    }
+    store_direct<C, MAP, OutT>(Cout, N, t.row0, t.row_end, t.n0, wm, wn, lane, lane_dst,
+                          [&](int i, int j, int q) -> OutT {
+                            if constexpr (C::GATEUP)
+                              return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
+                            else if constexpr (C::OUT_F32)
+                              return acc[0][i][j][q];
+                            else
+                              return f32_to_bf16(acc[0][i][j][q]);
+                          });
   }
 }
 
@@ -865,44 +922,65 @@ inline int device_cus() {
   return n;
 }
 
-template <class C>
-void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
-                const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream,
-                const void* aux_in = nullptr, void* aux_out = nullptr, int32_t kb1 = 0) {
+template <class C, bool MAP>
+void launch_kernel(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
+                   const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn,
+                   hipStream_t stream, const void* aux_in, void* aux_out, int32_t kb1, const int32_t* out_rows,
+                   int32_t out_n) {
   const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
   // the persistent form has the plain store epilogue only
   if (C::EPI == kEpiStore && !C::BT && persistent) {
     const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
     const int64_t g = upper < slots ? upper : slots;
     if constexpr (C::EPI == kEpiStore && !C::BT)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C>), dim3(static_cast<unsigned>(g)),
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn);
+                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n);
   } else {
     // at most one workgroup per CU slot; each walks its tiles (even rounds);
     // register-staged tiles: one workgroup per tile
     const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
     const int64_t g = C::RS || upper < slots ? upper : slots;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C>), dim3(static_cast<unsigned>(g)),
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C, MAP>), dim3(static_cast<unsigned>(g)),
                        dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                        static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn,
-                       static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1);
+                       static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1, out_rows, out_n);
   }
+}
+
+// One GEMM launch; a row map (out_rows) selects the kernels built with it,
+// which exist for plain-store tiles that are not gate/up tiles.
+template <class C>
+void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
+                const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream,
+                const void* aux_in = nullptr, void* aux_out = nullptr, int32_t kb1 = 0,
+                const int32_t* out_rows = nullptr, int32_t out_n = 0) {
+  if constexpr (C::EPI == kEpiStore && !C::GATEUP) {
+    if (out_rows) {
+      launch_kernel<C, true>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in,
+                             aux_out, kb1, out_rows, out_n);
+      return;
+    }
+  }
+  launch_kernel<C, false>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in, aux_out,
+                          kb1, nullptr, 0);
 }
 
 template <class GU, class DF, class DB, bool PERSIST>
 int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
-                void* z, int32_t z_dtype, const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles,
-                hipStream_t stream) {
+                void* z, int32_t z_dtype, const int32_t* z_rows, int32_t z_n, const TileEntry* tiles,
+                const int32_t* n_tiles, int32_t max_tiles, hipStream_t stream) {
   const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
   const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
   MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
   launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
-    launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
+    launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
+                   z_rows, z_n);
   else
-    launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream);
+    launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
+                   z_rows, z_n);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

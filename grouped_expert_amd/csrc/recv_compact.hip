@@ -14,7 +14,10 @@
 //
 // Launches: the shared bucket-rank passes over rows in (source, row) order
 // with bucket = header id (pass 3 writes row_slot), then a row copy that
-// moves every accepted row to its slot and marks the header rows -1.  With
+// moves every accepted row to its slot and marks the header rows -1; the
+// same pass records each slot's pool row (slot_row) and clears the return
+// rows of every row without a slot, for a receiver whose expert GEMM stores
+// its results straight into pool-row order (pooled wave 03).  With
 // fp8 records in the pools ("M6.2 - Expert Parallelism and DeepSeek MoE",
 // 0x0AC) the copy dequantizes each accepted row with its own scales into the
 // bf16 arrays, so the expert GEMM reads bf16 as before.
@@ -61,19 +64,41 @@ constexpr int kRowsPerBlock = 4;   // one wavefront per incoming row
 // fp8 records: one wavefront per incoming row; every lane dequantizes 8
 // values at a time (codes and the group's scale from the same record) and
 // stores them as 16 bytes of bf16.
+// Return-row side of the copy: rows without a slot get zero return rows
+// (ret_vecs 16-byte pieces each), accepted rows record their pool row.
+struct RowSide {
+  int32_t* slot_row;
+  vec16* ret;
+  int64_t ret_vecs;
+  __device__ void reject(int64_t row, int lane) const {
+    if (!ret) return;
+    const vec16 zero = {0u, 0u, 0u, 0u};
+    vec16* out = ret + row * ret_vecs;
+    for (int64_t c = lane; c < ret_vecs; c += kWave) st_stream(zero, out + c);
+  }
+  __device__ void accept(int64_t row, int32_t slot, int lane) const {
+    if (slot_row && lane == 0) slot_row[slot] = static_cast<int32_t>(row);
+  }
+};
+
 template <bool ROW>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_fp8_rows_kernel(
     const uint8_t* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t H, int64_t rb, int32_t d,
-    int32_t* __restrict__ row_slot, bf16_t* __restrict__ compact) {
+    int32_t* __restrict__ row_slot, bf16_t* __restrict__ compact, RowSide side) {
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= n_rows) return;
   if (row % P1 < H) {
     if (lane == 0) row_slot[row] = -1;
+    side.reject(row, lane);
     return;
   }
   const int32_t slot = row_slot[row];
-  if (slot < 0) return;
+  if (slot < 0) {
+    side.reject(row, lane);
+    return;
+  }
+  side.accept(row, slot, lane);
   const uint8_t* in = pools + row * rb;
   bf16_t* out = compact + static_cast<int64_t>(slot) * d;
   for (int32_t c = lane * 8; c < d; c += kWave * 8) {
@@ -85,16 +110,21 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_fp8_rows_kernel
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void compact_rows_kernel(
     const vec16* __restrict__ pools, int64_t n_rows, int64_t P1, int64_t H, int64_t row_vecs,
-    int32_t* __restrict__ row_slot, vec16* __restrict__ compact) {
+    int32_t* __restrict__ row_slot, vec16* __restrict__ compact, RowSide side) {
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= n_rows) return;
   if (row % P1 < H) {
     if (lane == 0) row_slot[row] = -1;
+    side.reject(row, lane);
     return;
   }
   const int32_t slot = row_slot[row];
-  if (slot < 0) return;
+  if (slot < 0) {
+    side.reject(row, lane);
+    return;
+  }
+  side.accept(row, slot, lane);
   const vec16* in = pools + row * row_vecs;
   vec16* out = compact + static_cast<int64_t>(slot) * row_vecs;
   for (int64_t c = lane; c < row_vecs; c += kWave) st_stream(ld_stream(in + c), out + c);
@@ -113,8 +143,9 @@ MOE_API size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int3
 MOE_API int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n_src, int32_t pool_rows, int32_t d,
                              int32_t n_local,
                              int32_t cap, int32_t src_rotation, void* compact, int32_t* counts, int32_t* arrived,
-                             int32_t* row_slot, int32_t* recv_dropped, void* ws, size_t ws_bytes,
-                             uint32_t* dev_flags, hipStream_t stream) {
+                             int32_t* row_slot, int32_t* recv_dropped, int32_t* slot_row, void* ret,
+                             int32_t ret_dtype, void* ws, size_t ws_bytes, uint32_t* dev_flags,
+                             hipStream_t stream) {
   using namespace moe;
   MOE_CHECK(n_src >= 0 && pool_rows >= 0 && n_local >= 1 && n_local <= MOE_MAX_EXPERTS && cap >= 0, MOE_EINVAL);
   MOE_CHECK(d >= 8 && d % 8 == 0, MOE_EINVAL);
@@ -130,6 +161,10 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n
   MOE_CHECK(n_src == 0 || (pools_in && row_slot), MOE_EINVAL);
   MOE_CHECK(n_src == 0 || cap == 0 || compact, MOE_EINVAL);
   MOE_CHECK((pools_in == nullptr || aligned16(pools_in)) && (compact == nullptr || aligned16(compact)), MOE_EINVAL);
+  MOE_CHECK(ret == nullptr || ((ret_dtype == MOE_F32 || ret_dtype == MOE_BF16) && aligned16(ret)), MOE_EINVAL);
+  MOE_CHECK(slot_row == nullptr || aligned4(slot_row), MOE_EINVAL);
+  const RowSide side{slot_row, static_cast<vec16*>(ret),
+                     static_cast<int64_t>(d) * (ret_dtype == MOE_F32 ? 4 : 2) / 16};
   const int64_t n = static_cast<int64_t>(n_src) * pool_rows;
   const RankGeom g = rank_geom(n, n_local);
   const size_t tb = rank_table_bytes(g);
@@ -149,15 +184,15 @@ MOE_API int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n
     if (pool_dtype == MOE_BF16)
       hipLaunchKernelGGL(compact_rows_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, stream,
                          static_cast<const vec16*>(pools_in), n_rows, P1, H, static_cast<int64_t>(d) / 8, row_slot,
-                         static_cast<vec16*>(compact));
+                         static_cast<vec16*>(compact), side);
     else if (pool_dtype == MOE_FP8_ROW)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(compact_fp8_rows_kernel<true>), dim3(blocks), dim3(kRowsPerBlock * kWave),
                          0, stream, static_cast<const uint8_t*>(pools_in), n_rows, P1, H, rb, d, row_slot,
-                         static_cast<bf16_t*>(compact));
+                         static_cast<bf16_t*>(compact), side);
     else
       hipLaunchKernelGGL(HIP_KERNEL_NAME(compact_fp8_rows_kernel<false>), dim3(blocks), dim3(kRowsPerBlock * kWave),
                          0, stream, static_cast<const uint8_t*>(pools_in), n_rows, P1, H, rb, d, row_slot,
-                         static_cast<bf16_t*>(compact));
+                         static_cast<bf16_t*>(compact), side);
     MOE_LAUNCH_CHECK();
   }
   return MOE_OK;

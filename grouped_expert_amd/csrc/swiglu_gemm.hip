@@ -14,7 +14,11 @@
 //      (expert, first row, segment end) M-tiles.
 //   2. gate/up: per (M-tile, N-tile) workgroup, G and U tiles on bf16 MFMA
 //      with fp32 accumulation; epilogue H = SiLU(G) * U rounded to bf16.
-//   3. down: Z = H W_d^T on bf16 MFMA, fp32 accumulation, stored bf16 or fp32.
+//   3. down: Z = H W_d^T on bf16 MFMA, fp32 accumulation, stored bf16 or fp32;
+//      with a row map, row i of Z is stored as row z_rows[i] of the output
+//      (the receiver writes expert results straight into pool-row order, so
+//      no separate expansion pass reads them back: "Fixed pooled-wave
+//      all-to-all for the 8-of-384 MoE", 03).
 //
 // Data layout (all row-major, K contiguous for both operands):
 //   x [rows, d], W_g / W_u [E, d_ff, d], W_d [E, d, d_ff], H [rows, d_ff]
@@ -41,7 +45,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
                                                                int32_t K, int32_t N,
                                                                const TileEntry* __restrict__ tiles,
                                                                const int32_t* __restrict__ n_tiles_ptr,
-                                                               int32_t n_tiles_n) {
+                                                               int32_t n_tiles_n,
+                                                               const int32_t* __restrict__ out_rows,
+                                                               int32_t out_n) {
   constexpr int NB = GATEUP ? 2 : 1;
   __shared__ float As[kF32BK][kF32BM + 4];
   __shared__ float Bs[NB][kF32BK][kF32BN + 4];
@@ -88,11 +94,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   for (int i = 0; i < 4; ++i) {
     const int32_t row = row0 + ty * 4 + i;
     if (row >= row_end) continue;
+    const int32_t orow = dest_row(out_rows, out_n, row);
+    if (orow < 0) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
       const float v = GATEUP ? silu_f32(acc[0][i][j]) * acc[NB - 1][i][j] : acc[0][i][j];
-      C[static_cast<int64_t>(row) * N + col] = v;
+      C[static_cast<int64_t>(orow) * N + col] = v;
     }
   }
 }
@@ -138,7 +146,8 @@ MOE_API size_t moe_grouped_swiglu_workspace(int64_t rows, int32_t E, int32_t d_f
 MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t d_ff, int32_t E,
                                const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
                                const void* w_gate, const void* w_up, const void* w_down, void* z, int32_t z_dtype,
-                               void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream) {
+                               const int32_t* z_rows, int64_t z_n_rows, void* ws, size_t ws_bytes,
+                               uint32_t* dev_flags, hipStream_t stream) {
   using namespace moe;
   MOE_CHECK(dtype == MOE_F32 || dtype == MOE_BF16, MOE_EINVAL);
   MOE_CHECK(z_dtype == MOE_F32 || z_dtype == MOE_BF16, MOE_EINVAL);
@@ -151,6 +160,10 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
                 static_cast<int64_t>(d) * d_ff * 2 < (int64_t(1) << 32), MOE_EUNSUPPORTED);
   MOE_CHECK(seg_start && seg_count && w_gate && w_up && w_down, MOE_EINVAL);
   MOE_CHECK(rows == 0 || (x && z), MOE_EINVAL);
+  // without a map z has `rows` rows; with one, z_n_rows rows (int32 row indexes)
+  MOE_CHECK(z_rows == nullptr || (z_n_rows >= 0 && aligned4(z_rows)), MOE_EINVAL);
+  MOE_CHECK(z_n_rows <= INT32_MAX, MOE_EUNSUPPORTED);
+  const int32_t z_n = z_rows ? static_cast<int32_t>(z_n_rows) : 0;
   MOE_CHECK((x == nullptr || aligned16(x)) && (z == nullptr || aligned16(z)), MOE_EINVAL);
   MOE_CHECK(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down), MOE_EINVAL);
   const WsLayout L = ws_layout(rows, E, d_ff, dtype);
@@ -169,23 +182,25 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
     const int nt1 = d_ff / kF32BN, nt2 = d / kF32BN;
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_f32_kernel<true>), dim3(L.max_tiles * nt1), dim3(256), 0,
                        stream, static_cast<const float*>(x), static_cast<const float*>(w_gate),
-                       static_cast<const float*>(w_up), static_cast<float*>(H), d, d_ff, tiles, n_tiles, nt1);
+                       static_cast<const float*>(w_up), static_cast<float*>(H), d, d_ff, tiles, n_tiles, nt1,
+                       static_cast<const int32_t*>(nullptr), 0);
     MOE_LAUNCH_CHECK();
     hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_f32_kernel<false>), dim3(L.max_tiles * nt2), dim3(256), 0,
                        stream, static_cast<const float*>(H), static_cast<const float*>(w_down),
-                       static_cast<const float*>(nullptr), static_cast<float*>(z), d_ff, d, tiles, n_tiles, nt2);
+                       static_cast<const float*>(nullptr), static_cast<float*>(z), d_ff, d, tiles, n_tiles, nt2,
+                       z_rows, z_n);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
   switch (pick_tiles(rows, E)) {
     case kLarge:
-      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
                                                     L.max_tiles, stream);
     case kMedium:
-      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
                                                     L.max_tiles, stream);
     default:
-      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, tiles, n_tiles,
+      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
                                                     L.max_tiles, stream);
   }
 }

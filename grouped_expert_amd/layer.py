@@ -6,8 +6,8 @@ stream with no host synchronisation ("M6.6 - MoE Runtime Systems", 0x0CC
 forward blueprint, reduced to one GPU).  ``loopback_wave`` is one wave of
 the pooled-wave receiver path fed with a sender's pools ("Fixed pooled-wave
 all-to-all for the 8-of-384 MoE", 03): compaction -> batched SwiGLU over the
-static arrays -> expansion to pool rows -> sender combine into the FP32
-accumulator.
+static arrays, its results stored straight into pool rows (compaction zeroes
+the rows without a slot) -> sender combine into the FP32 accumulator.
 """
 from __future__ import annotations
 
@@ -61,9 +61,11 @@ def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: tor
                   y: torch.Tensor, flags: Optional[torch.Tensor] = None, bufs: Optional[dict] = None,
                   rotation: int = 0, ret_dtype: torch.dtype = torch.float32, payload: Optional[str] = None):
     """One wave of the receiver path; adds the wave's contributions into ``y``.
+    Returns ``(rc, ret)``: the compaction's outputs and the return rows
+    ``[n_src * pool_height, d]`` in pool-row order.
 
     ``pools_w`` is ``[n_src, pool_height, d]`` (one wave's pools, header rows
-    included).  ``bufs`` may hold preallocated ``compact``/``z``/``ret``
+    included).  ``bufs`` may hold preallocated ``compact``/``slot_row``/``ret``
     tensors to reuse; ``rotation`` is the receiver's first source.  With
     ``ret_dtype`` bf16 the expert rows leave the GEMM as bf16 and the return
     buffer is bf16 ("M6.6 - MoE Runtime Systems", 0x0AE); the combine still
@@ -73,12 +75,14 @@ def loopback_wave(pools_w: torch.Tensor, wave: int, n_waves: int, route_loc: tor
     L = w_gate.shape[0]
     d = w_down.shape[1]
     bufs = {} if bufs is None else bufs
+    ret = bufs.get("ret")
+    if ret is None:
+        ret = torch.empty((S * P1, d), dtype=ret_dtype, device=pools_w.device)
     rc = B.recv_compact(pools_w, L, cap, compact=bufs.get("compact"), flags=flags, rotation=rotation,
-                        payload=payload, d=d)
+                        payload=payload, d=d, slot_row=bufs.get("slot_row", True), ret=ret)
     starts = torch.arange(L, dtype=torch.int32, device=pools_w.device) * cap
-    z = B.grouped_swiglu(rc["compact"].view(L * cap, d), starts, rc["counts"], w_gate, w_up, w_down,
-                         z_dtype=ret_dtype, z=bufs.get("z"), flags=flags)
-    ret = B.expand_rows(z, rc["row_slot"], ret_dtype=ret_dtype, ret=bufs.get("ret"), flags=flags)
+    B.grouped_swiglu(rc["compact"].view(L * cap, d), starts, rc["counts"], w_gate, w_up, w_down,
+                     z=ret, z_rows=rc["slot_row"], flags=flags)
     lo = wave * S * P1
     B.unpermute_combine(ret, route_loc, gates, T, k, lo=lo, hi=lo + S * P1, y=y, accumulate=True, flags=flags)
-    return rc, z, ret
+    return rc, ret

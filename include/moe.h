@@ -304,18 +304,28 @@ int moe_permute_noalloc(const void* x, int32_t x_dtype, int64_t T, int32_t d,
  *   d % 64 == 0, d_ff % 64 == 0, 1 <= E
  *   seg_start, seg_count   device int32 [E] (e.g. offsets and counts of
  *              moe_permute, or e*cap and counts of moe_recv_compact)
- *   rows       rows of x and z (upper bound of every segment end): T*k for a
+ *   rows       rows of x (upper bound of every segment end): T*k for a
  *              permuted batch, n_local*cap for static arrays
  *   w_gate, w_up  device [E, d_ff, d] of dtype; w_down device [E, d, d_ff]
- *   z          device [rows, d] of z_dtype
+ *   z          device of z_dtype: [rows, d] without a row map, where row i of
+ *              the result is z row i; [z_n_rows, d] with one
+ *   z_rows     NULL, or device int32 [rows]: row i of the result is stored
+ *              as z row z_rows[i], and not at all when z_rows[i] is outside
+ *              [0, z_n_rows) (the values are not otherwise checked; two rows
+ *              mapped to one z row race).  With moe_recv_compact's slot_row
+ *              this writes the experts' outputs straight into pool-row order
+ *              ("Fixed pooled-wave all-to-all for the 8-of-384 MoE", 03:
+ *              the receiver returns results in the pools' layout), the rows
+ *              that compaction rejected being zeroed by that call.
+ *   z_n_rows   rows of z when z_rows is given (<= INT32_MAX; ignored otherwise)
  *   ws         device workspace of moe_grouped_swiglu_workspace(rows, E, d_ff, dtype)
  * ------------------------------------------------------------------------- */
 size_t moe_grouped_swiglu_workspace(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype);
 int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t d_ff, int32_t E,
                        const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
                        const void* w_gate, const void* w_up, const void* w_down,
-                       void* z, int32_t z_dtype, void* ws, size_t ws_bytes,
-                       uint32_t* dev_flags, hipStream_t stream);
+                       void* z, int32_t z_dtype, const int32_t* z_rows, int64_t z_n_rows,
+                       void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_unpermute_combine -- inverse permutation + gate-weighted FP32 combine.
@@ -476,6 +486,13 @@ int moe_pool_pack(const void* x, int32_t x_dtype, int32_t pool_dtype, int64_t T,
  *   recv_dropped = sum_h arrived[h] - counts[h]
  * Header ids >= n_local other than 0xFFFF set MOE_FLAG_BAD_HEADER and the
  * row is ignored.  compact rows at or past counts[h] are not written.
+ * Optional outputs for a receiver that writes its results in pool-row order
+ * (moe_grouped_swiglu with z_rows = slot_row) instead of expanding them:
+ *   slot_row[j] = n  for every accepted row n = s*PH + H + i with
+ *                    row_slot[n] = j (the inverse of row_slot; entries of
+ *                    slots at or past counts[h] are not written)
+ *   ret[n][:] = 0    for every row n with row_slot[n] == -1 (header, empty
+ *                    and receiver-dropped rows); accepted rows not written
  *
  *   pools_in   device [n_src][PH] rows of pool_dtype (MOE_BF16, MOE_FP8_ROW,
  *              MOE_FP8_B128), d % 8 == 0
@@ -483,12 +500,16 @@ int moe_pool_pack(const void* x, int32_t x_dtype, int32_t pool_dtype, int64_t T,
  *   compact    device bf16 [n_local][cap][d]
  *   counts int32 [n_local]; arrived int32 [n_local] or NULL;
  *   row_slot int32 [n_src*PH]; recv_dropped int32 [1]
+ *   slot_row   device int32 [n_local*cap], or NULL
+ *   ret        device [n_src*PH][d] of ret_dtype (MOE_F32 or MOE_BF16), or NULL
+ *              (ret_dtype then ignored)
  *   ws         device workspace of moe_recv_compact_workspace(n_src, pool_rows, n_local)
  * ------------------------------------------------------------------------- */
 size_t moe_recv_compact_workspace(int32_t n_src, int32_t pool_rows, int32_t n_local);
 int moe_recv_compact(const void* pools_in, int32_t pool_dtype, int32_t n_src, int32_t pool_rows, int32_t d,
                      int32_t n_local, int32_t cap, int32_t src_rotation, void* compact, int32_t* counts,
                      int32_t* arrived, int32_t* row_slot, int32_t* recv_dropped,
+                     int32_t* slot_row, void* ret, int32_t ret_dtype,
                      void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -99,8 +99,15 @@ def test_swiglu_validation():
     p, _keep = _fake()
     ws = lib.moe_grouped_swiglu_workspace(1000, 8, 256, 1)
     assert ws >= 1000 * 256 * 2
-    args = [p, 1, 128, 256, 8, p, p, 1000, p, p, p, p, 1, p, ws, NULL, NULL]
-    assert lib.moe_grouped_swiglu(*args[:14], ws - 1, NULL, NULL) == EWS
+    args = [p, 1, 128, 256, 8, p, p, 1000, p, p, p, p, 1, NULL, 0, p, ws, NULL, NULL]
+    assert lib.moe_grouped_swiglu(*args[:16], ws - 1, NULL, NULL) == EWS
+    q = ctypes.c_void_p(p.value + 2)
+    bad = list(args); bad[13] = q; bad[14] = 10                     # misaligned row map
+    assert lib.moe_grouped_swiglu(*bad) == EINVAL
+    bad = list(args); bad[13] = p; bad[14] = -1                     # negative z rows
+    assert lib.moe_grouped_swiglu(*bad) == EINVAL
+    bad = list(args); bad[13] = p; bad[14] = 1 << 31                # z rows past int32 indexes
+    assert lib.moe_grouped_swiglu(*bad) == EUNSUP
     bad = list(args); bad[2] = 100                                  # d not a multiple of 64
     assert lib.moe_grouped_swiglu(*bad) == EUNSUP
     bad = list(args); bad[1] = 0; bad[12] = 1                       # fp32 in, bf16 out
@@ -147,7 +154,7 @@ def test_pool_pack_validation():
 def test_recv_compact_validation():
     p, _keep = _fake()
     ws = lib.moe_recv_compact_workspace(64, 3004, 6)
-    args = [p, 1, 64, 3004, 3072, 6, 33497, 0, p, p, p, p, p, p, ws, NULL, NULL]
+    args = [p, 1, 64, 3004, 3072, 6, 33497, 0, p, p, p, p, p, NULL, NULL, 0, p, ws, NULL, NULL]
     bad = list(args); bad[6] = -1                                   # negative capacity
     assert lib.moe_recv_compact(*bad) == EINVAL
     bad = list(args); bad[5] = 0                                    # no local experts
@@ -156,8 +163,14 @@ def test_recv_compact_validation():
     assert lib.moe_recv_compact(*bad) == EINVAL
     bad = list(args); bad[7] = -1                                   # negative rotation
     assert lib.moe_recv_compact(*bad) == EINVAL
-    bad = list(args); bad[14] = 0                                   # workspace
+    bad = list(args); bad[17] = 0                                   # workspace
     assert lib.moe_recv_compact(*bad) == EWS
+    bad = list(args); bad[14] = p; bad[15] = 2                      # return rows must be fp32 or bf16
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[14] = ctypes.c_void_p(p.value + 4); bad[15] = 0   # misaligned return rows
+    assert lib.moe_recv_compact(*bad) == EINVAL
+    bad = list(args); bad[13] = ctypes.c_void_p(p.value + 2)         # misaligned slot map
+    assert lib.moe_recv_compact(*bad) == EINVAL
     bad = list(args); bad[3] = 1 << 26                              # pool rows past int32 row indexes
     assert lib.moe_recv_compact(*bad) == EUNSUP
     bad = list(args); bad[1] = 7                                    # unknown pool dtype

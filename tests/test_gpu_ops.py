@@ -244,6 +244,54 @@ def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     assert int(to_np(flags)[0]) == 0
 
 
+@pytest.mark.parametrize("E,rows,d,d_ff,dt,zdt,mode", [
+    (8, 512, 128, 256, "f32", "f32", "packed"),          # fp32 FMA path
+    (16, 300, 384, 64, "bf16", "bf16", "packed"),        # 32-row tiles
+    (5, 700, 128, 192, "bf16", "f32", "packed"),         # 128-row tiles
+    (2, 2100, 128, 128, "bf16", "f32", "static"),        # 256-row tiles, direct fp32 stores
+    (3, 2400, 192, 256, "bf16", "bf16", "packed"),       # 256-row tiles, stores staged through LDS
+])
+def test_grouped_swiglu_row_map(ge, E, rows, d, d_ff, dt, zdt, mode):
+    """With z_rows, row i of the result lands in z row z_rows[i]: the rows
+    equal the unmapped call's bit for bit (and the oracle's within the
+    tolerance); rows mapped to -1 or past the end of z are not stored, and
+    z rows no segment row maps to keep their contents."""
+    rng = np.random.default_rng(rows + 7 * E)
+    starts, counts = _segments(rng, E, rows, mode)
+    x32 = rng.standard_normal((rows, d)).astype(np.float32)
+    ws = [(0.05 * rng.standard_normal(s)).astype(np.float32) for s in
+          [(E, d_ff, d), (E, d_ff, d), (E, d, d_ff)]]
+    if dt == "bf16":
+        x = _bf16(x32)
+        ws = [_bf16(w) for w in ws]
+    else:
+        x = x32
+    zt = torch.float32 if zdt == "f32" else torch.bfloat16
+    n_out = rows + 37
+    zmap = rng.permutation(n_out)[:rows].astype(np.int32)
+    zmap[rng.choice(rows, size=rows // 10, replace=False)] = -1
+    zmap[rng.choice(rows, size=rows // 20, replace=False)] = n_out + 5       # out of range: dropped
+    gw = [to_gpu(w) for w in ws]
+    flags = ge.new_flags("cuda")
+    plain = ge.grouped_swiglu(to_gpu(x), to_gpu(starts), to_gpu(counts), *gw,
+                              z=torch.zeros((rows, d), dtype=zt, device="cuda"), flags=flags)
+    mapped = torch.full((n_out, d), 7.0, dtype=zt, device="cuda")
+    ge.grouped_swiglu(to_gpu(x), to_gpu(starts), to_gpu(counts), *gw, z=mapped, z_rows=to_gpu(zmap), flags=flags)
+    torch.cuda.synchronize()
+    assert int(to_np(flags)[0]) == 0
+    covered = np.zeros(rows, bool)
+    for s0, c in zip(starts, counts):
+        covered[s0:s0 + c] = True
+    live = covered & (zmap >= 0) & (zmap < n_out)
+    got, ref = as_f64(mapped), as_f64(plain)
+    assert np.array_equal(got[zmap[live]], ref[live])
+    untouched = np.ones(n_out, bool)
+    untouched[zmap[live]] = False
+    assert np.all(got[untouched] == 7.0)
+    want = O.run_segments(x, starts, counts, O.swiglu_bank(lambda e: (ws[0][e], ws[1][e], ws[2][e])))
+    assert_rows_close(got[zmap[live]], want[live], what="swiglu through the row map")
+
+
 def test_grouped_swiglu_bad_segment_flag(ge):
     rng = np.random.default_rng(1)
     E, rows, d, d_ff = 3, 256, 128, 64
@@ -396,6 +444,19 @@ def test_recv_compact(ge, S, P, d, L, cap, rot):
     assert to_np(out["row_slot"]).tolist() == rc["row_slot"].tolist()
     assert int(to_np(out["recv_dropped"])[0]) == rc["recv_dropped"]
     assert (int(to_np(flags)[0]) & 4 != 0) == (rc["bad_header"] > 0)
+    # the same call with the slot map and the return rows of the fused receiver
+    for rdt in (torch.float32, torch.bfloat16):
+        ret = torch.full((S * (P + H), d), 3.0, dtype=rdt, device="cuda")
+        slot_row = torch.full((L * cap,), -7, dtype=torch.int32, device="cuda")
+        out2 = ge.recv_compact(to_gpu(pools), L, cap, compact=compact0, rotation=rot, slot_row=slot_row, ret=ret)
+        row_slot = rc["row_slot"]
+        assert to_np(out2["row_slot"]).tolist() == row_slot.tolist()
+        want = np.full(L * cap, -7, dtype=np.int64)
+        acc = np.nonzero(row_slot >= 0)[0]
+        want[row_slot[acc]] = acc                               # the inverse of row_slot
+        assert to_np(slot_row).tolist() == want.tolist()
+        r = as_f64(ret)
+        assert np.all(r[row_slot < 0] == 0) and np.all(r[row_slot >= 0] == 3.0)
 
 
 # ---------------------------------------------------------------------------

@@ -235,7 +235,10 @@ def test_recv_share(ge, name, rotation):
     sources visited from source 17.  Every wave: the compaction byte for byte,
     all counters and row slots; expert outputs on whole 256-row GEMM tiles
     (each expert's first and last tile) plus random rows; the fp32 expansion
-    of those rows, and zero rows for dropped ones."""
+    of those rows, and zero rows for dropped ones.  The fused form (slot map
+    and zero rows from the compaction, GEMM results stored through the map
+    into pool rows) gives the expansion's return rows bit for bit, and the
+    slot map is the inverse of the row slots."""
     w = W.WORKLOADS[name]
     wg, wu, wd = W.all_expert_weights(w, n_experts=w.n_local)
     bank = O.swiglu_bank(lambda e: (wg[e], wu[e], wd[e]))
@@ -244,6 +247,8 @@ def test_recv_share(ge, name, rotation):
     P1 = O.header_rows(w.pool_rows, d) + w.pool_rows
     compact = torch.empty((L, cap, d), dtype=torch.bfloat16, device="cuda")
     z = torch.empty((L * cap, d), dtype=torch.float32, device="cuda")
+    fused = torch.empty((S * P1, d), dtype=torch.float32, device="cuda")
+    slot_row = torch.empty(L * cap, dtype=torch.int32, device="cuda")
     starts = torch.arange(L, dtype=torch.int32, device="cuda") * cap
     rng = np.random.default_rng(1)
     total_drop = 0
@@ -256,8 +261,17 @@ def test_recv_share(ge, name, rotation):
         rc = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags, rotation=rotation)
         ge.grouped_swiglu(compact.view(L * cap, d), starts, rc["counts"], *gw, z=z, flags=flags)
         ret = ge.unpermute_combine(z, rc["row_slot"], None, S * P1, 1, flags=flags)
+        print(f"{name} wave {wave}: fused compact + GEMM into pool rows", flush=True)
+        fused.fill_(float("nan"))                       # every row must be written
+        rcf = ge.recv_compact(to_gpu(pools), L, cap, compact=compact, flags=flags, rotation=rotation,
+                              slot_row=slot_row, ret=fused)
+        ge.grouped_swiglu(compact.view(L * cap, d), starts, rcf["counts"], *gw, z=fused, z_rows=slot_row,
+                          flags=flags)
         torch.cuda.synchronize()
         assert int(to_np(flags)[0]) == 0
+        assert torch.equal(rcf["row_slot"], rc["row_slot"]) and torch.equal(rcf["counts"], rc["counts"])
+        assert torch.equal(fused, ret)                  # bit for bit, no NaN left
+        del rcf
         orc = O.recv_compact(pools, L, cap, with_rows=True, rotation=rotation)
         counts = to_np(rc["counts"])
         assert np.array_equal(counts, orc["counts"])
@@ -283,6 +297,10 @@ def test_recv_share(ge, name, rotation):
         inv_slot[row_slot[live]] = live
         srcrows = inv_slot[slots]
         assert np.all(srcrows >= 0)
+        sr = to_np(slot_row)
+        for h in range(L):
+            n = int(counts[h])
+            assert np.array_equal(sr[h * cap:h * cap + n], inv_slot[h * cap:h * cap + n]), (wave, h)
         want = np.zeros((slots.size, d))
         for h in range(L):
             m = slots // cap == h
@@ -321,13 +339,12 @@ def test_loopback_sender_to_receiver(ge, send_case, cap_kind, ret):
     y = torch.zeros((ws.T, ws.d), dtype=torch.float32, device="cuda")
     rdt = torch.bfloat16 if ret == "bf16" else torch.float32
     rot = 5 if ret == "bf16" else 0
-    bufs = dict(compact=torch.empty((wr.n_local, cap, ws.d), dtype=torch.bfloat16, device="cuda"),
-                z=torch.empty((wr.n_local * cap, ws.d), dtype=rdt, device="cuda"))
+    bufs = dict(compact=torch.empty((wr.n_local, cap, ws.d), dtype=torch.bfloat16, device="cuda"))
     slots, drops = [], 0
     for wave in range(ws.n_waves):
-        rc, _, _ = ge.loopback_wave(pk_g["pools"][wave], wave, ws.n_waves, pk_g["route_loc"], gates_g, ws.T, ws.k,
-                                    *gw, cap, y, flags=flags, bufs=bufs, rotation=rot, ret_dtype=rdt,
-                                    payload=ws.payload)
+        rc, _ = ge.loopback_wave(pk_g["pools"][wave], wave, ws.n_waves, pk_g["route_loc"], gates_g, ws.T, ws.k,
+                                 *gw, cap, y, flags=flags, bufs=bufs, rotation=rot, ret_dtype=rdt,
+                                 payload=ws.payload)
         slots.append(to_np(rc["row_slot"]))
         drops += int(to_np(rc["recv_dropped"])[0])
     torch.cuda.synchronize()
