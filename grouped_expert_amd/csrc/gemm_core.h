@@ -110,6 +110,55 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// 16-byte LDS store the compiler does not see as an LDS access (so it adds no
+// wait for LDS DMA in flight before it); the caller orders it with lgkmcnt
+// waits and barriers.  LDS operations complete in order, so the compiler's
+// own lgkmcnt waits for its LDS reads stay correct (at worst conservative).
+__device__ __forceinline__ void ds_write_b128_asm(uint32_t addr, vec16 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v));
+}
+
+// Loads the compiler does not track.  With an LDS DMA in flight the compiler
+// waits for every outstanding load (vmcnt(0)) before any LDS store, its own
+// or inline, since it cannot tell LDS regions apart; a K loop that keeps DMA
+// in flight across LDS stores therefore issues its loads itself and orders
+// them with explicit vmcnt waits.  buffer_load_b128_asm's result register is
+// written when the load returns: only a later inline LDS store, behind an
+// explicit wait, may read it.
+__device__ __forceinline__ void dma_b128_asm(uint32_t lds_dst, const void* src) {
+  // LDS DMA: 16 bytes per lane from src to LDS at M0 + 16 * lane (M0 is
+  // wave-uniform); one wait state between the M0 write and its use
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_dst), "v"(src) : "memory");
+}
+
+__device__ __forceinline__ void buffer_load_b128_asm(vec16& r, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                                     uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// vmcnt wait as inline asm: ordered with the inline loads and stores above and,
+// through the memory clobber, with every memory access of the compiler (a
+// builtin wait may be scheduled past unrelated instructions).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_asm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>());
+  }
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
 // SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
@@ -122,7 +171,7 @@ constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
           int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore,
-          bool BT_ = false>
+          bool BT_ = false, int AST_ = 2>
 struct Cfg {
   static constexpr int EPI = EPI_;
   // BT: B is stored K-major, [K][N] per expert with N contiguous (a weight
@@ -138,6 +187,9 @@ struct Cfg {
   // two register stages, so two B slices are in flight with a two-stage LDS
   // ring; the A rows keep the direct LDS DMA (else: everything by DMA)
   static constexpr bool RS = RS_;
+  // AST (register staging only): LDS stages of A rows; the A DMA runs
+  // AST - 1 slices ahead of the slice being consumed
+  static constexpr int AST = AST_;
   static constexpr int THREADS = NW * 64;
   static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
   static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
@@ -156,6 +208,9 @@ struct Cfg {
   static constexpr int NB = GATEUP ? 2 : 1;
   static constexpr int ROWS = BM + BNB;                   // LDS rows per slice
   static constexpr int SLICE = ROWS * BK;                 // bf16 elements per slice
+  // bf16 elements of the LDS ring: STAGES slices, or with register staging
+  // AST stages of A rows followed by two stages of B rows
+  static constexpr int RING = RS ? AST * BM * BK + 2 * BNB * BK : STAGES * SLICE;
   static constexpr int LOADS = ROWS / RPI / NW;           // load instructions per wavefront per slice
   static_assert(BK == 32 || BK == 64, "slice depth");
   static_assert(ROWS % (RPI * NW) == 0 && BM % RPI == 0 && (BNB / 2) % RPI == 0, "slice rows vs DMA blocks");
@@ -164,6 +219,7 @@ struct Cfg {
   static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
   static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
+  static_assert(AST == 2 || (RS && AST == 3), "three A stages only with register-staged B rows");
   static_assert(EPI == kEpiStore || GATEUP, "the SwiGLU backward epilogue needs gate/up tiles");
   static_assert(!BT || (!GATEUP && !RS_ && BK == 64 && (BNB == 128 || BNB == 256)), "K-major B tiles");
   static constexpr int BRB = BNB * 2;                     // BT: bytes per k-row of the B region
@@ -376,7 +432,7 @@ __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles, uint32_t total,
     int32_t n_tiles_n, const bf16_t* __restrict__ aux_in, bf16_t* __restrict__ aux_out, int32_t kb1,
-    const int32_t* __restrict__ out_rows, int32_t out_n, bf16_t (&ring)[C::STAGES * C::SLICE], uint32_t logical) {
+    const int32_t* __restrict__ out_rows, int32_t out_n, bf16_t (&ring)[C::RING], uint32_t logical) {
   int mt, nt;
   if (C::EXPERT_BLOCKED) {
     // all N-tiles of one expert form a block; inside it the M-tiles of one
@@ -474,30 +530,31 @@ __device__ __forceinline__ void gemm_tile(
   // refill the freed stage with slice kt + STAGES - 1, consume slice kt.
   const int KT = K / C::BK;
   if constexpr (C::RS) {
-    // Two-stage LDS ring; A rows by LDS DMA one slice ahead, B rows through
-    // register stages rb0 / rb1: B of slice s is loaded at step s - 3 (or in
-    // the prologue), written to LDS at step s - 1 and consumed at step s, so
-    // during the compute of slice kt the B loads of slices kt + 2 and kt + 3
-    // are in flight.  Step kt: wait for this wave's DMA of slice kt (exactly
-    // the LB loads of B(kt + 2) are younger) and for its LDS writes, then the
-    // barrier publishes slice kt and frees the other stage, which takes the
-    // register copy of B(kt + 1) and the DMA of A(kt + 1).  Loads past the
-    // last slice re-read the last slice into the stage that is free at that
+    // A rows by LDS DMA into a ring of AST stages, AD = AST - 1 slices ahead;
+    // B rows through register stages rb0 / rb1 into a two-stage B ring: B of
+    // slice s is loaded at step s - 3 (or in the prologue), written to LDS at
+    // step s - 1 and consumed at step s.  Step j issues, spread over its MFMA
+    // groups: the LDS write of B(j + 1) into the free B stage, the DMA of
+    // A(j + AD) into the A stage consumed at step j - 1, and the loads of
+    // B(j + 3) into the registers just written out.  At step kt the DMA of
+    // A(kt) (issued at step kt - AD) must have landed: exactly LB + (AD - 1)
+    // (LA + LB) younger loads of this wave may stay in flight.  Loads past the
+    // last slice re-read the last slice into stages that are free at that
     // step (never consumed), so every step issues the same instructions and
-    // the compiler's own waits for the register loads stay exact.  Inside a
-    // step the LDS writes come before the DMA (an LDS write behind an
-    // outstanding LDS DMA would make the compiler wait for it) and the DMA
-    // before the B loads (the vmcnt count above).
+    // the vmcnt counts stay exact.  The B writes are issued as inline
+    // ds_write_b128: as compiler-visible LDS stores they would wait for every
+    // LDS DMA in flight (the compiler cannot tell the stages apart), which
+    // would pull the A DMA back to one slice ahead.  The compiler still waits
+    // for their source registers, and the step barrier waits for them
+    // (lgkmcnt(0)).
+    constexpr int AS = C::AST, AD = AS - 1;
+    constexpr int ASTEP = C::BM * C::BK, BSTEP = C::BNB * C::BK;     // elements per A / B stage
     vec16 rb0[C::LB], rb1[C::LB];
     auto clamp = [&](int slice) { return slice < KT ? slice : KT - 1; };
-    // A rows by LDS DMA.  (The global form: the compiler does not track it
-    // as an LDS write, so it adds no waits of its own before LDS accesses.)
-    auto dma_a = [&](int stage, int slice) {
-      bf16_t* st = ring + stage * (C::BM * C::BK);
-#pragma unroll
-      for (int i = 0; i < C::LA; ++i)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base[i] + (off[i] + static_cast<uint32_t>(slice * C::BK))),
-                                         (lds_ptr_t)(st + C::block(wave, i) * 512), 16, 0, 0);
+    // A rows: LDS DMA of 16 bytes per lane to the wave's 1 KB block of the stage
+    auto dma_a1 = [&](int stage, int slice, int i) {
+      dma_b128_asm(lds_addr(ring + stage * ASTEP + C::block(wave, i) * 512),
+                   base[i] + (off[i] + static_cast<uint32_t>(slice * C::BK)));
     };
     // B loads are buffer loads over the wave's weight matrix (all B rows of a
     // wavefront come from one of gate / up): a per-lane byte offset fixed for
@@ -510,72 +567,74 @@ __device__ __forceinline__ void gemm_tile(
     uint32_t boff[C::LB];
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) boff[i] = off[C::LA + i] * 2u;
-    auto gload_b = [&](vec16 (&r)[C::LB], int slice) {
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i)
-        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, static_cast<int>(boff[i]), slice * C::BK * 2, 0);
+    auto gload_b1 = [&](vec16 (&r)[C::LB], int slice, int i) {
+      buffer_load_b128_asm(r[i], rsrc_b, boff[i], static_cast<uint32_t>(slice * C::BK * 2));
     };
-    bf16_t* const ring_b = ring + 2 * C::BM * C::BK;
-    auto lstore_b = [&](int stage, const vec16 (&r)[C::LB]) {
-      bf16_t* st = ring_b + stage * (C::BNB * C::BK) + lane * 8;
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i)
-        *reinterpret_cast<vec16*>(st + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) = r[i];
+    // LDS byte address of this lane's 16 bytes of B piece 0 in B stage 0;
+    // piece i of a stage lies a wave-uniform number of 1 KB blocks further
+    bf16_t* const ring_b = ring + AS * ASTEP;
+    const uint32_t b_lds = lds_addr(ring_b) + static_cast<uint32_t>(lane) * 16u;
+    auto lstore_b1 = [&](int stage, const vec16 (&r)[C::LB], int i) {
+      ds_write_b128_asm(b_lds + static_cast<uint32_t>((stage * BSTEP + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) * 2),
+                        r[i]);
     };
-    // The loads and LDS writes of one step, spread over its MFMA groups: the
-    // register copy of B(s + 1) into the free stage first (no LDS DMA is in
-    // flight then, so the compiler adds no wait before the writes), then the
-    // LDS DMA of A(s + 1), then the loads of B(s + 3) into the registers just
-    // written out.  Issued all at once after the barrier, these left the
-    // matrix cores of the whole CU idle for several hundred cycles per step.
-    auto step_mem = [&](int stage, vec16 (&r)[C::LB], int a_slice, int b_slice) {
-      bf16_t* stw = ring_b + stage * (C::BNB * C::BK) + lane * 8;
-      bf16_t* sta = ring + stage * (C::BM * C::BK);
-      return [&, stw, sta, a_slice, b_slice](int g) {
-        if (g < C::LB) {
-          *reinterpret_cast<vec16*>(stw + (C::block(wave, C::LA + g) - C::BM / C::RPI) * 512) = r[g];
-        } else if (g < C::LB + C::LA) {
-          const int i = g - C::LB;
-          __builtin_amdgcn_global_load_lds(
-              (gbl_ptr_t)(base[i] + (off[i] + static_cast<uint32_t>(a_slice * C::BK))),
-              (lds_ptr_t)(sta + C::block(wave, i) * 512), 16, 0, 0);
-        } else if (g < 2 * C::LB + C::LA) {
-          const int i = g - C::LB - C::LA;
-          r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, static_cast<int>(boff[i]), b_slice * C::BK * 2, 0);
-        }
+    // In a step the B registers written out were loaded two steps before:
+    // the DMA of A(j + AD - 1) and the loads of B(j + 2) of the step before
+    // may stay in flight.
+    auto step_mem = [&](int a_stage, int b_stage, vec16 (&r)[C::LB], int a_slice, int b_slice) {
+      return [&, a_stage, b_stage, a_slice, b_slice](int g) {
+        if (g == 0) wait_vmcnt_asm<C::LA + C::LB>();
+        if (g < C::LB) lstore_b1(b_stage, r, g);
+        else if (g < C::LB + C::LA) dma_a1(a_stage, a_slice, g - C::LB);
+        else if (g < 2 * C::LB + C::LA) gload_b1(r, b_slice, g - C::LB - C::LA);
       };
     };
+    static_assert(2 * C::LB + C::LA <= (C::BK / 16) * C::NB * C::TN, "one memory instruction per MFMA group");
     auto step_sync = [&]() {
-      wait_vmcnt<C::LB>();
+      wait_vmcnt_asm<C::LB + (AD - 1) * (C::LA + C::LB)>();
       __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
       barrier_nofence();
     };
-    const bf16_t* const a0 = ring;
-    const bf16_t* const a1 = ring + C::BM * C::BK;
-    const bf16_t* const b0 = ring_b;
-    const bf16_t* const b1 = ring_b + C::BNB * C::BK;
-    dma_a(0, 0);
-    gload_b(rb0, 0);
-    lstore_b(0, rb0);
-    asm volatile("" ::: "memory");
-    gload_b(rb1, clamp(1));
-    asm volatile("" ::: "memory");           // B(1) strictly older than B(2)
-    gload_b(rb0, clamp(2));
-    int kt = 0;
-    static_assert(2 * C::LB + C::LA <= (C::BK / 16) * C::NB * C::TN, "one memory instruction per MFMA group");
-    for (; kt + 1 < KT; kt += 2) {             // an even and an odd step; no early exit
-      step_sync();
-      // B(kt + 1) to stage 1, A(kt + 1) to stage 1, B(kt + 3) to registers
-      compute_slice<C>(a0, b0, acc, wm, wn, lane, step_mem(1, rb1, kt + 1, clamp(kt + 3)));
-      step_sync();
-      // B(kt + 2) to stage 0, A(kt + 2) to stage 0, B(kt + 4) to registers (repeats past the end)
-      compute_slice<C>(a1, b1, acc, wm, wn, lane, step_mem(0, rb0, clamp(kt + 2), clamp(kt + 4)));
+    // prologue: the issue order of steps -3 .. -1 (B(0); A(0), B(1) with AD = 2;
+    // the write of B(0), A(AD - 1), B(2))
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) gload_b1(rb0, 0, i);
+    if constexpr (AD == 2) {
+#pragma unroll
+      for (int i = 0; i < C::LA; ++i) dma_a1(0, 0, i);
     }
-    if (kt < KT) {                             // odd slice count: the last slice is in stage 0
-      step_sync();
-      compute_slice<C>(a0, b0, acc, wm, wn, lane);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) gload_b1(rb1, clamp(1), i);
+    wait_vmcnt_asm<(AD - 1) * C::LA + C::LB>();  // B(0) has landed
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) lstore_b1(0, rb0, i);
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) dma_a1(AD - 1, clamp(AD - 1), i);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) gload_b1(rb0, clamp(2), i);
+    // steps in groups of U (stage indices repeat every U steps); a group's
+    // steps past the last slice are skipped
+    constexpr int U = AS == 2 ? 2 : 6;
+    for (int kt = 0; kt < KT; kt += U) {
+      static_for<U>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u == 0 || kt + u < KT) {
+          const int s = kt + u;
+          step_sync();
+          compute_slice<C>(ring + (u % AS) * ASTEP, ring_b + (u % 2) * BSTEP, acc, wm, wn, lane,
+                           step_mem((u + AD) % AS, (u + 1) % 2, (u % 2) ? rb0 : rb1, clamp(s + AD), clamp(s + 3)));
+        }
+      });
     }
-    wait_vmcnt<0>();                           // no DMA may still land in the ring
+    // no DMA may still land in the ring and no load in a staging register:
+    // the registers of the last (never stored) B loads stay allocated until
+    // this wait, which no instruction of the epilogue may pass
+    static_assert(C::LB == 4, "staging registers tied to the final wait");
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(rb0[0]), "+v"(rb0[1]), "+v"(rb0[2]), "+v"(rb0[3]), "+v"(rb1[0]), "+v"(rb1[1]),
+                   "+v"(rb1[2]), "+v"(rb1[3])
+                 :
+                 : "memory");
   } else {
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
@@ -733,7 +792,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
   // come first and the B rows of the two stages follow.  (One LDS array only:
   // with several, the compiler tracks the LDS DMA per array and waits for it
   // before every LDS read of that array.)
-  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
   if constexpr (C::RS) {
     if (blockIdx.x < total)
@@ -776,7 +835,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
     int32_t out_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t ring[C::STAGES * C::SLICE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
@@ -889,9 +948,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
 //          (144 KB), persistent -- decode-like segments of a few rows.
 // Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
 // hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true>;
-using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true>;
-using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true>;
+using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
+using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
+using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
 using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
 using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
 using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
