@@ -161,6 +161,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// fp32 -> bf16, round to nearest even, with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32, two values per instruction when the compiler pairs them).
+__device__ __forceinline__ bf16_t bf16_hw(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
+
 // SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
@@ -414,13 +418,24 @@ __device__ __forceinline__ void store_direct(void* __restrict__ Cout, int32_t N,
         dst[q] = dst[q] < 0 ? -1 : m;
       }
     }
+    // one row address per destination row; the wave's TN column blocks are
+    // immediate offsets from it (N is a multiple of 64, so a 32-column block
+    // is either inside the matrix or wholly past its end)
+    const int col0 = n0 + wn * C::WTN + lr;
+    const bool all_cols = n0 + wn * C::WTN + C::TN * 32 <= N;          // wave-uniform
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int col = n0 + wn * C::WTN + j * 32 + lr;
-      if (col >= N) continue;
+    for (int q = 0; q < 16; ++q) {
+      if (dst[q] < 0) continue;
+      OutT* rowp = static_cast<OutT*>(Cout) +
+                   static_cast<uint64_t>(static_cast<uint32_t>(dst[q])) * static_cast<uint32_t>(N) + col0;
+      if (all_cols) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (dst[q] >= 0) static_cast<OutT*>(Cout)[static_cast<int64_t>(dst[q]) * N + col] = value(i, j, q);
+        for (int j = 0; j < C::TN; ++j) rowp[j * 32] = value(i, j, q);
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          if (col0 - lr + j * 32 < N) rowp[j * 32] = value(i, j, q);
+      }
     }
   }
 }
@@ -696,7 +711,7 @@ __device__ __forceinline__ void gemm_tile(
               const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
               val = o == 0 ? dh * u * (sg * (1.0f + g * (1.0f - sg))) : dh * (g * sg);
             }
-            *reinterpret_cast<bf16_t*>(t1 + r * TROW + cc * 2) = f32_to_bf16(val);
+            *reinterpret_cast<bf16_t*>(t1 + r * TROW + cc * 2) = bf16_hw(val);
           }
       __syncthreads();
       for (int v = threadIdx.x; v < C::BM * VPR; v += C::THREADS) {
@@ -715,11 +730,11 @@ __device__ __forceinline__ void gemm_tile(
   constexpr bool STAGED = C::BM * OUT_ROW <= static_cast<int>(sizeof(ring));  // tile fits the ring
   auto value = [&](int i, int j, int q) -> OutT {
     if constexpr (C::GATEUP) {
-      return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
+      return bf16_hw(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
     } else if constexpr (C::OUT_F32) {
       return acc[0][i][j][q];
     } else {
-      return f32_to_bf16(acc[0][i][j][q]);
+      return bf16_hw(acc[0][i][j][q]);
     }
   };
   if constexpr (STAGED) {
@@ -921,11 +936,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
     store_direct<C, MAP, OutT>(Cout, N, t.row0, t.row_end, t.n0, wm, wn, lane, lane_dst,
                           [&](int i, int j, int q) -> OutT {
                             if constexpr (C::GATEUP)
-                              return f32_to_bf16(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
+                              return bf16_hw(silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]);
                             else if constexpr (C::OUT_F32)
                               return acc[0][i][j][q];
                             else
-                              return f32_to_bf16(acc[0][i][j][q]);
+                              return bf16_hw(acc[0][i][j][q]);
                           });
   }
 }
