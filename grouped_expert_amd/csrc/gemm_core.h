@@ -165,6 +165,14 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 // (v_cvt_pk_bf16_f32, two values per instruction when the compiler pairs them).
 __device__ __forceinline__ bf16_t bf16_hw(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
 
+// Two values in one v_cvt_pk_bf16_f32: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t bf16x2_hw(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2));
+}
+
 // SiLU with the hardware reciprocal (about 1 ulp), for the GEMM epilogue.
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
@@ -175,7 +183,7 @@ constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
           int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore,
-          bool BT_ = false, int AST_ = 2>
+          bool BT_ = false, int AST_ = 2, int PB_ = 1, int PA_ = 1, bool SW_ = false>
 struct Cfg {
   static constexpr int EPI = EPI_;
   // BT: B is stored K-major, [K][N] per expert with N contiguous (a weight
@@ -194,6 +202,13 @@ struct Cfg {
   // AST (register staging only): LDS stages of A rows; the A DMA runs
   // AST - 1 slices ahead of the slice being consumed
   static constexpr int AST = AST_;
+  // MFMA fragment prefetch distances in MFMA groups (B fragment, A fragments)
+  static constexpr int PB = PB_, PA = PA_;
+  // SW: the MFMA takes the weight fragment as its first operand, so a lane's
+  // accumulator holds 4 consecutive output columns of one row (instead of 4
+  // consecutive rows of one column) and the epilogue moves 8- or 16-byte
+  // pieces; plain-store tiles staged through LDS only
+  static constexpr bool SW = SW_;
   static constexpr int THREADS = NW * 64;
   static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
   static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
@@ -314,33 +329,32 @@ __device__ __forceinline__ void compute_slice(const bf16_t* a_stage, const bf16_
       return *reinterpret_cast<const bf16x8*>(bbase + swz_off<C::RB>(brow, kk * 2 + lk));
     }
   };
-  bf16x8 a_cur[C::TM], a_nxt[C::TM];
+  // Fragment schedule over the slice's KS * NF groups (group g = k-step g / NF,
+  // B fragment g % NF): the B fragment of group g is read PB groups ahead, the
+  // A fragments of a k-step PA groups before the k-step starts.
+  constexpr int G = KS * NF;
+  constexpr int PB = C::PB, PA = C::PA;
+  static_assert(PB >= 1 && PB <= 3 && PA >= 1 && PA <= NF, "fragment prefetch distances");
+  bf16x8 bq[G], aq[KS][C::TM];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) a_cur[i] = a_frag(0, i);
-  bf16x8 b_cur = b_frag(0, 0), b_nxt;
+  for (int i = 0; i < C::TM; ++i) aq[0][i] = a_frag(0, i);
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
+  for (int g = 0; g < PB && g < G; ++g) bq[g] = b_frag(g / NF, g % NF);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + 1 < NF) {
-        b_nxt = b_frag(kk, f + 1);
-      } else if (kk + 1 < KS) {
-        b_nxt = b_frag(kk + 1, 0);
+  for (int g = 0; g < G; ++g) {
+    const int kk = g / NF, f = g % NF;
+    if (g + PB < G) bq[g + PB] = b_frag((g + PB) / NF, (g + PB) % NF);
+    if (kk + 1 < KS && f == NF - PA) {
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) a_nxt[i] = a_frag(kk + 1, i);
-      }
-      const int h = f / C::TN, j = f % C::TN;
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i], b_cur, acc[h][i][j], 0, 0, 0);
-      mem(kk * NF + f);
-      __builtin_amdgcn_sched_barrier(0);
-      b_cur = b_nxt;
+      for (int i = 0; i < C::TM; ++i) aq[kk + 1][i] = a_frag(kk + 1, i);
     }
-    if (kk + 1 < KS) {
+    const int h = f / C::TN, j = f % C::TN;
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) a_cur[i] = a_nxt[i];
-    }
+    for (int i = 0; i < C::TM; ++i)
+      acc[h][i][j] = C::SW ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[g], aq[kk][i], acc[h][i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk][i], bq[g], acc[h][i][j], 0, 0, 0);
+    mem(g);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -737,7 +751,88 @@ __device__ __forceinline__ void gemm_tile(
       return bf16_hw(acc[0][i][j][q]);
     }
   };
-  if constexpr (STAGED) {
+  if constexpr (C::SW) {
+    // Acc value q of 32 x 32 block (i, j) is C[m][n] at m = i*32 + lane%32 of
+    // the wave's rows and n = j*32 + 8*(q/4) + 4*(lane/32) + q%4 of its
+    // columns: each lane writes groups of 4 consecutive columns into a
+    // row-major LDS tile whose rows are padded by 16 bytes (the 16 lanes of
+    // one LDS cycle write 16 different rows, which the padding puts in
+    // different banks), PASS_ROWS rows at a time; then all threads store
+    // whole rows with 16-byte writes (with a row map their destination rows
+    // are fetched first, all at once).
+    static_assert(C::EPI == kEpiStore, "plain store epilogue");
+    constexpr int ROWP = OUT_ROW + 16;
+    constexpr int PROWS = C::BM * ROWP <= static_cast<int>(sizeof(ring))
+                              ? C::BM
+                              : static_cast<int>(sizeof(ring)) / ROWP / C::WTM * C::WTM;
+    static_assert(PROWS >= C::WTM && C::BM % PROWS == 0, "whole waves per pass");
+    constexpr int PASSES = C::BM / PROWS;
+    constexpr int VPR = OUT_ROW / 16;
+    constexpr int ITERS = (PROWS * VPR + C::THREADS - 1) / C::THREADS;
+    const int rows_here = row_end - row0 < C::BM ? row_end - row0 : C::BM;
+    const int cols_here = N - n0 < C::BN_OUT ? N - n0 : C::BN_OUT;
+    const int vec_cols = cols_here * static_cast<int>(sizeof(OutT)) / 16;   // N is a multiple of 64
+    auto fval = [&](int i, int j, int q) -> float {
+      if constexpr (C::GATEUP) return silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q];
+      else return acc[0][i][j][q];
+    };
+    char* tile = reinterpret_cast<char*>(ring);
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int pr0 = pass * PROWS;
+      int32_t orow[MAP ? ITERS : 1];
+      if constexpr (MAP) {
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+          const int r = pr0 + (static_cast<int>(threadIdx.x) + it * C::THREADS) / VPR;
+          orow[it] = r < rows_here ? dest_row(out_rows, out_n, row0 + r) : -1;
+        }
+      }
+      barrier_nofence();                                 // the ring (or the previous pass) is free
+      if (wm * C::WTM / PROWS == pass) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int r = wm * C::WTM - pr0 + i * 32 + lr;
+              const int c0 = wn * C::WTN + j * 32 + 8 * g4 + 4 * lk;
+              char* dst = tile + r * ROWP + c0 * static_cast<int>(sizeof(OutT));
+              if constexpr (sizeof(OutT) == 4) {
+                vec16 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = __float_as_uint(fval(i, j, 4 * g4 + t));
+                *reinterpret_cast<vec16*>(dst) = v;
+              } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                u32x2 v;
+                v[0] = bf16x2_hw(fval(i, j, 4 * g4), fval(i, j, 4 * g4 + 1));
+                v[1] = bf16x2_hw(fval(i, j, 4 * g4 + 2), fval(i, j, 4 * g4 + 3));
+                *reinterpret_cast<u32x2*>(dst) = v;
+              }
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int v = static_cast<int>(threadIdx.x) + it * C::THREADS;
+        const int r = v / VPR, cv = v % VPR;
+        if (r >= PROWS || cv >= vec_cols) continue;
+        int64_t drow;
+        if constexpr (MAP) {
+          if (orow[it] < 0) continue;
+          drow = orow[it];
+        } else {
+          if (pr0 + r >= rows_here) continue;
+          drow = row0 + pr0 + r;
+        }
+        const vec16 val = *reinterpret_cast<const vec16*>(tile + r * ROWP + cv * 16);
+        *reinterpret_cast<vec16*>(static_cast<char*>(Cout) + (drow * N + n0) * static_cast<int64_t>(sizeof(OutT)) +
+                                  cv * 16) = val;
+      }
+    }
+  } else if constexpr (STAGED) {
     // Transpose through LDS: every wave writes its fragments into a row-major
     // BM x BN_OUT tile, then all threads store whole rows with 16-byte writes
     // (thread tid stores pieces v = tid + it*THREADS, row v / VPR; with a row
@@ -852,6 +947,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
     int32_t out_n) {
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+  static_assert(!C::SW, "the persistent form stores directly in the unswapped layout");
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
   uint32_t slot, G;
@@ -963,7 +1059,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
 //          (144 KB), persistent -- decode-like segments of a few rows.
 // Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
 // hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
+using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3, 1, 1, true>;
 using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
 using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
 using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
@@ -1003,10 +1099,10 @@ void launch_kernel(bool persistent, const void* a, const void* b0, const void* b
                    int32_t out_n) {
   const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
   // the persistent form has the plain store epilogue only
-  if (C::EPI == kEpiStore && !C::BT && persistent) {
+  if (C::EPI == kEpiStore && !C::BT && !C::SW && persistent) {
     const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
     const int64_t g = upper < slots ? upper : slots;
-    if constexpr (C::EPI == kEpiStore && !C::BT)
+    if constexpr (C::EPI == kEpiStore && !C::BT && !C::SW)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                          static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n);
