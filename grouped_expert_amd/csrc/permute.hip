@@ -88,6 +88,218 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void scatter_rows_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused rank and scatter for problems whose chunk table is small (T*k <=
+// kFuseMaxRoutes): after the count pass (chunks of 64*steps routes, at most
+// kFuseMaxChunks of them), one launch does the rest.  Every block takes
+// kFuseTok tokens (routes r0 .. r0 + kFuseTok*k) and, redundantly and
+// identically in every block:
+//   sel[e] = sum over chunks of table[c][e], counts = min(sel, cap), offsets
+//   = exclusive prefix of counts (one block also writes them out);
+// then for its own routes the route-order rank pos_r = (routes of expert e in
+// chunks before the chunk c0 holding r0) + (routes of e in [c0 * chunk, r0))
+// + (rank among the block's own routes, ballots over the expert code); inv,
+// src and the row copies follow as in the three-pass path.  The block's
+// first term sums a column of the table, the second reads at most one
+// chunk of ids.
+constexpr int kFuseTok = 4;                       // tokens (wavefronts) per block (4 * k <= 64 routes)
+static_assert(kFuseTok * MOE_MAX_TOPK <= kWave, "a block's routes fit one wavefront");
+constexpr int kFuseThreads = kFuseTok * kWave;
+constexpr int kFuseMaxChunks = 32;
+constexpr int64_t kFuseMaxRoutes = 64ll * kRankMaxSteps * kFuseMaxChunks;
+
+// Count-pass geometry of the fused path: as many steps per chunk as keep the
+// table at kFuseMaxChunks rows (at least 4 steps).
+inline RankGeom rank_geom_fused(int64_t n, int32_t B) {
+  RankGeom g = rank_geom(n, B);
+  const int64_t s = (n + 64ll * kFuseMaxChunks - 1) / (64ll * kFuseMaxChunks);
+  g.steps = static_cast<int32_t>(s < 4 ? 4 : (s > kRankMaxSteps ? kRankMaxSteps : s));
+  const int64_t chunk = 64ll * g.steps;
+  g.chunks = (n + chunk - 1) / chunk;
+  return g;
+}
+
+// Exclusive prefix of v[0 .. n) in LDS, in place, by all kFuseThreads
+// threads (each scans a run of consecutive entries, then the runs' totals
+// are scanned across the block); returns the grand total.
+__device__ __forceinline__ int32_t block_scan_lds(int32_t* v, int n, int32_t* wave_tot) {
+  const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
+  const int per = (n + kFuseThreads - 1) / kFuseThreads;
+  const int b0 = t * per, b1 = b0 + per < n ? b0 + per : n;
+  int32_t run = 0;
+  for (int b = b0; b < b1; ++b) run += v[b];
+  int32_t incl = run;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t u = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int32_t wbase = 0, total = 0;
+  for (int i = 0; i < kFuseTok; ++i) {
+    if (i < w) wbase += wave_tot[i];
+    total += wave_tot[i];
+  }
+  int32_t acc = wbase + incl - run;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t x = v[b];
+    v[b] = acc;
+    acc += x;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
+    const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ ids,
+    int32_t E, int64_t cap, RankGeom g, const int32_t* __restrict__ table, int32_t* __restrict__ inv,
+    int32_t* __restrict__ src, int32_t* __restrict__ sel_out, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ dropped_out, vec16* __restrict__ x_perm) {
+  extern __shared__ int32_t lds[];
+  int32_t* sel = lds;                 // [E]   routes per expert
+  int32_t* base = lds + E;            // [E]   running route-order rank base of the block
+  int32_t* offs = lds + 2 * E;        // [E+1] offsets of the accepted counts
+  __shared__ int32_t slot_of[kFuseTok * MOE_MAX_TOPK];
+  __shared__ int32_t wave_tot[kFuseTok];
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int64_t R = T * k;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFuseTok;
+  const int64_t r0 = t0 * k;
+  const int64_t r1 = r0 + kFuseTok * k < R ? r0 + kFuseTok * k : R;
+  const int64_t chunk = 64ll * g.steps;
+  const int64_t c0 = r0 / chunk;
+  const int64_t t = t0 + w;                               // this wavefront's token
+  const bool copy = t < T && x_perm != nullptr;
+  // Every load that depends on no other result is issued first: the table
+  // column pieces, the ids of chunk c0 before r0, the block's own ids and the
+  // first piece of the token row (its latency hides behind the rank work).
+  // table entries per thread and batch (one batch holds the whole table up to
+  // 128 experts)
+  constexpr int kTabPer = kFuseMaxChunks * 128 / kFuseThreads;
+  const int64_t entries = g.chunks * E;
+  int32_t tv[kTabPer];
+#pragma unroll
+  for (int u = 0; u < kTabPer; ++u) {
+    const int64_t idx = tid + static_cast<int64_t>(u) * kFuseThreads;
+    tv[u] = idx < entries ? table[idx] : 0;
+  }
+  constexpr int kPrePer = 64 * kRankMaxSteps / kFuseThreads;                 // chunk ids per thread, at most
+  int32_t pv[kPrePer];
+#pragma unroll
+  for (int u = 0; u < kPrePer; ++u) {
+    const int64_t r = c0 * chunk + tid + u * kFuseThreads;
+    pv[u] = r < r0 ? ids[r] : -1;
+  }
+  const int64_t rme = r0 + lane;
+  const int32_t my_id = (w == 0 && rme < r1) ? ids[rme] : -1;
+  vec16 v[kPiece];
+  const vec16* in = x + (copy ? t : 0) * row_vecs;
+#pragma unroll
+  for (int u = 0; u < kPiece; ++u) {
+    const int64_t c = u * kWave + lane;
+    if (copy && c < row_vecs) v[u] = ld_stream(in + c);
+  }
+  for (int b = tid; b < E; b += kFuseThreads) sel[b] = 0, base[b] = 0;
+  __syncthreads();
+  // expert totals and the routes of every expert in the chunks before c0
+  for (int64_t b0 = 0; b0 < entries; b0 += static_cast<int64_t>(kTabPer) * kFuseThreads) {
+    if (b0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kTabPer; ++u) {
+        const int64_t idx = b0 + tid + static_cast<int64_t>(u) * kFuseThreads;
+        tv[u] = idx < entries ? table[idx] : 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTabPer; ++u) {
+      const int64_t idx = b0 + tid + static_cast<int64_t>(u) * kFuseThreads;
+      if (idx < entries) {
+        const int64_t c = idx / E;
+        const int b = static_cast<int>(idx - c * E);
+        atomicAdd(&sel[b], tv[u]);
+        if (c < c0) atomicAdd(&base[b], tv[u]);
+      }
+    }
+  }
+  // routes of chunk c0 before the block's first route
+#pragma unroll
+  for (int u = 0; u < kPrePer; ++u)
+    if (pv[u] >= 0 && pv[u] < E) atomicAdd(&base[pv[u]], 1);
+  __syncthreads();
+  for (int b = tid; b < E; b += kFuseThreads) offs[b] = cap < 0 ? sel[b] : (sel[b] < cap ? sel[b] : static_cast<int32_t>(cap));
+  __syncthreads();
+  const int32_t A = block_scan_lds(offs, E, wave_tot);
+  if (tid == 0) offs[E] = A;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int b = tid; b < E; b += kFuseThreads) {
+      if (sel_out) sel_out[b] = sel[b];
+      counts_out[b] = cap < 0 ? sel[b] : (sel[b] < cap ? sel[b] : static_cast<int32_t>(cap));
+      offsets_out[b] = offs[b];
+    }
+    if (tid == 0) {
+      offsets_out[E] = A;
+      dropped_out[0] = static_cast<int32_t>(R - A);
+    }
+  }
+  // src entries past the accepted total
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kFuseThreads + tid;
+  if (A + gid < R) src[A + gid] = -1;
+  // the block's routes (at most 64: wavefront 0): stable ranks by ballots over
+  // the expert code
+  if (w == 0) {
+    int nbits = 0;
+    while ((1 << nbits) <= E) ++nbits;
+    const bool inb = rme < r1;
+    const bool valid = my_id >= 0 && my_id < E;
+    const int code = valid ? my_id : E;
+    uint64_t peers = ~0ull;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (code >> bit) & 1;
+      const uint64_t m = ballot(on);
+      peers &= on ? m : ~m;
+    }
+    int32_t slot = -1;
+    if (valid) {
+      const int32_t pos = base[my_id] + __popcll(peers & lanemask_lt());
+      if (cap < 0 || pos < cap) slot = offs[my_id] + pos;
+    }
+    if (inb) {
+      inv[rme] = slot;
+      if (slot >= 0) src[slot] = static_cast<int32_t>(rme);
+      slot_of[lane] = slot;
+    }
+  }
+  __syncthreads();
+  // row copies: one wavefront per token, the row read once
+  if (!copy) return;
+  int32_t slot[MOE_MAX_TOPK];
+  int live = 0;
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = slot_of[w * k + j];
+    if (p >= 0) slot[live++] = p;
+  }
+  if (live == 0) return;
+  for (int64_t cc = 0; cc < row_vecs; cc += kPiece * kWave) {
+    if (cc > 0) {
+#pragma unroll
+      for (int u = 0; u < kPiece; ++u) {
+        const int64_t c = cc + u * kWave + lane;
+        if (c < row_vecs) v[u] = ld_stream(in + c);
+      }
+    }
+    for (int j = 0; j < live; ++j) {
+      vec16* out = x_perm + static_cast<int64_t>(slot[j]) * row_vecs;
+#pragma unroll
+      for (int u = 0; u < kPiece; ++u) {
+        const int64_t c = cc + u * kWave + lane;
+        if (c < row_vecs) out[c] = v[u];
+      }
+    }
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -146,8 +358,25 @@ int permute_launch(const void* x, int32_t x_dtype, int64_t T, int32_t d, const i
                    int32_t E, int64_t capacity, void* x_perm, int32_t* src, int32_t* inv, int32_t* sel_counts,
                    int32_t* counts, int32_t* offsets, int32_t* n_dropped, int32_t* table, uint32_t* dev_flags,
                    hipStream_t stream) {
-  const RankGeom g = rank_geom(T * k, E);
   const int64_t R = T * k;
+  if (R > 0 && R <= kFuseMaxRoutes) {
+    // count pass, then the fused rank and scatter
+    const RankGeom g = rank_geom_fused(R, E);
+    const unsigned cblocks = static_cast<unsigned>((g.chunks + kRankWaves - 1) / kRankWaves);
+    const size_t clds = static_cast<size_t>(kRankWaves) * g.B * sizeof(int32_t);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(rank_count_kernel<ExpertBucket>), dim3(cblocks), dim3(kRankThreads), clds,
+                       stream, ExpertBucket{topk_ids, E}, g, table, dev_flags);
+    MOE_LAUNCH_CHECK();
+    const int64_t row_vecs = x_perm ? row_bytes(x_dtype, d) / 16 : 0;
+    const unsigned blocks = static_cast<unsigned>((T + kFuseTok - 1) / kFuseTok);
+    const size_t lds = static_cast<size_t>(3 * E + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(permute_fused_kernel, dim3(blocks), dim3(kFuseThreads), lds, stream,
+                       static_cast<const vec16*>(x), T, row_vecs, k, topk_ids, E, capacity, g, table, inv, src,
+                       sel_counts, counts, offsets, n_dropped, static_cast<vec16*>(x_perm));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
+  const RankGeom g = rank_geom(T * k, E);
   RankScanOut out{sel_counts, counts, offsets, n_dropped, 1};
   int st = bucket_rank(g, ExpertBucket{topk_ids, E}, PermuteEmit{capacity, R, offsets, inv, src}, capacity, out,
                        table, dev_flags, stream);
