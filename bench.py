@@ -103,19 +103,30 @@ def sources_digest(call):
     return h.hexdigest()
 
 
+def _cfg_args(kernel):
+    """Template arguments of a GEMM kernel's tile configuration (Cfg<...>)."""
+    m = re.search(r"Cfg<([^<>]*)>", kernel)
+    return m.group(1).split(", ") if m else []
+
+
+def _is_bwd_gemm(kernel):
+    """Expert-backward GEMMs carry the SwiGLU-backward epilogue (tile argument
+    14, EPI) or K-major B tiles (argument 15, BT)."""
+    a = _cfg_args(kernel)
+    return (len(a) > 13 and a[13] != "0") or (len(a) > 14 and a[14] == "true")
+
+
 def _call_of(kernel, train=False):
     """The library call a dispatched kernel belongs to (None: not ours).
     Bucket-rank and tile-table kernels serve several calls and are given to
     the call of the next dispatch, by the caller of this function ("rank").
-    The expert backward's GEMMs carry the SwiGLU-backward epilogue or K-major
-    B tiles (the last two tile parameters); in a training step the fp32
-    combine is the token-gradient pass."""
+    In a training step the fp32 combine is the token-gradient pass."""
     if "grouped_gemm_" in kernel:
-        m = re.search(r"Cfg<[^<>]*, (\d+), (true|false)>", kernel)
-        return "swiglu_bwd" if m and (m.group(1) != "0" or m.group(2) == "true") else "swiglu"
-    table = (("route_topk_kernel", "route"), ("route_grouped_kernel", "route"), ("build_tiles_kernel", "rank"),
+        return "swiglu_bwd" if _is_bwd_gemm(kernel) else "swiglu"
+    table = (("route_list_kernel", "route"), ("route_topk_kernel", "route"), ("route_grouped_kernel", "route"),
+             ("build_tiles_kernel", "rank"),
              ("transpose_rows_kernel", "swiglu_bwd"), ("grouped_wgrad_kernel", "swiglu_bwd"),
-             ("scatter_rows_kernel", "permute"), ("pack_kernel", "pool_pack"),
+             ("scatter_rows_kernel", "permute"), ("permute_fused_kernel", "permute"), ("pack_kernel", "pool_pack"),
              ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
              ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),
              ("combine_backward_kernel", "combine_bwd"), ("rank_", "rank"))
@@ -128,10 +139,17 @@ def _call_of(kernel, train=False):
 
 
 # one dispatch per call instance: counts the launches of each call
-_ANCHORS = {"route": "route_", "swiglu": "grouped_gemm_", "permute": "scatter_rows_kernel",
-            "combine": "combine_kernel", "expand": "expand_rows_kernel", "pool_pack": "pack_kernel",
-            "recv_compact": "compact_", "quantize": "quantize_kernel", "combine_bwd": "combine_backward_kernel",
-            "swiglu_bwd": ", 1, false>", "dx_combine": "combine_kernel"}
+_ANCHORS = {"route": lambda n: "route_" in n,
+            "swiglu": lambda n: "grouped_gemm_" in n,
+            "permute": lambda n: "scatter_rows_kernel" in n or "permute_fused_kernel" in n,
+            "combine": lambda n: "combine_kernel" in n,
+            "expand": lambda n: "expand_rows_kernel" in n,
+            "pool_pack": lambda n: "pack_kernel" in n,
+            "recv_compact": lambda n: "compact_" in n,
+            "quantize": lambda n: "quantize_kernel" in n,
+            "combine_bwd": lambda n: "combine_backward_kernel" in n,
+            "swiglu_bwd": lambda n: "grouped_gemm_" in n and len(_cfg_args(n)) > 13 and _cfg_args(n)[13] == "1",
+            "dx_combine": lambda n: "combine_kernel" in n}
 # calls whose anchor kernel is dispatched more than once per call
 _ANCHOR_PER_CALL = {"swiglu": 2}
 
@@ -164,7 +182,7 @@ def record_traffic(args):
             if not c:
                 continue
             kib[c] = kib.get(c, 0.0) + float(rows[i]["Counter_Value"])
-            if _ANCHORS[c] in names[i]:
+            if _ANCHORS[c](names[i]):
                 launches[c] = launches.get(c, 0) + 1
         launches = {c: v // _ANCHOR_PER_CALL.get(c, 1) for c, v in launches.items()}
         per[counter] = dict(factor=factor, bytes={c: kib[c] * 1024.0 * factor / launches[c] for c in kib},

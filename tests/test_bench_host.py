@@ -31,11 +31,9 @@ def _write_counters(path, counter, rows):
 
 def test_record_traffic_attributes_kernels_to_calls(tmp_path, monkeypatch):
     calib_kib = bench.COPY_CALIB_BYTES / 1024
-    step = [("void moe::(anonymous namespace)::route_topk_kernel<2>(float const*)", 10.0),
-            ("void moe::(anonymous namespace)::rank_count_kernel<ExpertBucket>(x)", 1.0),
-            ("moe::(anonymous namespace)::rank_scan_kernel(x)", 2.0),
-            ("void moe::(anonymous namespace)::rank_emit_kernel<ExpertBucket, PermuteEmit>(x)", 3.0),
-            ("moe::(anonymous namespace)::scatter_rows_kernel(x)", 100.0),
+    step = [("void moe::(anonymous namespace)::route_list_kernel<16, 8, 8, true>(float const*)", 10.0),
+            ("void moe::(anonymous namespace)::rank_count_kernel<ExpertBucket>(x)", 6.0),
+            ("moe::(anonymous namespace)::permute_fused_kernel(x)", 100.0),
             ("moe::(anonymous namespace)::build_tiles_kernel(x)", 0.5),
             ("void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<Cfg<...> >(x)", 1000.0),
             ("void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<Cfg<...> >(y)", 500.0),
@@ -76,8 +74,10 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
     call of the next dispatch, and the fp32 combine is the token-gradient pass."""
     calib_kib = bench.COPY_CALIB_BYTES / 1024
     ns = "moe::(anonymous namespace)::"
-    gemm = "void " + ns + "grouped_gemm_bf16_kernel<" + ns + "Cfg<128, 256, 2, 4, 3, {}, {}, false, 64, 1, 2, 8, false, {}, {}> >(x)"
-    step = [("void " + ns + "route_topk_kernel<2>(float const*)", 1.0),
+    # tile arguments as the library names them: ..., EPI, BT, A stages, fragment distances, swapped layout
+    gemm = ("void " + ns + "grouped_gemm_bf16_kernel<" + ns +
+            "Cfg<128, 256, 2, 4, 3, {}, {}, false, 64, 1, 2, 8, false, {}, {}, 2, 1, 1, false>, false>(x)")
+    step = [("void " + ns + "route_list_kernel<16, 8, 8, true>(float const*)", 1.0),
             ("void " + ns + "rank_count_kernel<ExpertBucket>(x)", 1.0),
             (ns + "scatter_rows_kernel(x)", 10.0),
             (ns + "build_tiles_kernel(x)", 0.5),
