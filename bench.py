@@ -126,6 +126,7 @@ def _call_of(kernel, train=False):
     table = (("route_list_kernel", "route"), ("route_topk_kernel", "route"), ("route_grouped_kernel", "route"),
              ("build_tiles_kernel", "rank"),
              ("transpose_rows_kernel", "swiglu_bwd"), ("grouped_wgrad_kernel", "swiglu_bwd"),
+             ("swiglu_bwd_rows_kernel", "swiglu_bwd"),
              ("scatter_rows_kernel", "permute"), ("permute_fused_kernel", "permute"), ("pack_kernel", "pool_pack"),
              ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
              ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),
@@ -148,7 +149,10 @@ _ANCHORS = {"route": lambda n: "route_" in n,
             "recv_compact": lambda n: "compact_" in n,
             "quantize": lambda n: "quantize_kernel" in n,
             "combine_bwd": lambda n: "combine_backward_kernel" in n,
-            "swiglu_bwd": lambda n: "grouped_gemm_" in n and len(_cfg_args(n)) > 13 and _cfg_args(n)[13] == "1",
+            # dG | dU come from the gate/up GEMM's SwiGLU-backward epilogue, or
+            # from the saved activations in a row pass: one of the two per call
+            "swiglu_bwd": lambda n: ("grouped_gemm_" in n and len(_cfg_args(n)) > 13 and _cfg_args(n)[13] == "1")
+            or "swiglu_bwd_rows_kernel" in n,
             "dx_combine": lambda n: "combine_kernel" in n}
 # calls whose anchor kernel is dispatched more than once per call
 _ANCHOR_PER_CALL = {"swiglu": 2}
@@ -405,16 +409,17 @@ def layer_setup(torch, w, banks):
     return host, bank_list
 
 
-def layer_step(ge, timer, w, bank, flags):
+def layer_step(ge, timer, w, bank, flags, save_act=False):
     import torch
     T = w.T
     ids, gates = timer.run("route", ge.route_topk, bank["logits"], w.k, flags=flags)
     plan = timer.run("permute", ge.permute, bank["x"], ids, w.E, w.capacity, flags=flags)
     zdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    act = ge.new_act(T * w.k, w.d_ff, bank["x"].device) if save_act else None
     z = timer.run("swiglu", ge.grouped_swiglu, plan["x_perm"], plan["offsets"], plan["counts"], bank["wg"],
-                  bank["wu"], bank["wd"], z_dtype=zdt, flags=flags)
+                  bank["wu"], bank["wd"], z_dtype=zdt, flags=flags, act=act)
     y = timer.run("combine", ge.unpermute_combine, z, plan["inv"], gates, T, w.k, flags=flags)
-    return dict(y=y, ids=ids, gates=gates, plan=plan, z=z)
+    return dict(y=y, ids=ids, gates=gates, plan=plan, z=z, act=act)
 
 
 def layer_ledger(w, counts):
@@ -458,32 +463,37 @@ def train_setup(torch, w, banks):
 
 
 def train_step(ge, timer, w, bank, flags):
-    """Forward of the layer, then its backward: route and gate gradients, the
-    expert backward (route-input and weight gradients), and the token
-    gradients through the inverse map."""
-    out = layer_step(ge, timer, w, bank, flags)
+    """Forward of the layer saving the experts' activations, then its
+    backward: route and gate gradients, the expert backward (route-input and
+    weight gradients, from the saved activations), and the token gradients
+    through the inverse map."""
+    out = layer_step(ge, timer, w, bank, flags, save_act=True)
     plan, T, k = out["plan"], w.T, w.k
     dz, dg = timer.run("combine_bwd", ge.combine_backward, bank["dy"], out["z"], plan["inv"], out["gates"], k,
                        flags=flags)
     bw = timer.run("swiglu_bwd", ge.grouped_swiglu_backward, plan["x_perm"], dz, plan["offsets"], plan["counts"],
-                   bank["wg"], bank["wu"], bank["wd"], flags=flags)
+                   bank["wg"], bank["wu"], bank["wd"], flags=flags, act=out["act"])
     dx = timer.run("dx_combine", ge.unpermute_combine, bw["dx"], plan["inv"], None, T, k, flags=flags)
     out.update(dx=dx, dgates=dg, grads=bw)
     return out
 
 
 def train_ledger(w, counts):
-    """The forward ledger plus the backward calls.  The expert backward does
-    16 A d d_ff flops (dH, the recomputed gate/up, dX, dW_d, dW_g and dW_u)
-    and moves x and dZ rows in, dX rows out (fp32), the active experts'
-    weights in and every expert's fp32 weight gradients out."""
+    """The forward ledger plus the backward calls.  The forward also writes
+    the saved activations (G | U and H, bf16: 3 A d_ff values).  The expert
+    backward does 12 A d d_ff flops (dH, dX, dW_d, dW_g and dW_u; G, U and H
+    are read, not recomputed) and moves x and dZ rows and the saved
+    activations in, dX rows out (fp32), the active experts' weights in and
+    every expert's fp32 weight gradients out."""
     led = layer_ledger(w, counts)
     A = int(counts.sum())
     E_act = int((counts > 0).sum())
     T, k, d, dff, E = w.T, w.k, w.d, w.d_ff, w.E
+    led["swiglu"]["bytes"] += A * 3 * dff * 2
     led["combine_bwd"] = dict(bytes=4 * T * d + A * d * 2 + A * d * 2 + 12 * T * k, flops=2 * A * d)
-    led["swiglu_bwd"] = dict(bytes=2 * A * d * 2 + E_act * 3 * d * dff * 2 + A * d * 4 + E * 3 * d * dff * 4,
-                             flops=16 * A * d * dff)
+    led["swiglu_bwd"] = dict(bytes=2 * A * d * 2 + A * 3 * dff * 2 + E_act * 3 * d * dff * 2 + A * d * 4 +
+                                   E * 3 * d * dff * 4,
+                             flops=12 * A * d * dff)
     led["dx_combine"] = dict(bytes=A * d * 4 + 4 * T * k + 4 * T * d, flops=A * d)
     return led
 

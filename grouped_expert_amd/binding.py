@@ -52,12 +52,12 @@ _SIGS = {
                                            _p, _p, _p]),
     "moe_grouped_swiglu_workspace": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_grouped_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _i32, _p,
-                                          _i64, _p, _sz, _p, _p]),
+                                          _i64, _p, _p, _sz, _p, _p]),
     "moe_unpermute_combine": (ctypes.c_int, [_p, _i32, _i32, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p]),
     "moe_combine_backward": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _i64, _p, _p, _i32, _p, _i32, _p, _p, _p]),
     "moe_grouped_swiglu_backward_workspace": (_sz, [_i64, _i32, _i32, _i32]),
-    "moe_grouped_swiglu_backward": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _i32,
-                                                   _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_grouped_swiglu_backward": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
+                                                   _i32, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_pool_pack_workspace": (_sz, [_i64, _i32, _i32]),
     "moe_pool_pack": (ctypes.c_int, [_p, _i32, _i32, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p,
                                      _p, _p, _p, _p, _sz, _p, _p]),
@@ -275,9 +275,12 @@ def permute_noalloc(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, c
 def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor, w_gate: torch.Tensor,
                    w_up: torch.Tensor, w_down: torch.Tensor, z_dtype=torch.float32,
                    z: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None,
-                   z_rows: Optional[torch.Tensor] = None):
+                   z_rows: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None):
     """Runs expert ``e`` on rows ``[seg_start[e], seg_start[e]+seg_count[e])``
     of ``x``; returns ``z`` (rows outside every segment are left as allocated).
+
+    With ``act`` (bf16, :func:`new_act` of ``x``'s rows and ``d_ff``) the call
+    also saves the activations :func:`grouped_swiglu_backward` can take.
 
     With ``z_rows`` (int32 ``[rows]``, e.g. ``recv_compact``'s ``slot_row``)
     row ``i`` of the result is stored as row ``z_rows[i]`` of ``z``, which
@@ -296,8 +299,12 @@ def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Te
         _expect("z", z, (None, d), _FLOATS)
     else:
         _expect("z", z, (rows, d), _FLOATS)
+    if act is not None:
+        _expect("act", act, (3 * rows * d_ff,), torch.bfloat16)
+        if x.dtype != torch.bfloat16:
+            raise ValueError("act: saved activations need the bf16 path")
     _flags_ok(flags)
-    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags, z_rows)
+    _need_gpu(x, seg_start, seg_count, w_gate, w_up, w_down, z, flags, z_rows, act)
     dev = x.device
     if z is None:
         z = torch.empty((rows, d), dtype=z_dtype, device=dev)
@@ -305,9 +312,15 @@ def grouped_swiglu(x: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Te
     ws = _ws(lib.moe_grouped_swiglu_workspace(rows, E, d_ff, dt), dev)
     _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
         _ptr(x), dt, d, d_ff, E, _ptr(seg_start), _ptr(seg_count), rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-        _ptr(z), _dtype_code(z), _ptr(z_rows), z.shape[0] if z_rows is not None else 0, _ptr(ws), ws.numel(),
-        _ptr(flags), _stream(dev)))
+        _ptr(z), _dtype_code(z), _ptr(z_rows), z.shape[0] if z_rows is not None else 0, _ptr(act), _ptr(ws),
+        ws.numel(), _ptr(flags), _stream(dev)))
     return z
+
+
+def new_act(rows: int, d_ff: int, device) -> torch.Tensor:
+    """Buffer for the saved activations of :func:`grouped_swiglu` (G | U, then
+    H: ``3 * rows * d_ff`` bf16)."""
+    return torch.empty(3 * rows * d_ff, dtype=torch.bfloat16, device=device)
 
 
 def unpermute_combine(z: torch.Tensor, idx: torch.Tensor, gates: Optional[torch.Tensor], T: int, k: int,
@@ -428,9 +441,11 @@ def combine_backward(dy: torch.Tensor, z: torch.Tensor, idx: torch.Tensor, gates
 def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.Tensor, seg_count: torch.Tensor,
                             w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                             dx_dtype: torch.dtype = torch.float32, dx: Optional[torch.Tensor] = None,
-                            flags: Optional[torch.Tensor] = None):
+                            flags: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None):
     """Expert backward over the segments; returns a dict with dx (route-input
-    gradients, rows of x), dw_gate, dw_up, dw_down (fp32)."""
+    gradients, rows of x), dw_gate, dw_up, dw_down (fp32).  With ``act`` (the
+    activations a :func:`grouped_swiglu` call saved for the same ``x`` and
+    segments) G, U and H are taken from it instead of recomputed."""
     _expect("x", x, (None, None), torch.bfloat16)
     rows, d = x.shape
     _expect("dz", dz, (rows, d), torch.bfloat16)
@@ -440,8 +455,10 @@ def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.
     _expect("w_down", w_down, (E, d, d_ff), torch.bfloat16)
     _segments_ok(seg_start, seg_count, E)
     _expect("dx", dx, (rows, d), _FLOATS)
+    if act is not None:
+        _expect("act", act, (3 * rows * d_ff,), torch.bfloat16)
     _flags_ok(flags)
-    _need_gpu(x, dz, seg_start, seg_count, w_gate, w_up, w_down, dx, flags)
+    _need_gpu(x, dz, seg_start, seg_count, w_gate, w_up, w_down, dx, flags, act)
     dev = x.device
     if dx is None:
         dx = torch.empty((rows, d), dtype=dx_dtype, device=dev)
@@ -451,8 +468,8 @@ def grouped_swiglu_backward(x: torch.Tensor, dz: torch.Tensor, seg_start: torch.
     ws = _ws(lib.moe_grouped_swiglu_backward_workspace(rows, E, d, d_ff), dev)
     _check("moe_grouped_swiglu_backward", lib.moe_grouped_swiglu_backward(
         _ptr(x), d, d_ff, E, _ptr(seg_start), _ptr(seg_count), rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-        _ptr(dz), _ptr(dx), _dtype_code(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(ws), ws.numel(), _ptr(flags),
-        _stream(dev)))
+        _ptr(dz), _ptr(act), _ptr(dx), _dtype_code(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(ws), ws.numel(),
+        _ptr(flags), _stream(dev)))
     return dict(dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd)
 
 

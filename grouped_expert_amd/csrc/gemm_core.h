@@ -33,8 +33,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int64_t rows, int32_t BM, int32_t max_tiles,
                                                            TileEntry* __restrict__ tiles,
                                                            int32_t* __restrict__ n_tiles, uint32_t* flags,
-                                                           int32_t* __restrict__ exp_first = nullptr,
-                                                           int32_t* __restrict__ exp_ntile = nullptr) {
+                                                           int32_t* __restrict__ exp_rows = nullptr) {
   __shared__ int32_t sh16[17];
   const int t = threadIdx.x;
   int32_t s = 0, c = 0;
@@ -55,9 +54,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   const int32_t keep = pre >= max_tiles ? 0 : (cnt < max_tiles - pre ? cnt : max_tiles - pre);
   for (int32_t i = 0; i < keep; ++i)
     tiles[pre + i] = TileEntry{t, s + i * BM, s + c, pre, keep, 0, 0, 0};
-  if (exp_first && t < E) {              // per-expert run of tiles (for K-ragged products)
-    exp_first[t] = pre < max_tiles ? pre : max_tiles;
-    exp_ntile[t] = keep;
+  if (exp_rows && t < E) {               // per expert: first row and the rows its tiles cover
+    exp_rows[2 * t] = s;
+    exp_rows[2 * t + 1] = c < keep * BM ? c : keep * BM;
   }
   if (t == 0) {
     n_tiles[0] = total < max_tiles ? total : max_tiles;
@@ -183,7 +182,7 @@ constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
           int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore,
-          bool BT_ = false, int AST_ = 2, int PB_ = 1, int PA_ = 1, bool SW_ = false>
+          bool BT_ = false, int AST_ = 2, int PB_ = 1, int PA_ = 1, bool SW_ = false, bool SV_ = false>
 struct Cfg {
   static constexpr int EPI = EPI_;
   // BT: B is stored K-major, [K][N] per expert with N contiguous (a weight
@@ -209,6 +208,10 @@ struct Cfg {
   // consecutive rows of one column) and the epilogue moves 8- or 16-byte
   // pieces; plain-store tiles staged through LDS only
   static constexpr bool SW = SW_;
+  // SV (gate/up tiles): the epilogue also stores the pre-activations G and U
+  // (bf16) into a [rows, 2 N] buffer (G in columns [0, N), U in [N, 2 N)),
+  // for a backward that takes them instead of recomputing them
+  static constexpr bool SV = SV_;
   static constexpr int THREADS = NW * 64;
   static constexpr int GROUP_M = GM_;                     // M-tiles per band of the grouped order (1 = off)
   static constexpr int BM = BM_, BNB = BNB_, WM = WM_, WN = WN_, STAGES = STAGES_, BK = BK_;
@@ -239,6 +242,7 @@ struct Cfg {
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
   static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
   static_assert(AST == 2 || (RS && AST == 3), "three A stages only with register-staged B rows");
+  static_assert(!SV || (GATEUP && !SW), "saved pre-activations: gate/up tiles in the unswapped layout");
   static_assert(EPI == kEpiStore || GATEUP, "the SwiGLU backward epilogue needs gate/up tiles");
   static_assert(!BT || (!GATEUP && !RS_ && BK == 64 && (BNB == 128 || BNB == 256)), "K-major B tiles");
   static constexpr int BRB = BNB * 2;                     // BT: bytes per k-row of the B region
@@ -412,8 +416,23 @@ __device__ __forceinline__ int32_t lane_dest_row(const int32_t* __restrict__ out
 // block (i, j) of the wave's tile) to row m of Cout, or with a row map to the
 // row held by lane_dst of the lane that owns m (lane_dest_row).
 template <class C, bool MAP, class OutT, class Value>
+__device__ __forceinline__ void store_direct_at(void* __restrict__ Cout, int32_t ld, int32_t col_off, int32_t N,
+                                                int32_t row0, int32_t row_end, int32_t n0, int wm, int wn, int lane,
+                                                int32_t lane_dst, Value value);
+
+// Direct-store epilogue into a row-major [*, N] matrix.
+template <class C, bool MAP, class OutT, class Value>
 __device__ __forceinline__ void store_direct(void* __restrict__ Cout, int32_t N, int32_t row0, int32_t row_end,
                                              int32_t n0, int wm, int wn, int lane, int32_t lane_dst, Value value) {
+  store_direct_at<C, MAP, OutT>(Cout, N, 0, N, row0, row_end, n0, wm, wn, lane, lane_dst, value);
+}
+
+// The same into columns [col_off, col_off + N) of a matrix with row stride ld
+// (columns of the tile at or past N are not stored).
+template <class C, bool MAP, class OutT, class Value>
+__device__ __forceinline__ void store_direct_at(void* __restrict__ Cout, int32_t ld, int32_t col_off, int32_t N,
+                                                int32_t row0, int32_t row_end, int32_t n0, int wm, int wn, int lane,
+                                                int32_t lane_dst, Value value) {
   const int lr = lane % 32, lk = lane / 32;
   const bool full_rows = row0 + C::BM <= row_end;
 #pragma unroll
@@ -441,7 +460,7 @@ __device__ __forceinline__ void store_direct(void* __restrict__ Cout, int32_t N,
     for (int q = 0; q < 16; ++q) {
       if (dst[q] < 0) continue;
       OutT* rowp = static_cast<OutT*>(Cout) +
-                   static_cast<uint64_t>(static_cast<uint32_t>(dst[q])) * static_cast<uint32_t>(N) + col0;
+                   static_cast<uint64_t>(static_cast<uint32_t>(dst[q])) * static_cast<uint32_t>(ld) + col_off + col0;
       if (all_cols) {
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) rowp[j * 32] = value(i, j, q);
@@ -885,6 +904,13 @@ __device__ __forceinline__ void gemm_tile(
   } else {
     store_direct<C, MAP, OutT>(Cout, N, row0, row_end, n0, wm, wn, lane, lane_dst, value);
   }
+  if constexpr (C::SV) {
+    // the pre-activations G | U of the tile's rows into aux_out [rows, 2 N]
+    store_direct_at<C, false, bf16_t>(aux_out, 2 * N, 0, N, row0, row_end, n0, wm, wn, lane, 0,
+                                      [&](int i, int j, int q) { return bf16_hw(acc[0][i][j][q]); });
+    store_direct_at<C, false, bf16_t>(aux_out, 2 * N, N, N, row0, row_end, n0, wm, wn, lane, 0,
+                                      [&](int i, int j, int q) { return bf16_hw(acc[1][i][j][q]); });
+  }
 }
 
 // Workgroups walk the tile list with even rounds (one tile at a time: the
@@ -944,7 +970,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
-    int32_t out_n) {
+    int32_t out_n, bf16_t* __restrict__ aux_out) {
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
   static_assert(!C::SW, "the persistent form stores directly in the unswapped layout");
@@ -1038,6 +1064,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
                             else
                               return bf16_hw(acc[0][i][j][q]);
                           });
+    if constexpr (C::SV) {
+      // the pre-activations G | U of the tile's rows into aux_out [rows, 2 N]
+      store_direct_at<C, false, bf16_t>(aux_out, 2 * N, 0, N, t.row0, t.row_end, t.n0, wm, wn, lane, 0,
+                                        [&](int i, int j, int q) { return bf16_hw(acc[0][i][j][q]); });
+      store_direct_at<C, false, bf16_t>(aux_out, 2 * N, N, N, t.row0, t.row_end, t.n0, wm, wn, lane, 0,
+                                        [&](int i, int j, int q) { return bf16_hw(acc[1][i][j][q]); });
+    }
   }
 }
 
@@ -1066,6 +1099,11 @@ using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
 using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
 using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
 using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
+// gate/up tiles that also save the pre-activations G | U (training forward):
+// the same tilings in the unswapped layout
+using CfgLgGUS = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3, 1, 1, false, true>;
+using CfgMdGUS = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8, false, kEpiStore, false, 2, 1, 1, false, true>;
+using CfgSmGUS = Cfg<32, 256, 1, 4, 4, true, false, false, 64, 1, 1, 4, false, kEpiStore, false, 2, 1, 1, false, true>;
 using CfgSmDF = Cfg<32, 256, 1, 4, 4, false, true>;
 using CfgSmDB = Cfg<32, 256, 1, 4, 4, false, false>;
 
@@ -1105,7 +1143,8 @@ void launch_kernel(bool persistent, const void* a, const void* b0, const void* b
     if constexpr (C::EPI == kEpiStore && !C::BT && !C::SW)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n);
+                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n,
+                         static_cast<bf16_t*>(aux_out));
   } else {
     // at most one workgroup per CU slot; each walks its tiles (even rounds);
     // register-staged tiles: one workgroup per tile
@@ -1136,14 +1175,20 @@ void launch_one(bool persistent, const void* a, const void* b0, const void* b1, 
                           kb1, nullptr, 0);
 }
 
-template <class GU, class DF, class DB, bool PERSIST>
+// Gate/up then down projection.  With gu_save the gate/up tiles GUS also
+// store the pre-activations G | U there ([rows, 2 d_ff], bf16).
+template <class GU, class GUS, class DF, class DB, bool PERSIST>
 int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
                 void* z, int32_t z_dtype, const int32_t* z_rows, int32_t z_n, const TileEntry* tiles,
-                const int32_t* n_tiles, int32_t max_tiles, hipStream_t stream) {
+                const int32_t* n_tiles, int32_t max_tiles, void* gu_save, hipStream_t stream) {
+  static_assert(GU::BM == GUS::BM && GU::BN_OUT == GUS::BN_OUT, "one tiling with and without the saved G | U");
   const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
   const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
   MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
-  launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
+  if (gu_save)
+    launch_one<GUS>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, gu_save);
+  else
+    launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
     launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,

@@ -146,7 +146,7 @@ MOE_API size_t moe_grouped_swiglu_workspace(int64_t rows, int32_t E, int32_t d_f
 MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t d_ff, int32_t E,
                                const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
                                const void* w_gate, const void* w_up, const void* w_down, void* z, int32_t z_dtype,
-                               const int32_t* z_rows, int64_t z_n_rows, void* ws, size_t ws_bytes,
+                               const int32_t* z_rows, int64_t z_n_rows, void* act, void* ws, size_t ws_bytes,
                                uint32_t* dev_flags, hipStream_t stream) {
   using namespace moe;
   MOE_CHECK(dtype == MOE_F32 || dtype == MOE_BF16, MOE_EINVAL);
@@ -166,10 +166,14 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   const int32_t z_n = z_rows ? static_cast<int32_t>(z_n_rows) : 0;
   MOE_CHECK((x == nullptr || aligned16(x)) && (z == nullptr || aligned16(z)), MOE_EINVAL);
   MOE_CHECK(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down), MOE_EINVAL);
+  // saved activations: bf16 path only
+  MOE_CHECK(act == nullptr || dtype == MOE_BF16, MOE_EUNSUPPORTED);
+  MOE_CHECK(act == nullptr || aligned16(act), MOE_EINVAL);
   const WsLayout L = ws_layout(rows, E, d_ff, dtype);
   MOE_CHECK(ws && ws_bytes >= L.total && aligned16(ws), MOE_EWORKSPACE);
   char* wsb = static_cast<char*>(ws);
-  void* H = wsb + L.h_off;
+  // H in the workspace, or in the H plane of the saved activations
+  void* H = act ? static_cast<char*>(act) + static_cast<size_t>(rows) * 2 * d_ff * 2 : wsb + L.h_off;
   TileEntry* tiles = reinterpret_cast<TileEntry*>(wsb + L.tiles_off);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + L.ntiles_off);
 
@@ -194,13 +198,13 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   }
   switch (pick_tiles(rows, E)) {
     case kLarge:
-      return launch_bf16<CfgLgGU, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
-                                                    L.max_tiles, stream);
+      return launch_bf16<CfgLgGU, CfgLgGUS, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+                                                                z_n, tiles, n_tiles, L.max_tiles, act, stream);
     case kMedium:
-      return launch_bf16<CfgMdGU, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
-                                                    L.max_tiles, stream);
+      return launch_bf16<CfgMdGU, CfgMdGUS, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+                                                                z_n, tiles, n_tiles, L.max_tiles, act, stream);
     default:
-      return launch_bf16<CfgSmGU, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows, z_n, tiles, n_tiles,
-                                                    L.max_tiles, stream);
+      return launch_bf16<CfgSmGU, CfgSmGUS, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+                                                                z_n, tiles, n_tiles, L.max_tiles, act, stream);
   }
 }

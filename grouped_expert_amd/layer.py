@@ -20,19 +20,22 @@ from . import binding as B
 
 def moe_layer(x: torch.Tensor, logits: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
               w_down: torch.Tensor, k: int, capacity: int = -1, z_dtype: Optional[torch.dtype] = None,
-              flags: Optional[torch.Tensor] = None):
+              flags: Optional[torch.Tensor] = None, save_act: bool = False):
     """Returns ``(y fp32 [T, d], state)`` where state holds the intermediate
-    routing and dispatch tensors."""
+    routing and dispatch tensors; with ``save_act`` (bf16) also the experts'
+    activations for :func:`moe_layer_backward`, which then reads each weight
+    once instead of recomputing the gate/up product."""
     E = w_gate.shape[0]
     T = x.shape[0]
     if z_dtype is None:
         z_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
     ids, gates = B.route_topk(logits, k, flags=flags)
     plan = B.permute(x, ids, E, capacity, flags=flags)
+    act = B.new_act(plan["x_perm"].shape[0], w_gate.shape[1], x.device) if save_act else None
     z = B.grouped_swiglu(plan["x_perm"], plan["offsets"], plan["counts"], w_gate, w_up, w_down,
-                         z_dtype=z_dtype, flags=flags)
+                         z_dtype=z_dtype, flags=flags, act=act)
     y = B.unpermute_combine(z, plan["inv"], gates, T, k, flags=flags)
-    return y, dict(ids=ids, gates=gates, plan=plan, z=z)
+    return y, dict(ids=ids, gates=gates, plan=plan, z=z, act=act)
 
 
 def moe_layer_backward(dy: torch.Tensor, x: torch.Tensor, state: dict, w_gate: torch.Tensor, w_up: torch.Tensor,
@@ -50,7 +53,7 @@ def moe_layer_backward(dy: torch.Tensor, x: torch.Tensor, state: dict, w_gate: t
     T, k = state["ids"].shape
     dz, dg = B.combine_backward(dy, state["z"], plan["inv"], state["gates"], k, dz_dtype=x.dtype, flags=flags)
     bw = B.grouped_swiglu_backward(plan["x_perm"], dz, plan["offsets"], plan["counts"], w_gate, w_up, w_down,
-                                   flags=flags)
+                                   flags=flags, act=state.get("act"))
     dx = B.unpermute_combine(bw["dx"], plan["inv"], None, T, k, flags=flags)
     return dx, dict(dgates=dg, dw_gate=bw["dw_gate"], dw_up=bw["dw_up"], dw_down=bw["dw_down"], dz=dz,
                     dx_rows=bw["dx"])

@@ -318,13 +318,22 @@ int moe_permute_noalloc(const void* x, int32_t x_dtype, int64_t T, int32_t d,
  *              the receiver returns results in the pools' layout), the rows
  *              that compaction rejected being zeroed by that call.
  *   z_n_rows   rows of z when z_rows is given (<= INT32_MAX; ignored otherwise)
+ *   act        NULL, or (bf16 path only, 16-byte aligned) device bf16
+ *              [3 * rows * d_ff] that receives, for every row of a segment,
+ *              the activations the expert backward needs ("M6.2 - Expert
+ *              Parallelism and DeepSeek MoE", 0x03D: saved forward state):
+ *              plane 1, [rows, 2 d_ff]: G (columns [0, d_ff)) and U
+ *              ([d_ff, 2 d_ff)) rounded to bf16; plane 2, [rows, d_ff] at
+ *              element offset 2 * rows * d_ff: H as the down product reads
+ *              it.  Rows outside every segment are not written.  Results and
+ *              z are the same with or without act.
  *   ws         device workspace of moe_grouped_swiglu_workspace(rows, E, d_ff, dtype)
  * ------------------------------------------------------------------------- */
 size_t moe_grouped_swiglu_workspace(int64_t rows, int32_t E, int32_t d_ff, int32_t dtype);
 int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t d_ff, int32_t E,
                        const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
                        const void* w_gate, const void* w_up, const void* w_down,
-                       void* z, int32_t z_dtype, const int32_t* z_rows, int64_t z_n_rows,
+                       void* z, int32_t z_dtype, const int32_t* z_rows, int64_t z_n_rows, void* act,
                        void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -379,7 +388,8 @@ int moe_combine_backward(const float* dy, int64_t T, int32_t d, const void* z, i
  * route-input and parameter gradients; the segments are backward state),
  * through the SwiGLU of "M6.6 - MoE Runtime Systems", 0x04A.  For every
  * expert e with rows X_e = x[seg_start[e] .. + seg_count[e]) and route
- * gradients dZ_e (same rows of dz), with G, U, H recomputed from X_e:
+ * gradients dZ_e (same rows of dz), with G, U, H recomputed from X_e, or
+ * taken from the activations the forward saved (act):
  *   dH = dZ_e W_d[e],  dG = dH * U * SiLU'(G),  dU = dH * SiLU(G)
  *   dx rows   = dG W_g[e] + dU W_u[e]                 (dx_dtype)
  *   dw_down[e] = dZ_e^T H,  dw_gate[e] = dG^T X_e,  dw_up[e] = dU^T X_e   (fp32)
@@ -390,6 +400,11 @@ int moe_combine_backward(const float* dy, int64_t T, int32_t d, const void* z, i
  *
  *   x, dz      device bf16 [rows, d]; d % 64 == 0, d_ff % 64 == 0
  *   w_gate, w_up  device bf16 [E, d_ff, d]; w_down device bf16 [E, d, d_ff]
+ *   act        NULL (recompute G, U and H: W_gate and W_up are read twice),
+ *              or moe_grouped_swiglu's saved activations of the same x and
+ *              segments (bf16, 16-byte aligned; layout in moe_grouped_swiglu):
+ *              dG, dU come from dH and the saved G, U (bf16), H from its
+ *              plane, and each weight is read once
  *   dx         device [rows, d] of dx_dtype (rows outside every segment not written)
  *   dw_gate, dw_up  device fp32 [E, d_ff, d]; dw_down device fp32 [E, d, d_ff]
  *   ws         device workspace of moe_grouped_swiglu_backward_workspace(rows, E, d, d_ff)
@@ -398,7 +413,7 @@ size_t moe_grouped_swiglu_backward_workspace(int64_t rows, int32_t E, int32_t d,
 int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, int32_t E,
                                 const int32_t* seg_start, const int32_t* seg_count, int64_t rows,
                                 const void* w_gate, const void* w_up, const void* w_down,
-                                const void* dz, void* dx, int32_t dx_dtype,
+                                const void* dz, const void* act, void* dx, int32_t dx_dtype,
                                 float* dw_gate, float* dw_up, float* dw_down,
                                 void* ws, size_t ws_bytes, uint32_t* dev_flags, hipStream_t stream);
 

@@ -99,8 +99,8 @@ def test_swiglu_validation():
     p, _keep = _fake()
     ws = lib.moe_grouped_swiglu_workspace(1000, 8, 256, 1)
     assert ws >= 1000 * 256 * 2
-    args = [p, 1, 128, 256, 8, p, p, 1000, p, p, p, p, 1, NULL, 0, p, ws, NULL, NULL]
-    assert lib.moe_grouped_swiglu(*args[:16], ws - 1, NULL, NULL) == EWS
+    args = [p, 1, 128, 256, 8, p, p, 1000, p, p, p, p, 1, NULL, 0, NULL, p, ws, NULL, NULL]
+    assert lib.moe_grouped_swiglu(*args[:17], ws - 1, NULL, NULL) == EWS
     q = ctypes.c_void_p(p.value + 2)
     bad = list(args); bad[13] = q; bad[14] = 10                     # misaligned row map
     assert lib.moe_grouped_swiglu(*bad) == EINVAL
@@ -115,6 +115,10 @@ def test_swiglu_validation():
     bad = list(args); bad[8] = NULL                                 # no gate weights
     assert lib.moe_grouped_swiglu(*bad) == EINVAL
     bad = list(args); bad[4] = 0                                    # no experts
+    assert lib.moe_grouped_swiglu(*bad) == EINVAL
+    bad = list(args); bad[1] = 0; bad[15] = p                       # saved activations on the fp32 path
+    assert lib.moe_grouped_swiglu(*bad) == EUNSUP
+    bad = list(args); bad[15] = ctypes.c_void_p(p.value + 2)        # misaligned saved activations
     assert lib.moe_grouped_swiglu(*bad) == EINVAL
 
 

@@ -110,6 +110,15 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
     assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 180.0 + 12.0 + 400.0) * 1024)
     assert c["combine"]["write_bytes"] == int(5.0 * 1024) and c["dx_combine"]["write_bytes"] == int(9.0 * 1024)
     assert c["combine_bwd"]["read_bytes"] == int(7.0 * 1024 * 2)
+    # from saved activations: a row pass forms dG | dU in place of the gate/up GEMM
+    saved = [e if e[0] != gemm.format("true", "false", 1, "false") else (ns + "swiglu_bwd_rows_kernel(x)", 20.0)
+             for e in step]
+    _write_counters(tmp_path / "f", "FETCH_SIZE", head + [("__amd_rocclr_copyBuffer", calib_kib / 2)] + saved * 2)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", head + [("__amd_rocclr_copyBuffer", calib_kib)] + saved * 2)
+    bench.record_traffic(bench.parse())
+    c = json.load(open(out))["mid_bf16_train"]["calls"]
+    assert all(v["launches"] == 2 for v in c.values())
+    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 140.0 + 12.0 + 400.0) * 1024)
 
 
 def test_record_mfma_busy_fraction(tmp_path, monkeypatch):
