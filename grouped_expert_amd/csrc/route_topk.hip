@@ -397,6 +397,7 @@ void launch_list_v(int V, const float* logits, int64_t T, int32_t E, int32_t k, 
                    float* w, uint32_t* flags, hipStream_t s) {
   if (V <= 8) launch_list<L, 8, KL, true>(logits, T, E, k, full, ids, w, flags, s);
   else if (V <= 16) launch_list<L, 16, KL, true>(logits, T, E, k, full, ids, w, flags, s);
+  else if (V <= 24) launch_list<L, 24, KL, true>(logits, T, E, k, full, ids, w, flags, s);
   else if (V <= 32) launch_list<L, 32, KL, true>(logits, T, E, k, full, ids, w, flags, s);
   else if (V <= 48) launch_list<L, 48, KL, true>(logits, T, E, k, full, ids, w, flags, s);
   else launch_list<L, 64, KL, true>(logits, T, E, k, full, ids, w, flags, s);
