@@ -65,27 +65,37 @@ struct WgCfg {
   static __device__ __forceinline__ int sw(int r) { return ((r % 4) * 4) % CPR; }
 };
 
-// MFMA fragment (k = 8 (lane / 32) + 0..7 of the 16-row step kk, column
-// col0 + lane % 32) from a region of k-rows RB bytes long.
+// Byte offset, inside a region of k-rows RB bytes long, of the 8-byte row
+// the lane addresses in the first transposing read of a fragment whose 32
+// columns start at col0 (k-step 0).  The swizzle of k-row kr depends on kr % 4
+// only, which is the lane's (lane % 16) / 4 at every k-step and read, so the
+// read for k-step kk and half q is this offset plus (16 kk + 4 q) RB.
 template <class W, int RB, int CPR>
-__device__ __forceinline__ bf16x8 wg_frag(const char* region, int kk, int col0, int lane) {
+__device__ __forceinline__ int wg_frag_off(int col0, int lane) {
   const int g = lane / 16, r = lane % 16;
   const int n = col0 + 16 * (g % 2) + 4 * (r % 4);
+  const int kr = 8 * (g / 2) + r / 4;
+  return kr * RB + (((n / 8) ^ W::template sw<CPR>(kr)) * 16) + (n % 8) * 2;
+}
+
+// MFMA fragment: k = 8 (lane / 32) + 0..7 of k-step kk, column col0 + lane % 32
+// (two transposing reads: in each 16-lane group, lane j receives value i of
+// the 8-byte row addressed by lane 4i + j/4, element j % 4).
+template <int RB>
+__device__ __forceinline__ bf16x8 wg_frag(const char* region, int off, int kk) {
   v4s part[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int kr = kk * 16 + 8 * (g / 2) + 4 * q + r / 4;
-    const int byte = kr * RB + (((n / 8) ^ W::template sw<CPR>(kr)) * 16) + (n % 8) * 2;
-    part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(const_cast<char*>(region) + byte));
-  }
+  for (int q = 0; q < 2; ++q)
+    part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s_ptr)(const_cast<char*>(region) + off + (16 * kk + 4 * q) * RB));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One slice: 4 k-steps of 16 rows.  MASK: only the slice's first kvalid rows
-// count (the expert's last slice).
+// One slice: 4 k-steps of 16 rows, with the lane offsets of wg_frag_off.
+// MASK: only the slice's first kvalid rows count (the expert's last slice).
 template <class W, bool MASK>
-__device__ __forceinline__ void wg_compute(const char* stage, f32x16 (&acc)[W::TM][W::TN], int wm, int wn, int lane,
-                                           int kvalid) {
+__device__ __forceinline__ void wg_compute(const char* stage, f32x16 (&acc)[W::TM][W::TN], const int (&aoff)[W::TM],
+                                           const int (&boff)[W::TN], int lane, int kvalid) {
   const char* areg = stage;
   const char* breg = stage + W::A_BYTES;
 #pragma unroll
@@ -93,7 +103,7 @@ __device__ __forceinline__ void wg_compute(const char* stage, f32x16 (&acc)[W::T
     bf16x8 a[W::TM], b[W::TN];
 #pragma unroll
     for (int i = 0; i < W::TM; ++i) {
-      a[i] = wg_frag<W, W::ARB, W::ACPR>(areg, kk, wm * W::WTM + i * 32, lane);
+      a[i] = wg_frag<W::ARB>(areg, aoff[i], kk);
       if constexpr (MASK) {
         // element e holds k = k0 + e: keep the first nv (branch-free selects)
         const int nv = kvalid - (kk * 16 + 8 * (lane / 32));
@@ -105,7 +115,7 @@ __device__ __forceinline__ void wg_compute(const char* stage, f32x16 (&acc)[W::T
       }
     }
 #pragma unroll
-    for (int j = 0; j < W::TN; ++j) b[j] = wg_frag<W, W::BRB, W::BCPR>(breg, kk, wn * W::WTN + j * 32, lane);
+    for (int j = 0; j < W::TN; ++j) b[j] = wg_frag<W::BRB>(breg, boff[j], kk);
 #pragma unroll
     for (int i = 0; i < W::TM; ++i)
 #pragma unroll
@@ -113,116 +123,173 @@ __device__ __forceinline__ void wg_compute(const char* stage, f32x16 (&acc)[W::T
   }
 }
 
-// One workgroup per (expert, M-tile, N-tile), N-tiles of one M-tile adjacent;
-// the expert's rows (first row, count) come from the tile-table pass, which
-// validated the segments; an expert without rows writes zeros.  The tile
-// leaves through LDS as whole fp32 row pieces.  Several workgroups share a
-// CU, so one's loads and stores overlap another's matrix-core work.
+// Persistent: G workgroups (one per CU) walk the tiles slot, slot + G, ...
+// (tile = (expert, M-tile, N-tile), N-tiles of one M-tile adjacent; the
+// expert's first row and row count come from the tile-table pass, which
+// validated the segments; an expert without rows writes zeros).  Slice k of
+// a tile sits in ring stage k % 3.  After a tile's K loop the next tile's
+// slice 0 is loaded into stage 0 while the fp32 result is staged through
+// stages 1-2 (two passes of BM/2 rows) and stored as whole 16-byte row
+// pieces; its slice 1 follows into stage 1 once the staging area is read, so
+// the next tile's loads overlap this tile's epilogue.  Each thread issues the
+// same number of stores per tile (pieces outside the output go to a junk
+// line of its own), so the wait for the prefetched slice counts exactly.
 template <class W>
-__global__ __launch_bounds__(W::THREADS, W::OCC) void grouped_wgrad_kernel(
+__global__ __launch_bounds__(W::THREADS, 1) void grouped_wgrad_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int32_t M, int32_t N, int32_t M0,
     float* __restrict__ C0, float* __restrict__ C1, const int32_t* __restrict__ exp_rows, int32_t n_mt,
-    int32_t n_nt) {
+    int32_t n_nt, int32_t total, vec16* __restrict__ junk) {
+  static_assert(W::STAGES == 3 && W::WM == 2 && W::WTM * 2 == W::BM, "three stages, two row halves");
+  constexpr int OUT_ROW = W::BN * 4, VPR = OUT_ROW / 16;
+  constexpr int HALF = W::BM / 2;
+  static_assert(HALF * OUT_ROW <= 2 * W::SLICE_BYTES, "half a tile fits stages 1-2");
+  static_assert((HALF * VPR) % W::THREADS == 0, "equal stores per thread");
+  constexpr int PST = HALF * VPR / W::THREADS;          // stores per thread and pass
+  constexpr int NST = 2 * PST;                          // store instructions per wavefront and tile
+  static_assert(NST + W::LOADS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char ring[W::STAGES * W::SLICE_BYTES];
-  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_e = n_mt * n_nt;
-  const int e = static_cast<int>(logical) / per_e;
-  const int rem = static_cast<int>(logical) - e * per_e;
-  const int mt = rem / n_nt, nt = rem - mt * n_nt;
-  const int m0 = mt * W::BM, n0 = nt * W::BN;
-  const int2 er = reinterpret_cast<const int2*>(exp_rows)[e];
-  const int32_t row0 = er.x, nrows = er.y;
-  const int KT = (nrows + W::BK - 1) / W::BK;
+  const uint32_t G = gridDim.x;
+  uint32_t tile = xcd_remap(blockIdx.x, G);
+  if (tile >= static_cast<uint32_t>(total)) return;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / W::WN, wn = wave % W::WN;
-  // per load: the source matrix, its row stride, the k-row in the slice and
-  // the element column (clamped into the matrix; such columns are not stored)
-  const bf16_t* src[W::LOADS];
-  int32_t ld[W::LOADS], kr[W::LOADS], col[W::LOADS];
-#pragma unroll
-  for (int i = 0; i < W::LOADS; ++i) {
-    const int blk = wave * W::LOADS + i;
-    if (blk < W::ALOADS) {
-      kr[i] = blk * W::ARPI + lane / W::ACPR;
-      const int c = (lane % W::ACPR) ^ W::template sw<W::ACPR>(kr[i]);
-      col[i] = m0 + 8 * c < M ? m0 + 8 * c : M - 8;
-      src[i] = A;
-      ld[i] = M;
-    } else {
-      kr[i] = (blk - W::ALOADS) * W::BRPI + lane / W::BCPR;
-      const int c = (lane % W::BCPR) ^ W::template sw<W::BCPR>(kr[i]);
-      col[i] = n0 + 8 * c < N ? n0 + 8 * c : N - 8;
-      src[i] = B;
-      ld[i] = N;
-    }
-  }
+  struct Tile { int32_t e, m0, n0, row0, nrows, KT; };
+  const int per_e = n_mt * n_nt;
+  auto info = [&](uint32_t t) {
+    Tile r;
+    r.e = static_cast<int>(t) / per_e;
+    const int rem = static_cast<int>(t) - r.e * per_e;
+    r.m0 = (rem / n_nt) * W::BM;
+    r.n0 = (rem % n_nt) * W::BN;
+    const int2 er = reinterpret_cast<const int2*>(exp_rows)[r.e];
+    r.row0 = er.x;
+    r.nrows = er.y;
+    r.KT = (er.y + W::BK - 1) / W::BK;
+    return r;
+  };
   // The slices' LDS DMA is issued as inline asm and waited for explicitly
   // (vmcnt, then a barrier): seen as LDS writes, the compiler would wait for
   // every DMA in flight, the prefetched slices included, before each slice's
   // first LDS read.
-  auto issue = [&](int kt) {
-    char* stage = ring + (kt % W::STAGES) * W::SLICE_BYTES;
+  // load i of the wavefront fills k-rows of A (blocks < ALOADS) or of B; a
+  // lane's LDS position holds the swizzled chunk of its k-row (recomputed
+  // per slice from the lane: arrays of them would cost registers)
+  auto issue = [&](const Tile& t, int k) {
+    char* stage = ring + (k % W::STAGES) * W::SLICE_BYTES;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));                        // keeps the address math here (not hoisted, no spills)
 #pragma unroll
     for (int i = 0; i < W::LOADS; ++i) {
-      const int r = kt * W::BK + kr[i] < nrows ? kt * W::BK + kr[i] : nrows - 1;
-      const bf16_t* p = src[i] + (static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(ld[i]) + col[i]);
-      dma_b128_asm(lds_addr(stage + (wave * W::LOADS + i) * 1024), p);
+      const int blk = wave * W::LOADS + i;              // wave-uniform
+      const bool a = blk < W::ALOADS;
+      const int kr = a ? blk * W::ARPI + ln / W::ACPR : (blk - W::ALOADS) * W::BRPI + ln / W::BCPR;
+      const int cc = a ? 8 * ((ln % W::ACPR) ^ W::template sw<W::ACPR>(kr))
+                       : 8 * ((ln % W::BCPR) ^ W::template sw<W::BCPR>(kr));
+      const int r = k * W::BK + kr < t.nrows ? k * W::BK + kr : t.nrows - 1;
+      const int lim = a ? M : N;
+      int col = (a ? t.m0 : t.n0) + cc;
+      col = col < lim ? col : lim - 8;
+      const bf16_t* p = (a ? A : B) + (static_cast<uint32_t>(t.row0 + r) * static_cast<uint32_t>(lim) + col);
+      dma_b128_asm(lds_addr(stage + blk * 1024), p);
     }
   };
-  f32x16 acc[W::TM][W::TN];
-#pragma unroll
-  for (int i = 0; i < W::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < W::TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < W::STAGES - 1; ++s)
-    if (s < KT) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + W::STAGES - 2 < KT)
-      wait_vmcnt_asm<(W::STAGES - 2) * W::LOADS>();
-    else
-      wait_vmcnt_asm<0>();
+  auto lds_barrier = [&]() {                           // LDS accesses done; DMA may stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_nofence();
-    if (kt + W::STAGES - 1 < KT) issue(kt + W::STAGES - 1);
-    const char* stage = ring + (kt % W::STAGES) * W::SLICE_BYTES;
-    const int kvalid = nrows - kt * W::BK;
-    if (kvalid < W::BK)
-      wg_compute<W, true>(stage, acc, wm, wn, lane, kvalid);
-    else
-      wg_compute<W, false>(stage, acc, wm, wn, lane, W::BK);
-  }
+  };
 
+  int aoff[W::TM], boff[W::TN];
+#pragma unroll
+  for (int i = 0; i < W::TM; ++i) aoff[i] = wg_frag_off<W, W::ARB, W::ACPR>(wm * W::WTM + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < W::TN; ++j) boff[j] = wg_frag_off<W, W::BRB, W::BCPR>(wn * W::WTN + j * 32, lane);
+
+  Tile cur = info(tile);
+  if (cur.KT > 0) issue(cur, 0);
+  if (cur.KT > 1) issue(cur, 1);
+  bool stores_after_s0 = false;          // the previous tile's stores were issued after slice 0
   const int lr = lane % 32, lk = lane / 32;
-  constexpr int OUT_ROW = W::BN * 4;
-  static_assert(W::BM * OUT_ROW <= static_cast<int>(sizeof(ring)), "fp32 tile fits the ring");
-  char* tile = ring;
-  barrier_nofence();
+  for (;;) {
+    const uint32_t next_t = tile + G;
+    const bool has_next = next_t < static_cast<uint32_t>(total);
+    const Tile nxt = has_next ? info(next_t) : Tile{0, 0, 0, 0, 0, 0};
+    f32x16 acc[W::TM][W::TN];
 #pragma unroll
-  for (int i = 0; i < W::TM; ++i)
+    for (int i = 0; i < W::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < W::TN; ++j)
+      for (int j = 0; j < W::TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = wm * W::WTM + i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
-        const int cc = wn * W::WTN + j * 32 + lr;
-        *reinterpret_cast<float*>(tile + r * OUT_ROW + cc * 4) = acc[i][j][q];
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    for (int k = 0; k < cur.KT; ++k) {
+      // memory instructions issued after slice k: at k = 0 the previous
+      // tile's stores (when slice 0 was loaded before them), then slice 1;
+      // later, slice k + 1
+      if (k == 0) {
+        if (stores_after_s0) {
+          if (cur.KT > 1) wait_vmcnt_asm<NST + W::LOADS>();
+          else wait_vmcnt_asm<NST>();
+        } else {
+          if (cur.KT > 1) wait_vmcnt_asm<W::LOADS>();
+          else wait_vmcnt_asm<0>();
+        }
+      } else {
+        if (k + 1 < cur.KT) wait_vmcnt_asm<W::LOADS>();
+        else wait_vmcnt_asm<0>();
       }
-  __syncthreads();
-  constexpr int VPR = OUT_ROW / 16;
-  const int rows_here = M - m0 < W::BM ? M - m0 : W::BM;
-  const int vec_cols = (N - n0 < W::BN ? N - n0 : W::BN) / 4;
-  for (int v = threadIdx.x; v < W::BM * VPR; v += W::THREADS) {
-    const int r = v / VPR, cv = v % VPR;
-    if (r >= rows_here || cv >= vec_cols) continue;
-    const int m = m0 + r;
-    float* dst = m < M0 ? C0 + (static_cast<int64_t>(e) * M0 + m) * N
-                        : C1 + (static_cast<int64_t>(e) * (M - M0) + (m - M0)) * N;
-    *reinterpret_cast<vec16*>(dst + n0 + cv * 4) = *reinterpret_cast<const vec16*>(tile + r * OUT_ROW + cv * 16);
+      barrier_nofence();
+      if (k + 2 < cur.KT) issue(cur, k + 2);
+      const char* stage = ring + (k % W::STAGES) * W::SLICE_BYTES;
+      const int kvalid = cur.nrows - k * W::BK;
+      if (kvalid < W::BK)
+        wg_compute<W, true>(stage, acc, aoff, boff, lane, kvalid);
+      else
+        wg_compute<W, false>(stage, acc, aoff, boff, lane, W::BK);
+    }
+    lds_barrier();                                      // every wave is done with the ring
+    if (nxt.KT > 0) issue(nxt, 0);
+    // epilogue: rows [pass * BM/2, + BM/2) through stages 1-2
+    char* tile_lds = ring + W::SLICE_BYTES;
+    const int vec_cols = (N - cur.n0 < W::BN ? N - cur.n0 : W::BN) / 4;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
+#pragma unroll
+        for (int i = 0; i < W::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < W::TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = i * 32 + 8 * (q / 4) + 4 * lk + (q % 4);
+              const int c = wn * W::WTN + j * 32 + lr;
+              *reinterpret_cast<float*>(tile_lds + r * OUT_ROW + c * 4) = acc[i][j][q];
+            }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int it = 0; it < PST; ++it) {
+        const int v = tid + it * W::THREADS;
+        const int r = v / VPR, cv = v % VPR;
+        const int m = cur.m0 + pass * HALF + r;
+        const vec16 val = *reinterpret_cast<const vec16*>(tile_lds + r * OUT_ROW + cv * 16);
+        vec16* dst = junk + tid;
+        if (m < M && cv < vec_cols) {
+          float* row = m < M0 ? C0 + (static_cast<int64_t>(cur.e) * M0 + m) * N
+                              : C1 + (static_cast<int64_t>(cur.e) * (M - M0) + (m - M0)) * N;
+          dst = reinterpret_cast<vec16*>(row + cur.n0 + cv * 4);
+        }
+        *dst = val;
+      }
+      lds_barrier();                                    // the staging area is read
+    }
+    if (nxt.KT > 1) issue(nxt, 1);
+    if (!has_next) break;
+    stores_after_s0 = nxt.KT > 0;
+    tile = next_t;
+    cur = nxt;
   }
+  wait_vmcnt_asm<0>();
 }
 
 // SwiGLU backward from saved pre-activations, over the rows of the M-tiles:
@@ -290,7 +357,7 @@ static_assert(CfgLgGB::BM == CfgLgGU::BM && CfgMdGB::BM == CfgMdGU::BM && CfgSmG
 using CfgWg = WgCfg<128, 256, 2, 4, 3, 1>;
 
 struct BwdLayout {
-  size_t tiles, ntiles, erows, dH, dGU, H, total;
+  size_t tiles, ntiles, erows, junk, dH, dGU, H, total;
   int32_t max_tiles, bm;
 };
 
@@ -309,6 +376,7 @@ inline BwdLayout bwd_layout(int64_t rows, int32_t E, int32_t d, int32_t d_ff) {
   w.tiles = take(static_cast<size_t>(w.max_tiles) * sizeof(TileEntry));
   w.ntiles = take(4);
   w.erows = take(e * 8);
+  w.junk = take(static_cast<size_t>(CfgWg::THREADS) * 16);
   w.dH = take(r * F * 2);
   w.dGU = take(r * 2 * F * 2);
   w.H = take(r * F * 2);
@@ -420,17 +488,22 @@ MOE_API int moe_grouped_swiglu_backward(const void* x, int32_t d, int32_t d_ff, 
   using C = CfgWg;
   const bf16_t* zsrc = static_cast<const bf16_t*>(dz);
   const bf16_t* xsrc = static_cast<const bf16_t*>(x);
+  vec16* junk = reinterpret_cast<vec16*>(w + L.junk);
+  const int cus = device_cus();
   {
     const int n_mt = (d + C::BM - 1) / C::BM, n_nt = (d_ff + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_wgrad_kernel<C>), dim3(static_cast<unsigned>(E * n_mt * n_nt)),
-                       dim3(C::THREADS), 0, stream, zsrc, H, d, d_ff, d, dw_down, dw_down, erows, n_mt, n_nt);
+    const int total = E * n_mt * n_nt;
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_wgrad_kernel<C>), dim3(static_cast<unsigned>(total < cus ? total : cus)),
+                       dim3(C::THREADS), 0, stream, zsrc, H, d, d_ff, d, dw_down, dw_down, erows, n_mt, n_nt, total,
+                       junk);
     MOE_LAUNCH_CHECK();
   }
   {
     const int n_mt = (2 * d_ff + C::BM - 1) / C::BM, n_nt = (d + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_wgrad_kernel<C>), dim3(static_cast<unsigned>(E * n_mt * n_nt)),
-                       dim3(C::THREADS), 0, stream, dGU, xsrc, 2 * d_ff, d, d_ff, dw_gate, dw_up, erows, n_mt,
-                       n_nt);
+    const int total = E * n_mt * n_nt;
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_wgrad_kernel<C>), dim3(static_cast<unsigned>(total < cus ? total : cus)),
+                       dim3(C::THREADS), 0, stream, dGU, xsrc, 2 * d_ff, d, d_ff, dw_gate, dw_up, erows, n_mt, n_nt,
+                       total, junk);
     MOE_LAUNCH_CHECK();
   }
   return MOE_OK;
