@@ -126,8 +126,7 @@ def _call_of(kernel, train=False):
         return "swiglu_bwd" if _is_bwd_gemm(kernel) else "swiglu"
     table = (("route_list_kernel", "route"), ("route_topk_kernel", "route"), ("route_grouped_kernel", "route"),
              ("build_tiles_kernel", "rank"),
-             ("transpose_rows_kernel", "swiglu_bwd"), ("grouped_wgrad_kernel", "swiglu_bwd"),
-             ("swiglu_bwd_rows_kernel", "swiglu_bwd"),
+             ("grouped_wgrad_kernel", "swiglu_bwd"), ("swiglu_bwd_rows_kernel", "swiglu_bwd"),
              ("scatter_rows_kernel", "permute"), ("permute_fused_kernel", "permute"), ("pack_kernel", "pool_pack"),
              ("compact_rows_kernel", "recv_compact"), ("compact_fp8_rows_kernel", "recv_compact"),
              ("quantize_kernel", "quantize"), ("expand_rows_kernel", "expand"),

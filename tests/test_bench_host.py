@@ -90,8 +90,7 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
             (gemm.format("false", "false", 0, "true"), 40.0),
             (gemm.format("true", "false", 1, "false"), 60.0),
             (gemm.format("false", "true", 0, "true"), 80.0)]
-    step += [(ns + "transpose_rows_kernel(x)", 3.0)] * 4
-    step += [("void " + ns + "grouped_wgrad_kernel<" + ns + "Cfg<128, 256> >(x)", 200.0)] * 2
+    step += [("void " + ns + "grouped_wgrad_kernel<" + ns + "WgCfg<128, 256, 2, 4, 3, 1> >(x)", 206.0)] * 2
     step += [("void " + ns + "combine_kernel<float>(x)", 9.0)]
     head = [("__amd_rocclr_copyBuffer", 99.0)]
     fetch = head + [("__amd_rocclr_copyBuffer", calib_kib / 2)] + step * 3
@@ -107,7 +106,7 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
     assert set(c) == {"route", "permute", "swiglu", "combine", "combine_bwd", "swiglu_bwd", "dx_combine"}
     assert all(v["launches"] == 3 for v in c.values())
     assert c["swiglu"]["write_bytes"] == int(150.5 * 1024)
-    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 180.0 + 12.0 + 400.0) * 1024)
+    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 180.0 + 412.0) * 1024)
     assert c["combine"]["write_bytes"] == int(5.0 * 1024) and c["dx_combine"]["write_bytes"] == int(9.0 * 1024)
     assert c["combine_bwd"]["read_bytes"] == int(7.0 * 1024 * 2)
     # from saved activations: a row pass forms dG | dU in place of the gate/up GEMM
@@ -118,7 +117,7 @@ def test_record_traffic_splits_a_training_step(tmp_path, monkeypatch):
     bench.record_traffic(bench.parse())
     c = json.load(open(out))["mid_bf16_train"]["calls"]
     assert all(v["launches"] == 2 for v in c.values())
-    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 140.0 + 12.0 + 400.0) * 1024)
+    assert c["swiglu_bwd"]["write_bytes"] == int((0.5 + 140.0 + 412.0) * 1024)
 
 
 def test_record_mfma_busy_fraction(tmp_path, monkeypatch):
