@@ -546,6 +546,177 @@ __global__ __launch_bounds__(kTokensPerBlock * kWave) void route_grouped_kernel(
   if (token_bad && lane == 0) flag_or(flags, MOE_FLAG_NONFINITE_LOGIT);
 }
 
+// The same router with 16 lanes per token (4 tokens per wavefront), for
+// shapes where every lane holds the same groups: V = E / 16 values per lane
+// (expert e = l + 16 v) and M = G / 16 values of each group per lane (value v
+// in group v / M).  Every reduction runs over the token's 16 lanes (one DPP
+// row) instead of the wavefront, which cuts the instructions per token.  The
+// decisions are those of route_grouped_kernel: group scores from the same
+// keys (V3: the fp32 sum of the two largest, a multiset of the group's keys;
+// V2: the largest), topk_group rounds taking the largest score and the lowest
+// group among equals, then k rounds taking the largest key and the lowest
+// expert among equals, the winner's key cleared.
+__device__ __forceinline__ uint32_t row16_umax(uint32_t v) {
+  v = umax(v, dpp<0xB1>(v));
+  v = umax(v, dpp<0x4E>(v));
+  v = umax(v, dpp<0x141>(v));
+  return umax(v, dpp<0x140>(v));
+}
+__device__ __forceinline__ uint32_t row16_umin(uint32_t v) {
+  v = umin(v, dpp<0xB1>(v));
+  v = umin(v, dpp<0x4E>(v));
+  v = umin(v, dpp<0x141>(v));
+  return umin(v, dpp<0x140>(v));
+}
+__device__ __forceinline__ uint32_t row16_or(uint32_t v) {
+  v |= dpp<0xB1>(v);
+  v |= dpp<0x4E>(v);
+  v |= dpp<0x141>(v);
+  return v | dpp<0x140>(v);
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __uint_as_float(dpp<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x141>(__float_as_uint(v)));
+  return v + __uint_as_float(dpp<0x140>(__float_as_uint(v)));
+}
+
+template <int V, int M>
+__global__ __launch_bounds__(256) void route_grouped16_kernel(
+    const float* __restrict__ logits, int64_t T, int32_t E, int32_t k, int32_t sigmoid_bias, int32_t topk_group,
+    float route_scale, const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ weights,
+    uint32_t* flags) {
+  constexpr int L = 16, NG = V / M;
+  static_assert(V % M == 0 && NG <= 32, "whole groups per lane");
+  const int l = threadIdx.x % L;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / L) + threadIdx.x / L;
+  const bool live = t < T;                              // a missing token's lanes compute on zeros
+  const float* row = logits + (live ? t : 0) * E;
+
+  uint32_t key[V];
+  float val[V];
+  bool bad = false;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = l + L * v;
+    const float z = live ? __builtin_nontemporal_load(row + e) : 0.0f;
+    bad |= !isfinite(z);
+    if (sigmoid_bias) {
+      // as in route_grouped_kernel: fp64 sigmoid rounded once to fp32, plus the bias in fp32
+      const float sg = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(z))));
+      const float c = sg + (bias ? bias[e] : 0.0f);
+      bad |= !isfinite(c);
+      key[v] = order_key(c);
+      val[v] = sg;
+    } else {
+      key[v] = order_key(z);
+      val[v] = z;
+    }
+  }
+  const bool token_bad = row16_or(bad ? 1u : 0u) != 0;
+
+  // group scores (every lane of the token ends with all of them)
+  uint32_t gkey[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    uint32_t k1 = 0, k2 = 0;                            // two largest keys, k1 >= k2
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint32_t x = key[g * M + i];
+      k2 = umax(k2, umin(k1, x));
+      k1 = umax(k1, x);
+    }
+    if (sigmoid_bias) {
+#define MOE_TOP2_STEP(CT)                                              \
+  {                                                                    \
+    const uint32_t b1 = dpp<CT>(k1), b2 = dpp<CT>(k2);                 \
+    k2 = umax(umin(k1, b1), umax(k2, b2));                             \
+    k1 = umax(k1, b1);                                                 \
+  }
+      MOE_TOP2_STEP(0xB1)
+      MOE_TOP2_STEP(0x4E)
+      MOE_TOP2_STEP(0x141)
+      MOE_TOP2_STEP(0x140)
+#undef MOE_TOP2_STEP
+      gkey[g] = order_key(key_value(k1) + key_value(k2));
+    } else {
+      gkey[g] = row16_umax(k1);
+    }
+  }
+  // topk_group rounds: the largest score, the lowest group among equals
+  uint32_t kept = 0;
+  for (int r = 0; r < topk_group; ++r) {
+    uint32_t best = 0;
+    int bg = -1;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if (!((kept >> g) & 1u) && gkey[g] > best) {
+        best = gkey[g];
+        bg = g;
+      }
+    if (bg >= 0) kept |= 1u << bg;
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (!((kept >> (v / M)) & 1u)) key[v] = 0;
+
+  // k rounds over the token's lanes
+  int32_t mine_e = 0;
+  float mine_val = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lmax = key[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) lmax = umax(lmax, key[v]);
+    const uint32_t K = row16_umax(lmax);
+    uint32_t lmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int v = V - 1; v >= 0; --v) lmin = key[v] == K ? static_cast<uint32_t>(l + L * v) : lmin;
+    const uint32_t ew = row16_umin(lmin);
+    const int vw = static_cast<int>(ew / L), lw = static_cast<int>(ew % L);
+    uint32_t vb = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (v == vw && l == lw) {
+        vb = __float_as_uint(val[v]);
+        key[v] = 0;
+      }
+    const float wv = __uint_as_float(row16_or(vb));      // the winner's value (the other lanes give 0 bits)
+    if (l == j) {
+      mine_e = static_cast<int32_t>(ew);
+      mine_val = wv;
+    }
+  }
+
+  float gate;
+  if (sigmoid_bias) {
+    const float ssum = row16_sum(l < k ? mine_val : 0.0f);
+    gate = route_scale * mine_val / ssum;
+  } else {
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) lmax = umax(lmax, order_key(val[v]));
+    const float zmax = key_value(row16_umax(lmax));
+    float mass = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) mass += expf(val[v] - zmax);
+    const float denom = row16_sum(mass);
+    gate = route_scale * expf(mine_val - zmax) / denom;
+  }
+  if (live && l < k) {
+    ids[t * k + l] = token_bad ? -1 : mine_e;
+    weights[t * k + l] = token_bad ? 0.0f : gate;
+  }
+  if (live && token_bad && l == 0) flag_or(flags, MOE_FLAG_NONFINITE_LOGIT);
+}
+
+template <int V, int M>
+void launch_grouped16(const float* logits, int64_t T, int32_t E, int32_t k, int32_t sigmoid_bias, int32_t topk_group,
+                      float scale, const float* bias, int32_t* ids, float* w, uint32_t* flags, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((T + 15) / 16);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(route_grouped16_kernel<V, M>), dim3(blocks), dim3(256), 0, s, logits, T, E, k,
+                     sigmoid_bias, topk_group, scale, bias, ids, w, flags);
+}
+
 template <int V>
 void launch_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t sigmoid_bias, int32_t n_group,
                     int32_t topk_group, float scale, const float* bias, int32_t* ids, float* w, uint32_t* flags,
@@ -612,6 +783,22 @@ MOE_API int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, in
   if (T == 0) return MOE_OK;
   MOE_CHECK(logits && topk_ids && topk_w, MOE_EINVAL);
   MOE_CHECK(aligned4(logits) && aligned4(topk_ids) && aligned4(topk_w) && (!bias || aligned4(bias)), MOE_EINVAL);
+  // 16 lanes per token where the groups fall evenly on the lanes
+  const int G = E / n_group;
+  if (E % 16 == 0 && G % 16 == 0 && k <= 16) {
+    const int V16 = E / 16, M16 = G / 16;
+    bool done = true;
+    if (V16 == 16 && M16 == 1) launch_grouped16<16, 1>(logits, T, E, k, sig, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+    else if (V16 == 16 && M16 == 2) launch_grouped16<16, 2>(logits, T, E, k, sig, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+    else if (V16 == 16 && M16 == 4) launch_grouped16<16, 4>(logits, T, E, k, sig, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+    else if (V16 == 8 && M16 == 1) launch_grouped16<8, 1>(logits, T, E, k, sig, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+    else if (V16 == 8 && M16 == 2) launch_grouped16<8, 2>(logits, T, E, k, sig, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
+    else done = false;
+    if (done) {
+      MOE_LAUNCH_CHECK();
+      return MOE_OK;
+    }
+  }
   const int V = (E + kWave - 1) / kWave;
   if (V <= 1) launch_grouped<1>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
   else if (V <= 2) launch_grouped<2>(logits, T, E, k, sig, n_group, topk_group, route_scale, bias, topk_ids, topk_w, dev_flags, stream);
