@@ -80,7 +80,10 @@ def test_route_topk_v1(ge, T, E, k):
 
 @pytest.mark.parametrize("T,E,k,ng,tg,scale", [(300, 160, 6, 8, 3, 16.0), (257, 64, 4, 4, 2, 1.0),
                                               (120, 256, 8, 8, 4, 2.0), (64, 1024, 16, 64, 5, 1.0),
-                                              (33, 16, 3, 1, 1, 1.0)])
+                                              (33, 16, 3, 1, 1, 1.0),
+                                              # 16 lanes per token: groups of 16, 32 and 64 experts
+                                              (301, 256, 16, 16, 5, 1.0), (77, 128, 5, 8, 2, 2.0),
+                                              (130, 256, 7, 4, 2, 1.0), (45, 128, 6, 4, 3, 1.0)])
 def test_route_grouped_v2(ge, T, E, k, ng, tg, scale):
     z = _route_inputs(T, E, 3 * T + E)
     flags = ge.new_flags("cuda")
@@ -126,7 +129,10 @@ def _v3_exact(z, bias, gids, gw, k, ng, tg, scale):
 
 
 @pytest.mark.parametrize("T,E,k,ng,tg,scale", [(300, 256, 8, 8, 4, 2.5), (200, 64, 6, 8, 3, 1.0),
-                                              (100, 384, 8, 16, 4, 2.5), (40, 12, 4, 4, 2, 2.5)])
+                                              (100, 384, 8, 16, 4, 2.5), (40, 12, 4, 4, 2, 2.5),
+                                              # 16 lanes per token: groups of 16, 32 and 64 experts
+                                              (257, 256, 16, 16, 6, 2.5), (99, 128, 8, 8, 4, 1.0),
+                                              (150, 256, 8, 4, 2, 2.5), (61, 128, 3, 4, 1, 1.0)])
 def test_route_grouped_v3(ge, T, E, k, ng, tg, scale):
     z = _route_inputs(T, E, 5 * T + E)
     bias = (0.05 * np.random.default_rng(E).standard_normal(E)).astype(np.float32)
