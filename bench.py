@@ -125,6 +125,7 @@ def _call_of(kernel, train=False):
     if "grouped_gemm_" in kernel:
         return "swiglu_bwd" if _is_bwd_gemm(kernel) else "swiglu"
     table = (("route_list_kernel", "route"), ("route_topk_kernel", "route"), ("route_grouped_kernel", "route"),
+             ("route_grouped16_kernel", "route"),
              ("build_tiles_kernel", "rank"),
              ("grouped_wgrad_kernel", "swiglu_bwd"), ("swiglu_bwd_rows_kernel", "swiglu_bwd"),
              ("scatter_rows_kernel", "permute"), ("permute_fused_kernel", "permute"), ("pack_kernel", "pool_pack"),
