@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
   // 128 experts)
   constexpr int kTabPer = kFuseMaxChunks * 128 / kFuseThreads;
   const int64_t entries = g.chunks * E;
+  const int32_t q = kFuseThreads / E, rr = kFuseThreads % E;
   int32_t tv[kTabPer];
 #pragma unroll
   for (int u = 0; u < kTabPer; ++u) {
@@ -211,14 +212,34 @@ __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
         tv[u] = idx < entries ? table[idx] : 0;
       }
     }
+    // entry idx is (chunk idx / E, expert idx % E); stepping idx by the block
+    // size steps the chunk by q and the expert by rr (with one carry), so the
+    // loop divides nothing.  Where E divides the block size every entry of a
+    // thread is one expert's: sum in registers, two LDS atomics per thread.
+    int64_t c = (b0 + tid) / E;
+    int b = static_cast<int>((b0 + tid) - c * E);
+    if (rr == 0) {
+      int32_t all = 0, before = 0;
 #pragma unroll
-    for (int u = 0; u < kTabPer; ++u) {
-      const int64_t idx = b0 + tid + static_cast<int64_t>(u) * kFuseThreads;
-      if (idx < entries) {
-        const int64_t c = idx / E;
-        const int b = static_cast<int>(idx - c * E);
-        atomicAdd(&sel[b], tv[u]);
-        if (c < c0) atomicAdd(&base[b], tv[u]);
+      for (int u = 0; u < kTabPer; ++u) {
+        const int64_t idx = b0 + tid + static_cast<int64_t>(u) * kFuseThreads;
+        const int32_t x = idx < entries ? tv[u] : 0;
+        all += x;
+        before += c + u * q < c0 ? x : 0;
+      }
+      if (all != 0) atomicAdd(&sel[b], all);
+      if (before != 0) atomicAdd(&base[b], before);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kTabPer; ++u) {
+        const int64_t idx = b0 + tid + static_cast<int64_t>(u) * kFuseThreads;
+        if (idx < entries) {
+          atomicAdd(&sel[b], tv[u]);
+          if (c < c0) atomicAdd(&base[b], tv[u]);
+        }
+        c += q;
+        b += rr;
+        if (b >= E) b -= E, ++c;
       }
     }
   }
