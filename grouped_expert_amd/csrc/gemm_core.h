@@ -135,6 +135,25 @@ __device__ __forceinline__ void dma_b128_asm(uint32_t lds_dst, const void* src) 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_dst), "v"(src) : "memory");
 }
 
+// Lane index formed by instructions the compiler cannot merge with an
+// earlier copy: per-lane constants derived from it are recomputed where
+// used instead of being kept live (or spilled) across a long loop.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// LDS DMA through a buffer resource: 16 bytes per lane from the buffer at
+// voff + soff to LDS at M0 + 16 * lane (a 32-bit per-lane offset instead of a
+// 64-bit address).
+__device__ __forceinline__ void dma_buf_b128_asm(uint32_t lds_dst, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                                 uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_dst), "v"(voff),
+               "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 __device__ __forceinline__ void buffer_load_b128_asm(vec16& r, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
                                                      uint32_t soff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
@@ -473,14 +492,11 @@ __device__ __forceinline__ void store_direct_at(void* __restrict__ Cout, int32_t
   }
 }
 
-// One output tile (logical tile index `logical` of `total`).  MAP: results
-// are stored through the row map out_rows (dest_row).
-template <class C, bool MAP>
-__device__ __forceinline__ void gemm_tile(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles, uint32_t total,
-    int32_t n_tiles_n, const bf16_t* __restrict__ aux_in, bf16_t* __restrict__ aux_out, int32_t kb1,
-    const int32_t* __restrict__ out_rows, int32_t out_n, bf16_t (&ring)[C::RING], uint32_t logical) {
+// M-tile (entry of the tile table) and N-tile of logical tile `logical` of
+// `total`, in the workgroup order of configuration C.
+template <class C>
+__device__ __forceinline__ void tile_mn(const TileEntry* __restrict__ tiles, uint32_t logical, uint32_t total,
+                                        int32_t n_tiles_n, int* mt_out, int* nt_out) {
   int mt, nt;
   if (C::EXPERT_BLOCKED) {
     // all N-tiles of one expert form a block; inside it the M-tiles of one
@@ -503,6 +519,20 @@ __device__ __forceinline__ void gemm_tile(
     mt = static_cast<int>(logical / n_tiles_n);
     nt = static_cast<int>(logical % n_tiles_n);
   }
+  *mt_out = mt;
+  *nt_out = nt;
+}
+
+// One output tile (logical tile index `logical` of `total`).  MAP: results
+// are stored through the row map out_rows (dest_row).
+template <class C, bool MAP>
+__device__ __forceinline__ void gemm_tile(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles, uint32_t total,
+    int32_t n_tiles_n, const bf16_t* __restrict__ aux_in, bf16_t* __restrict__ aux_out, int32_t kb1,
+    const int32_t* __restrict__ out_rows, int32_t out_n, bf16_t (&ring)[C::RING], uint32_t logical) {
+  int mt, nt;
+  tile_mn<C>(tiles, logical, total, n_tiles_n, &mt, &nt);
   const TileEntry te = tiles[mt];
   const int64_t e = te.expert;
   const int32_t row0 = te.row0, row_end = te.row_end;
@@ -1074,6 +1104,287 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
   }
 }
 
+// Persistent form of the register-staged tiles (plain direct-store epilogue,
+// unswapped layout).  G workgroups walk their tiles with a static stride
+// (even rounds), and a workgroup's tiles form one sequence of K slices: the
+// A DMA (AD slices ahead) and the B register loads (three slices ahead) run
+// on across tile boundaries, so the first slices of the next tile are
+// already loading while the current tile's last slices are consumed and its
+// epilogue stores run -- neither the pipeline fill nor a new workgroup's
+// start-up leaves the CU idle between tiles.  The stage indices repeat every
+// U = 6 slices and K / BK is a multiple of U (checked on the host), so every
+// tile starts at a group boundary.  After a tile's stores the wave waits for
+// all its memory operations (vmcnt(0)): the stores are younger than the
+// prefetches in flight, and the counter does not tell loads from stores.
+template <class C, bool MAP>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
+    int32_t out_n, uint32_t out_bytes) {
+  static_assert(C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SW && !C::SV && !C::BT,
+                "register-staged tiles with three A stages and the plain direct-store epilogue");
+  static_assert(C::LB == 4, "staging registers tied to the final wait");
+  __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
+  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+  constexpr int AS = C::AST, AD = AS - 1, U = 6;
+  constexpr int ASTEP = C::BM * C::BK, BSTEP = C::BNB * C::BK;     // elements per A / B stage
+
+  const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
+  uint32_t slot, G;
+  if (!even_rounds(total, &slot, &G)) return;
+  const int mine = static_cast<int>((total - slot + G - 1) / G);    // tiles of this workgroup (>= 1)
+  const int KT = K / C::BK;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  struct Coord {
+    int64_t e;
+    int32_t row0, row_end, n0;
+  };
+  auto coord = [&](int j) {
+    int mt, nt;
+    tile_mn<C>(tiles, slot + static_cast<uint32_t>(j) * G, total, n_tiles_n, &mt, &nt);
+    const TileEntry te = tiles[mt];
+    return Coord{te.expert, te.row0, te.row_end, nt * C::BN_OUT};
+  };
+
+  // A loader: the j-th tile's rows by LDS DMA through a buffer resource
+  // based at the tile's first row, per-lane byte offsets (rows past the
+  // segment read its last row; their results are never stored)
+  __amdgpu_buffer_rsrc_t rsrc_a;
+  uint32_t aoff[C::LA];
+  int a_j = 0, a_k = 0;
+  auto set_a = [&](const Coord& t) {
+    const int32_t last = t.row_end - 1 - t.row0;
+    const int ln = lane_fresh();
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) {
+      const int rr = C::block(wave, i) * C::RPI + ln / C::CPR;
+      const int c = (ln % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
+      const int32_t row = rr < last ? rr : last;
+      aoff[i] = (static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + c * 8) * 2u;
+    }
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(A + static_cast<int64_t>(t.row0) * K), 0,
+                                               static_cast<int>(static_cast<uint32_t>(C::BM) * static_cast<uint32_t>(K) * 2u),
+                                               0x00020000);
+  };
+  // B loader: buffer loads over the wave's weight matrix (all B rows of a
+  // wavefront come from one of gate / up), per-lane byte offsets
+  __amdgpu_buffer_rsrc_t rsrc_b;
+  uint32_t boff[C::LB];
+  int b_j = 0, b_k = 0;
+  auto set_b = [&](const Coord& t) {
+    bool up = false;
+    const int ln = lane_fresh();
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) {
+      const int rr = C::block(wave, C::LA + i) * C::RPI + ln / C::CPR;
+      const int c = (ln % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
+      const int r = rr - C::BM;
+      up = C::GATEUP && r >= C::BNB / 2;                  // wave-uniform
+      int n = t.n0 + (up ? r - C::BNB / 2 : r);
+      n = n < N ? n : N - 1;
+      boff[i] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8) * 2u;
+    }
+    const bf16_t* bm = (up ? B1 : B0) + t.e * N * static_cast<int64_t>(K);
+    rsrc_b = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(bm), 0,
+                                               static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 2u),
+                                               0x00020000);
+  };
+  // one slice further.  A loader is at slice s + AD after step s and B at
+  // s + 4, so with K / BK a multiple of U the A loader can only leave its
+  // tile after group step 3 and the B loader after step 2 (WRAP); past the
+  // last slice of the workgroup's last tile they re-read that slice into
+  // stages that are never consumed.
+  // The B loader enters a new tile first (group step 2) and keeps its
+  // coordinates in nx for the A loader (step 3) and the epilogue.
+  Coord nx = coord(0);
+  auto adv_a = [&](auto wrap) {
+    ++a_k;
+    if constexpr (decltype(wrap)::value) {
+      if (a_k == KT) {
+        if (a_j + 1 < mine) {
+          a_k = 0;
+          ++a_j;
+          set_a(nx);
+        } else {
+          a_k = KT - 1;
+        }
+      }
+    }
+  };
+  auto adv_b = [&](auto wrap) {
+    ++b_k;
+    if constexpr (decltype(wrap)::value) {
+      if (b_k == KT) {
+        if (b_j + 1 < mine) {
+          b_k = 0;
+          nx = coord(++b_j);
+          set_b(nx);
+        } else {
+          b_k = KT - 1;
+        }
+      }
+    }
+  };
+  using NoWrap = std::false_type;
+  vec16 rb0[C::LB], rb1[C::LB];
+  auto dma_a1 = [&](int stage, int i) {
+    dma_buf_b128_asm(lds_addr(ring + stage * ASTEP + C::block(wave, i) * 512), rsrc_a, aoff[i],
+                     static_cast<uint32_t>(a_k * C::BK * 2));
+  };
+  auto gload_b1 = [&](vec16 (&r)[C::LB], int i) {
+    buffer_load_b128_asm(r[i], rsrc_b, boff[i], static_cast<uint32_t>(b_k * C::BK * 2));
+  };
+  bf16_t* const ring_b = ring + AS * ASTEP;
+  const uint32_t b_lds = lds_addr(ring_b) + static_cast<uint32_t>(lane) * 16u;
+  auto lstore_b1 = [&](int stage, const vec16 (&r)[C::LB], int i) {
+    ds_write_b128_asm(b_lds + static_cast<uint32_t>((stage * BSTEP + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) * 2),
+                      r[i]);
+  };
+  // step memory work, spread over the MFMA groups as in the one-tile form:
+  // the write of B(s + 1) from the registers loaded two steps before, the DMA
+  // of A(s + AD), the loads of B(s + 3)
+  auto step_mem = [&](int a_stage, int b_stage, vec16 (&r)[C::LB]) {
+    return [&, a_stage, b_stage](int g) {
+      if (g == 0) wait_vmcnt_asm<C::LA + C::LB>();
+      if (g < C::LB) lstore_b1(b_stage, r, g);
+      else if (g < C::LB + C::LA) dma_a1(a_stage, g - C::LB);
+      else if (g < 2 * C::LB + C::LA) gload_b1(r, g - C::LB - C::LA);
+    };
+  };
+  static_assert(2 * C::LB + C::LA <= (C::BK / 16) * C::NB * C::TN, "one memory instruction per MFMA group");
+  auto step_sync = [&]() {
+    wait_vmcnt_asm<C::LB + (AD - 1) * (C::LA + C::LB)>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
+    barrier_nofence();
+  };
+
+  // prologue: B(0); A(0), B(1); the write of B(0), A(1), B(2)
+  set_a(nx);
+  set_b(nx);
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) gload_b1(rb0, i);
+  adv_b(NoWrap());
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) dma_a1(0, i);
+  adv_a(NoWrap());
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) gload_b1(rb1, i);
+  adv_b(NoWrap());
+  wait_vmcnt_asm<(AD - 1) * C::LA + C::LB>();  // B(0) has landed
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) lstore_b1(0, rb0, i);
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) dma_a1(1, i);
+  adv_a(NoWrap());
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) gload_b1(rb0, i);
+  adv_b(NoWrap());
+
+  f32x16 acc[C::NB][C::TM][C::TN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int h = 0; h < C::NB; ++h)
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
+  };
+  zero_acc();
+  Coord ct = nx;
+  int32_t lane_dst = lane_dest_row<C, MAP>(out_rows, out_n, ct.row0, ct.row_end, wm, lane);
+  int c_j = 0, c_k = 0;
+  for (;;) {
+    static_for<U>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      step_sync();
+      compute_slice<C>(ring + (u % AS) * ASTEP, ring_b + (u % 2) * BSTEP, acc, wm, wn, lane,
+                       step_mem((u + AD) % AS, (u + 1) % 2, (u % 2) ? rb0 : rb1));
+      adv_a(std::integral_constant<bool, u == 3>());
+      adv_b(std::integral_constant<bool, u == 2>());
+    });
+    c_k += U;
+    if (c_k < KT) continue;
+    // epilogue: value q of 32 x 32 block (i, j) is C[m][n] at m = 8*(q/4) +
+    // 4*(lane/32) + q%4, n = lane%32 of the block.  Stores go through a
+    // buffer resource over the output from column n0 on: rows outside the
+    // segment (or mapped to no row) get an offset past its end, which the
+    // hardware drops, so the stores need no branches.  The destination row
+    // of the lane's value q is the row-map entry held by lane m % 64 (read
+    // with readlane: both halves of the wave take one of two known lanes).
+    {
+      const int lk = lane / 32;
+      const __amdgpu_buffer_rsrc_t rsrc_o = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<OutT*>(Cout) + ct.n0, 0, static_cast<int>(out_bytes - static_cast<uint32_t>(ct.n0) * sizeof(OutT)),
+          0x00020000);
+      const uint32_t col_b = static_cast<uint32_t>(wn * C::WTN + lane % 32) * sizeof(OutT);
+      const uint32_t row_b = static_cast<uint32_t>(N) * sizeof(OutT);
+      const int32_t rel_end = ct.row_end - ct.row0 - wm * C::WTM;      // wave rows < rel_end are valid
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m0 = i * 32 + 8 * (q / 4) + (q % 4);               // the lower half's row
+          const int local = m0 + 4 * lk;
+          int32_t d;
+          if constexpr (MAP) {
+            const int32_t d0 = __builtin_amdgcn_readlane(lane_dst, m0), d1 = __builtin_amdgcn_readlane(lane_dst, m0 + 4);
+            d = lk ? d1 : d0;
+          } else {
+            d = ct.row0 + wm * C::WTM + local;
+          }
+          const uint32_t voff = (local < rel_end && d >= 0) ? static_cast<uint32_t>(d) * row_b + col_b : 0xFFFFF000u;
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j) {
+            // a 32-column block at or past N (N is a multiple of 64) is not stored
+            const uint32_t o = ct.n0 + wn * C::WTN + j * 32 < N ? voff + j * 32 * sizeof(OutT) : 0xFFFFF000u;
+            const float v = acc[0][i][j][q];
+            if constexpr (C::GATEUP) {
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  __builtin_bit_cast(uint16_t, bf16_hw(silu_fast(v) * acc[C::NB - 1][i][j][q])), rsrc_o,
+                  static_cast<int>(o), 0, 0);
+            } else if constexpr (C::OUT_F32) {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc_o, static_cast<int>(o), 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf16_hw(v)), rsrc_o,
+                                                    static_cast<int>(o), 0, 0);
+            }
+          }
+        }
+    }
+    if (++c_j == mine) break;
+    // next tile: its row-map entries load while the stores drain; then
+    // nothing of this wave is in flight (the next slices' loads landed
+    // during the epilogue)
+    ct = nx;
+    int32_t raw = -1;
+    {
+      const int32_t row = ct.row0 + wm * C::WTM + lane_fresh() % C::WTM;
+      if (MAP && row < ct.row_end) raw = out_rows[row];
+      else if (!MAP) raw = row;
+    }
+    wait_vmcnt_asm<0>();
+    lane_dst = MAP ? (raw >= 0 && raw < out_n ? raw : -1) : raw;
+    zero_acc();
+    c_k = 0;
+    // the loaders' per-lane offsets are formed again here rather than kept
+    // live across the epilogue (registers); both loaders are in tile c_j
+    set_a(ct);
+    set_b(ct);
+  }
+  // no DMA may still land in the ring and no load in a staging register
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(rb0[0]), "+v"(rb0[1]), "+v"(rb0[2]), "+v"(rb0[3]), "+v"(rb1[0]), "+v"(rb1[1]),
+                 "+v"(rb1[2]), "+v"(rb1[3])
+               :
+               : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1130,12 +1441,42 @@ inline int device_cus() {
   return n;
 }
 
+#ifndef MOE_RS_PERSIST
+#define MOE_RS_PERSIST 1
+#endif
+
+// Register-staged tiles whose one-tile form stores directly from registers
+// (the tile does not fit the LDS ring) run in the persistent register-staged
+// form when the slice count K / BK is a multiple of its 6-slice stage cycle.
+template <class C>
+constexpr bool rs_persistent_ok() {
+  using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+  return C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SW && !C::SV && !C::BT &&
+         C::BM * C::BN_OUT * static_cast<int>(sizeof(OutT)) > C::RING * 2;
+}
+
 template <class C, bool MAP>
 void launch_kernel(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
                    const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn,
                    hipStream_t stream, const void* aux_in, void* aux_out, int32_t kb1, const int32_t* out_rows,
-                   int32_t out_n) {
+                   int32_t out_n, int64_t c_rows) {
   const int64_t upper = static_cast<int64_t>(max_tiles) * ntn;
+  if constexpr (rs_persistent_ok<C>()) {
+    // the output is addressed through a buffer resource with 32-bit offsets
+    // (an offset of 0xFFFFF000 and above marks a row that is not stored)
+    using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
+    const int64_t out_bytes = c_rows * N * static_cast<int64_t>(sizeof(OutT));
+    const int32_t kt = K / C::BK;
+    if (MOE_RS_PERSIST && kt >= 6 && kt % 6 == 0 && c_rows > 0 && out_bytes < 0xFFFFF000ll) {
+      const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
+      const int64_t g = upper < slots ? upper : slots;
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_rs_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
+                         dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n,
+                         static_cast<uint32_t>(out_bytes));
+      return;
+    }
+  }
   // the persistent form has the plain store epilogue only
   if (C::EPI == kEpiStore && !C::BT && !C::SW && persistent) {
     const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
@@ -1163,24 +1504,25 @@ template <class C>
 void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
                 const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream,
                 const void* aux_in = nullptr, void* aux_out = nullptr, int32_t kb1 = 0,
-                const int32_t* out_rows = nullptr, int32_t out_n = 0) {
+                const int32_t* out_rows = nullptr, int32_t out_n = 0, int64_t c_rows = -1) {
   if constexpr (C::EPI == kEpiStore && !C::GATEUP) {
     if (out_rows) {
       launch_kernel<C, true>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in,
-                             aux_out, kb1, out_rows, out_n);
+                             aux_out, kb1, out_rows, out_n, out_n);
       return;
     }
   }
   launch_kernel<C, false>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in, aux_out,
-                          kb1, nullptr, 0);
+                          kb1, nullptr, 0, c_rows);
 }
 
 // Gate/up then down projection.  With gu_save the gate/up tiles GUS also
 // store the pre-activations G | U there ([rows, 2 d_ff], bf16).
 template <class GU, class GUS, class DF, class DB, bool PERSIST>
-int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const void* wu, const void* wdn, void* H,
-                void* z, int32_t z_dtype, const int32_t* z_rows, int32_t z_n, const TileEntry* tiles,
-                const int32_t* n_tiles, int32_t max_tiles, void* gu_save, hipStream_t stream) {
+int launch_bf16(const void* x, int64_t rows, int32_t d, int32_t d_ff, const void* wg, const void* wu,
+                const void* wdn, void* H, void* z, int32_t z_dtype, const int32_t* z_rows, int32_t z_n,
+                const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, void* gu_save,
+                hipStream_t stream) {
   static_assert(GU::BM == GUS::BM && GU::BN_OUT == GUS::BN_OUT, "one tiling with and without the saved G | U");
   const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
   const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
@@ -1192,10 +1534,10 @@ int launch_bf16(const void* x, int32_t d, int32_t d_ff, const void* wg, const vo
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
     launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
-                   z_rows, z_n);
+                   z_rows, z_n, rows);
   else
     launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
-                   z_rows, z_n);
+                   z_rows, z_n, rows);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -198,13 +198,13 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
   }
   switch (pick_tiles(rows, E)) {
     case kLarge:
-      return launch_bf16<CfgLgGU, CfgLgGUS, CfgLgDF, CfgLgDB, kPersistLg>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+      return launch_bf16<CfgLgGU, CfgLgGUS, CfgLgDF, CfgLgDB, kPersistLg>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
     case kMedium:
-      return launch_bf16<CfgMdGU, CfgMdGUS, CfgMdDF, CfgMdDB, kPersistMd>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+      return launch_bf16<CfgMdGU, CfgMdGUS, CfgMdDF, CfgMdDB, kPersistMd>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
     default:
-      return launch_bf16<CfgSmGU, CfgSmGUS, CfgSmDF, CfgSmDB, kPersistSm>(x, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
+      return launch_bf16<CfgSmGU, CfgSmGUS, CfgSmDF, CfgSmDB, kPersistSm>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
   }
 }

@@ -223,6 +223,10 @@ def _segments(rng, E, rows, mode):
     (2, 2100, 128, 128, "bf16", "f32", "static"),       # >= 768 rows per expert: 256-row tiles
     (3, 2400, 192, 256, "bf16", "bf16", "packed"),     # 256-row tiles, odd slice count (d / 64 = 3)
     (2, 1700, 320, 192, "bf16", "f32", "static"),      # 256-row tiles, odd slice counts, partial N-tiles
+    # 256-row tiles with 6 slices per down tile and more tiles than CUs: the
+    # persistent register-staged down kernel, several tiles per workgroup,
+    # ragged segment ends and a partial last N-tile
+    (3, 70000, 320, 384, "bf16", "f32", "static"),
 ])
 def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     rng = np.random.default_rng(rows + E)
@@ -256,6 +260,7 @@ def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     (5, 700, 128, 192, "bf16", "f32", "packed"),         # 128-row tiles
     (2, 2100, 128, 128, "bf16", "f32", "static"),        # 256-row tiles, direct fp32 stores
     (3, 2400, 192, 256, "bf16", "bf16", "packed"),       # 256-row tiles, stores staged through LDS
+    (3, 70000, 320, 384, "bf16", "f32", "packed"),       # persistent register-staged down tiles
 ])
 def test_grouped_swiglu_row_map(ge, E, rows, d, d_ff, dt, zdt, mode):
     """With z_rows, row i of the result lands in z row z_rows[i]: the rows
