@@ -1122,8 +1122,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
     int32_t out_n, uint32_t out_bytes) {
-  static_assert(C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SW && !C::SV && !C::BT,
-                "register-staged tiles with three A stages and the plain direct-store epilogue");
+  static_assert(C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SV && !C::BT && (!C::SW || C::GATEUP),
+                "register-staged tiles with three A stages and the plain store epilogue");
   static_assert(C::LB == 4, "staging registers tied to the final wait");
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
@@ -1176,14 +1176,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
   uint32_t boff[C::LB];
   int b_j = 0, b_k = 0;
   auto set_b = [&](const Coord& t) {
-    bool up = false;
+    // every B row of the wavefront lies in the gate half, or every one in the up half
+    const bool up = C::GATEUP && C::block(wave, C::LA) * C::RPI - C::BM >= C::BNB / 2;
     const int ln = lane_fresh();
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
       const int rr = C::block(wave, C::LA + i) * C::RPI + ln / C::CPR;
       const int c = (ln % C::CPR) ^ ((rr / (256 / C::RB)) % C::CPR);
       const int r = rr - C::BM;
-      up = C::GATEUP && r >= C::BNB / 2;                  // wave-uniform
       int n = t.n0 + (up ? r - C::BNB / 2 : r);
       n = n < N ? n : N - 1;
       boff[i] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(K) + c * 8) * 2u;
@@ -1310,52 +1310,114 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     });
     c_k += U;
     if (c_k < KT) continue;
-    // epilogue: value q of 32 x 32 block (i, j) is C[m][n] at m = 8*(q/4) +
-    // 4*(lane/32) + q%4, n = lane%32 of the block.  Stores go through a
-    // buffer resource over the output from column n0 on: rows outside the
-    // segment (or mapped to no row) get an offset past its end, which the
-    // hardware drops, so the stores need no branches.  The destination row
-    // of the lane's value q is the row-map entry held by lane m % 64 (read
-    // with readlane: both halves of the wave take one of two known lanes).
-    {
-      const int lk = lane / 32;
+    if constexpr (C::SW) {
+      // Swapped layout (gate/up tiles): value q of block (i, j) is H[m][n] at
+      // m = i*32 + lane%32 of the wave's rows, n = j*32 + 8*(q/4) +
+      // 4*(lane/32) + q%4 of its columns.  The tile is staged in the two
+      // ring stages the last slice used (A stage 2, B stage 1: the next
+      // tile's first slices sit in the others), rows [0, BM/2) in one and
+      // [BM/2, BM) in the other; chunk c of row r at position c ^ (r % 16)
+      // (the lanes writing one chunk of 16 rows, and the threads reading 16
+      // chunks of a row, hit 16 different positions).  Then every thread
+      // stores whole 16-byte row pieces through a buffer resource (rows past
+      // the segment, and columns past N, get an offset past its end).
+      constexpr int TROW = C::BN_OUT * static_cast<int>(sizeof(OutT));
+      constexpr int HALF = C::BM / 2;
+      constexpr int CH = TROW / 16;                                   // 16-byte chunks per row
+      static_assert(CH == 16 && HALF * TROW <= ASTEP * 2 && HALF * TROW <= BSTEP * 2 && C::WTM <= HALF,
+                    "each half of the tile fits a free stage");
+      char* const reg0 = reinterpret_cast<char*>(ring + 2 * ASTEP);
+      char* const reg1 = reinterpret_cast<char*>(ring_b + BSTEP);
+      const int lf = lane_fresh(), lr = lf % 32, lk = lf / 32;
+      barrier_nofence();                 // every wave is done reading the last slice's stages
+      {
+        char* const reg = wm * C::WTM < HALF ? reg0 : reg1;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          const int r = (wm * C::WTM) % HALF + i * 32 + lr;
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int chunk = (wn * C::WTN + j * 32 + 8 * g4) / 8;
+              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+              u32x2 v;
+              auto f = [&](int q) { return silu_fast(acc[0][i][j][q]) * acc[C::NB - 1][i][j][q]; };
+              v[0] = bf16x2_hw(f(4 * g4), f(4 * g4 + 1));
+              v[1] = bf16x2_hw(f(4 * g4 + 2), f(4 * g4 + 3));
+              *reinterpret_cast<u32x2*>(reg + r * TROW + ((chunk ^ (r % 16)) << 4) + lk * 8) = v;
+            }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+      barrier_nofence();
       const __amdgpu_buffer_rsrc_t rsrc_o = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<OutT*>(Cout) + ct.n0, 0, static_cast<int>(out_bytes - static_cast<uint32_t>(ct.n0) * sizeof(OutT)),
           0x00020000);
-      const uint32_t col_b = static_cast<uint32_t>(wn * C::WTN + lane % 32) * sizeof(OutT);
-      const uint32_t row_b = static_cast<uint32_t>(N) * sizeof(OutT);
-      const int32_t rel_end = ct.row_end - ct.row0 - wm * C::WTM;      // wave rows < rel_end are valid
+      const int rows_here = ct.row_end - ct.row0;
+      const int chunks_here = (N - ct.n0) * static_cast<int>(sizeof(OutT)) / 16;
+      constexpr int ITERS = C::BM * CH / C::THREADS;
+      static_assert(ITERS * C::THREADS == C::BM * CH, "whole pieces per thread");
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m0 = i * 32 + 8 * (q / 4) + (q % 4);               // the lower half's row
-          const int local = m0 + 4 * lk;
-          int32_t d;
-          if constexpr (MAP) {
-            const int32_t d0 = __builtin_amdgcn_readlane(lane_dst, m0), d1 = __builtin_amdgcn_readlane(lane_dst, m0 + 4);
-            d = lk ? d1 : d0;
-          } else {
-            d = ct.row0 + wm * C::WTM + local;
-          }
-          const uint32_t voff = (local < rel_end && d >= 0) ? static_cast<uint32_t>(d) * row_b + col_b : 0xFFFFF000u;
-#pragma unroll
-          for (int j = 0; j < C::TN; ++j) {
-            // a 32-column block at or past N (N is a multiple of 64) is not stored
-            const uint32_t o = ct.n0 + wn * C::WTN + j * 32 < N ? voff + j * 32 * sizeof(OutT) : 0xFFFFF000u;
-            const float v = acc[0][i][j][q];
-            if constexpr (C::GATEUP) {
-              __builtin_amdgcn_raw_buffer_store_b16(
-                  __builtin_bit_cast(uint16_t, bf16_hw(silu_fast(v) * acc[C::NB - 1][i][j][q])), rsrc_o,
-                  static_cast<int>(o), 0, 0);
-            } else if constexpr (C::OUT_F32) {
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc_o, static_cast<int>(o), 0, 0);
+      for (int it = 0; it < ITERS; ++it) {
+        const int v = threadIdx.x + it * C::THREADS;
+        const int r = v / CH, cv = v % CH;
+        const int rr = r % HALF;
+        const char* src = (r < HALF ? reg0 : reg1) + rr * TROW + ((cv ^ (rr % 16)) << 4);
+        const vec16 val = *reinterpret_cast<const vec16*>(src);
+        const uint32_t o = (r < rows_here && cv < chunks_here)
+                               ? static_cast<uint32_t>(ct.row0 + r) * static_cast<uint32_t>(N * sizeof(OutT)) + cv * 16u
+                               : 0xFFFFF000u;
+        __builtin_amdgcn_raw_buffer_store_b128(val, rsrc_o, static_cast<int>(o), 0, 0);
+      }
+    } else {
+      // epilogue: value q of 32 x 32 block (i, j) is C[m][n] at m = 8*(q/4) +
+      // 4*(lane/32) + q%4, n = lane%32 of the block.  Stores go through a
+      // buffer resource over the output from column n0 on: rows outside the
+      // segment (or mapped to no row) get an offset past its end, which the
+      // hardware drops, so the stores need no branches.  The destination row
+      // of the lane's value q is the row-map entry held by lane m % 64 (read
+      // with readlane: both halves of the wave take one of two known lanes).
+      {
+        const int lk = lane / 32;
+        const __amdgpu_buffer_rsrc_t rsrc_o = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<OutT*>(Cout) + ct.n0, 0, static_cast<int>(out_bytes - static_cast<uint32_t>(ct.n0) * sizeof(OutT)),
+            0x00020000);
+        const uint32_t col_b = static_cast<uint32_t>(wn * C::WTN + lane % 32) * sizeof(OutT);
+        const uint32_t row_b = static_cast<uint32_t>(N) * sizeof(OutT);
+        const int32_t rel_end = ct.row_end - ct.row0 - wm * C::WTM;      // wave rows < rel_end are valid
+  #pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+  #pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int m0 = i * 32 + 8 * (q / 4) + (q % 4);               // the lower half's row
+            const int local = m0 + 4 * lk;
+            int32_t d;
+            if constexpr (MAP) {
+              const int32_t d0 = __builtin_amdgcn_readlane(lane_dst, m0), d1 = __builtin_amdgcn_readlane(lane_dst, m0 + 4);
+              d = lk ? d1 : d0;
             } else {
-              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf16_hw(v)), rsrc_o,
-                                                    static_cast<int>(o), 0, 0);
+              d = ct.row0 + wm * C::WTM + local;
+            }
+            const uint32_t voff = (local < rel_end && d >= 0) ? static_cast<uint32_t>(d) * row_b + col_b : 0xFFFFF000u;
+  #pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+              // a 32-column block at or past N (N is a multiple of 64) is not stored
+              const uint32_t o = ct.n0 + wn * C::WTN + j * 32 < N ? voff + j * 32 * sizeof(OutT) : 0xFFFFF000u;
+              const float v = acc[0][i][j][q];
+              if constexpr (C::GATEUP) {
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    __builtin_bit_cast(uint16_t, bf16_hw(silu_fast(v) * acc[C::NB - 1][i][j][q])), rsrc_o,
+                    static_cast<int>(o), 0, 0);
+              } else if constexpr (C::OUT_F32) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc_o, static_cast<int>(o), 0, 0);
+              } else {
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf16_hw(v)), rsrc_o,
+                                                      static_cast<int>(o), 0, 0);
+              }
             }
           }
-        }
+      }
     }
     if (++c_j == mine) break;
     // next tile: its row-map entries load while the stores drain; then
@@ -1445,14 +1507,16 @@ inline int device_cus() {
 #define MOE_RS_PERSIST 1
 #endif
 
-// Register-staged tiles whose one-tile form stores directly from registers
-// (the tile does not fit the LDS ring) run in the persistent register-staged
-// form when the slice count K / BK is a multiple of its 6-slice stage cycle.
+// Register-staged tiles run in the persistent register-staged form when the
+// slice count K / BK is a multiple of its 6-slice stage cycle: tiles whose
+// one-tile form stores directly from registers (the tile does not fit the
+// LDS ring), and swapped gate/up tiles (staged through two free stages).
 template <class C>
 constexpr bool rs_persistent_ok() {
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
-  return C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SW && !C::SV && !C::BT &&
-         C::BM * C::BN_OUT * static_cast<int>(sizeof(OutT)) > C::RING * 2;
+  return C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SV && !C::BT &&
+         (C::SW ? C::GATEUP && C::BN_OUT * static_cast<int>(sizeof(OutT)) == 256
+                : C::BM * C::BN_OUT * static_cast<int>(sizeof(OutT)) > C::RING * 2);
 }
 
 template <class C, bool MAP>
@@ -1530,7 +1594,8 @@ int launch_bf16(const void* x, int64_t rows, int32_t d, int32_t d_ff, const void
   if (gu_save)
     launch_one<GUS>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, gu_save);
   else
-    launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream);
+    launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, nullptr, 0,
+                   nullptr, 0, rows);
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
     launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,

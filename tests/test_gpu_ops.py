@@ -227,6 +227,11 @@ def _segments(rng, E, rows, mode):
     # persistent register-staged down kernel, several tiles per workgroup,
     # ragged segment ends and a partial last N-tile
     (3, 70000, 320, 384, "bf16", "f32", "static"),
+    # both launches persistent (d / 64 = 6 gate/up slices), a partial last
+    # down N-tile
+    (3, 70000, 384, 384, "bf16", "f32", "static"),
+    # persistent gate/up tiles with a partial last N-tile (d_ff = 448)
+    (2, 60000, 384, 448, "bf16", "bf16", "packed"),
 ])
 def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     rng = np.random.default_rng(rows + E)
@@ -261,6 +266,7 @@ def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     (2, 2100, 128, 128, "bf16", "f32", "static"),        # 256-row tiles, direct fp32 stores
     (3, 2400, 192, 256, "bf16", "bf16", "packed"),       # 256-row tiles, stores staged through LDS
     (3, 70000, 320, 384, "bf16", "f32", "packed"),       # persistent register-staged down tiles
+    (3, 70000, 384, 384, "bf16", "f32", "packed"),       # both launches persistent
 ])
 def test_grouped_swiglu_row_map(ge, E, rows, d, d_ff, dt, zdt, mode):
     """With z_rows, row i of the result lands in z row z_rows[i]: the rows
