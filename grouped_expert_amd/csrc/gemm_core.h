@@ -35,6 +35,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ n_tiles, uint32_t* flags,
                                                            int32_t* __restrict__ exp_rows = nullptr) {
   __shared__ int32_t sh16[17];
+  __shared__ int32_t first_sh[1024], keep_sh[1024], start_sh[1024], end_sh[1024];
   const int t = threadIdx.x;
   int32_t s = 0, c = 0;
   if (t < E) {
@@ -52,8 +53,26 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   // an expert whose tiles would run past the table (only with overlapping
   // segments) keeps the tiles that fit, so its run stays self-consistent
   const int32_t keep = pre >= max_tiles ? 0 : (cnt < max_tiles - pre ? cnt : max_tiles - pre);
-  for (int32_t i = 0; i < keep; ++i)
-    tiles[pre + i] = TileEntry{t, s + i * BM, s + c, pre, keep, 0, 0, 0};
+  first_sh[t] = pre;
+  keep_sh[t] = keep;
+  start_sh[t] = s;
+  end_sh[t] = s + c;
+  __syncthreads();
+  // every thread writes tiles v = t, t + 1024, ...: the expert of tile v is
+  // the last expert whose first tile is <= v (binary search over the
+  // nondecreasing first-tile table: an expert without tiles shares its first
+  // tile with the next expert, which the search prefers)
+  const int32_t n_out = total < max_tiles ? total : max_tiles;
+  for (int32_t v = t; v < n_out; v += 1024) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (first_sh[mid] <= v) lo = mid;
+      else hi = mid - 1;
+    }
+    const int32_t f = first_sh[lo], kp = keep_sh[lo];
+    if (v - f < kp) tiles[v] = TileEntry{lo, start_sh[lo] + (v - f) * BM, end_sh[lo], f, kp, 0, 0, 0};
+  }
   if (exp_rows && t < E) {               // per expert: first row and the rows its tiles cover
     exp_rows[2 * t] = s;
     exp_rows[2 * t + 1] = c < keep * BM ? c : keep * BM;
@@ -1113,14 +1132,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
 // epilogue stores run -- neither the pipeline fill nor a new workgroup's
 // start-up leaves the CU idle between tiles.  The stage indices repeat every
 // U = 6 slices and K / BK is a multiple of U (checked on the host), so every
-// tile starts at a group boundary.  After a tile's stores the wave waits for
-// all its memory operations (vmcnt(0)): the stores are younger than the
-// prefetches in flight, and the counter does not tell loads from stores.
+// tile starts at a group boundary.
 template <class C, bool MAP>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* __restrict__ out_rows,
+    const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* out_rows,
     int32_t out_n, uint32_t out_bytes) {
   static_assert(C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SV && !C::BT && (!C::SW || C::GATEUP),
                 "register-staged tiles with three A stages and the plain store epilogue");
@@ -1262,6 +1279,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     barrier_nofence();
   };
 
+  Coord ct = nx;
+  // Row map: the raw entry of the wave's row wm*WTM + lane of a tile is
+  // loaded one epilogue ahead -- before the previous tile's stores -- and
+  // checked (row inside the segment, entry inside [0, out_n)) only when its
+  // own epilogue starts, so the wait for it never stalls a K loop.
+  auto map_raw = [&](const Coord& t) -> int32_t {
+    if constexpr (!MAP) return 0;
+    const int32_t row = t.row0 + wm * C::WTM + lane_fresh() % C::WTM;
+    // (out_rows is not declared restrict here: the load then stays ahead of
+    // the memory barrier that follows it instead of sinking behind the stores)
+    return out_rows[row < t.row_end ? row : t.row_end - 1];   // rows past the segment: checked at use
+  };
+  int32_t raw_cur = map_raw(ct);
+  if constexpr (MAP) asm volatile("" ::"v"(raw_cur));   // the first entry is waited for here, before any slice load
   // prologue: B(0); A(0), B(1); the write of B(0), A(1), B(2)
   set_a(nx);
   set_b(nx);
@@ -1296,8 +1327,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
           for (int q = 0; q < 16; ++q) acc[h][i][j][q] = 0.0f;
   };
   zero_acc();
-  Coord ct = nx;
-  int32_t lane_dst = lane_dest_row<C, MAP>(out_rows, out_n, ct.row0, ct.row_end, wm, lane);
   int c_j = 0, c_k = 0;
   for (;;) {
     static_for<U>([&](auto uc) {
@@ -1310,6 +1339,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     });
     c_k += U;
     if (c_k < KT) continue;
+    const int32_t lane_dst =
+        ct.row0 + wm * C::WTM + lane_fresh() % C::WTM < ct.row_end && raw_cur >= 0 && raw_cur < out_n ? raw_cur : -1;
+    // nx: the next tile (the B loader's), or this one after the last tile
+    if constexpr (MAP) {
+      raw_cur = map_raw(nx);
+      asm volatile("" ::: "memory");     // issued before the stores below
+    }
     if constexpr (C::SW) {
       // Swapped layout (gate/up tiles): value q of block (i, j) is H[m][n] at
       // m = i*32 + lane%32 of the wave's rows, n = j*32 + 8*(q/4) +
@@ -1399,7 +1435,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
             } else {
               d = ct.row0 + wm * C::WTM + local;
             }
-            const uint32_t voff = (local < rel_end && d >= 0) ? static_cast<uint32_t>(d) * row_b + col_b : 0xFFFFF000u;
+            // 32-bit product as one instruction of our own: the compiler's
+            // 64-bit multiply-add form would take an arbitrary register as
+            // the unused high half of its addend -- possibly the row-map
+            // entry still loading -- and wait for it
+            uint32_t prod;
+            asm("v_mul_lo_u32 %0, %1, %2" : "=v"(prod) : "v"(d), "s"(row_b));
+            const uint32_t voff = (local < rel_end && d >= 0) ? prod + col_b : 0xFFFFF000u;
   #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
               // a 32-column block at or past N (N is a multiple of 64) is not stored
@@ -1420,18 +1462,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
       }
     }
     if (++c_j == mine) break;
-    // next tile: its row-map entries load while the stores drain; then
-    // nothing of this wave is in flight (the next slices' loads landed
-    // during the epilogue)
+    // next tile.  The epilogue's stores need no wait here: vector memory
+    // operations complete in issue order, so the next step's count-based
+    // wait (at most so many operations in flight, stores included) still
+    // proves that the slices it needs have landed.
     ct = nx;
-    int32_t raw = -1;
-    {
-      const int32_t row = ct.row0 + wm * C::WTM + lane_fresh() % C::WTM;
-      if (MAP && row < ct.row_end) raw = out_rows[row];
-      else if (!MAP) raw = row;
-    }
-    wait_vmcnt_asm<0>();
-    lane_dst = MAP ? (raw >= 0 && raw < out_n ? raw : -1) : raw;
     zero_acc();
     c_k = 0;
     // the loaders' per-lane offsets are formed again here rather than kept
