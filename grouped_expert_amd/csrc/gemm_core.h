@@ -1488,10 +1488,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
 // Three tile shapes, chosen from the mean rows per expert (rows / E), which the
 // host knows without reading the device counts:
 //   large  (mean >= 768 rows): 256 x 256 tiles, 8 wavefronts (two per SIMD, so
-//          one wave's MFMAs cover the other's waits), 2-slice ring (128 KB)
-//          with the weight rows register-staged two slices ahead, bands of 4
-//          M-tiles for L2 reuse -- long MFMA-bound segments (static receiver
-//          arrays);
+//          one wave's MFMAs cover the other's waits), LDS for three A and two
+//          B slices (160 KB) with the weight rows register-staged three
+//          slices ahead, persistent where K / 64 is a multiple of 6 (the
+//          slice pipeline runs on across tiles), bands of 8 M-tiles for L2
+//          reuse (the fp32 / gate-up tiles; 2, 4, 12, 16 measured slower) --
+//          long MFMA-bound segments (static receiver arrays);
 //   medium (mean >= 48 rows):  128 x 256 tiles, 8 wavefronts, 3-slice ring
 //          (144 KB), persistent (the ring runs on across tiles; measured
 //          3.5 % faster than one tile per workgroup on the mid layer) --
@@ -1500,8 +1502,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
 //          (144 KB), persistent -- decode-like segments of a few rows.
 // Gate/up tiles hold 128 gate + 128 up rows of B (128 H columns); down tiles
 // hold 256 output columns.
-using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3, 1, 1, true>;
-using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
+using CfgLgGU = Cfg<256, 256, 4, 2, 2, true, false, false, 64, 1, 8, 8, true, kEpiStore, false, 3, 1, 1, true>;
+using CfgLgDF = Cfg<256, 256, 4, 2, 2, false, true, false, 64, 1, 8, 8, true, kEpiStore, false, 3>;
 using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true, kEpiStore, false, 3>;
 using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
 using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
