@@ -151,11 +151,22 @@ __device__ __forceinline__ int32_t block_scan_lds(int32_t* v, int n, int32_t* wa
   return total;
 }
 
+// FULL (short route lists, R <= kFullScanMaxRoutes): no count pass and no
+// table -- every block reads all R expert ids itself and counts, per expert,
+// all routes and the routes before its first one (LDS atomics); block 0 also
+// flags invalid ids, as the count pass does.  Decode-sized lists (512
+// routes): 18.8 -> 11.6 us per call.  At the mid layer's 16,384 routes the
+// per-block scan (64 KB, two atomics per route) costs more than the count
+// pass it replaces (25.7 -> 26.7 us), hence the bound.
+constexpr int64_t kFullScanMaxRoutes = 4096;
+
+template <bool FULL>
 __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
     const vec16* __restrict__ x, int64_t T, int64_t row_vecs, int32_t k, const int32_t* __restrict__ ids,
     int32_t E, int64_t cap, RankGeom g, const int32_t* __restrict__ table, int32_t* __restrict__ inv,
     int32_t* __restrict__ src, int32_t* __restrict__ sel_out, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ offsets_out, int32_t* __restrict__ dropped_out, vec16* __restrict__ x_perm) {
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ dropped_out, vec16* __restrict__ x_perm,
+    uint32_t* flags) {
   extern __shared__ int32_t lds[];
   int32_t* sel = lds;                 // [E]   routes per expert
   int32_t* base = lds + E;            // [E]   running route-order rank base of the block
@@ -177,20 +188,22 @@ __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
   // table entries per thread and batch (one batch holds the whole table up to
   // 128 experts)
   constexpr int kTabPer = kFuseMaxChunks * 128 / kFuseThreads;
-  const int64_t entries = g.chunks * E;
+  const int64_t entries = FULL ? 0 : g.chunks * E;
   const int32_t q = kFuseThreads / E, rr = kFuseThreads % E;
   int32_t tv[kTabPer];
-#pragma unroll
-  for (int u = 0; u < kTabPer; ++u) {
-    const int64_t idx = tid + static_cast<int64_t>(u) * kFuseThreads;
-    tv[u] = idx < entries ? table[idx] : 0;
-  }
   constexpr int kPrePer = 64 * kRankMaxSteps / kFuseThreads;                 // chunk ids per thread, at most
   int32_t pv[kPrePer];
+  if constexpr (!FULL) {
 #pragma unroll
-  for (int u = 0; u < kPrePer; ++u) {
-    const int64_t r = c0 * chunk + tid + u * kFuseThreads;
-    pv[u] = r < r0 ? ids[r] : -1;
+    for (int u = 0; u < kTabPer; ++u) {
+      const int64_t idx = tid + static_cast<int64_t>(u) * kFuseThreads;
+      tv[u] = idx < entries ? table[idx] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kPrePer; ++u) {
+      const int64_t r = c0 * chunk + tid + u * kFuseThreads;
+      pv[u] = r < r0 ? ids[r] : -1;
+    }
   }
   const int64_t rme = r0 + lane;
   const int32_t my_id = (w == 0 && rme < r1) ? ids[rme] : -1;
@@ -203,6 +216,29 @@ __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
   }
   for (int b = tid; b < E; b += kFuseThreads) sel[b] = 0, base[b] = 0;
   __syncthreads();
+  if constexpr (FULL) {
+    // every route's expert: the totals, and the routes before this block's first
+    constexpr int kScanUnroll = 8;
+    for (int64_t r00 = 0; r00 < R; r00 += static_cast<int64_t>(kScanUnroll) * kFuseThreads) {
+      int32_t e8[kScanUnroll];
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int64_t r = r00 + tid + u * kFuseThreads;
+        e8[u] = r < R ? ids[r] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int64_t r = r00 + tid + u * kFuseThreads;
+        const int32_t e = e8[u];
+        if (e >= 0 && e < E) {
+          atomicAdd(&sel[e], 1);
+          if (r < r0) atomicAdd(&base[e], 1);
+        } else if (e != -1 && r < R && blockIdx.x == 0) {
+          flag_or(flags, MOE_FLAG_BAD_EXPERT);
+        }
+      }
+    }
+  }
   // expert totals and the routes of every expert in the chunks before c0
   for (int64_t b0 = 0; b0 < entries; b0 += static_cast<int64_t>(kTabPer) * kFuseThreads) {
     if (b0 > 0) {
@@ -244,9 +280,11 @@ __global__ __launch_bounds__(kFuseThreads) void permute_fused_kernel(
     }
   }
   // routes of chunk c0 before the block's first route
+  if constexpr (!FULL) {
 #pragma unroll
-  for (int u = 0; u < kPrePer; ++u)
-    if (pv[u] >= 0 && pv[u] < E) atomicAdd(&base[pv[u]], 1);
+    for (int u = 0; u < kPrePer; ++u)
+      if (pv[u] >= 0 && pv[u] < E) atomicAdd(&base[pv[u]], 1);
+  }
   __syncthreads();
   for (int b = tid; b < E; b += kFuseThreads) offs[b] = cap < 0 ? sel[b] : (sel[b] < cap ? sel[b] : static_cast<int32_t>(cap));
   __syncthreads();
@@ -380,6 +418,19 @@ int permute_launch(const void* x, int32_t x_dtype, int64_t T, int32_t d, const i
                    int32_t* counts, int32_t* offsets, int32_t* n_dropped, int32_t* table, uint32_t* dev_flags,
                    hipStream_t stream) {
   const int64_t R = T * k;
+  if (R > 0 && R <= kFullScanMaxRoutes) {
+    // one launch: every block counts all routes, then ranks and scatters its own
+    const RankGeom g = rank_geom_fused(R, E);
+    const int64_t row_vecs = x_perm ? row_bytes(x_dtype, d) / 16 : 0;
+    const unsigned blocks = static_cast<unsigned>((T + kFuseTok - 1) / kFuseTok);
+    const size_t lds = static_cast<size_t>(3 * E + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(permute_fused_kernel<true>), dim3(blocks), dim3(kFuseThreads), lds, stream,
+                       static_cast<const vec16*>(x), T, row_vecs, k, topk_ids, E, capacity, g,
+                       static_cast<const int32_t*>(nullptr), inv, src, sel_counts, counts, offsets, n_dropped,
+                       static_cast<vec16*>(x_perm), dev_flags);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   if (R > 0 && R <= kFuseMaxRoutes) {
     // count pass, then the fused rank and scatter
     const RankGeom g = rank_geom_fused(R, E);
@@ -391,9 +442,9 @@ int permute_launch(const void* x, int32_t x_dtype, int64_t T, int32_t d, const i
     const int64_t row_vecs = x_perm ? row_bytes(x_dtype, d) / 16 : 0;
     const unsigned blocks = static_cast<unsigned>((T + kFuseTok - 1) / kFuseTok);
     const size_t lds = static_cast<size_t>(3 * E + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(permute_fused_kernel, dim3(blocks), dim3(kFuseThreads), lds, stream,
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(permute_fused_kernel<false>), dim3(blocks), dim3(kFuseThreads), lds, stream,
                        static_cast<const vec16*>(x), T, row_vecs, k, topk_ids, E, capacity, g, table, inv, src,
-                       sel_counts, counts, offsets, n_dropped, static_cast<vec16*>(x_perm));
+                       sel_counts, counts, offsets, n_dropped, static_cast<vec16*>(x_perm), dev_flags);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
