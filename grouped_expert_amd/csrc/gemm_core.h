@@ -220,9 +220,12 @@ constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
 
 template <int BM_, int BNB_, int WM_, int WN_, int STAGES_, bool GATEUP_, bool OUT_F32_, bool EB_ = false,
           int BK_ = 64, int OCC_ = 1, int GM_ = 1, int NW_ = 4, bool RS_ = false, int EPI_ = kEpiStore,
-          bool BT_ = false, int AST_ = 2, int PB_ = 1, int PA_ = 1, bool SW_ = false, bool SV_ = false>
+          bool BT_ = false, int AST_ = 2, int PB_ = 1, int PA_ = 1, bool SW_ = false, bool SV_ = false, int NR_ = 2>
 struct Cfg {
   static constexpr int EPI = EPI_;
+  // NR (register staging): register stages of B rows; B slices are loaded
+  // NR + 1 steps ahead of their use (the one-tile form: NR = 2 only)
+  static constexpr int NR = NR_;
   // BT: B is stored K-major, [K][N] per expert with N contiguous (a weight
   // used transposed, as in the data-gradient products of the backward).  The
   // slice's B region then holds BK rows of BNB values, filled by LDS DMA, and
@@ -279,7 +282,8 @@ struct Cfg {
   static_assert(ROWS % 32 == 0 && BM % 16 == 0, "slice rows");
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "pipeline depth");
   static_assert(!RS || STAGES == 2, "register staging uses a two-stage ring");
-  static_assert(AST == 2 || (RS && AST == 3), "three A stages only with register-staged B rows");
+  static_assert(AST == 2 || (RS && (AST == 3 || AST == 4)), "three or four A stages only with register-staged B rows");
+  static_assert(NR == 2 || (RS && NR >= 2 && NR <= 4), "register stages of B rows");
   static_assert(!SV || (GATEUP && !SW), "saved pre-activations: gate/up tiles in the unswapped layout");
   static_assert(EPI == kEpiStore || GATEUP, "the SwiGLU backward epilogue needs gate/up tiles");
   static_assert(!BT || (!GATEUP && !RS_ && BK == 64 && (BNB == 128 || BNB == 256)), "K-major B tiles");
@@ -1123,6 +1127,40 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
   }
 }
 
+// Smallest slice count K / 64 of a tile for the persistent register-staged
+// pipeline: a multiple of its stage cycle, and at least the B loader's lead
+// (NR + 2 slices), so that no loader runs more than one tile ahead.
+template <class C>
+constexpr int rs_min_slices();
+
+// Stage cycle of the persistent register-staged pipeline: the A ring, the
+// two B stages in LDS and the NR register stages all repeat after U slices.
+template <class C>
+constexpr int rs_cycle() {
+  auto gcd = [](int a, int b) {
+    while (b) {
+      const int t = a % b;
+      a = b;
+      b = t;
+    }
+    return a;
+  };
+  const int u = C::AST * 2 / gcd(C::AST, 2);
+  return u * C::NR / gcd(u, C::NR);
+}
+
+template <class C>
+constexpr int rs_min_slices() {
+  const int u = rs_cycle<C>();
+  return u >= C::NR + 2 ? u : u * ((C::NR + 2 + u - 1) / u);
+}
+
+// K / 64 runs the persistent register-staged pipeline of C
+template <class C>
+constexpr bool rs_slices_ok(int32_t kt) {
+  return kt >= rs_min_slices<C>() && kt % rs_cycle<C>() == 0;
+}
+
 // Persistent form of the register-staged tiles (plain direct-store epilogue,
 // unswapped layout).  G workgroups walk their tiles with a static stride
 // (even rounds), and a workgroup's tiles form one sequence of K slices: the
@@ -1131,20 +1169,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_persiste
 // already loading while the current tile's last slices are consumed and its
 // epilogue stores run -- neither the pipeline fill nor a new workgroup's
 // start-up leaves the CU idle between tiles.  The stage indices repeat every
-// U = 6 slices and K / BK is a multiple of U (checked on the host), so every
-// tile starts at a group boundary.
+// U slices (rs_cycle) and K / BK is a multiple of U and at least the B
+// loader's lead (rs_min_slices, checked on the host), so every tile starts
+// at a group boundary and the loaders run at most one tile ahead.
 template <class C, bool MAP>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     void* __restrict__ Cout, int32_t K, int32_t N, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles_ptr, int32_t n_tiles_n, const int32_t* out_rows,
     int32_t out_n, uint32_t out_bytes) {
-  static_assert(C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SV && !C::BT && (!C::SW || C::GATEUP),
-                "register-staged tiles with three A stages and the plain store epilogue");
+  static_assert(C::RS && C::AST >= 3 && C::EPI == kEpiStore && !C::SV && !C::BT && (!C::SW || C::GATEUP),
+                "register-staged tiles with three or four A stages and the plain store epilogue");
   static_assert(C::LB == 4, "staging registers tied to the final wait");
   __shared__ __attribute__((aligned(16))) bf16_t ring[C::RING];
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
-  constexpr int AS = C::AST, AD = AS - 1, U = 6;
+  constexpr int AS = C::AST, AD = AS - 1, NR = C::NR, U = rs_cycle<C>();
   constexpr int ASTEP = C::BM * C::BK, BSTEP = C::BNB * C::BK;     // elements per A / B stage
 
   const uint32_t total = static_cast<uint32_t>(*n_tiles_ptr) * n_tiles_n;
@@ -1210,11 +1249,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
                                                static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 2u),
                                                0x00020000);
   };
-  // one slice further.  A loader is at slice s + AD after step s and B at
-  // s + 4, so with K / BK a multiple of U the A loader can only leave its
-  // tile after group step 3 and the B loader after step 2 (WRAP); past the
-  // last slice of the workgroup's last tile they re-read that slice into
-  // stages that are never consumed.
+  // one slice further.  After step s the A loader is at slice s + AD + 1
+  // and the B loader at s + NR + 2, so with K / BK a multiple of the stage
+  // cycle U each can only leave its tile after one fixed step of a group
+  // (WRAP: A after step UA, B after step UB, B first); past the last slice
+  // of the workgroup's last tile they re-read that slice into stages that
+  // are never consumed.
   // The B loader enters a new tile first (group step 2) and keeps its
   // coordinates in nx for the A loader (step 3) and the epilogue.
   Coord nx = coord(0);
@@ -1247,7 +1287,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     }
   };
   using NoWrap = std::false_type;
-  vec16 rb0[C::LB], rb1[C::LB];
+  constexpr int UA = (U - (AD + 1) % U) % U, UB = (U - (NR + 2) % U) % U;
+  static_assert(UA != UB && NR + 2 > AD + 1, "the loaders change tiles at different steps (B first)");
+  vec16 rb[NR][C::LB];
   auto dma_a1 = [&](int stage, int i) {
     dma_buf_b128_asm(lds_addr(ring + stage * ASTEP + C::block(wave, i) * 512), rsrc_a, aoff[i],
                      static_cast<uint32_t>(a_k * C::BK * 2));
@@ -1261,18 +1303,27 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     ds_write_b128_asm(b_lds + static_cast<uint32_t>((stage * BSTEP + (C::block(wave, C::LA + i) - C::BM / C::RPI) * 512) * 2),
                       r[i]);
   };
-  // step memory work, spread over the MFMA groups as in the one-tile form:
-  // the write of B(s + 1) from the registers loaded two steps before, the DMA
-  // of A(s + AD), the loads of B(s + 3)
+  // step memory work, spread over the step's MFMA groups (operation o of
+  // the M after group o, or after group o * NG / M when there are more
+  // operations than groups): the LDS write of B(s + 1) from the
+  // registers loaded NR steps before, the DMA of A(s + AD), the loads of
+  // B(s + NR + 1) into the registers just written out.  Before them, the
+  // loads of those registers must have landed: (NR - 1) (LA + LB) younger
+  // loads of the wave may stay in flight.
+  constexpr int NG = (C::BK / 16) * C::NB * C::TN, M = 2 * C::LB + C::LA;
   auto step_mem = [&](int a_stage, int b_stage, vec16 (&r)[C::LB]) {
     return [&, a_stage, b_stage](int g) {
-      if (g == 0) wait_vmcnt_asm<C::LA + C::LB>();
-      if (g < C::LB) lstore_b1(b_stage, r, g);
-      else if (g < C::LB + C::LA) dma_a1(a_stage, g - C::LB);
-      else if (g < 2 * C::LB + C::LA) gload_b1(r, g - C::LB - C::LA);
+      if (g == 0) wait_vmcnt_asm<(NR - 1) * (C::LA + C::LB)>();
+#pragma unroll
+      for (int o = 0; o < M; ++o) {
+        if ((M <= NG ? o : o * NG / M) != g) continue;
+        if (o < C::LB) lstore_b1(b_stage, r, o);
+        else if (o < C::LB + C::LA) dma_a1(a_stage, o - C::LB);
+        else gload_b1(r, o - C::LB - C::LA);
+      }
     };
   };
-  static_assert(2 * C::LB + C::LA <= (C::BK / 16) * C::NB * C::TN, "one memory instruction per MFMA group");
+  static_assert((NR - 1) * (C::LA + C::LB) < 64 && C::LB + (AD - 1) * (C::LA + C::LB) < 64, "vmcnt range");
   auto step_sync = [&]() {
     wait_vmcnt_asm<C::LB + (AD - 1) * (C::LA + C::LB)>();
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes have landed
@@ -1293,27 +1344,39 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
   };
   int32_t raw_cur = map_raw(ct);
   if constexpr (MAP) asm volatile("" ::"v"(raw_cur));   // the first entry is waited for here, before any slice load
-  // prologue: B(0); A(0), B(1); the write of B(0), A(1), B(2)
+  // prologue: B(0) through the registers of stage 0 into LDS B stage 0,
+  // B(1) .. B(NR) into register stages 1 .. NR (B(NR) reusing stage 0 once
+  // B(0) is written out), A(0) .. A(AD - 1) by DMA; then the wave waits for
+  // all of them, so every count-based wait of the steps holds from step 0
+  // on (each later slice has exactly the younger loads the counts assume)
   set_a(nx);
   set_b(nx);
+  static_assert(AD <= NR + 1, "prologue order");
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) gload_b1(rb0, i);
+  for (int i = 0; i < C::LB; ++i) gload_b1(rb[0], i);
   adv_b(NoWrap());
+  static_for<NR + 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;             // 0 .. NR
+    if constexpr (j < AD) {
 #pragma unroll
-  for (int i = 0; i < C::LA; ++i) dma_a1(0, i);
-  adv_a(NoWrap());
+      for (int i = 0; i < C::LA; ++i) dma_a1(j, i);
+      adv_a(NoWrap());
+    }
+    if constexpr (j >= 1 && j < NR) {
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) gload_b1(rb1, i);
-  adv_b(NoWrap());
-  wait_vmcnt_asm<(AD - 1) * C::LA + C::LB>();  // B(0) has landed
+      for (int i = 0; i < C::LB; ++i) gload_b1(rb[j], i);
+      adv_b(NoWrap());
+    }
+    if constexpr (j == NR) {
+      wait_vmcnt_asm<0>();
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) lstore_b1(0, rb0, i);
+      for (int i = 0; i < C::LB; ++i) lstore_b1(0, rb[0], i);
 #pragma unroll
-  for (int i = 0; i < C::LA; ++i) dma_a1(1, i);
-  adv_a(NoWrap());
-#pragma unroll
-  for (int i = 0; i < C::LB; ++i) gload_b1(rb0, i);
-  adv_b(NoWrap());
+      for (int i = 0; i < C::LB; ++i) gload_b1(rb[0], i);
+      adv_b(NoWrap());
+      wait_vmcnt_asm<0>();
+    }
+  });
 
   f32x16 acc[C::NB][C::TM][C::TN];
   auto zero_acc = [&]() {
@@ -1333,9 +1396,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
       constexpr int u = decltype(uc)::value;
       step_sync();
       compute_slice<C>(ring + (u % AS) * ASTEP, ring_b + (u % 2) * BSTEP, acc, wm, wn, lane,
-                       step_mem((u + AD) % AS, (u + 1) % 2, (u % 2) ? rb0 : rb1));
-      adv_a(std::integral_constant<bool, u == 3>());
-      adv_b(std::integral_constant<bool, u == 2>());
+                       step_mem((u + AD) % AS, (u + 1) % 2, rb[(u + 1) % NR]));
+      adv_b(std::integral_constant<bool, u == UB>());
+      adv_a(std::integral_constant<bool, u == UA>());
     });
     c_k += U;
     if (c_k < KT) continue;
@@ -1475,11 +1538,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_rs_persistent
     set_b(ct);
   }
   // no DMA may still land in the ring and no load in a staging register
-  asm volatile("s_waitcnt vmcnt(0)"
-               : "+v"(rb0[0]), "+v"(rb0[1]), "+v"(rb0[2]), "+v"(rb0[3]), "+v"(rb1[0]), "+v"(rb1[1]),
-                 "+v"(rb1[2]), "+v"(rb1[3])
-               :
-               : "memory");
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(rb[j][0]), "+v"(rb[j][1]), "+v"(rb[j][2]), "+v"(rb[j][3])::"memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -1508,6 +1569,12 @@ using CfgLgDB = Cfg<256, 256, 4, 2, 2, false, false, false, 64, 1, 4, 8, true, k
 using CfgMdGU = Cfg<128, 256, 2, 4, 3, true, false, false, 64, 1, 2, 8>;
 using CfgMdDF = Cfg<128, 256, 2, 4, 3, false, true, false, 64, 1, 2, 8>;
 using CfgMdDB = Cfg<128, 256, 2, 4, 3, false, false, false, 64, 1, 2, 8>;
+// medium tiles with the weight rows through four register stages (five
+// slices ahead) and four A stages (three slices ahead), persistent: where
+// K / 64 is a multiple of 4 for both products
+using CfgMdGUr = Cfg<128, 256, 2, 4, 2, true, false, false, 64, 1, 2, 8, true, kEpiStore, false, 4, 1, 1, false, false, 4>;
+using CfgMdDFr = Cfg<128, 256, 2, 4, 2, false, true, false, 64, 1, 2, 8, true, kEpiStore, false, 4, 1, 1, false, false, 4>;
+using CfgMdDBr = Cfg<128, 256, 2, 4, 2, false, false, false, 64, 1, 2, 8, true, kEpiStore, false, 4, 1, 1, false, false, 4>;
 using CfgSmGU = Cfg<32, 256, 1, 4, 4, true, false>;
 // gate/up tiles that also save the pre-activations G | U (training forward):
 // the same tilings in the unswapped layout
@@ -1551,13 +1618,13 @@ inline int device_cus() {
 template <class C>
 constexpr bool rs_persistent_ok() {
   using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
-  return C::RS && C::AST == 3 && C::EPI == kEpiStore && !C::SV && !C::BT &&
+  return C::RS && C::AST >= 3 && C::EPI == kEpiStore && !C::SV && !C::BT &&
          (C::SW ? C::GATEUP && C::BN_OUT * static_cast<int>(sizeof(OutT)) == 256
-                : C::BM * C::BN_OUT * static_cast<int>(sizeof(OutT)) > C::RING * 2);
+                : C::NR > 2 || C::BM * C::BN_OUT * static_cast<int>(sizeof(OutT)) > C::RING * 2);
 }
 
 template <class C, bool MAP>
-void launch_kernel(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
+int launch_kernel(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
                    const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn,
                    hipStream_t stream, const void* aux_in, void* aux_out, int32_t kb1, const int32_t* out_rows,
                    int32_t out_n, int64_t c_rows) {
@@ -1568,53 +1635,56 @@ void launch_kernel(bool persistent, const void* a, const void* b0, const void* b
     using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
     const int64_t out_bytes = c_rows * N * static_cast<int64_t>(sizeof(OutT));
     const int32_t kt = K / C::BK;
-    if (MOE_RS_PERSIST && kt >= 6 && kt % 6 == 0 && c_rows > 0 && out_bytes < 0xFFFFF000ll) {
+    if (MOE_RS_PERSIST && rs_slices_ok<C>(kt) && c_rows > 0 && out_bytes < 0xFFFFF000ll) {
       const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
       const int64_t g = upper < slots ? upper : slots;
       hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_rs_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
                          dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
                          static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n,
                          static_cast<uint32_t>(out_bytes));
-      return;
+      return MOE_OK;
     }
   }
-  // the persistent form has the plain store epilogue only
-  if (C::EPI == kEpiStore && !C::BT && !C::SW && persistent) {
-    const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
-    const int64_t g = upper < slots ? upper : slots;
-    if constexpr (C::EPI == kEpiStore && !C::BT && !C::SW)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
-                         dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n,
-                         static_cast<bf16_t*>(aux_out));
+  if constexpr (C::NR > 2) {
+    return MOE_EUNSUPPORTED;        // deeper register staging exists in the persistent form only
   } else {
-    // at most one workgroup per CU slot; each walks its tiles (even rounds);
-    // register-staged tiles: one workgroup per tile
-    const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
-    const int64_t g = C::RS || upper < slots ? upper : slots;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C, MAP>), dim3(static_cast<unsigned>(g)),
-                       dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
-                       static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn,
-                       static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1, out_rows, out_n);
+    // the persistent form has the plain store epilogue only
+    if (C::EPI == kEpiStore && !C::BT && !C::SW && persistent) {
+      const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;  // C::OCC workgroups per CU
+      const int64_t g = upper < slots ? upper : slots;
+      if constexpr (C::EPI == kEpiStore && !C::BT && !C::SW)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
+                           dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                           static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn, out_rows, out_n,
+                           static_cast<bf16_t*>(aux_out));
+    } else {
+      // at most one workgroup per CU slot; each walks its tiles (even rounds);
+      // register-staged tiles: one workgroup per tile
+      const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
+      const int64_t g = C::RS || upper < slots ? upper : slots;
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_bf16_kernel<C, MAP>), dim3(static_cast<unsigned>(g)),
+                         dim3(C::THREADS), 0, stream, static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0),
+                         static_cast<const bf16_t*>(b1), out, K, N, tiles, n_tiles, ntn,
+                         static_cast<const bf16_t*>(aux_in), static_cast<bf16_t*>(aux_out), kb1, out_rows, out_n);
+    }
+    return MOE_OK;
   }
 }
 
 // One GEMM launch; a row map (out_rows) selects the kernels built with it,
 // which exist for plain-store tiles that are not gate/up tiles.
 template <class C>
-void launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
+int launch_one(bool persistent, const void* a, const void* b0, const void* b1, void* out, int32_t K, int32_t N,
                 const TileEntry* tiles, const int32_t* n_tiles, int32_t max_tiles, int32_t ntn, hipStream_t stream,
                 const void* aux_in = nullptr, void* aux_out = nullptr, int32_t kb1 = 0,
                 const int32_t* out_rows = nullptr, int32_t out_n = 0, int64_t c_rows = -1) {
   if constexpr (C::EPI == kEpiStore && !C::GATEUP) {
-    if (out_rows) {
-      launch_kernel<C, true>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in,
-                             aux_out, kb1, out_rows, out_n, out_n);
-      return;
-    }
+    if (out_rows)
+      return launch_kernel<C, true>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in,
+                                    aux_out, kb1, out_rows, out_n, out_n);
   }
-  launch_kernel<C, false>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in, aux_out,
-                          kb1, nullptr, 0, c_rows);
+  return launch_kernel<C, false>(persistent, a, b0, b1, out, K, N, tiles, n_tiles, max_tiles, ntn, stream, aux_in,
+                                 aux_out, kb1, nullptr, 0, c_rows);
 }
 
 // Gate/up then down projection.  With gu_save the gate/up tiles GUS also
@@ -1628,18 +1698,21 @@ int launch_bf16(const void* x, int64_t rows, int32_t d, int32_t d_ff, const void
   const int nt1 = (d_ff + GU::BN_OUT - 1) / GU::BN_OUT;
   const int nt2 = (d + DF::BN_OUT - 1) / DF::BN_OUT;
   MOE_CHECK(static_cast<int64_t>(max_tiles) * (nt1 > nt2 ? nt1 : nt2) <= INT32_MAX, MOE_EUNSUPPORTED);
+  int st;
   if (gu_save)
-    launch_one<GUS>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, gu_save);
+    st = launch_one<GUS>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, gu_save);
   else
-    launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, nullptr, 0,
-                   nullptr, 0, rows);
+    st = launch_one<GU>(PERSIST, x, wg, wu, H, d, d_ff, tiles, n_tiles, max_tiles, nt1, stream, nullptr, nullptr, 0,
+                        nullptr, 0, rows);
+  if (st != MOE_OK) return st;
   MOE_LAUNCH_CHECK();
   if (z_dtype == MOE_F32)
-    launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
-                   z_rows, z_n, rows);
+    st = launch_one<DF>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr,
+                        0, z_rows, z_n, rows);
   else
-    launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr, 0,
-                   z_rows, z_n, rows);
+    st = launch_one<DB>(PERSIST, H, wdn, nullptr, z, d_ff, d, tiles, n_tiles, max_tiles, nt2, stream, nullptr, nullptr,
+                        0, z_rows, z_n, rows);
+  if (st != MOE_OK) return st;
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -114,6 +114,8 @@ inline int32_t tile_bm(int32_t dtype, TileKind t) {
 }
 static_assert(CfgLgGU::BM == CfgLgDF::BM && CfgLgGU::BM == CfgLgDB::BM, "one M tiling per kind");
 static_assert(CfgMdGU::BM == CfgMdDF::BM && CfgMdGU::BM == CfgMdDB::BM, "one M tiling per kind");
+static_assert(CfgMdGUr::BM == CfgMdGU::BM && CfgMdDFr::BM == CfgMdGU::BM && CfgMdDBr::BM == CfgMdGU::BM,
+              "one M tiling per kind");
 static_assert(CfgSmGU::BM == CfgSmDF::BM && CfgSmGU::BM == CfgSmDB::BM, "one M tiling per kind");
 
 struct WsLayout {
@@ -201,6 +203,10 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
       return launch_bf16<CfgLgGU, CfgLgGUS, CfgLgDF, CfgLgDB, kPersistLg>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
     case kMedium:
+      if (rs_slices_ok<CfgMdGUr>(d / 64) && rs_slices_ok<CfgMdDFr>(d_ff / 64))
+        return launch_bf16<CfgMdGUr, CfgMdGUS, CfgMdDFr, CfgMdDBr, kPersistMd>(x, rows, d, d_ff, w_gate, w_up, w_down, H,
+                                                                              z, z_dtype, z_rows, z_n, tiles, n_tiles,
+                                                                              L.max_tiles, act, stream);
       return launch_bf16<CfgMdGU, CfgMdGUS, CfgMdDF, CfgMdDB, kPersistMd>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
     default:

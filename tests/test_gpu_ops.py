@@ -232,6 +232,13 @@ def _segments(rng, E, rows, mode):
     (3, 70000, 384, 384, "bf16", "f32", "static"),
     # persistent gate/up tiles with a partial last N-tile (d_ff = 448)
     (2, 60000, 384, 448, "bf16", "bf16", "packed"),
+    # 128-row tiles with K / 64 a multiple of 4 and at least 6 for both
+    # products: the weight rows through four register stages, persistent;
+    # several tiles per workgroup in the second case.  (d = 256, 4 slices,
+    # is below the weight loads' lead: the DMA-ring tiles.)
+    (8, 2000, 512, 512, "bf16", "f32", "packed"),
+    (64, 40000, 512, 512, "bf16", "bf16", "packed"),
+    (64, 40000, 256, 512, "bf16", "bf16", "packed"),
 ])
 def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     rng = np.random.default_rng(rows + E)
@@ -267,6 +274,8 @@ def test_grouped_swiglu(ge, E, rows, d, d_ff, dt, zdt, mode):
     (3, 2400, 192, 256, "bf16", "bf16", "packed"),       # 256-row tiles, stores staged through LDS
     (3, 70000, 320, 384, "bf16", "f32", "packed"),       # persistent register-staged down tiles
     (3, 70000, 384, 384, "bf16", "f32", "packed"),       # both launches persistent
+    (8, 2000, 512, 512, "bf16", "f32", "packed"),        # 128-row register-staged tiles, fp32 through the map
+    (64, 40000, 512, 768, "bf16", "bf16", "static"),     # the same, bf16, several tiles per workgroup
 ])
 def test_grouped_swiglu_row_map(ge, E, rows, d, d_ff, dt, zdt, mode):
     """With z_rows, row i of the result lands in z row z_rows[i]: the rows
