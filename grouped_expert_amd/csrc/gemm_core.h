@@ -1607,10 +1607,6 @@ inline int device_cus() {
   return n;
 }
 
-#ifndef MOE_RS_PERSIST
-#define MOE_RS_PERSIST 1
-#endif
-
 // Register-staged tiles run in the persistent register-staged form when the
 // slice count K / BK is a multiple of its 6-slice stage cycle: tiles whose
 // one-tile form stores directly from registers (the tile does not fit the
@@ -1635,7 +1631,7 @@ int launch_kernel(bool persistent, const void* a, const void* b0, const void* b1
     using OutT = typename std::conditional<C::OUT_F32 && !C::GATEUP, float, bf16_t>::type;
     const int64_t out_bytes = c_rows * N * static_cast<int64_t>(sizeof(OutT));
     const int32_t kt = K / C::BK;
-    if (MOE_RS_PERSIST && rs_slices_ok<C>(kt) && c_rows > 0 && out_bytes < 0xFFFFF000ll) {
+    if (rs_slices_ok<C>(kt) && c_rows > 0 && out_bytes < 0xFFFFF000ll) {
       const int64_t slots = static_cast<int64_t>(device_cus()) * C::OCC;
       const int64_t g = upper < slots ? upper : slots;
       hipLaunchKernelGGL(HIP_KERNEL_NAME(grouped_gemm_rs_persistent<C, MAP>), dim3(static_cast<unsigned>(g)),
