@@ -1,6 +1,7 @@
 // Grouped bf16 MFMA GEMM core shared by the forward and backward expert
 // calls: tile table, the LDS-ring GEMM kernels (one tile per workgroup, and
-// persistent), the tile configurations and their launch helpers.
+// persistent), the persistent register-staged kernel, the tile
+// configurations and their launch helpers.
 //
 // C[m, n] = sum_k A[m, k] * B[n, k], both operands K-contiguous (each MFMA
 // lane reads 8 consecutive K values of one row), A rows taken from ragged
@@ -969,8 +970,10 @@ __device__ __forceinline__ void gemm_tile(
 // Workgroups walk the tile list with even rounds (one tile at a time: the
 // ring drains at the end of each tile, whose epilogue may stage through it;
 // backward data-gradient GEMMs about 5 % faster than one tile per
-// workgroup).  Register-staged tiles keep one tile per workgroup (the loop
-// costs them spilled registers).
+// workgroup).  Register-staged tiles here keep one tile per workgroup (the
+// loop costs this form spilled registers); they normally run in the
+// persistent register-staged kernel, and come here only when their slice
+// count does not fit its stage cycle.
 template <class C, bool MAP>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
@@ -1161,11 +1164,12 @@ constexpr bool rs_slices_ok(int32_t kt) {
   return kt >= rs_min_slices<C>() && kt % rs_cycle<C>() == 0;
 }
 
-// Persistent form of the register-staged tiles (plain direct-store epilogue,
-// unswapped layout).  G workgroups walk their tiles with a static stride
-// (even rounds), and a workgroup's tiles form one sequence of K slices: the
-// A DMA (AD slices ahead) and the B register loads (three slices ahead) run
-// on across tile boundaries, so the first slices of the next tile are
+// Persistent form of the register-staged tiles (direct-store epilogue, or
+// for swapped gate/up tiles one staged through the two ring stages the last
+// slice freed).  G workgroups walk their tiles with a static stride (even
+// rounds), and a workgroup's tiles form one sequence of K slices: the A DMA
+// (AD slices ahead) and the B register loads (NR + 1 slices ahead, through
+// NR register stages) run on across tile boundaries, so the first slices of the next tile are
 // already loading while the current tile's last slices are consumed and its
 // epilogue stores run -- neither the pipeline fill nor a new workgroup's
 // start-up leaves the CU idle between tiles.  The stage indices repeat every
