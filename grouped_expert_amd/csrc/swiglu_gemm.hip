@@ -203,7 +203,11 @@ MOE_API int moe_grouped_swiglu(const void* x, int32_t dtype, int32_t d, int32_t 
       return launch_bf16<CfgLgGU, CfgLgGUS, CfgLgDF, CfgLgDB, kPersistLg>(x, rows, d, d_ff, w_gate, w_up, w_down, H, z, z_dtype, z_rows,
                                                                 z_n, tiles, n_tiles, L.max_tiles, act, stream);
     case kMedium:
-      if (rs_slices_ok<CfgMdGUr>(d / 64) && rs_slices_ok<CfgMdDFr>(d_ff / 64))
+      // (both products must also fit the persistent form's 32-bit output
+      // offsets; it has no one-tile fallback at this staging depth)
+      if (rs_slices_ok<CfgMdGUr>(d / 64) && rs_slices_ok<CfgMdDFr>(d_ff / 64) &&
+          rows * d_ff * 2 < 0xFFFFF000ll &&
+          (z_rows ? z_n_rows : rows) > 0 && (z_rows ? z_n_rows : rows) * d * (z_dtype == MOE_F32 ? 4 : 2) < 0xFFFFF000ll)
         return launch_bf16<CfgMdGUr, CfgMdGUS, CfgMdDFr, CfgMdDBr, kPersistMd>(x, rows, d, d_ff, w_gate, w_up, w_down, H,
                                                                               z, z_dtype, z_rows, z_n, tiles, n_tiles,
                                                                               L.max_tiles, act, stream);
